@@ -1,0 +1,267 @@
+#!/usr/bin/env python3
+"""Benchmark of the routed-MoE expert layer on one MI355X.
+
+A step is one moe_forward: dispatch -> gate-up grouped GEMM + SiLU epilogue ->
+down grouped GEMM -> weighted combine, over one batch of synthetic input that
+is already resident in HBM.  The default workload is the Mixtral-style layer
+(8 experts, top-2, hidden 4096, intermediate 14336, 4096 tokens); --config
+selects another workload of the same family (see workloads.CONFIGS).
+
+Printed (one JSON line): expert-compute TFLOP/s of the layer (value), µs per
+layer, HBM GB/s, the roofline of the dominant kernel (the gate-up grouped
+GEMM, timed alone with HIP events on the stream it is launched on), and the
+CPU oracle timed on a bounded sample of the same workload.
+
+Algorithmic work (what the method must do, not what an implementation moves):
+  F = 6*H*I*R flop, R = valid dispatched rows (2*H*2I gate-up + 2*I*H down per row)
+  B = 6*H*I*n_touched + 2*H*T (x) + 2*H*T (out) + 8*T*K (ids, weights) bytes
+  gate-up kernel: F_gu = 4*H*I*R flop,
+                  B_gu = 4*H*I*n_touched (weights) + 2*H*R (rows read) + 2*I*R (h written)
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import statistics
+import sys
+import time
+
+REPO = os.path.dirname(os.path.abspath(__file__))
+if REPO not in sys.path:
+    sys.path.insert(0, REPO)
+
+METRIC = "µs/MoE layer + expert-compute TFLOPS (and HBM GB/s) vs roofline, 1 GPU"
+PEAK_BF16_TFLOPS = 2500.0      # MI355X dense BF16 MFMA
+PEAK_HBM_GBPS = 8000.0         # MI355X HBM3E
+RIDGE = PEAK_BF16_TFLOPS * 1e12 / (PEAK_HBM_GBPS * 1e9)
+
+DESCR = {
+    "tiny": "tiny: 8 experts, top-2, hidden 256, intermediate 512, 64 tokens",
+    "mixtral": "mixtral-style: 8 experts, top-2, hidden 4096, intermediate 14336, 4096 tokens",
+}
+
+
+def describe(cfg):
+    if cfg.name in DESCR:
+        return DESCR[cfg.name]
+    routing = {"ep_uniform": "uniform", "ep_zipf": f"zipf s={cfg.zipf_s}",
+               "softmax_topk": "softmax top-k"}[cfg.routing]
+    return (f"{cfg.name}: {cfg.num_experts} local of {cfg.pool} experts, top-{cfg.top_k}, "
+            f"hidden {cfg.hidden}, intermediate {cfg.intermediate}, {cfg.num_tokens} tokens, "
+            f"{routing} routing")
+
+
+def pmc_traffic(kernel_key: str, src_hash: str, units: int):
+    """HBM bytes per launch from a committed rocprofv3 counter summary, or None
+    when there is none for this kernel/workload or the kernel sources changed
+    since the counters were taken."""
+    path = os.path.join(REPO, "profiles", "pmc_traffic.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as fh:
+        data = json.load(fh)
+    ent = data.get(kernel_key)
+    if not ent or ent.get("src_sha256") != src_hash:
+        return None
+    return ent.get("bytes_per_launch")
+
+
+def kernel_src_hash() -> str:
+    h = hashlib.sha256()
+    csrc = os.path.join(REPO, "mixture_experts_routed_02_amd", "csrc")
+    for name in sorted(os.listdir(csrc)):
+        with open(os.path.join(csrc, name), "rb") as fh:
+            h.update(name.encode() + b"\0" + fh.read())
+    return h.hexdigest()
+
+
+def cpu_baseline(inp_host, wgu, wd, cfg, budget_tokens: int):
+    """The oracle, as it stands, on the first `budget_tokens` tokens."""
+    import numpy as np
+    import torch
+
+    import oracle
+
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([int(i.get("num_threads", 1)) for i in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        cores = os.cpu_count() or 1
+    toks = np.arange(min(budget_tokens, cfg.num_tokens))
+    ids = inp_host["topk_ids"].numpy()
+    used = sorted({int(e) for e in ids[toks].reshape(-1) if 0 <= e < cfg.num_experts})
+
+    def bits(t):
+        return t.contiguous().view(torch.int16).numpy().view(np.uint16)
+
+    class Experts:
+        def __init__(self, w):
+            self.host = {e: bits(w[e].cpu()) for e in used}
+            self.n = w.shape[0]
+
+        def __len__(self):
+            return self.n
+
+        def __getitem__(self, e):
+            return self.host[int(e)]
+
+    xg, wug, wdg = bits(inp_host["x"]), Experts(wgu), Experts(wd)
+    t0 = time.perf_counter()
+    oracle.forward_tokens(xg, ids, inp_host["topk_weights"].numpy(), wug, wdg, toks)
+    dt = time.perf_counter() - t0
+    rows = int(((ids[toks] >= 0) & (ids[toks] < cfg.num_experts)).sum())
+    flops = 6.0 * cfg.hidden * cfg.intermediate * rows
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": cores, "kind": "oracle",
+            "sample": f"first {len(toks)} tokens of the same inputs ({rows} expert rows), "
+                      f"float64 numpy, {dt:.1f} s"}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawTextHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--config", default="mixtral")
+    ap.add_argument("--seed", type=int, default=0)
+    ap.add_argument("--hint", type=int, default=0, help="grouped-GEMM plan (0 auto, 1-3 forced)")
+    ap.add_argument("--cold", action="store_true",
+                    help="overwrite a 512 MiB buffer before each step (outside the timed "
+                         "events) so weights are read from HBM, not L2/MALL")
+    ap.add_argument("--kernel-reps", type=int, default=10)
+    ap.add_argument("--cpu-tokens", type=int, default=None,
+                    help="tokens in the oracle's timed sample (default by workload)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(json.dumps({"error": "this benchmark measures the single-GPU expert path; "
+                          "runs on more than one GPU are not part of it", "n_gpus": args.gpus}))
+        sys.exit(2)
+
+    import torch
+
+    import mixture_experts_routed_02_amd as moe
+    from mixture_experts_routed_02_amd import ops
+    import workloads as W
+
+    if not torch.cuda.is_available():
+        raise SystemExit("bench.py needs a GPU")
+    moe.lib()
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    cfg = W.CONFIGS[args.config]
+    T, K, E, H, I = cfg.num_tokens, cfg.top_k, cfg.num_experts, cfg.hidden, cfg.intermediate
+
+    x_h = W.make_x(cfg, args.seed)
+    ids_h, w_h = W.make_routing(cfg, args.seed)
+    wgu, wd = W.make_weights(cfg, args.seed, dev)
+    x, ids, w = x_h.to(dev), ids_h.to(dev), w_h.to(dev)
+    p = moe.problem(T, K, E, H, I, cfg.capacity, args.hint)
+    ws = ops.make_workspace(p, dev)
+    out = torch.empty((T, H), dtype=torch.bfloat16, device=dev)
+    off = torch.empty((E + 1,), dtype=torch.int32, device=dev)
+    scratch = torch.empty((512 << 20,), dtype=torch.uint8, device=dev) if args.cold else None
+
+    def step():
+        ops.forward(p, x, ids, w, wgu, wd, expert_offsets=off, out=out, workspace=ws)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    offs = off.cpu().tolist()
+    R = offs[-1]
+    touched = sum(1 for e in range(E) if offs[e + 1] > offs[e])
+    F = 6.0 * H * I * R
+    B = 6.0 * H * I * touched + 4.0 * H * T + 8.0 * T * K
+
+    # ---- timed region: exactly `steps` layer calls ------------------------
+    stream = torch.cuda.current_stream(dev)
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        if scratch is not None:
+            scratch.fill_(i & 0xFF)
+        ev[i][0].record(stream)
+        step()
+        ev[i][1].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    per = [a.elapsed_time(b) for a, b in ev]          # ms
+    ms_step = statistics.fmean(per) if args.cold else wall * 1e3 / args.steps
+    sec = ms_step / 1e3
+
+    # ---- dominant kernel alone: the gate-up grouped GEMM ------------------
+    x_disp, off2, _, _ = ops.dispatch(p, x, ids)
+    hbuf = torch.empty((p.capacity or T * K, I), dtype=torch.bfloat16, device=dev)
+    ops.gate_up(p, x_disp, off2, wgu, h=hbuf)
+    kev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(args.kernel_reps)]
+    torch.cuda.synchronize()
+    for i in range(args.kernel_reps):
+        if scratch is not None:
+            scratch.fill_(i & 0xFF)
+        kev[i][0].record(stream)
+        ops.gate_up(p, x_disp, off2, wgu, h=hbuf)
+        kev[i][1].record(stream)
+    torch.cuda.synchronize()
+    k_ms = statistics.fmean(a.elapsed_time(b) for a, b in kev)
+    F_gu = 4.0 * H * I * R
+    B_gu = 4.0 * H * I * touched + 2.0 * H * R + 2.0 * I * R
+    mfma_bound = (F_gu / max(B_gu, 1.0)) >= RIDGE
+    # the host plan rule of the library: forced hint, else rows per expert T*K/E
+    kind = args.hint if args.hint in (1, 2, 3) else (1 if T * K / E <= 24 else 2 if T * K / E <= 96 else 3)
+    kernel_name = "gemm_skinny_kernel" if kind == 1 else "gemm_tiled_kernel"
+    traffic = pmc_traffic(f"{kernel_name}<gated>@{cfg.name}", kernel_src_hash(), 1)
+    if mfma_bound:
+        ach = F_gu / (k_ms / 1e3) / 1e12
+        roof = {"bound": "mfma", "achieved": ach, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                "frac": ach / PEAK_BF16_TFLOPS, "traffic": traffic}
+    else:
+        ach = B_gu / (k_ms / 1e3) / 1e9
+        roof = {"bound": "hbm", "achieved": ach, "peak": PEAK_HBM_GBPS, "unit": "GB/s",
+                "frac": ach / PEAK_HBM_GBPS, "traffic": traffic}
+    roof.update({"kernel": f"{kernel_name} (gate-up + SiLU epilogue)", "avg_launch_us": k_ms * 1e3,
+                 "algorithmic_flop": F_gu, "algorithmic_bytes": B_gu})
+
+    result = {
+        "metric": METRIC,
+        "value": F / sec / 1e12,
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_step,
+        "us_per_layer": ms_step * 1e3,
+        "us_per_layer_median": statistics.median(per) * 1e3,
+        "hbm_gbps": B / sec / 1e9,
+        "layer_roofline": {"mfma_frac": F / sec / 1e12 / PEAK_BF16_TFLOPS,
+                           "hbm_frac": B / sec / 1e9 / PEAK_HBM_GBPS,
+                           "binding": "mfma" if F / max(B, 1.0) >= RIDGE else "hbm"},
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": describe(cfg), "tokens": T, "top_k": K, "experts": E,
+                   "global_experts": cfg.pool, "hidden": H, "intermediate": I,
+                   "capacity": p.capacity or T * K, "valid_rows": R, "experts_touched": touched,
+                   "seed": args.seed, "timing": "cold (L2/MALL evicted per step)" if args.cold
+                   else "back-to-back", "kernel_hint": args.hint},
+        "roofline": roof,
+    }
+    if not args.no_cpu_baseline:
+        budget = args.cpu_tokens
+        if budget is None:
+            budget = {"mixtral": 256, "tiny": 64}.get(cfg.name, max(16, min(T, 64)))
+        result["cpu_baseline"] = cpu_baseline({"x": x_h, "topk_ids": ids_h, "topk_weights": w_h},
+                                              wgu, wd, cfg, budget)
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,175 @@
+/*
+ * moe_mi355x.h -- C ABI of the routed-MoE expert path for one AMD Instinct
+ * MI355X (gfx950).  Exported by libmoe_mi355x.so.
+ *
+ * The layer computes, for every valid token t (t < T_v):
+ *
+ *   out[t,:] = sum_{j : 0 <= ids[t,j] < E}  w[t,j] * W_down[e] ( silu(W_gate[e] x[t]) * (W_up[e] x[t]) ),
+ *   e = ids[t,j],  W_gate[e] = W_gateup[e, 0:I, :],  W_up[e] = W_gateup[e, I:2I, :],
+ *
+ * as the composition local dispatch -> dispatched-expert compute -> combine
+ * (TileOps PR #1738 "[Refactor][MoE] Separate dispatched expert compute",
+ * Summary), with the routing weights applied only in the combine (same
+ * Summary), one (tokens, hidden) output (FlashInfer PR #3980, Summary), a
+ * tight no-pad expert-major batch whose expert_offsets stay on the GPU and
+ * end in the valid-row count (TileOps PR #1738, Scope), and a static capacity
+ * whose tail rows are unspecified (same Scope).
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ *  - bf16 tensors are passed as uint16_t bit patterns; all tensors are dense
+ *    row-major, device memory, caller-owned.  bf16 pointers and the workspace
+ *    must be 16-byte aligned, int32/fp32 pointers 4-byte aligned.  A pointer
+ *    to an empty tensor (T = 0, or capacity 0) may be NULL.
+ *  - `stream` is a hipStream_t (NULL = the legacy default stream).  Every call
+ *    only enqueues work on it: no host synchronisation, no device-to-host
+ *    read, no allocation, no memset.  All calls are therefore safe to record
+ *    into a HIP graph.
+ *  - Assignment a = t*K + j is valid iff t < T_v and 0 <= topk_ids[a] < E.
+ *    Ids outside [0, E) (for example experts owned by another rank) are
+ *    dropped, not errors.  T_v = T, or min(max(*num_tokens_dev, 0), T) when
+ *    num_tokens_dev (a device int32) is given; it is read on the GPU.
+ *  - Dispatched rows of one expert are ordered by increasing a (stable).
+ *    Rows [R, capacity) of every dispatched buffer, and output rows t >= T_v,
+ *    are left unspecified / untouched.
+ *  - Arguments are checked on the host before anything is enqueued; a bad
+ *    argument returns MOE_ERROR_INVALID_VALUE or MOE_ERROR_NOT_SUPPORTED and
+ *    enqueues nothing (fail closed).  A failed launch returns
+ *    MOE_ERROR_LAUNCH.  No entry point aborts or throws.
+ *  - Arithmetic: bf16 inputs, fp32 accumulation, one round-to-nearest-even to
+ *    bf16 for each of h, y and out.  No floating-point atomics: results are
+ *    bit-reproducible run to run for a fixed problem and kernel plan.
+ *  - A workspace must not be used by two calls that may run concurrently.
+ */
+#ifndef MOE_MI355X_H
+#define MOE_MI355X_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#if defined(__GNUC__) || defined(__clang__)
+#define MOE_API __attribute__((visibility("default")))
+#else
+#define MOE_API
+#endif
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef struct moe_problem {
+    int32_t num_tokens;    /* T >= 0: rows of x and out (buffer rows)                  */
+    int32_t top_k;         /* K, 1..64                                                 */
+    int32_t num_experts;   /* E, 1..512: local experts (leading dim of the weights)    */
+    int32_t hidden;        /* H > 0, multiple of 64                                    */
+    int32_t intermediate;  /* I > 0, multiple of 64                                    */
+    int32_t capacity;      /* rows of the dispatched buffers; 0 => T*K; must be >= T*K */
+    int32_t kernel_hint;   /* grouped-GEMM plan: 0 auto (chosen from T*K/E on the host),
+                              1 skinny (16-row tiles, in-workgroup split-K),
+                              2 tiled 64-row, 3 tiled 128-row                         */
+} moe_problem_t;
+
+typedef enum moe_status {
+    MOE_SUCCESS = 0,
+    MOE_ERROR_INVALID_VALUE = 1,
+    MOE_ERROR_NOT_SUPPORTED = 2,
+    MOE_ERROR_LAUNCH = 3
+} moe_status_t;
+
+/* Human-readable text of a status (static storage). */
+MOE_API const char* moe_status_string(moe_status_t status);
+
+/* Bytes of device workspace every entry point below needs for `p` (the
+ * largest of them, moe_forward).  Host-only.  Returns MOE_ERROR_* for an
+ * invalid problem and leaves *bytes untouched. */
+MOE_API moe_status_t moe_workspace_size(const moe_problem_t* p, size_t* bytes);
+
+/* Local dispatch (TileOps PR #1738, Summary: local dispatch into a tight
+ * expert-major batch; Scope: GPU-resident expert_offsets[-1:] valid-row view).
+ *   x               bf16 [T, H]
+ *   topk_ids        int32 [T, K]
+ *   num_tokens_dev  device int32 scalar or NULL (see T_v above)
+ *   x_disp          out bf16 [capacity, H]: row r = x[row_src[r] / K]
+ *   expert_offsets  out int32 [E+1]: exclusive prefix of per-expert counts;
+ *                   expert_offsets[E] = R, the valid-row count
+ *   row_src         out int32 [capacity]: assignment a of row r (r < R)
+ *   token_row       out int32 [T*K]: row of assignment a, -1 if dropped
+ *   workspace       >= moe_workspace_size bytes (ws_bytes is checked)
+ * Results are exact integers / bit copies. */
+MOE_API moe_status_t moe_dispatch(const moe_problem_t* p, const uint16_t* x, const int32_t* topk_ids,
+                          const int32_t* num_tokens_dev, uint16_t* x_disp,
+                          int32_t* expert_offsets, int32_t* row_src, int32_t* token_row,
+                          void* workspace, size_t ws_bytes, void* stream);
+
+/* Dispatched-expert compute over a tight expert-major batch (TileOps PR
+ * #1738, Summary and Review follow-up: gate-up grouped GEMM, fused gated
+ * pointwise epilogue, down grouped GEMM).  Routing weights are not inputs.
+ *   x_disp          bf16 [capacity, H]; rows [0, R) are read
+ *   expert_offsets  int32 [E+1] on the device (as written by moe_dispatch)
+ *   w_gateup        bf16 [E, 2I, H]: rows [0, I) gate, rows [I, 2I) up
+ *   w_down          bf16 [E, H, I]
+ *   y_disp          out bf16 [capacity, H]: rows [0, R) written
+ *   workspace       holds h = bf16(silu(gate) * up) [capacity, I] */
+MOE_API moe_status_t moe_expert_compute(const moe_problem_t* p, const uint16_t* x_disp,
+                                const int32_t* expert_offsets, const uint16_t* w_gateup,
+                                const uint16_t* w_down, uint16_t* y_disp,
+                                void* workspace, size_t ws_bytes, void* stream);
+
+/* The two grouped GEMMs of moe_expert_compute as separate calls (TileOps PR
+ * #1738, Review follow-up: gate-up and down grouped-GEMM sub-ops), for
+ * callers that schedule or time them individually.
+ *   moe_gate_up: h [capacity, I] = bf16( silu(x_disp W_gate[e]^T) * (x_disp W_up[e]^T) )
+ *   moe_down:    y_disp [capacity, H] = bf16( h W_down[e]^T )
+ * for every dispatched row r < R of expert e (expert_offsets[e] <= r <
+ * expert_offsets[e+1]), fp32 accumulation.  Same kernels and plan as
+ * moe_expert_compute, so the pair reproduces it bit for bit. */
+MOE_API moe_status_t moe_gate_up(const moe_problem_t* p, const uint16_t* x_disp,
+                                 const int32_t* expert_offsets, const uint16_t* w_gateup,
+                                 uint16_t* h, void* stream);
+MOE_API moe_status_t moe_down(const moe_problem_t* p, const uint16_t* h,
+                              const int32_t* expert_offsets, const uint16_t* w_down,
+                              uint16_t* y_disp, void* stream);
+
+/* Weighted top-k combine back to token order (TileOps PR #1738, Summary:
+ * weights stay outside expert compute; FlashInfer PR #3980, Summary: one
+ * (tokens, hidden) output).  For t < T_v:
+ *   out[t,:] = bf16( sum_{j ascending, token_row[t*K+j] >= 0} w[t,j] * y_disp[token_row[t*K+j], :] )
+ * accumulated in fp32 (a zero row when no assignment is valid).
+ *   y_disp bf16 [capacity, H], token_row int32 [T*K], topk_weights fp32 [T, K],
+ *   out bf16 [T, H] (rows t >= T_v untouched). */
+MOE_API moe_status_t moe_combine(const moe_problem_t* p, const uint16_t* y_disp, const int32_t* token_row,
+                         const float* topk_weights, const int32_t* num_tokens_dev,
+                         uint16_t* out, void* stream);
+
+/* The whole layer: dispatch, expert compute (the row gather fused into the
+ * gate-up GEMM's operand loads) and combine, enqueued back to back.
+ *   expert_offsets  out int32 [E+1] (the GPU-resident valid-row view)
+ *   out             bf16 [T, H]
+ * Equal bit for bit to moe_dispatch + moe_expert_compute + moe_combine with
+ * the same kernel plan. */
+MOE_API moe_status_t moe_forward(const moe_problem_t* p, const uint16_t* x, const int32_t* topk_ids,
+                         const float* topk_weights, const uint16_t* w_gateup,
+                         const uint16_t* w_down, const int32_t* num_tokens_dev,
+                         int32_t* expert_offsets, uint16_t* out,
+                         void* workspace, size_t ws_bytes, void* stream);
+
+/* Static-capacity graph replay (TileOps PR #1738, Summary: GPU-resident row
+ * counts, static capacity and graph replay).  Records one moe_forward with
+ * these fixed pointers into an instantiated HIP graph; every launch in it has
+ * a fixed grid and reads T_v and all row counts on the GPU, so the caller
+ * replays it after writing new x / topk_ids / topk_weights / *num_tokens_dev
+ * into the same buffers.  *graph_out receives an opaque handle owned by the
+ * caller (release with moe_graph_destroy). */
+MOE_API moe_status_t moe_graph_create(const moe_problem_t* p, const uint16_t* x, const int32_t* topk_ids,
+                              const float* topk_weights, const uint16_t* w_gateup,
+                              const uint16_t* w_down, const int32_t* num_tokens_dev,
+                              int32_t* expert_offsets, uint16_t* out,
+                              void* workspace, size_t ws_bytes, void** graph_out);
+MOE_API moe_status_t moe_graph_launch(void* graph, void* stream);
+MOE_API moe_status_t moe_graph_destroy(void* graph);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MOE_MI355X_H */

@@ -1,0 +1,308 @@
+// Host side of libmoe_mi355x.so: argument checks (fail closed, before any
+// enqueue), workspace layout, kernel-plan choice and the stream-ordered
+// launches of each entry point declared in include/moe_mi355x.h.
+#include "../../include/moe_mi355x.h"
+#include "moe_internal.h"
+
+#include <new>
+
+using moe::GemmPlan;
+using moe::Shape;
+
+namespace {
+
+constexpr size_t kAlign = 256;
+
+size_t align_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
+
+bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
+
+moe_status_t check_problem(const moe_problem_t* p, Shape* s) {
+    if (!p) return MOE_ERROR_INVALID_VALUE;
+    if (p->num_tokens < 0 || p->top_k < 1 || p->num_experts < 1 || p->hidden <= 0 ||
+        p->intermediate <= 0 || p->capacity < 0)
+        return MOE_ERROR_INVALID_VALUE;
+    if (p->top_k > 64 || p->num_experts > moe::kMaxExperts) return MOE_ERROR_NOT_SUPPORTED;
+    if (p->hidden % 64 != 0 || p->intermediate % 64 != 0) return MOE_ERROR_NOT_SUPPORTED;
+    if (p->kernel_hint < 0 || p->kernel_hint > moe::kTiled128) return MOE_ERROR_INVALID_VALUE;
+    const long long tk = (long long)p->num_tokens * p->top_k;
+    if (tk > (1ll << 28)) return MOE_ERROR_NOT_SUPPORTED;
+    const long long cap = p->capacity ? p->capacity : tk;
+    if (cap < tk) return MOE_ERROR_INVALID_VALUE;
+    s->T = p->num_tokens;
+    s->K = p->top_k;
+    s->E = p->num_experts;
+    s->H = p->hidden;
+    s->I = p->intermediate;
+    s->cap = (int)cap;
+    return MOE_SUCCESS;
+}
+
+// Workspace layout (every region 256-byte aligned):
+//   blk_counts int32 [nblk * E]   (multi-block dispatch only)
+//   row_src    int32 [cap]        (moe_forward)
+//   token_row  int32 [T*K]        (moe_forward)
+//   h          bf16  [cap, I]     (expert compute)
+//   y_disp     bf16  [cap, H]     (moe_forward)
+struct Layout {
+    size_t counts, row_src, token_row, h, y, total;
+};
+
+Layout layout(const Shape& s) {
+    Layout L{};
+    const int nblk = moe::dispatch_blocks(s);
+    size_t off = 0;
+    L.counts = off;
+    off += align_up(nblk > 1 ? (size_t)nblk * s.E * 4 : 0);
+    L.row_src = off;
+    off += align_up((size_t)s.cap * 4);
+    L.token_row = off;
+    off += align_up((size_t)s.T * s.K * 4);
+    L.h = off;
+    off += align_up((size_t)s.cap * s.I * 2);
+    L.y = off;
+    off += align_up((size_t)s.cap * s.H * 2);
+    L.total = off;
+    return L;
+}
+
+template <typename T>
+T* at(void* ws, size_t off) {
+    return reinterpret_cast<T*>(static_cast<char*>(ws) + off);
+}
+
+moe_status_t launched(hipError_t e) { return e == hipSuccess ? MOE_SUCCESS : MOE_ERROR_LAUNCH; }
+
+// A pointer is acceptable if it is aligned and non-null, or null for an
+// empty tensor (T = 0).
+bool bad_bf16(const void* p, long long n = 1) { return p ? !aligned(p, 16) : n != 0; }
+bool bad_i32(const void* p, long long n = 1) { return p ? !aligned(p, 4) : n != 0; }
+
+moe_status_t check_ws(const Shape& s, const void* ws, size_t ws_bytes) {
+    if (!ws || !aligned(ws, 16)) return MOE_ERROR_INVALID_VALUE;
+    if (ws_bytes < layout(s).total) return MOE_ERROR_INVALID_VALUE;
+    return MOE_SUCCESS;
+}
+
+moe_status_t expert_compute_impl(const Shape& s, const GemmPlan& plan, const uint16_t* a,
+                                 const int32_t* row_src, const int32_t* offsets,
+                                 const uint16_t* wgu, const uint16_t* wd, uint16_t* h,
+                                 uint16_t* y, hipStream_t st) {
+    hipError_t e = moe::launch_grouped_gemm(s, plan, true, a, row_src, s.K, offsets, wgu, h, s.H,
+                                            s.I, st);
+    if (e != hipSuccess) return MOE_ERROR_LAUNCH;
+    e = moe::launch_grouped_gemm(s, plan, false, h, nullptr, 1, offsets, wd, y, s.I, s.H, st);
+    return launched(e);
+}
+
+moe_status_t check_forward_args(const moe_problem_t* p, Shape* s, const uint16_t* x,
+                                const int32_t* ids, const float* w, const uint16_t* wgu,
+                                const uint16_t* wd, const int32_t* ntok, const int32_t* offsets,
+                                const uint16_t* out, const void* ws, size_t ws_bytes) {
+    moe_status_t st = check_problem(p, s);
+    if (st != MOE_SUCCESS) return st;
+    const long long tk = (long long)s->T * s->K;
+    if (bad_bf16(x, s->T) || bad_i32(ids, tk) || bad_i32(w, tk) || bad_bf16(wgu) ||
+        bad_bf16(wd) || bad_i32(offsets) || bad_bf16(out, s->T))
+        return MOE_ERROR_INVALID_VALUE;
+    if (ntok && !aligned(ntok, 4)) return MOE_ERROR_INVALID_VALUE;
+    return check_ws(*s, ws, ws_bytes);
+}
+
+moe_status_t forward_impl(const Shape& s, int hint, const uint16_t* x, const int32_t* ids,
+                          const float* w, const uint16_t* wgu, const uint16_t* wd,
+                          const int32_t* ntok, int32_t* offsets, uint16_t* out, void* ws,
+                          hipStream_t st) {
+    const Layout L = layout(s);
+    int32_t* counts = at<int32_t>(ws, L.counts);
+    int32_t* row_src = at<int32_t>(ws, L.row_src);
+    int32_t* token_row = at<int32_t>(ws, L.token_row);
+    uint16_t* h = at<uint16_t>(ws, L.h);
+    uint16_t* y = at<uint16_t>(ws, L.y);
+    if (moe::launch_dispatch(s, ids, ntok, offsets, row_src, token_row, counts, st) != hipSuccess)
+        return MOE_ERROR_LAUNCH;
+    const GemmPlan plan = moe::choose_plan(s, hint);
+    moe_status_t r = expert_compute_impl(s, plan, x, row_src, offsets, wgu, wd, h, y, st);
+    if (r != MOE_SUCCESS) return r;
+    if (s.T == 0) return MOE_SUCCESS;
+    return launched(moe::launch_combine(s, y, token_row, w, ntok, out, st));
+}
+
+struct GraphHandle {
+    hipGraphExec_t exec;
+};
+
+}  // namespace
+
+extern "C" {
+
+const char* moe_status_string(moe_status_t status) {
+    switch (status) {
+        case MOE_SUCCESS: return "MOE_SUCCESS";
+        case MOE_ERROR_INVALID_VALUE: return "MOE_ERROR_INVALID_VALUE: bad argument (null/misaligned pointer, size out of range, capacity < T*K, workspace too small)";
+        case MOE_ERROR_NOT_SUPPORTED: return "MOE_ERROR_NOT_SUPPORTED: shape outside the supported range (H, I multiples of 64; K <= 64; E <= 512; T*K <= 2^28)";
+        case MOE_ERROR_LAUNCH: return "MOE_ERROR_LAUNCH: a kernel launch failed";
+    }
+    return "unknown moe_status_t";
+}
+
+moe_status_t moe_workspace_size(const moe_problem_t* p, size_t* bytes) {
+    Shape s;
+    moe_status_t st = check_problem(p, &s);
+    if (st != MOE_SUCCESS) return st;
+    if (!bytes) return MOE_ERROR_INVALID_VALUE;
+    *bytes = layout(s).total;
+    return MOE_SUCCESS;
+}
+
+moe_status_t moe_dispatch(const moe_problem_t* p, const uint16_t* x, const int32_t* topk_ids,
+                          const int32_t* num_tokens_dev, uint16_t* x_disp,
+                          int32_t* expert_offsets, int32_t* row_src, int32_t* token_row,
+                          void* workspace, size_t ws_bytes, void* stream) {
+    Shape s;
+    moe_status_t st = check_problem(p, &s);
+    if (st != MOE_SUCCESS) return st;
+    const long long tk = (long long)s.T * s.K;
+    if (bad_bf16(x, s.T) || bad_i32(topk_ids, tk) || bad_bf16(x_disp, s.cap) ||
+        bad_i32(expert_offsets) || bad_i32(row_src, s.cap) || bad_i32(token_row, tk))
+        return MOE_ERROR_INVALID_VALUE;
+    if (num_tokens_dev && !aligned(num_tokens_dev, 4)) return MOE_ERROR_INVALID_VALUE;
+    if ((st = check_ws(s, workspace, ws_bytes)) != MOE_SUCCESS) return st;
+    hipStream_t hs = static_cast<hipStream_t>(stream);
+    int32_t* counts = at<int32_t>(workspace, layout(s).counts);
+    if (moe::launch_dispatch(s, topk_ids, num_tokens_dev, expert_offsets, row_src, token_row,
+                             counts, hs) != hipSuccess)
+        return MOE_ERROR_LAUNCH;
+    return launched(moe::launch_gather(s, x, expert_offsets, row_src, x_disp, hs));
+}
+
+moe_status_t moe_expert_compute(const moe_problem_t* p, const uint16_t* x_disp,
+                                const int32_t* expert_offsets, const uint16_t* w_gateup,
+                                const uint16_t* w_down, uint16_t* y_disp, void* workspace,
+                                size_t ws_bytes, void* stream) {
+    Shape s;
+    moe_status_t st = check_problem(p, &s);
+    if (st != MOE_SUCCESS) return st;
+    if (bad_bf16(x_disp, s.cap) || bad_i32(expert_offsets) || bad_bf16(w_gateup) ||
+        bad_bf16(w_down) || bad_bf16(y_disp, s.cap))
+        return MOE_ERROR_INVALID_VALUE;
+    if ((st = check_ws(s, workspace, ws_bytes)) != MOE_SUCCESS) return st;
+    const GemmPlan plan = moe::choose_plan(s, p->kernel_hint);
+    uint16_t* h = at<uint16_t>(workspace, layout(s).h);
+    return expert_compute_impl(s, plan, x_disp, nullptr, expert_offsets, w_gateup, w_down, h,
+                               y_disp, static_cast<hipStream_t>(stream));
+}
+
+moe_status_t moe_gate_up(const moe_problem_t* p, const uint16_t* x_disp,
+                         const int32_t* expert_offsets, const uint16_t* w_gateup, uint16_t* h,
+                         void* stream) {
+    Shape s;
+    moe_status_t st = check_problem(p, &s);
+    if (st != MOE_SUCCESS) return st;
+    if (bad_bf16(x_disp, s.cap) || bad_i32(expert_offsets) || bad_bf16(w_gateup) ||
+        bad_bf16(h, s.cap))
+        return MOE_ERROR_INVALID_VALUE;
+    const GemmPlan plan = moe::choose_plan(s, p->kernel_hint);
+    return launched(moe::launch_grouped_gemm(s, plan, true, x_disp, nullptr, s.K, expert_offsets,
+                                             w_gateup, h, s.H, s.I,
+                                             static_cast<hipStream_t>(stream)));
+}
+
+moe_status_t moe_down(const moe_problem_t* p, const uint16_t* h, const int32_t* expert_offsets,
+                      const uint16_t* w_down, uint16_t* y_disp, void* stream) {
+    Shape s;
+    moe_status_t st = check_problem(p, &s);
+    if (st != MOE_SUCCESS) return st;
+    if (bad_bf16(h, s.cap) || bad_i32(expert_offsets) || bad_bf16(w_down) ||
+        bad_bf16(y_disp, s.cap))
+        return MOE_ERROR_INVALID_VALUE;
+    const GemmPlan plan = moe::choose_plan(s, p->kernel_hint);
+    return launched(moe::launch_grouped_gemm(s, plan, false, h, nullptr, 1, expert_offsets,
+                                             w_down, y_disp, s.I, s.H,
+                                             static_cast<hipStream_t>(stream)));
+}
+
+moe_status_t moe_combine(const moe_problem_t* p, const uint16_t* y_disp, const int32_t* token_row,
+                         const float* topk_weights, const int32_t* num_tokens_dev, uint16_t* out,
+                         void* stream) {
+    Shape s;
+    moe_status_t st = check_problem(p, &s);
+    if (st != MOE_SUCCESS) return st;
+    const long long tk = (long long)s.T * s.K;
+    if (bad_bf16(y_disp, s.cap) || bad_i32(token_row, tk) || bad_i32(topk_weights, tk) ||
+        bad_bf16(out, s.T))
+        return MOE_ERROR_INVALID_VALUE;
+    if (num_tokens_dev && !aligned(num_tokens_dev, 4)) return MOE_ERROR_INVALID_VALUE;
+    if (s.T == 0) return MOE_SUCCESS;
+    return launched(moe::launch_combine(s, y_disp, token_row, topk_weights, num_tokens_dev, out,
+                                        static_cast<hipStream_t>(stream)));
+}
+
+moe_status_t moe_forward(const moe_problem_t* p, const uint16_t* x, const int32_t* topk_ids,
+                         const float* topk_weights, const uint16_t* w_gateup,
+                         const uint16_t* w_down, const int32_t* num_tokens_dev,
+                         int32_t* expert_offsets, uint16_t* out, void* workspace,
+                         size_t ws_bytes, void* stream) {
+    Shape s;
+    moe_status_t st = check_forward_args(p, &s, x, topk_ids, topk_weights, w_gateup, w_down,
+                                         num_tokens_dev, expert_offsets, out, workspace, ws_bytes);
+    if (st != MOE_SUCCESS) return st;
+    return forward_impl(s, p->kernel_hint, x, topk_ids, topk_weights, w_gateup, w_down,
+                        num_tokens_dev, expert_offsets, out, workspace,
+                        static_cast<hipStream_t>(stream));
+}
+
+moe_status_t moe_graph_create(const moe_problem_t* p, const uint16_t* x, const int32_t* topk_ids,
+                              const float* topk_weights, const uint16_t* w_gateup,
+                              const uint16_t* w_down, const int32_t* num_tokens_dev,
+                              int32_t* expert_offsets, uint16_t* out, void* workspace,
+                              size_t ws_bytes, void** graph_out) {
+    Shape s;
+    moe_status_t st = check_forward_args(p, &s, x, topk_ids, topk_weights, w_gateup, w_down,
+                                         num_tokens_dev, expert_offsets, out, workspace, ws_bytes);
+    if (st != MOE_SUCCESS) return st;
+    if (!graph_out) return MOE_ERROR_INVALID_VALUE;
+    hipStream_t cs = nullptr;
+    if (hipStreamCreateWithFlags(&cs, hipStreamNonBlocking) != hipSuccess) return MOE_ERROR_LAUNCH;
+    hipGraph_t graph = nullptr;
+    moe_status_t r = MOE_SUCCESS;
+    if (hipStreamBeginCapture(cs, hipStreamCaptureModeThreadLocal) != hipSuccess) {
+        (void)hipStreamDestroy(cs);
+        return MOE_ERROR_LAUNCH;
+    }
+    r = forward_impl(s, p->kernel_hint, x, topk_ids, topk_weights, w_gateup, w_down,
+                     num_tokens_dev, expert_offsets, out, workspace, cs);
+    hipError_t ec = hipStreamEndCapture(cs, &graph);
+    (void)hipStreamDestroy(cs);
+    if (r != MOE_SUCCESS || ec != hipSuccess || !graph) {
+        if (graph) (void)hipGraphDestroy(graph);
+        return MOE_ERROR_LAUNCH;
+    }
+    hipGraphExec_t exec = nullptr;
+    hipError_t ei = hipGraphInstantiate(&exec, graph, nullptr, nullptr, 0);
+    (void)hipGraphDestroy(graph);
+    if (ei != hipSuccess) return MOE_ERROR_LAUNCH;
+    GraphHandle* gh = new (std::nothrow) GraphHandle{exec};
+    if (!gh) {
+        (void)hipGraphExecDestroy(exec);
+        return MOE_ERROR_LAUNCH;
+    }
+    *graph_out = gh;
+    return MOE_SUCCESS;
+}
+
+moe_status_t moe_graph_launch(void* graph, void* stream) {
+    if (!graph) return MOE_ERROR_INVALID_VALUE;
+    GraphHandle* gh = static_cast<GraphHandle*>(graph);
+    return launched(hipGraphLaunch(gh->exec, static_cast<hipStream_t>(stream)));
+}
+
+moe_status_t moe_graph_destroy(void* graph) {
+    if (!graph) return MOE_ERROR_INVALID_VALUE;
+    GraphHandle* gh = static_cast<GraphHandle*>(graph);
+    (void)hipGraphExecDestroy(gh->exec);
+    delete gh;
+    return MOE_SUCCESS;
+}
+
+}  // extern "C"

@@ -1,0 +1,185 @@
+// Local dispatch of top-k routed assignments into a tight, unpadded,
+// expert-major batch (TileOps PR #1738 "[Refactor][MoE] Separate dispatched
+// expert compute", Summary and Scope): per-expert histogram, exclusive scan
+// into expert_offsets (last entry = valid-row count, left on the GPU), and a
+// stable scatter that keeps the rows of one expert in increasing assignment
+// order a = t*K + j.
+//
+// Small problems (T*K <= kDispatchSingleMax) run as one 1024-thread block.
+// Larger ones run two fixed grids: a per-block histogram into the workspace,
+// then a scatter pass in which every block rebuilds its own prefix from those
+// histograms (no atomics across blocks, nothing to reset between calls).
+// Within a block, ranks among equal experts come from wave64 ballots: each
+// round takes the expert of the lowest remaining lane, ballots the lanes that
+// share it, and gives each such lane the popcount of the matching lanes below
+// it; per-wave counts are then scanned across waves in LDS.
+#include "moe_internal.h"
+
+namespace moe {
+namespace {
+
+__global__ __launch_bounds__(kDispatchThreads) void dispatch_count_kernel(
+    const int32_t* __restrict__ ids, const int32_t* __restrict__ ntok, int T, int K, int E,
+    int32_t* __restrict__ blk_counts) {
+    __shared__ int s_hist[kMaxExperts];
+    const int tv = moe_valid_tokens(ntok, T);
+    const long long nvalid = (long long)tv * K;
+    for (int e = threadIdx.x; e < E; e += blockDim.x) s_hist[e] = 0;
+    __syncthreads();
+    const long long a0 = (long long)blockIdx.x * kDispatchChunk;
+    const long long a1 = (a0 + kDispatchChunk < nvalid) ? a0 + kDispatchChunk : nvalid;
+    for (long long a = a0 + threadIdx.x; a < a1; a += blockDim.x) {
+        int e = ids[a];
+        if (e >= 0 && e < E) atomicAdd(&s_hist[e], 1);  // integer: order-independent
+    }
+    __syncthreads();
+    for (int e = threadIdx.x; e < E; e += blockDim.x)
+        blk_counts[(long long)blockIdx.x * E + e] = s_hist[e];
+}
+
+// SINGLE: one block handles all T*K assignments and builds its own histogram.
+// Otherwise block b handles assignments [b*chunk, (b+1)*chunk) and reads every
+// block's histogram from blk_counts.
+template <bool SINGLE>
+__global__ __launch_bounds__(kDispatchThreads) void dispatch_scatter_kernel(
+    const int32_t* __restrict__ ids, const int32_t* __restrict__ ntok, int T, int K, int E,
+    const int32_t* __restrict__ blk_counts, int nblk, int32_t* __restrict__ offsets,
+    int32_t* __restrict__ row_src, int32_t* __restrict__ token_row) {
+    constexpr int kWaves = kDispatchThreads / 64;
+    __shared__ int s_base[kMaxExperts];            // next row of each expert in this block
+    __shared__ int s_scan[kMaxExperts + 1];        // totals -> exclusive offsets
+    __shared__ int s_wcnt[kWaves * kMaxExperts];   // per-wave counts -> per-wave bases
+    __shared__ int s_wave[kWaves];
+
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int tv = moe_valid_tokens(ntok, T);
+    const long long nvalid = (long long)tv * K;
+    const long long ntotal = (long long)T * K;
+    const long long a0 = SINGLE ? 0 : (long long)blockIdx.x * kDispatchChunk;
+    const long long a1 = SINGLE ? ntotal : ((a0 + kDispatchChunk < ntotal) ? a0 + kDispatchChunk : ntotal);
+
+    // 1. per-expert totals and this block's start inside each expert
+    if (SINGLE) {
+        for (int e = tid; e < E; e += blockDim.x) { s_base[e] = 0; s_scan[e] = 0; }
+        __syncthreads();
+        for (long long a = tid; a < nvalid; a += blockDim.x) {
+            int e = ids[a];
+            if (e >= 0 && e < E) atomicAdd(&s_scan[e], 1);
+        }
+    } else {
+        for (int e = tid; e < E; e += blockDim.x) {
+            int pre = 0, tot = 0;
+            for (int b = 0; b < nblk; ++b) {
+                int c = blk_counts[(long long)b * E + e];
+                tot += c;
+                pre += (b < (int)blockIdx.x) ? c : 0;
+            }
+            s_base[e] = pre;
+            s_scan[e] = tot;
+        }
+    }
+    for (int i = tid; i < kWaves * E; i += blockDim.x) s_wcnt[i] = 0;
+    __syncthreads();
+
+    // 2. exclusive scan of the totals -> expert_offsets
+    moe_block_exclusive_scan(s_scan, E, s_wave);
+    if (blockIdx.x == 0)
+        for (int e = tid; e <= E; e += blockDim.x) offsets[e] = s_scan[e];
+    for (int e = tid; e < E; e += blockDim.x) s_base[e] += s_scan[e];
+    __syncthreads();
+
+    // 3. stable scatter, blockDim assignments at a time
+    for (long long sb = a0; sb < a1; sb += blockDim.x) {
+        const long long a = sb + tid;
+        const bool in = a < a1;
+        int e = -1;
+        if (in && a < nvalid) {
+            int v = ids[a];
+            if (v >= 0 && v < E) e = v;
+        }
+        int rank = 0;
+        unsigned long long rem = __ballot(e >= 0);
+        while (rem) {
+            const int leader = __ffsll((long long)rem) - 1;
+            const int ve = __shfl(e, leader, 64);
+            const unsigned long long m = __ballot(e == ve);
+            if (e == ve) rank = __popcll(m & ((1ull << lane) - 1ull));
+            if (lane == leader) s_wcnt[wave * E + ve] = __popcll(m);
+            rem &= ~m;
+        }
+        __syncthreads();
+        for (int x = tid; x < E; x += blockDim.x) {  // counts -> bases, wave order
+            int run = s_base[x];
+            for (int w = 0; w < kWaves; ++w) {
+                int c = s_wcnt[w * E + x];
+                s_wcnt[w * E + x] = run;
+                run += c;
+            }
+            s_base[x] = run;
+        }
+        __syncthreads();
+        if (in) {
+            if (e >= 0) {
+                const int r = s_wcnt[wave * E + e] + rank;
+                row_src[r] = (int)a;
+                token_row[a] = r;
+            } else {
+                token_row[a] = -1;
+            }
+        }
+        __syncthreads();
+        for (int i = tid; i < kWaves * E; i += blockDim.x) s_wcnt[i] = 0;
+        __syncthreads();
+    }
+}
+
+// x_disp[r, :] = x[row_src[r] / K, :] for r < R = offsets[E]; 16-byte copies.
+__global__ __launch_bounds__(256) void gather_rows_kernel(const uint4* __restrict__ x,
+                                                          const int32_t* __restrict__ offsets,
+                                                          const int32_t* __restrict__ row_src,
+                                                          int K, int E, int vec_per_row,
+                                                          uint4* __restrict__ x_disp) {
+    const long long R = offsets[E];
+    const long long n = R * vec_per_row;
+    for (long long i = (long long)blockIdx.x * blockDim.x + threadIdx.x; i < n;
+         i += (long long)gridDim.x * blockDim.x) {
+        const long long r = i / vec_per_row;
+        const int c = (int)(i - r * vec_per_row);
+        const long long t = row_src[r] / K;
+        x_disp[r * vec_per_row + c] = x[t * vec_per_row + c];
+    }
+}
+
+}  // namespace
+
+hipError_t launch_dispatch(const Shape& s, const int32_t* ids, const int32_t* ntok,
+                           int32_t* offsets, int32_t* row_src, int32_t* token_row,
+                           int32_t* blk_counts, hipStream_t st) {
+    const int nblk = dispatch_blocks(s);
+    if (nblk == 1) {
+        hipLaunchKernelGGL(dispatch_scatter_kernel<true>, dim3(1), dim3(kDispatchThreads), 0, st,
+                           ids, ntok, s.T, s.K, s.E, nullptr, 1, offsets, row_src, token_row);
+    } else {
+        hipLaunchKernelGGL(dispatch_count_kernel, dim3(nblk), dim3(kDispatchThreads), 0, st, ids,
+                           ntok, s.T, s.K, s.E, blk_counts);
+        hipLaunchKernelGGL(dispatch_scatter_kernel<false>, dim3(nblk), dim3(kDispatchThreads), 0,
+                           st, ids, ntok, s.T, s.K, s.E, blk_counts, nblk, offsets, row_src,
+                           token_row);
+    }
+    return hipGetLastError();
+}
+
+hipError_t launch_gather(const Shape& s, const uint16_t* x, const int32_t* offsets,
+                         const int32_t* row_src, uint16_t* x_disp, hipStream_t st) {
+    const int vec = s.H / 8;
+    long long work = (long long)s.cap * vec;
+    long long blocks = (work + 255) / 256;
+    if (blocks > 4 * kNumCUs * 4) blocks = 4 * kNumCUs * 4;
+    if (blocks < 1) blocks = 1;
+    hipLaunchKernelGGL(gather_rows_kernel, dim3((unsigned)blocks), dim3(256), 0, st,
+                       reinterpret_cast<const uint4*>(x), offsets, row_src, s.K, s.E, vec,
+                       reinterpret_cast<uint4*>(x_disp));
+    return hipGetLastError();
+}
+
+}  // namespace moe

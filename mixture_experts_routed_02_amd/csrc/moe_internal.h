@@ -1,0 +1,111 @@
+// Internal declarations shared by the kernels and the host entry points of
+// libmoe_mi355x.so (gfx950 / CDNA4, wave64).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace moe {
+
+constexpr int kMaxExperts = 512;
+constexpr int kDispatchThreads = 1024;
+constexpr int kDispatchChunk = 4096;     // assignments per block, multi-block dispatch
+constexpr int kDispatchSingleMax = 8192; // up to this many assignments: one block does it all
+constexpr int kNumCUs = 256;
+
+struct Shape {
+    int T, K, E, H, I, cap;
+};
+
+// Grouped-GEMM plan, chosen on the host from host-known sizes only.
+enum GemmKind { kSkinny = 1, kTiled64 = 2, kTiled128 = 3 };
+struct GemmPlan {
+    int kind;
+    int grid_gateup, grid_down;
+    int bn_gateup, bn_down;  // weight rows per tile (tiled kinds)
+};
+
+GemmPlan choose_plan(const Shape& s, int hint);
+
+inline int dispatch_blocks(const Shape& s) {
+    long long n = (long long)s.T * s.K;
+    if (n <= kDispatchSingleMax) return 1;
+    return (int)((n + kDispatchChunk - 1) / kDispatchChunk);
+}
+
+// ---- launches (each returns hipGetLastError() of its launches) ----------
+hipError_t launch_dispatch(const Shape& s, const int32_t* ids, const int32_t* ntok,
+                           int32_t* offsets, int32_t* row_src, int32_t* token_row,
+                           int32_t* blk_counts, hipStream_t st);
+hipError_t launch_gather(const Shape& s, const uint16_t* x, const int32_t* offsets,
+                         const int32_t* row_src, uint16_t* x_disp, hipStream_t st);
+// C[r, :] for the dispatched rows r < R:
+//   gated: C = bf16(silu(A W_gate^T) * (A W_up^T)), W = [E, 2N, Kd], C: [cap, N]
+//   plain: C = bf16(A W^T),                            W = [E, N, Kd],  C: [cap, N]
+// A row of dispatched row r is A[row_src ? row_src[r] / topk : r].
+hipError_t launch_grouped_gemm(const Shape& s, const GemmPlan& plan, bool gated,
+                               const uint16_t* A, const int32_t* row_src, int topk,
+                               const int32_t* offsets, const uint16_t* W, uint16_t* C,
+                               int Kd, int N, hipStream_t st);
+hipError_t launch_combine(const Shape& s, const uint16_t* y, const int32_t* token_row,
+                          const float* w, const int32_t* ntok, uint16_t* out, hipStream_t st);
+
+}  // namespace moe
+
+// ---------------------------------------------------------------------------
+// Device helpers
+// ---------------------------------------------------------------------------
+#if defined(__HIPCC__)
+typedef __bf16 moe_bf16x8 __attribute__((__vector_size__(8 * sizeof(__bf16))));
+typedef float moe_f32x4 __attribute__((__vector_size__(4 * sizeof(float))));
+typedef float moe_f32x16 __attribute__((__vector_size__(16 * sizeof(float))));
+
+__device__ __forceinline__ float moe_bf16_to_f32(uint16_t b) {
+    return __uint_as_float(((uint32_t)b) << 16);
+}
+
+// fp32 -> bf16, round to nearest even; NaN stays a quiet NaN.
+__device__ __forceinline__ uint16_t moe_f32_to_bf16(float f) {
+    uint32_t u = __float_as_uint(f);
+    if ((u & 0x7fffffffu) > 0x7f800000u) return (uint16_t)((u >> 16) | 0x40u);
+    u += 0x7fffu + ((u >> 16) & 1u);
+    return (uint16_t)(u >> 16);
+}
+
+__device__ __forceinline__ int moe_valid_tokens(const int32_t* ntok, int T) {
+    if (!ntok) return T;
+    int v = *ntok;
+    return v < 0 ? 0 : (v > T ? T : v);
+}
+
+// In-place exclusive scan of s[0..n) in LDS (one value per slot, any n);
+// s[n] receives the total.  s_wave needs blockDim.x/64 ints.  Every thread of
+// the block must call it; it ends with a barrier.
+__device__ __forceinline__ void moe_block_exclusive_scan(int* s, int n, int* s_wave) {
+    const int tid = threadIdx.x, nt = blockDim.x;
+    const int lane = tid & 63, wave = tid >> 6;
+    const int per = (n + nt - 1) / nt;
+    const int b = tid * per;
+    const int e = (b + per < n) ? b + per : n;
+    int sum = 0;
+    for (int i = b; i < e; ++i) sum += s[i];
+    int incl = sum;
+#pragma unroll
+    for (int d = 1; d < 64; d <<= 1) {
+        int v = __shfl_up(incl, d, 64);
+        if (lane >= d) incl += v;
+    }
+    if (lane == 63) s_wave[wave] = incl;
+    __syncthreads();
+    int run = incl - sum;
+    for (int w = 0; w < wave; ++w) run += s_wave[w];
+    for (int i = b; i < e; ++i) {
+        int v = s[i];
+        s[i] = run;
+        run += v;
+    }
+    if (tid == nt - 1) s[n] = run;
+    __syncthreads();
+}
+#endif

@@ -1,0 +1,224 @@
+"""Thin torch-tensor wrappers over the C ABI (argument marshalling only).
+
+PyTorch provides device memory and the current HIP stream; every step of the
+layer runs in libmoe_mi355x.so.  Each wrapper checks dtypes, shapes and
+devices, passes raw pointers and the stream, and raises MoeError on a
+non-success status.  Nothing here computes any part of the layer.
+"""
+from __future__ import annotations
+
+import ctypes
+from typing import Optional
+
+import torch
+
+from . import _lib
+from ._lib import MoeProblem, check, lib, problem, workspace_size
+
+__all__ = [
+    "problem", "workspace_size", "make_workspace", "dispatch", "expert_compute", "gate_up",
+    "down", "combine",
+    "forward", "MoEGraph", "MoeProblem",
+]
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream_ptr(device) -> ctypes.c_void_p:
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def _need(t: torch.Tensor, name: str, dtype, shape=None, device=None):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must live on a GPU")
+    if device is not None and t.device != device:
+        raise ValueError(f"{name} is on {t.device}, expected {device}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+
+
+def _cap(p: MoeProblem) -> int:
+    return p.capacity or p.num_tokens * p.top_k
+
+
+def make_workspace(p: MoeProblem, device) -> torch.Tensor:
+    """Device workspace for every entry point of problem p (uint8, 256-B aligned)."""
+    n = workspace_size(p)
+    return torch.empty(max(n, 256), dtype=torch.uint8, device=device)
+
+
+def _ntok(num_tokens_dev, device):
+    if num_tokens_dev is None:
+        return None
+    _need(num_tokens_dev, "num_tokens_dev", torch.int32, (1,), device)
+    return num_tokens_dev
+
+
+def dispatch(p: MoeProblem, x, topk_ids, num_tokens_dev=None, workspace=None, out=None):
+    """Local dispatch.  Returns (x_disp [cap,H], expert_offsets [E+1], row_src [cap],
+    token_row [T*K])."""
+    T, K, E, H = p.num_tokens, p.top_k, p.num_experts, p.hidden
+    dev = x.device
+    _need(x, "x", torch.bfloat16, (T, H))
+    _need(topk_ids, "topk_ids", torch.int32, (T, K), dev)
+    nt = _ntok(num_tokens_dev, dev)
+    cap = _cap(p)
+    if out is None:
+        out = (torch.empty((cap, H), dtype=torch.bfloat16, device=dev),
+               torch.empty((E + 1,), dtype=torch.int32, device=dev),
+               torch.empty((max(cap, 1),), dtype=torch.int32, device=dev),
+               torch.empty((max(T * K, 1),), dtype=torch.int32, device=dev))
+    x_disp, offsets, row_src, token_row = out
+    ws = make_workspace(p, dev) if workspace is None else workspace
+    check("moe_dispatch", lib().moe_dispatch(
+        ctypes.byref(p), _ptr(x), _ptr(topk_ids), _ptr(nt), _ptr(x_disp), _ptr(offsets),
+        _ptr(row_src), _ptr(token_row), _ptr(ws), ws.numel(), _stream_ptr(dev)))
+    return x_disp, offsets, row_src, token_row
+
+
+def expert_compute(p: MoeProblem, x_disp, expert_offsets, w_gateup, w_down, workspace=None,
+                   y_disp=None):
+    """Dispatched-expert MLP over a tight expert-major batch.  Returns y_disp [cap, H]."""
+    E, H, I = p.num_experts, p.hidden, p.intermediate
+    dev = x_disp.device
+    cap = _cap(p)
+    _need(x_disp, "x_disp", torch.bfloat16, (cap, H))
+    _need(expert_offsets, "expert_offsets", torch.int32, (E + 1,), dev)
+    _need(w_gateup, "w_gateup", torch.bfloat16, (E, 2 * I, H), dev)
+    _need(w_down, "w_down", torch.bfloat16, (E, H, I), dev)
+    if y_disp is None:
+        y_disp = torch.empty((cap, H), dtype=torch.bfloat16, device=dev)
+    _need(y_disp, "y_disp", torch.bfloat16, (cap, H), dev)
+    ws = make_workspace(p, dev) if workspace is None else workspace
+    check("moe_expert_compute", lib().moe_expert_compute(
+        ctypes.byref(p), _ptr(x_disp), _ptr(expert_offsets), _ptr(w_gateup), _ptr(w_down),
+        _ptr(y_disp), _ptr(ws), ws.numel(), _stream_ptr(dev)))
+    return y_disp
+
+
+def gate_up(p: MoeProblem, x_disp, expert_offsets, w_gateup, h=None):
+    """Gate-up grouped GEMM with the SiLU-gated epilogue.  Returns h [cap, I]."""
+    E, H, I = p.num_experts, p.hidden, p.intermediate
+    dev = x_disp.device
+    cap = _cap(p)
+    _need(x_disp, "x_disp", torch.bfloat16, (cap, H))
+    _need(expert_offsets, "expert_offsets", torch.int32, (E + 1,), dev)
+    _need(w_gateup, "w_gateup", torch.bfloat16, (E, 2 * I, H), dev)
+    if h is None:
+        h = torch.empty((cap, I), dtype=torch.bfloat16, device=dev)
+    _need(h, "h", torch.bfloat16, (cap, I), dev)
+    check("moe_gate_up", lib().moe_gate_up(ctypes.byref(p), _ptr(x_disp), _ptr(expert_offsets),
+                                           _ptr(w_gateup), _ptr(h), _stream_ptr(dev)))
+    return h
+
+
+def down(p: MoeProblem, h, expert_offsets, w_down, y_disp=None):
+    """Down grouped GEMM.  Returns y_disp [cap, H]."""
+    E, H, I = p.num_experts, p.hidden, p.intermediate
+    dev = h.device
+    cap = _cap(p)
+    _need(h, "h", torch.bfloat16, (cap, I))
+    _need(expert_offsets, "expert_offsets", torch.int32, (E + 1,), dev)
+    _need(w_down, "w_down", torch.bfloat16, (E, H, I), dev)
+    if y_disp is None:
+        y_disp = torch.empty((cap, H), dtype=torch.bfloat16, device=dev)
+    _need(y_disp, "y_disp", torch.bfloat16, (cap, H), dev)
+    check("moe_down", lib().moe_down(ctypes.byref(p), _ptr(h), _ptr(expert_offsets),
+                                     _ptr(w_down), _ptr(y_disp), _stream_ptr(dev)))
+    return y_disp
+
+
+def combine(p: MoeProblem, y_disp, token_row, topk_weights, num_tokens_dev=None, out=None):
+    """Weighted top-k combine.  Returns out [T, H] (rows t >= T_v untouched)."""
+    T, K, H = p.num_tokens, p.top_k, p.hidden
+    dev = y_disp.device
+    _need(y_disp, "y_disp", torch.bfloat16, (_cap(p), H))
+    _need(token_row, "token_row", torch.int32, None, dev)
+    if token_row.numel() < T * K:
+        raise ValueError("token_row must hold T*K entries")
+    _need(topk_weights, "topk_weights", torch.float32, (T, K), dev)
+    nt = _ntok(num_tokens_dev, dev)
+    if out is None:
+        out = torch.empty((T, H), dtype=torch.bfloat16, device=dev)
+    _need(out, "out", torch.bfloat16, (T, H), dev)
+    check("moe_combine", lib().moe_combine(
+        ctypes.byref(p), _ptr(y_disp), _ptr(token_row), _ptr(topk_weights), _ptr(nt), _ptr(out),
+        _stream_ptr(dev)))
+    return out
+
+
+def _forward_args(p, x, topk_ids, topk_weights, w_gateup, w_down, num_tokens_dev, offsets, out,
+                  workspace):
+    T, K, E, H, I = p.num_tokens, p.top_k, p.num_experts, p.hidden, p.intermediate
+    dev = x.device
+    _need(x, "x", torch.bfloat16, (T, H))
+    _need(topk_ids, "topk_ids", torch.int32, (T, K), dev)
+    _need(topk_weights, "topk_weights", torch.float32, (T, K), dev)
+    _need(w_gateup, "w_gateup", torch.bfloat16, (E, 2 * I, H), dev)
+    _need(w_down, "w_down", torch.bfloat16, (E, H, I), dev)
+    nt = _ntok(num_tokens_dev, dev)
+    if offsets is None:
+        offsets = torch.empty((E + 1,), dtype=torch.int32, device=dev)
+    _need(offsets, "expert_offsets", torch.int32, (E + 1,), dev)
+    if out is None:
+        out = torch.empty((T, H), dtype=torch.bfloat16, device=dev)
+    _need(out, "out", torch.bfloat16, (T, H), dev)
+    ws = make_workspace(p, dev) if workspace is None else workspace
+    return nt, offsets, out, ws
+
+
+def forward(p: MoeProblem, x, topk_ids, topk_weights, w_gateup, w_down, num_tokens_dev=None,
+            expert_offsets=None, out=None, workspace=None):
+    """The whole routed-expert layer.  Returns (out [T,H], expert_offsets [E+1])."""
+    nt, offsets, out, ws = _forward_args(p, x, topk_ids, topk_weights, w_gateup, w_down,
+                                         num_tokens_dev, expert_offsets, out, workspace)
+    check("moe_forward", lib().moe_forward(
+        ctypes.byref(p), _ptr(x), _ptr(topk_ids), _ptr(topk_weights), _ptr(w_gateup),
+        _ptr(w_down), _ptr(nt), _ptr(offsets), _ptr(out), _ptr(ws), ws.numel(),
+        _stream_ptr(x.device)))
+    return out, offsets
+
+
+class MoEGraph:
+    """One moe_forward recorded into a HIP graph with fixed buffers; replay with
+    launch() after writing new inputs (and *num_tokens_dev) into them."""
+
+    def __init__(self, p: MoeProblem, x, topk_ids, topk_weights, w_gateup, w_down,
+                 num_tokens_dev=None, expert_offsets=None, out=None, workspace=None):
+        nt, offsets, out, ws = _forward_args(p, x, topk_ids, topk_weights, w_gateup, w_down,
+                                             num_tokens_dev, expert_offsets, out, workspace)
+        self.p = p
+        self.device = x.device
+        # keep every buffer alive as long as the graph
+        self._keep = (x, topk_ids, topk_weights, w_gateup, w_down, nt, offsets, out, ws)
+        self.out, self.expert_offsets, self.workspace = out, offsets, ws
+        h = ctypes.c_void_p()
+        torch.cuda.synchronize(self.device)
+        check("moe_graph_create", lib().moe_graph_create(
+            ctypes.byref(p), _ptr(x), _ptr(topk_ids), _ptr(topk_weights), _ptr(w_gateup),
+            _ptr(w_down), _ptr(nt), _ptr(offsets), _ptr(out), _ptr(ws), ws.numel(),
+            ctypes.byref(h)))
+        self._h = h
+
+    def launch(self):
+        check("moe_graph_launch", lib().moe_graph_launch(self._h, _stream_ptr(self.device)))
+        return self.out
+
+    def close(self):
+        if self._h is not None and self._h.value:
+            check("moe_graph_destroy", lib().moe_graph_destroy(self._h))
+            self._h = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass

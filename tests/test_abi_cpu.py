@@ -1,0 +1,102 @@
+"""The C ABI without a GPU: the library loads, exports what the header
+declares, sizes workspaces, and fails closed on bad arguments before it
+enqueues anything (every call below is rejected by host validation, so no
+HIP call is made)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import mixture_experts_routed_02_amd as moe
+from mixture_experts_routed_02_amd import _lib
+
+HEADER = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "include",
+                      "moe_mi355x.h")
+
+A16 = 0x100000        # fake, 16-byte aligned "device" addresses: never dereferenced
+A4 = 0x200004
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"MOE_API\s+[\w\s\*]+?\b(moe_\w+)\s*\(", text)))
+
+
+def test_exports_every_declared_symbol():
+    names = declared_functions()
+    assert len(names) == 11, names
+    L = moe.lib()
+    for n in names:
+        assert hasattr(L, n), n
+    assert set(names) == set(_lib.EXPORTS)
+
+
+def test_status_strings():
+    for s in (0, 1, 2, 3):
+        assert moe.status_string(s).startswith("MOE_")
+
+
+def test_workspace_sizes():
+    p = moe.problem(4096, 2, 8, 4096, 14336)
+    n = moe.workspace_size(p)
+    cap = 4096 * 2
+    assert n >= cap * (14336 + 4096) * 2 + cap * 4 + 4096 * 2 * 4
+    assert n % 256 == 0
+    big = moe.workspace_size(moe.problem(4096, 2, 8, 4096, 14336, capacity=2 * cap))
+    assert big > n
+    assert moe.workspace_size(moe.problem(0, 2, 8, 256, 512)) >= 0
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(num_tokens=-1), _lib.MOE_ERROR_INVALID_VALUE),
+    (dict(top_k=0), _lib.MOE_ERROR_INVALID_VALUE),
+    (dict(top_k=65), _lib.MOE_ERROR_NOT_SUPPORTED),
+    (dict(num_experts=0), _lib.MOE_ERROR_INVALID_VALUE),
+    (dict(num_experts=513), _lib.MOE_ERROR_NOT_SUPPORTED),
+    (dict(hidden=250), _lib.MOE_ERROR_NOT_SUPPORTED),
+    (dict(intermediate=100), _lib.MOE_ERROR_NOT_SUPPORTED),
+    (dict(capacity=127), _lib.MOE_ERROR_INVALID_VALUE),
+    (dict(kernel_hint=7), _lib.MOE_ERROR_INVALID_VALUE),
+])
+def test_bad_problem_rejected(kw, status):
+    base = dict(num_tokens=64, top_k=2, num_experts=8, hidden=256, intermediate=512)
+    base.update(kw)
+    p = moe.problem(**base)
+    n = ctypes.c_size_t(0)
+    assert moe.lib().moe_workspace_size(ctypes.byref(p), ctypes.byref(n)) == status
+    r = moe.lib().moe_forward(ctypes.byref(p), A16, A4, A4, A16, A16, None, A4, A16, A16,
+                              1 << 40, None)
+    assert r == status
+
+
+def test_bad_pointers_rejected():
+    p = moe.problem(64, 2, 8, 256, 512)
+    ws = moe.workspace_size(p)
+    L = moe.lib()
+    fwd = lambda *a: L.moe_forward(ctypes.byref(p), *a)
+    good = [A16, A4, A4, A16, A16, None, A4, A16, A16, ws, None]
+    for i in (0, 1, 2, 3, 4, 6, 7, 8):      # each required pointer nulled
+        args = list(good)
+        args[i] = None
+        assert fwd(*args) == _lib.MOE_ERROR_INVALID_VALUE, i
+    for i in (0, 3, 4, 7, 8):               # bf16 / workspace pointers misaligned
+        args = list(good)
+        args[i] = A16 + 2
+        assert fwd(*args) == _lib.MOE_ERROR_INVALID_VALUE, i
+    args = list(good)
+    args[9] = ws - 1                        # workspace too small
+    assert fwd(*args) == _lib.MOE_ERROR_INVALID_VALUE
+    args = list(good)
+    args[5] = A4 + 1                        # misaligned num_tokens_dev
+    assert fwd(*args) == _lib.MOE_ERROR_INVALID_VALUE
+    # the staged entry points too
+    assert L.moe_dispatch(ctypes.byref(p), A16, None, None, A16, A4, A4, A4, A16, ws, None) == 1
+    assert L.moe_expert_compute(ctypes.byref(p), A16, A4, A16, A16, A16, A16, ws - 256, None) == 1
+    assert L.moe_combine(ctypes.byref(p), A16, A4, A4, None, A16 + 8, None) == 1
+    assert L.moe_graph_launch(None, None) == 1
+    assert L.moe_graph_destroy(None) == 1
+    h = ctypes.c_void_p()
+    assert L.moe_graph_create(ctypes.byref(p), A16, A4, A4, A16, A16, None, A4, A16, A16, 16,
+                              ctypes.byref(h)) == 1
+    assert h.value is None
