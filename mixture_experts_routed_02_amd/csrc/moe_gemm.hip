@@ -225,29 +225,31 @@ __global__ __launch_bounds__(256) void gemm_tiled_kernel(
 #pragma unroll
             for (int j = 0; j < MS; ++j) acc[i][j] = (moe_f32x4){0.f, 0.f, 0.f, 0.f};
 
-        uint4 rw[WPASS], ra[APASS];
+        {
+            uint4 rw[WPASS], ra[APASS];
 #pragma unroll
-        for (int p = 0; p < WPASS; ++p) rw[p] = *reinterpret_cast<const uint4*>(wsrc[p]);
+            for (int p = 0; p < WPASS; ++p) rw[p] = *reinterpret_cast<const uint4*>(wsrc[p]);
 #pragma unroll
-        for (int p = 0; p < APASS; ++p) ra[p] = *reinterpret_cast<const uint4*>(asrc[p]);
+            for (int p = 0; p < APASS; ++p) ra[p] = *reinterpret_cast<const uint4*>(asrc[p]);
 #pragma unroll
-        for (int p = 0; p < WPASS; ++p)
-            *reinterpret_cast<uint4*>(&s_w[0][(cp_row + 32 * p) * kPitch + cp_col]) = rw[p];
+            for (int p = 0; p < WPASS; ++p)
+                *reinterpret_cast<uint4*>(&s_w[0][(cp_row + 32 * p) * kPitch + cp_col]) = rw[p];
 #pragma unroll
-        for (int p = 0; p < APASS; ++p)
-            *reinterpret_cast<uint4*>(&s_a[0][(cp_row + 32 * p) * kPitch + cp_col]) = ra[p];
+            for (int p = 0; p < APASS; ++p)
+                *reinterpret_cast<uint4*>(&s_a[0][(cp_row + 32 * p) * kPitch + cp_col]) = ra[p];
+        }
         __syncthreads();
 
         for (int kt = 0; kt < nk; ++kt) {
             const int cur = kt & 1;
-            const bool more = kt + 1 < nk;
-            if (more) {
-                const size_t ko = (size_t)(kt + 1) * kBK;
+            // Prefetch the next k-step (the last iteration re-reads its own
+            // step, which lands in the idle buffer and is never consumed).
+            const size_t ko = (size_t)(kt + 1 < nk ? kt + 1 : kt) * kBK;
+            uint4 rw[WPASS], ra[APASS];
 #pragma unroll
-                for (int p = 0; p < WPASS; ++p) rw[p] = *reinterpret_cast<const uint4*>(wsrc[p] + ko);
+            for (int p = 0; p < WPASS; ++p) rw[p] = *reinterpret_cast<const uint4*>(wsrc[p] + ko);
 #pragma unroll
-                for (int p = 0; p < APASS; ++p) ra[p] = *reinterpret_cast<const uint4*>(asrc[p] + ko);
-            }
+            for (int p = 0; p < APASS; ++p) ra[p] = *reinterpret_cast<const uint4*>(asrc[p] + ko);
 #pragma unroll
             for (int kk = 0; kk < kBK / 32; ++kk) {
                 moe_bf16x8 fw[NS], fa[MS];
@@ -270,14 +272,12 @@ __global__ __launch_bounds__(256) void gemm_tiled_kernel(
                     for (int j = 0; j < MS; ++j)
                         acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fw[i], fa[j], acc[i][j], 0, 0, 0);
             }
-            if (more) {
 #pragma unroll
-                for (int p = 0; p < WPASS; ++p)
-                    *reinterpret_cast<uint4*>(&s_w[cur ^ 1][(cp_row + 32 * p) * kPitch + cp_col]) = rw[p];
+            for (int p = 0; p < WPASS; ++p)
+                *reinterpret_cast<uint4*>(&s_w[cur ^ 1][(cp_row + 32 * p) * kPitch + cp_col]) = rw[p];
 #pragma unroll
-                for (int p = 0; p < APASS; ++p)
-                    *reinterpret_cast<uint4*>(&s_a[cur ^ 1][(cp_row + 32 * p) * kPitch + cp_col]) = ra[p];
-            }
+            for (int p = 0; p < APASS; ++p)
+                *reinterpret_cast<uint4*>(&s_a[cur ^ 1][(cp_row + 32 * p) * kPitch + cp_col]) = ra[p];
             __syncthreads();
         }
 
