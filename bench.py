@@ -125,7 +125,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--config", default="mixtral")
     ap.add_argument("--seed", type=int, default=0)
-    ap.add_argument("--hint", type=int, default=0, help="grouped-GEMM plan (0 auto, 1-3 forced)")
+    ap.add_argument("--hint", type=int, default=0, help="grouped-GEMM plan (0 auto, 1-4 forced)")
     ap.add_argument("--cold", action="store_true",
                     help="overwrite a 512 MiB buffer before each step (outside the timed "
                          "events) so weights are read from HBM, not L2/MALL")
@@ -214,7 +214,8 @@ def main():
     B_gu = 4.0 * H * I * touched + 2.0 * H * R + 2.0 * I * R
     mfma_bound = (F_gu / max(B_gu, 1.0)) >= RIDGE
     # the host plan rule of the library: forced hint, else rows per expert T*K/E
-    kind = args.hint if args.hint in (1, 2, 3) else (1 if T * K / E <= 24 else 2 if T * K / E <= 96 else 3)
+    rpe = T * K / E
+    kind = args.hint if args.hint in (1, 2, 3, 4) else (1 if rpe <= 24 else 2 if rpe <= 96 else 4)
     kernel_name = "gemm_skinny_kernel" if kind == 1 else "gemm_tiled_kernel"
     traffic = pmc_traffic(f"{kernel_name}<gated>@{cfg.name}", kernel_src_hash(), 1)
     if mfma_bound:

@@ -10,7 +10,8 @@
  * as the composition local dispatch -> dispatched-expert compute -> combine
  * (TileOps PR #1738 "[Refactor][MoE] Separate dispatched expert compute",
  * Summary), with the routing weights applied only in the combine (same
- * Summary), one (tokens, hidden) output (FlashInfer PR #3980, Summary), a
+ * Summary), one (tokens, hidden) output (FlashInfer PR #3980, commit notes
+ * on the kernel API migration, launch/output), a
  * tight no-pad expert-major batch whose expert_offsets stay on the GPU and
  * end in the valid-row count (TileOps PR #1738, Scope), and a static capacity
  * whose tail rows are unspecified (same Scope).
@@ -66,7 +67,7 @@ typedef struct moe_problem {
     int32_t capacity;      /* rows of the dispatched buffers; 0 => T*K; must be >= T*K */
     int32_t kernel_hint;   /* grouped-GEMM plan: 0 auto (chosen from T*K/E on the host),
                               1 skinny (16-row tiles, in-workgroup split-K),
-                              2 tiled 64-row, 3 tiled 128-row                         */
+                              2 tiled 64-row, 3 tiled 128-row, 4 tiled 256-row        */
 } moe_problem_t;
 
 typedef enum moe_status {
@@ -131,8 +132,8 @@ MOE_API moe_status_t moe_down(const moe_problem_t* p, const uint16_t* h,
                               uint16_t* y_disp, void* stream);
 
 /* Weighted top-k combine back to token order (TileOps PR #1738, Summary:
- * weights stay outside expert compute; FlashInfer PR #3980, Summary: one
- * (tokens, hidden) output).  For t < T_v:
+ * weights stay outside expert compute; FlashInfer PR #3980, kernel API
+ * migration notes: one (tokens, hidden) output).  For t < T_v:
  *   out[t,:] = bf16( sum_{j ascending, token_row[t*K+j] >= 0} w[t,j] * y_disp[token_row[t*K+j], :] )
  * accumulated in fp32 (a zero row when no assignment is valid).
  *   y_disp bf16 [capacity, H], token_row int32 [T*K], topk_weights fp32 [T, K],

@@ -17,7 +17,7 @@ MOE_ERROR_NOT_SUPPORTED = 2
 MOE_ERROR_LAUNCH = 3
 
 # kernel_hint values
-HINT_AUTO, HINT_SKINNY, HINT_TILED64, HINT_TILED128 = 0, 1, 2, 3
+HINT_AUTO, HINT_SKINNY, HINT_TILED64, HINT_TILED128, HINT_TILED256 = 0, 1, 2, 3, 4
 
 EXPORTS = (
     "moe_status_string", "moe_workspace_size", "moe_dispatch", "moe_expert_compute",

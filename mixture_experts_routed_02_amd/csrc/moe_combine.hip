@@ -1,7 +1,8 @@
 // Weighted top-k combine back to token order (TileOps PR #1738 "[Refactor]
 // [MoE] Separate dispatched expert compute", Summary: the routing weights are
-// applied outside expert compute; FlashInfer PR #3980, Summary: a single
-// (tokens, hidden) output with the top-k reduction done inside the layer).
+// applied outside expert compute; FlashInfer PR #3980, commit notes on the
+// kernel API migration, launch/output: a single (tokens, hidden) output with
+// the top-k reduction done inside the layer).
 //
 // out[t,:] = bf16( sum over j = 0..K-1 with token_row[t*K+j] >= 0 of
 //                  w[t,j] * y[token_row[t*K+j], :] ),  fp32 fused multiply-adds

@@ -22,6 +22,8 @@
 // plain: W = [E, N, Kd],                                 C = bf16(acc)      [cap, N]
 #include "moe_internal.h"
 
+#include <cmath>
+
 namespace moe {
 namespace {
 
@@ -146,41 +148,90 @@ __global__ __launch_bounds__(256) void gemm_skinny_kernel(
 }
 
 // ---------------------------------------------------------------------------
-// Tiled kernel: BM token rows x BN weight rows per tile, BK = 64, operands
-// staged through double-buffered LDS (row pitch 72 bf16 = 144 B, so the 8
-// lanes of one 128-byte LDS access phase start 16 B apart in bank space).
-// 4 waves in a 2 (weight) x 2 (token) grid; each wave owns (BN/2) x (BM/2)
-// of the tile as 16x16 MFMA sub-tiles.  gated: tile rows [0, BN/2) are gate
-// columns n0.. and [BN/2, BN) the matching up columns, and each wave takes
-// the same column range from both halves so gate and up of one output meet
-// in one lane.
+// Tiled kernel: BM token rows x BN weight rows per tile, operands streamed
+// through a kStages-deep LDS ring, BK = 32 per stage, filled by direct
+// global->LDS loads (global_load_lds_dwordx4: no staging registers), so
+// kStages-1 stages of loads are in flight while one stage is multiplied.
+// The product runs on v_mfma_f32_32x32x16_bf16: measured on the device, it
+// sustains ~2.2 PFLOP/s where the 16x16x32 form stops near 1.3.
+//
+// Stage layout: 16-row groups of 1 KiB, token groups first, then weight
+// groups; row r of a stage holds its 32-element k-slice as four 16-byte
+// chunks, chunk c stored in slot c ^ f(r), f(r) = 2*bit2(r) + bit4(r).  A DMA
+// instruction fills one group (lane L -> row L/4, slot L%4); a 32x32x16
+// fragment read takes 32 rows x one chunk.  A ds_read_b128 pass on gfx950
+// serves lanes {0-7,16-23}, {8-15,24-31}, ...; with f those sixteen lanes hit
+// sixteen distinct 16-byte bank groups, so neither the DMA writes nor the
+// fragment reads have bank conflicts.
+//
+// WGM x WGN waves; each wave owns (BM/WGM) token rows x (BN/WGN) weight rows
+// of the tile as 32x32 MFMA sub-tiles (weights = MFMA rows, tokens = MFMA
+// columns).  gated: tile rows [0, BN/2) are gate columns n0.. and [BN/2, BN)
+// the matching up columns; each wave takes the same column range from both
+// halves so gate and up of one output meet in one lane.  Waits on the ring
+// are explicit (vmcnt + s_barrier): a full __syncthreads() would also drain
+// the loads that are meant to stay in flight.
 // ---------------------------------------------------------------------------
-constexpr int kBK = 64;
-constexpr int kPitch = 72;
+constexpr int kBK = 32;
+constexpr int kStages = 4;
 
-template <int BM, int BN, bool GATED>
-__global__ __launch_bounds__(256) void gemm_tiled_kernel(
+typedef __attribute__((address_space(3))) unsigned char lds_u8;
+
+// 16 bytes per lane from g into LDS at lds_base + 16 * lane (lds_base must be
+// wave-uniform).  Written as inline asm so that the compiler does not treat
+// the pending LDS writes as aliasing every later LDS read (it would then drain
+// the whole ring with vmcnt(0) before each read); the ring's own explicit
+// vmcnt waits and barriers order these writes against the reads.
+__device__ __forceinline__ void lds_dma16(const uint16_t* g, uint32_t lds_base) {
+    asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off"
+                 :: "v"(g), "s"(lds_base) : "memory", "m0");
+}
+
+__device__ __forceinline__ uint32_t lds_addr(const unsigned char* p) {
+    return (uint32_t)(uintptr_t)(const lds_u8*)p;
+}
+
+template <int N>
+__device__ __forceinline__ void wait_vmcnt_barrier() {
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+}
+
+// slot swizzle of stage row r (see above)
+__device__ __forceinline__ int ring_swz(int r) { return (((r >> 2) & 1) << 1) | ((r >> 4) & 1); }
+
+template <int BM, int BN, int WGM, int WGN, bool GATED>
+__global__ __launch_bounds__(64 * WGM * WGN) void gemm_tiled_kernel(
     const uint16_t* __restrict__ A, const int32_t* __restrict__ row_src, int topk,
     const int32_t* __restrict__ offsets, const uint16_t* __restrict__ W,
     uint16_t* __restrict__ C, int E, int Kd, int N) {
-    static_assert(BM % 32 == 0 && BN % 64 == 0, "tile shape");
-    constexpr int WN = BN / 2, WM = BM / 2;          // per-wave extent
-    constexpr int NS = WN / 16, MS = WM / 16;        // 16x16 sub-tiles per wave
-    constexpr int COLS = GATED ? BN / 2 : BN;        // output columns per tile
-    constexpr int WPASS = BN / 32, APASS = BM / 32;  // 16-B loads per thread per k-step
+    constexpr int NT = 64 * WGM * WGN, NW = NT / 64;  // threads, waves
+    constexpr int WM = BM / WGM, WN = BN / WGN;       // per-wave extent
+    constexpr int MS = WM / 32, NS = WN / 32;         // 32x32 sub-tiles per wave
+    constexpr int COLS = GATED ? BN / 2 : BN;         // output columns per tile
+    constexpr int AG = BM / 16;                       // token groups per stage
+    constexpr int GROUPS = (BM + BN) / 16;            // 1 KiB groups per stage
+    constexpr int GPW = GROUPS / NW;                  // DMA instructions per wave per stage
+    constexpr int TPW = (AG + NW - 1) / NW;           // token groups per wave (upper bound)
+    constexpr int STAGE = GROUPS * 1024;              // bytes per stage
+    static_assert(WM % 32 == 0 && WN % 32 == 0 && GROUPS % NW == 0, "tile shape");
+    static_assert(!GATED || NS % 2 == 0, "gated tiles pair gate and up sub-tiles");
+    static_assert(GPW * (kStages - 2) < 64, "vmcnt range");
 
     __shared__ int s_start[kMaxExperts + 1];
-    __shared__ int s_wave[4];
-    __shared__ __attribute__((aligned(16))) uint16_t s_w[2][BN * kPitch];
-    __shared__ __attribute__((aligned(16))) uint16_t s_a[2][BM * kPitch];
+    __shared__ int s_wave[NW];
+    __shared__ __attribute__((aligned(1024))) unsigned char s_ring[kStages * STAGE];
 
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int li = lane & 15, lg = lane >> 4;
-    const int wn = wave >> 1, wm = wave & 1;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int wm = wave % WGM, wn = wave / WGM;
     const int n_tiles = N / COLS;
     const int w_rows = GATED ? 2 * N : N;
     const int total = build_tile_table<BM>(offsets, E, n_tiles, s_start, s_wave);
     const int nk = Kd / kBK;
+    const uint32_t ring0 = lds_addr(s_ring);
 
     // XCD-aware order: workgroup b runs on XCD b % 8; give each XCD a
     // contiguous run of logical tiles so neighbouring m-tiles share its L2.
@@ -188,8 +239,28 @@ __global__ __launch_bounds__(256) void gemm_tiled_kernel(
     const int lb = (G % 8 == 0) ? ((int)(blockIdx.x % 8) * (G / 8) + (int)(blockIdx.x / 8))
                                 : (int)blockIdx.x;
 
-    // global -> LDS copy roles: 8 threads per 128-byte row segment
-    const int cp_row = tid >> 3, cp_col = (tid & 7) * 8;
+    // DMA role of this lane: row lane/4 of a group, slot lane%4
+    const int dma_row = lane >> 2;
+    const int dma_chunk_even = (lane & 3) ^ ring_swz(dma_row);        // groups with even index
+    const int dma_chunk_odd = (lane & 3) ^ ring_swz(dma_row + 16);    // odd index (row bit 4 set)
+    // fragment-read offsets of this lane inside a 32-row block, for the two
+    // 16-wide k halves: row l%32, chunk 2*s + l/32
+    const int fr = lane & 31, fh = lane >> 5;
+    int rd_off[2];
+#pragma unroll
+    for (int sk = 0; sk < 2; ++sk)
+        rd_off[sk] = (fr >> 4) * 1024 + (fr & 15) * 64 + (((2 * sk + fh) ^ ring_swz(fr)) << 4);
+    int ga[MS], gw[NS];   // 32-row blocks, in units of 1 KiB groups
+#pragma unroll
+    for (int j = 0; j < MS; ++j) ga[j] = (wm * WM + j * 32) / 16;
+#pragma unroll
+    for (int i = 0; i < NS; ++i) {
+        int trow;
+        if (GATED) trow = (i < NS / 2) ? (wn * (WN / 2) + i * 32)
+                                       : (BN / 2 + wn * (WN / 2) + (i - NS / 2) * 32);
+        else trow = wn * WN + i * 32;
+        gw[i] = AG + trow / 16;
+    }
 
     for (int tile = lb; tile < total; tile += G) {
         const int e = find_expert(s_start, E, tile);
@@ -200,126 +271,149 @@ __global__ __launch_bounds__(256) void gemm_tiled_kernel(
         const int m_tile = local % mt, n_tile = local / mt;
         const int r0 = row0 + m_tile * BM;
         const int mrows = (me - m_tile * BM) < BM ? (me - m_tile * BM) : BM;
+        // a wave whose token rows all lie past the valid rows skips its MFMAs
+        const bool active = wm * WM < mrows;
 
-        const uint16_t* wsrc[WPASS];
+        // global source of each group this wave fills (k-step 0): token groups
+        // gather rows through row_src; weight rows are affine in the group
+        const uint16_t* asrc[TPW];
 #pragma unroll
-        for (int p = 0; p < WPASS; ++p) {
-            const int tr = cp_row + 32 * p;
-            int wr;
-            if (GATED) wr = (tr < BN / 2) ? (n_tile * (BN / 2) + tr) : (N + n_tile * (BN / 2) + tr - BN / 2);
-            else wr = n_tile * BN + tr;
-            wsrc[p] = W + ((size_t)e * w_rows + wr) * (size_t)Kd + cp_col;
-        }
-        const uint16_t* asrc[APASS];
-#pragma unroll
-        for (int p = 0; p < APASS; ++p) {
-            const int tr = cp_row + 32 * p;
+        for (int q = 0; q < TPW; ++q) {
+            const int g = wave + NW * q;
+            const int tr = (g < AG ? g : 0) * 16 + dma_row;
             const int rr = r0 + (tr < mrows ? tr : mrows - 1);
             const long long arow = row_src ? (long long)(row_src[rr] / topk) : (long long)rr;
-            asrc[p] = A + (size_t)arow * Kd + cp_col;
+            asrc[q] = A + (size_t)arow * Kd + ((g & 1) ? dma_chunk_odd : dma_chunk_even) * 8;
         }
+        const uint16_t* wbase = W + (size_t)e * w_rows * Kd + (size_t)dma_row * Kd;
+        auto wrow0 = [&](int g) {   // first weight row of weight group g (wave-uniform)
+            const int tr = (g - AG) * 16;
+            if (GATED) return (tr < BN / 2) ? (n_tile * (BN / 2) + tr) : (N + n_tile * (BN / 2) + tr - BN / 2);
+            return n_tile * BN + tr;
+        };
+        auto issue = [&](int step, int buf) {
+            const int ks = step < nk ? step : nk - 1;   // past the end: a harmless reload
+#pragma unroll
+            for (int q = 0; q < GPW; ++q) {
+                const int g = wave + NW * q;
+                const uint32_t dst = ring0 + buf * STAGE + g * 1024;
+                const uint16_t* src =
+                    (g < AG) ? asrc[q < TPW ? q : 0]
+                             : wbase + (size_t)wrow0(g) * Kd + ((g & 1) ? dma_chunk_odd : dma_chunk_even) * 8;
+                lds_dma16(src + (size_t)ks * kBK, dst);
+            }
+        };
 
-        moe_f32x4 acc[NS][MS];
+        moe_f32x16 acc[NS][MS];
 #pragma unroll
         for (int i = 0; i < NS; ++i)
 #pragma unroll
-            for (int j = 0; j < MS; ++j) acc[i][j] = (moe_f32x4){0.f, 0.f, 0.f, 0.f};
+            for (int j = 0; j < MS; ++j)
+#pragma unroll
+                for (int q = 0; q < 16; ++q) acc[i][j][q] = 0.f;
 
-        {
-            uint4 rw[WPASS], ra[APASS];
+        // Software pipeline over k-steps: when step kt is multiplied its
+        // fragments are already in registers, and step kt+1's fragments are
+        // read from LDS in the shadow of those MFMAs (token fragments into a
+        // second register set, each weight fragment into its own registers
+        // right after its last MFMA of step kt).  The LDS buffer of step kt is
+        // refilled with step kt + kStages once every wave has read it.
+        moe_bf16x8 fw[2][NS];
+        auto read_a = [&](int step, moe_bf16x8 (*fa)[MS]) {
+            const unsigned char* st = s_ring + (step % kStages) * STAGE;
 #pragma unroll
-            for (int p = 0; p < WPASS; ++p) rw[p] = *reinterpret_cast<const uint4*>(wsrc[p]);
+            for (int sk = 0; sk < 2; ++sk)
 #pragma unroll
-            for (int p = 0; p < APASS; ++p) ra[p] = *reinterpret_cast<const uint4*>(asrc[p]);
+                for (int j = 0; j < MS; ++j)
+                    fa[sk][j] = *reinterpret_cast<const moe_bf16x8*>(st + ga[j] * 1024 + rd_off[sk]);
+        };
+        auto read_w = [&](int step, int sk, int i) {
+            const unsigned char* st = s_ring + (step % kStages) * STAGE;
+            fw[sk][i] = *reinterpret_cast<const moe_bf16x8*>(st + gw[i] * 1024 + rd_off[sk]);
+        };
+        // one step: wait until step kt+1 has landed, refill step kt's buffer
+        // with step kt + kStages, multiply step kt while reading step kt+1
+        auto step = [&](int kt, moe_bf16x8 (*fa_c)[MS], moe_bf16x8 (*fa_n)[MS]) {
+            wait_vmcnt_barrier<GPW * (kStages - 2)>();
+            issue(kt + kStages, kt % kStages);
+            if (active) {
+                const bool more = kt + 1 < nk;
+                if (more) read_a(kt + 1, fa_n);
 #pragma unroll
-            for (int p = 0; p < WPASS; ++p)
-                *reinterpret_cast<uint4*>(&s_w[0][(cp_row + 32 * p) * kPitch + cp_col]) = rw[p];
+                for (int sk = 0; sk < 2; ++sk)
 #pragma unroll
-            for (int p = 0; p < APASS; ++p)
-                *reinterpret_cast<uint4*>(&s_a[0][(cp_row + 32 * p) * kPitch + cp_col]) = ra[p];
-        }
-        __syncthreads();
-
-        for (int kt = 0; kt < nk; ++kt) {
-            const int cur = kt & 1;
-            // Prefetch the next k-step (the last iteration re-reads its own
-            // step, which lands in the idle buffer and is never consumed).
-            const size_t ko = (size_t)(kt + 1 < nk ? kt + 1 : kt) * kBK;
-            uint4 rw[WPASS], ra[APASS];
+                    for (int i = 0; i < NS; ++i) {
 #pragma unroll
-            for (int p = 0; p < WPASS; ++p) rw[p] = *reinterpret_cast<const uint4*>(wsrc[p] + ko);
-#pragma unroll
-            for (int p = 0; p < APASS; ++p) ra[p] = *reinterpret_cast<const uint4*>(asrc[p] + ko);
-#pragma unroll
-            for (int kk = 0; kk < kBK / 32; ++kk) {
-                moe_bf16x8 fw[NS], fa[MS];
-#pragma unroll
-                for (int i = 0; i < NS; ++i) {
-                    int trow;
-                    if (GATED) trow = (i < NS / 2) ? (wn * (WN / 2) + i * 16 + li)
-                                                   : (BN / 2 + wn * (WN / 2) + (i - NS / 2) * 16 + li);
-                    else trow = wn * WN + i * 16 + li;
-                    fw[i] = *reinterpret_cast<const moe_bf16x8*>(&s_w[cur][trow * kPitch + kk * 32 + lg * 8]);
-                }
-#pragma unroll
-                for (int j = 0; j < MS; ++j) {
-                    const int arow = wm * WM + j * 16 + li;
-                    fa[j] = *reinterpret_cast<const moe_bf16x8*>(&s_a[cur][arow * kPitch + kk * 32 + lg * 8]);
-                }
-#pragma unroll
-                for (int i = 0; i < NS; ++i)
-#pragma unroll
-                    for (int j = 0; j < MS; ++j)
-                        acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fw[i], fa[j], acc[i][j], 0, 0, 0);
+                        for (int j = 0; j < MS; ++j)
+                            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fw[sk][i], fa_c[sk][j], acc[i][j], 0, 0, 0);
+                        if (more) read_w(kt + 1, sk, i);
+                    }
             }
-#pragma unroll
-            for (int p = 0; p < WPASS; ++p)
-                *reinterpret_cast<uint4*>(&s_w[cur ^ 1][(cp_row + 32 * p) * kPitch + cp_col]) = rw[p];
-#pragma unroll
-            for (int p = 0; p < APASS; ++p)
-                *reinterpret_cast<uint4*>(&s_a[cur ^ 1][(cp_row + 32 * p) * kPitch + cp_col]) = ra[p];
-            __syncthreads();
-        }
+        };
 
-        // epilogue: lane holds D[n = 16*i + 4*lg + q][m = 16*j + li], q = 0..3
+#pragma unroll
+        for (int s = 0; s < kStages; ++s) issue(s, s);
+        moe_bf16x8 fa0[2][MS], fa1[2][MS];
+        wait_vmcnt_barrier<GPW * (kStages - 1)>();
+        if (active) {
+            read_a(0, fa0);
+#pragma unroll
+            for (int sk = 0; sk < 2; ++sk)
+#pragma unroll
+                for (int i = 0; i < NS; ++i) read_w(0, sk, i);
+        }
+        int kt = 0;
+        for (; kt + 2 <= nk; kt += 2) {
+            step(kt, fa0, fa1);
+            step(kt + 1, fa1, fa0);
+        }
+        if (kt < nk) step(kt, fa0, fa1);
+        // drain the ring before the next tile refills it
+        wait_vmcnt_barrier<0>();
+
+        // epilogue: lane holds D[n = 8*p + 4*fh + u][m = fr] in acc[..][16p..] : q = 4p + u
 #pragma unroll
         for (int j = 0; j < MS; ++j) {
-            const int m = wm * WM + j * 16 + li;
+            const int m = wm * WM + j * 32 + fr;
             if (m >= mrows) continue;
             uint16_t* crow = C + (size_t)(r0 + m) * N;
             if (GATED) {
 #pragma unroll
-                for (int i = 0; i < NS / 2; ++i) {
-                    const int col = n_tile * COLS + wn * (WN / 2) + i * 16 + lg * 4;
-                    uint16_t hv[4];
+                for (int i = 0; i < NS / 2; ++i)
 #pragma unroll
-                    for (int q = 0; q < 4; ++q)
-                        hv[q] = moe_f32_to_bf16(silu_f32(acc[i][j][q]) * acc[i + NS / 2][j][q]);
-                    uint2 pk;
-                    pk.x = (uint32_t)hv[0] | ((uint32_t)hv[1] << 16);
-                    pk.y = (uint32_t)hv[2] | ((uint32_t)hv[3] << 16);
-                    *reinterpret_cast<uint2*>(crow + col) = pk;
-                }
+                    for (int p = 0; p < 4; ++p) {
+                        const int col = n_tile * COLS + wn * (WN / 2) + i * 32 + p * 8 + fh * 4;
+                        uint16_t hv[4];
+#pragma unroll
+                        for (int u = 0; u < 4; ++u)
+                            hv[u] = moe_f32_to_bf16(silu_f32(acc[i][j][4 * p + u]) * acc[i + NS / 2][j][4 * p + u]);
+                        uint2 pk;
+                        pk.x = (uint32_t)hv[0] | ((uint32_t)hv[1] << 16);
+                        pk.y = (uint32_t)hv[2] | ((uint32_t)hv[3] << 16);
+                        *reinterpret_cast<uint2*>(crow + col) = pk;
+                    }
             } else {
 #pragma unroll
-                for (int i = 0; i < NS; ++i) {
-                    const int col = n_tile * COLS + wn * WN + i * 16 + lg * 4;
-                    uint2 pk;
-                    pk.x = (uint32_t)moe_f32_to_bf16(acc[i][j][0]) | ((uint32_t)moe_f32_to_bf16(acc[i][j][1]) << 16);
-                    pk.y = (uint32_t)moe_f32_to_bf16(acc[i][j][2]) | ((uint32_t)moe_f32_to_bf16(acc[i][j][3]) << 16);
-                    *reinterpret_cast<uint2*>(crow + col) = pk;
-                }
+                for (int i = 0; i < NS; ++i)
+#pragma unroll
+                    for (int p = 0; p < 4; ++p) {
+                        const int col = n_tile * COLS + wn * WN + i * 32 + p * 8 + fh * 4;
+                        uint2 pk;
+                        pk.x = (uint32_t)moe_f32_to_bf16(acc[i][j][4 * p]) | ((uint32_t)moe_f32_to_bf16(acc[i][j][4 * p + 1]) << 16);
+                        pk.y = (uint32_t)moe_f32_to_bf16(acc[i][j][4 * p + 2]) | ((uint32_t)moe_f32_to_bf16(acc[i][j][4 * p + 3]) << 16);
+                        *reinterpret_cast<uint2*>(crow + col) = pk;
+                    }
             }
         }
     }
 }
 
-template <int BM, int BN, bool GATED>
+template <int BM, int BN, int WGM, int WGN, bool GATED>
 hipError_t launch_tiled(int grid, const uint16_t* A, const int32_t* row_src, int topk,
                         const int32_t* offsets, const uint16_t* W, uint16_t* C, int E, int Kd,
                         int N, hipStream_t st) {
-    hipLaunchKernelGGL((gemm_tiled_kernel<BM, BN, GATED>), dim3(grid), dim3(256), 0, st, A,
-                       row_src, topk, offsets, W, C, E, Kd, N);
+    hipLaunchKernelGGL((gemm_tiled_kernel<BM, BN, WGM, WGN, GATED>), dim3(grid),
+                       dim3(64 * WGM * WGN), 0, st, A, row_src, topk, offsets, W, C, E, Kd, N);
     return hipGetLastError();
 }
 
@@ -328,16 +422,33 @@ hipError_t launch_tiled(int grid, const uint16_t* A, const int32_t* row_src, int
 GemmPlan choose_plan(const Shape& s, int hint) {
     GemmPlan p{};
     int kind = hint;
-    if (kind < kSkinny || kind > kTiled128) {
+    if (kind < kSkinny || kind > kTiled256) {
         const double rows_per_expert = (double)s.T * s.K / (double)s.E;
-        kind = rows_per_expert <= 24.0 ? kSkinny : (rows_per_expert <= 96.0 ? kTiled64 : kTiled128);
+        kind = rows_per_expert <= 24.0 ? kSkinny
+             : rows_per_expert <= 96.0 ? kTiled64 : kTiled256;
     }
     p.kind = kind;
     if (kind == kSkinny) {
         p.grid_gateup = p.grid_down = 4 * kNumCUs;
         p.bn_gateup = p.bn_down = 16;
+    } else if (kind == kTiled256) {
+        // gate-up: 128 gate + 128 up rows; down: 256 or 128 weight rows,
+        // whichever fills the last round of tiles better
+        p.bn_gateup = (s.I % 128 == 0) ? 256 : 128;
+        p.bn_down = (s.H % 128 == 0) ? 128 : 64;
+        if (s.H % 256 == 0) {
+            // expected m-tiles, with slack for experts that land just above a
+            // multiple of 256 rows (their last tile is nearly empty)
+            const double m_tiles = s.E * std::ceil(1.05 * s.T * s.K / s.E / 256.0);
+            auto fill = [&](int bn) {
+                const double t = m_tiles * (s.H / bn);
+                return t / (std::ceil(t / kNumCUs) * kNumCUs);
+            };
+            if (fill(256) >= 0.9 * fill(128)) p.bn_down = 256;
+        }
+        p.grid_gateup = p.grid_down = kNumCUs;
     } else {
-        p.bn_gateup = (s.I % 64 == 0) ? 128 : 64;   // 64 gate + 64 up rows
+        p.bn_gateup = 128;                          // 64 gate + 64 up rows
         p.bn_down = (s.H % 128 == 0) ? 128 : 64;
         p.grid_gateup = p.grid_down = 2 * kNumCUs;
     }
@@ -349,26 +460,30 @@ hipError_t launch_grouped_gemm(const Shape& s, const GemmPlan& plan, bool gated,
                                const int32_t* offsets, const uint16_t* W, uint16_t* C, int Kd,
                                int N, hipStream_t st) {
     const int grid = gated ? plan.grid_gateup : plan.grid_down;
-    if (plan.kind == kSkinny) {
-        if (gated)
-            hipLaunchKernelGGL(gemm_skinny_kernel<true>, dim3(grid), dim3(256), 0, st, A, row_src,
-                               topk, offsets, W, C, s.E, Kd, N);
-        else
-            hipLaunchKernelGGL(gemm_skinny_kernel<false>, dim3(grid), dim3(256), 0, st, A, row_src,
-                               topk, offsets, W, C, s.E, Kd, N);
-        return hipGetLastError();
-    }
     const int bn = gated ? plan.bn_gateup : plan.bn_down;
-    if (plan.kind == kTiled64) {
-        if (gated) return bn == 128 ? launch_tiled<64, 128, true>(grid, A, row_src, topk, offsets, W, C, s.E, Kd, N, st)
-                                    : launch_tiled<64, 64, true>(grid, A, row_src, topk, offsets, W, C, s.E, Kd, N, st);
-        return bn == 128 ? launch_tiled<64, 128, false>(grid, A, row_src, topk, offsets, W, C, s.E, Kd, N, st)
-                         : launch_tiled<64, 64, false>(grid, A, row_src, topk, offsets, W, C, s.E, Kd, N, st);
+#define MOE_TILED(BM, BN, WGM, WGN, G) \
+    launch_tiled<BM, BN, WGM, WGN, G>(grid, A, row_src, topk, offsets, W, C, s.E, Kd, N, st)
+    switch (plan.kind) {
+        case kSkinny:
+            if (gated)
+                hipLaunchKernelGGL(gemm_skinny_kernel<true>, dim3(grid), dim3(256), 0, st, A,
+                                   row_src, topk, offsets, W, C, s.E, Kd, N);
+            else
+                hipLaunchKernelGGL(gemm_skinny_kernel<false>, dim3(grid), dim3(256), 0, st, A,
+                                   row_src, topk, offsets, W, C, s.E, Kd, N);
+            return hipGetLastError();
+        case kTiled64:
+            if (gated) return MOE_TILED(64, 128, 2, 2, true);
+            return bn == 128 ? MOE_TILED(64, 128, 2, 2, false) : MOE_TILED(64, 64, 2, 2, false);
+        case kTiled128:
+            if (gated) return MOE_TILED(128, 128, 2, 2, true);
+            return bn == 128 ? MOE_TILED(128, 128, 2, 2, false) : MOE_TILED(128, 64, 2, 2, false);
+        default:
+            if (gated) return bn == 256 ? MOE_TILED(256, 256, 4, 2, true) : MOE_TILED(256, 128, 4, 2, true);
+            return bn == 256 ? MOE_TILED(256, 256, 4, 2, false)
+                 : bn == 128 ? MOE_TILED(256, 128, 4, 2, false) : MOE_TILED(128, 64, 2, 2, false);
     }
-    if (gated) return bn == 128 ? launch_tiled<128, 128, true>(grid, A, row_src, topk, offsets, W, C, s.E, Kd, N, st)
-                                : launch_tiled<128, 64, true>(grid, A, row_src, topk, offsets, W, C, s.E, Kd, N, st);
-    return bn == 128 ? launch_tiled<128, 128, false>(grid, A, row_src, topk, offsets, W, C, s.E, Kd, N, st)
-                     : launch_tiled<128, 64, false>(grid, A, row_src, topk, offsets, W, C, s.E, Kd, N, st);
+#undef MOE_TILED
 }
 
 }  // namespace moe

@@ -19,7 +19,7 @@ struct Shape {
 };
 
 // Grouped-GEMM plan, chosen on the host from host-known sizes only.
-enum GemmKind { kSkinny = 1, kTiled64 = 2, kTiled128 = 3 };
+enum GemmKind { kSkinny = 1, kTiled64 = 2, kTiled128 = 3, kTiled256 = 4 };
 struct GemmPlan {
     int kind;
     int grid_gateup, grid_down;

@@ -23,9 +23,10 @@ Sources (page title, then section):
     the last entry of expert_offsets is the valid-row count kept on the GPU,
     capacity-tail values are unspecified.  Review follow-up: gate/value
     pointwise epilogue after the gate-up grouped GEMM, then the down GEMM.
-  * FlashInfer PR #3980, Summary: one (tokens, hidden) output with the top-k
-    combine reduced inside the layer; Accuracy: checked against a dense
-    ground truth over all experts.
+  * FlashInfer PR #3980, commit notes on the kernel API migration
+    (launch/output): one (tokens, hidden) output with the top-k combine
+    reduced inside the layer; Accuracy: checked against a dense fp32 ground
+    truth over all experts.
 
 Readings where the pages leave a step open (the plainest one the rest
 supports): W_gateup holds the gate rows first and the up rows second
@@ -173,7 +174,7 @@ def expert_compute(x_disp, expert_offsets, w_gateup, w_down, rows=None):
 
 
 # ---------------------------------------------------------------------------
-# Weighted top-k combine (TileOps PR #1738 Summary; FlashInfer PR #3980 Summary)
+# Weighted top-k combine (TileOps PR #1738 Summary; FlashInfer PR #3980 API notes)
 # ---------------------------------------------------------------------------
 def combine(y_rows, token_row, topk_weights, num_valid_tokens: int | None = None):
     """out[t,:] = sum_j w[t,j] * y_rows[token_row[t*K+j], :] over the j with a
