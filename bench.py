@@ -127,8 +127,10 @@ def main():
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--hint", type=int, default=0, help="grouped-GEMM plan (0 auto, 1-4 forced)")
     ap.add_argument("--cold", action="store_true",
-                    help="overwrite a 512 MiB buffer before each step (outside the timed "
-                         "events) so weights are read from HBM, not L2/MALL")
+                    help="read a 1 GiB buffer before each step (outside the timed events) so "
+                         "the weights come from HBM, not L2/MALL")
+    ap.add_argument("--graph", action="store_true",
+                    help="time replays of the layer recorded as a HIP graph (moe_graph_*)")
     ap.add_argument("--kernel-reps", type=int, default=10)
     ap.add_argument("--cpu-tokens", type=int, default=None,
                     help="tokens in the oracle's timed sample (default by workload)")
@@ -163,10 +165,22 @@ def main():
     ws = ops.make_workspace(p, dev)
     out = torch.empty((T, H), dtype=torch.bfloat16, device=dev)
     off = torch.empty((E + 1,), dtype=torch.int32, device=dev)
-    scratch = torch.empty((512 << 20,), dtype=torch.uint8, device=dev) if args.cold else None
+    scratch = torch.ones((1 << 29,), dtype=torch.float16, device=dev) if args.cold else None
+
+    def evict():
+        # a read-only sweep: leaves L2/MALL full of clean lines of another buffer
+        if scratch is not None:
+            scratch.max()
+
+    graph = None
+    if args.graph:
+        graph = ops.MoEGraph(p, x, ids, w, wgu, wd, expert_offsets=off, out=out, workspace=ws)
 
     def step():
-        ops.forward(p, x, ids, w, wgu, wd, expert_offsets=off, out=out, workspace=ws)
+        if graph is not None:
+            graph.launch()
+        else:
+            ops.forward(p, x, ids, w, wgu, wd, expert_offsets=off, out=out, workspace=ws)
 
     for _ in range(args.warmup):
         step()
@@ -184,8 +198,7 @@ def main():
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(args.steps):
-        if scratch is not None:
-            scratch.fill_(i & 0xFF)
+        evict()
         ev[i][0].record(stream)
         step()
         ev[i][1].record(stream)
@@ -203,8 +216,7 @@ def main():
            for _ in range(args.kernel_reps)]
     torch.cuda.synchronize()
     for i in range(args.kernel_reps):
-        if scratch is not None:
-            scratch.fill_(i & 0xFF)
+        evict()
         kev[i][0].record(stream)
         ops.gate_up(p, x_disp, off2, wgu, h=hbuf)
         kev[i][1].record(stream)
@@ -251,8 +263,10 @@ def main():
         "config": {"workload": describe(cfg), "tokens": T, "top_k": K, "experts": E,
                    "global_experts": cfg.pool, "hidden": H, "intermediate": I,
                    "capacity": p.capacity or T * K, "valid_rows": R, "experts_touched": touched,
-                   "seed": args.seed, "timing": "cold (L2/MALL evicted per step)" if args.cold
-                   else "back-to-back", "kernel_hint": args.hint},
+                   "seed": args.seed, "timing": ("cold (L2/MALL evicted per step)" if args.cold
+                                                 else "back-to-back")
+                   + (", HIP graph replay" if args.graph else ", eager launches"),
+                   "kernel_hint": args.hint},
         "roofline": roof,
     }
     if not args.no_cpu_baseline:

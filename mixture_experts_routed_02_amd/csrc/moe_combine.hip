@@ -7,9 +7,12 @@
 // out[t,:] = bf16( sum over j = 0..K-1 with token_row[t*K+j] >= 0 of
 //                  w[t,j] * y[token_row[t*K+j], :] ),  fp32 fused multiply-adds
 // in increasing j, one round-to-nearest-even at the end; a zero row when no
-// assignment of t is valid; rows t >= T_v are not written.  Each token is
-// owned by one workgroup, so there are no atomics and the result is
-// bit-reproducible.  Loads and stores are 16 bytes (8 bf16) per lane.
+// assignment of t is valid; rows t >= T_v are not written.  Each output
+// vector (8 bf16) is owned by one thread, so there are no atomics and the
+// result is bit-reproducible.  A workgroup covers 256 vectors of one token
+// (blockIdx.y strides over tokens); each thread issues the loads of all of
+// its token's rows before it accumulates, so a small batch costs about one
+// memory round trip.
 #include "moe_internal.h"
 
 namespace moe {
@@ -17,6 +20,7 @@ namespace {
 
 constexpr int kCombineThreads = 256;
 constexpr int kMaxTopK = 64;
+constexpr int kCombineUnroll = 8;   // rows loaded together
 
 __global__ __launch_bounds__(kCombineThreads) void combine_kernel(
     const uint4* __restrict__ y, const int32_t* __restrict__ token_row,
@@ -25,24 +29,34 @@ __global__ __launch_bounds__(kCombineThreads) void combine_kernel(
     __shared__ int s_row[kMaxTopK];
     __shared__ float s_w[kMaxTopK];
     const int tv = moe_valid_tokens(ntok, T);
-    for (int t = blockIdx.x; t < tv; t += gridDim.x) {
+    const int c = blockIdx.x * kCombineThreads + threadIdx.x;
+    for (int t = blockIdx.y; t < tv; t += gridDim.y) {
         if (threadIdx.x < K) {
             s_row[threadIdx.x] = token_row[(long long)t * K + threadIdx.x];
             s_w[threadIdx.x] = w[(long long)t * K + threadIdx.x];
         }
         __syncthreads();
-        for (int c = threadIdx.x; c < vec; c += blockDim.x) {
+        if (c < vec) {
             float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-            for (int j = 0; j < K; ++j) {
-                const int r = s_row[j];
-                if (r < 0) continue;
-                const float wj = s_w[j];
-                const uint4 v = y[(long long)r * vec + c];
-                const uint32_t pk[4] = {v.x, v.y, v.z, v.w};
+            for (int j0 = 0; j0 < K; j0 += kCombineUnroll) {
+                uint4 v[kCombineUnroll];
 #pragma unroll
-                for (int q = 0; q < 4; ++q) {
-                    acc[2 * q] = fmaf(wj, __uint_as_float(pk[q] << 16), acc[2 * q]);
-                    acc[2 * q + 1] = fmaf(wj, __uint_as_float(pk[q] & 0xffff0000u), acc[2 * q + 1]);
+                for (int u = 0; u < kCombineUnroll; ++u) {
+                    const int j = j0 + u;
+                    const int r = j < K ? s_row[j] : -1;
+                    v[u] = r >= 0 ? y[(long long)r * vec + c] : make_uint4(0u, 0u, 0u, 0u);
+                }
+#pragma unroll
+                for (int u = 0; u < kCombineUnroll; ++u) {
+                    const int j = j0 + u;
+                    if (j >= K || s_row[j] < 0) continue;
+                    const float wj = s_w[j];
+                    const uint32_t pk[4] = {v[u].x, v[u].y, v[u].z, v[u].w};
+#pragma unroll
+                    for (int q = 0; q < 4; ++q) {
+                        acc[2 * q] = fmaf(wj, __uint_as_float(pk[q] << 16), acc[2 * q]);
+                        acc[2 * q + 1] = fmaf(wj, __uint_as_float(pk[q] & 0xffff0000u), acc[2 * q + 1]);
+                    }
                 }
             }
             uint4 o;
@@ -60,10 +74,12 @@ __global__ __launch_bounds__(kCombineThreads) void combine_kernel(
 
 hipError_t launch_combine(const Shape& s, const uint16_t* y, const int32_t* token_row,
                           const float* w, const int32_t* ntok, uint16_t* out, hipStream_t st) {
-    int grid = s.T < 8 * kNumCUs ? s.T : 8 * kNumCUs;
-    if (grid < 1) grid = 1;
-    hipLaunchKernelGGL(combine_kernel, dim3(grid), dim3(kCombineThreads), 0, st,
-                       reinterpret_cast<const uint4*>(y), token_row, w, ntok, s.T, s.K, s.H / 8,
+    const int vec = s.H / 8;
+    const int gx = (vec + kCombineThreads - 1) / kCombineThreads;
+    int gy = s.T < 65535 ? s.T : 65535;
+    if (gy < 1) gy = 1;
+    hipLaunchKernelGGL(combine_kernel, dim3(gx, gy), dim3(kCombineThreads), 0, st,
+                       reinterpret_cast<const uint4*>(y), token_row, w, ntok, s.T, s.K, vec,
                        reinterpret_cast<uint4*>(out));
     return hipGetLastError();
 }

@@ -61,8 +61,17 @@ __device__ __forceinline__ int find_expert(const int* s_start, int E, int tile) 
 // Tile = 16 weight rows x 16 token rows x the whole K, split over the 4 waves
 // of the workgroup (contiguous k ranges), reduced through LDS in wave order.
 // gated: the 16 weight rows are 8 gate rows and the 8 matching up rows, so a
-// tile produces 8 output columns; plain: 16 output columns.
+// tile produces 8 output columns; plain: 16 output columns.  Each wave keeps
+// two blocks of 8 k-steps (16 KB of weights) in flight: the next block is
+// loaded while the current one is multiplied.  Token rows past the expert's
+// valid rows load a valid row and are zeroed in registers (no branches).
 // ---------------------------------------------------------------------------
+constexpr int kSkU = 8;   // k-steps (of 32) per block
+
+// Plain loads: measured on the device, marking these one-use weight loads
+// non-temporal made the decode workloads 8-20% slower.
+__device__ __forceinline__ moe_bf16x8 stream_load(const moe_bf16x8* p) { return *p; }
+
 template <bool GATED>
 __global__ __launch_bounds__(256) void gemm_skinny_kernel(
     const uint16_t* __restrict__ A, const int32_t* __restrict__ row_src, int topk,
@@ -82,6 +91,8 @@ __global__ __launch_bounds__(256) void gemm_skinny_kernel(
 
     const int ksteps = Kd / 32;
     const int ks0 = (wave * ksteps) / 4, ks1 = ((wave + 1) * ksteps) / 4;
+    const int nblk = (ks1 - ks0) / kSkU;             // full blocks; the rest is a tail
+    const moe_bf16x8 zero = {};
 
     for (int tile = blockIdx.x; tile < total; tile += gridDim.x) {
         const int e = find_expert(s_start, E, tile);
@@ -96,29 +107,55 @@ __global__ __launch_bounds__(256) void gemm_skinny_kernel(
         int wrow;
         if (GATED) wrow = (li < 8) ? (n_tile * 8 + li) : (N + n_tile * 8 + (li - 8));
         else wrow = n_tile * 16 + li;
-        const uint16_t* wp = W + ((size_t)e * w_rows + wrow) * (size_t)Kd + lg * 8;
+        const moe_bf16x8* wp = reinterpret_cast<const moe_bf16x8*>(
+            W + ((size_t)e * w_rows + wrow) * (size_t)Kd + (size_t)ks0 * 32 + lg * 8);
+
+        moe_bf16x8 wa[kSkU], wb[kSkU], xa[kSkU], xb[kSkU];
+        // first weight block before the (dependent) row_src lookup
+        if (nblk > 0) {
+#pragma unroll
+            for (int u = 0; u < kSkU; ++u) wa[u] = stream_load(wp + u * 4);
+        }
         const bool mvalid = li < mrows;
         const int rr = r0 + (mvalid ? li : 0);
         const long long arow = row_src ? (long long)(row_src[rr] / topk) : (long long)rr;
-        const uint16_t* ap = A + (size_t)arow * Kd + lg * 8;
-
+        const moe_bf16x8* ap = reinterpret_cast<const moe_bf16x8*>(
+            A + (size_t)arow * Kd + (size_t)ks0 * 32 + lg * 8);
+        auto load_x = [&](moe_bf16x8* xv, int b) {
+#pragma unroll
+            for (int u = 0; u < kSkU; ++u) {
+                const moe_bf16x8 v = ap[(b * kSkU + u) * 4];
+                xv[u] = mvalid ? v : zero;
+            }
+        };
+        auto load_w = [&](moe_bf16x8* wv, int b) {
+#pragma unroll
+            for (int u = 0; u < kSkU; ++u) wv[u] = stream_load(wp + (b * kSkU + u) * 4);
+        };
         moe_f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-        const moe_bf16x8 zero = {};
-        int ks = ks0;
-        for (; ks + 8 <= ks1; ks += 8) {
-            moe_bf16x8 wv[8], av[8];
+        auto mma = [&](const moe_bf16x8* wv, const moe_bf16x8* xv) {
 #pragma unroll
-            for (int u = 0; u < 8; ++u) wv[u] = load16(wp + (size_t)(ks + u) * 32);
-#pragma unroll
-            for (int u = 0; u < 8; ++u) av[u] = mvalid ? load16(ap + (size_t)(ks + u) * 32) : zero;
-#pragma unroll
-            for (int u = 0; u < 8; ++u)
-                acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wv[u], av[u], acc, 0, 0, 0);
+            for (int u = 0; u < kSkU; ++u)
+                acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wv[u], xv[u], acc, 0, 0, 0);
+        };
+        if (nblk > 0) load_x(xa, 0);
+        int b = 0;
+        for (; b + 2 <= nblk; b += 2) {
+            load_w(wb, b + 1);
+            load_x(xb, b + 1);
+            mma(wa, xa);
+            if (b + 2 < nblk) {
+                load_w(wa, b + 2);
+                load_x(xa, b + 2);
+            }
+            mma(wb, xb);
         }
-        for (; ks < ks1; ++ks) {
-            const moe_bf16x8 wv = load16(wp + (size_t)ks * 32);
-            const moe_bf16x8 av = mvalid ? load16(ap + (size_t)ks * 32) : zero;
-            acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wv, av, acc, 0, 0, 0);
+        if (b < nblk) mma(wa, xa);
+        for (int ks = ks0 + nblk * kSkU; ks < ks1; ++ks) {   // tail k-steps
+            const int o = (ks - ks0) * 4;
+            const moe_bf16x8 v = ap[o];
+            acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(stream_load(wp + o),
+                                                         mvalid ? v : zero, acc, 0, 0, 0);
         }
 
 #pragma unroll
@@ -429,7 +466,7 @@ GemmPlan choose_plan(const Shape& s, int hint) {
     }
     p.kind = kind;
     if (kind == kSkinny) {
-        p.grid_gateup = p.grid_down = 4 * kNumCUs;
+        p.grid_gateup = p.grid_down = 3 * kNumCUs;   // 3 workgroups fit per CU
         p.bn_gateup = p.bn_down = 16;
     } else if (kind == kTiled256) {
         // gate-up: 128 gate + 128 up rows; down: 256 or 128 weight rows,
@@ -437,9 +474,7 @@ GemmPlan choose_plan(const Shape& s, int hint) {
         p.bn_gateup = (s.I % 128 == 0) ? 256 : 128;
         p.bn_down = (s.H % 128 == 0) ? 128 : 64;
         if (s.H % 256 == 0) {
-            // expected m-tiles, with slack for experts that land just above a
-            // multiple of 256 rows (their last tile is nearly empty)
-            const double m_tiles = s.E * std::ceil(1.05 * s.T * s.K / s.E / 256.0);
+            const double m_tiles = s.E * std::ceil((double)s.T * s.K / s.E / 256.0);
             auto fill = [&](int bn) {
                 const double t = m_tiles * (s.H / bn);
                 return t / (std::ceil(t / kNumCUs) * kNumCUs);
