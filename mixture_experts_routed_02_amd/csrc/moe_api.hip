@@ -119,11 +119,22 @@ moe_status_t forward_impl(const Shape& s, int hint, const uint16_t* x, const int
     int32_t* token_row = at<int32_t>(ws, L.token_row);
     uint16_t* h = at<uint16_t>(ws, L.h);
     uint16_t* y = at<uint16_t>(ws, L.y);
-    if (moe::launch_dispatch(s, ids, ntok, offsets, row_src, token_row, counts, st) != hipSuccess)
-        return MOE_ERROR_LAUNCH;
     const GemmPlan plan = moe::choose_plan(s, hint);
-    moe_status_t r = expert_compute_impl(s, plan, x, row_src, offsets, wgu, wd, h, y, st);
-    if (r != MOE_SUCCESS) return r;
+    if (plan.kind == moe::kSkinny && (long long)s.T * s.K <= moe::kFusedDispatchMax) {
+        // small batch: the gate-up kernel does the dispatch itself (one launch fewer)
+        if (moe::launch_gateup_fused_dispatch(s, plan, x, ids, ntok, offsets, row_src, token_row,
+                                              wgu, h, st) != hipSuccess)
+            return MOE_ERROR_LAUNCH;
+        if (moe::launch_grouped_gemm(s, plan, false, h, nullptr, 1, offsets, wd, y, s.I, s.H, st) !=
+            hipSuccess)
+            return MOE_ERROR_LAUNCH;
+    } else {
+        if (moe::launch_dispatch(s, ids, ntok, offsets, row_src, token_row, counts, st) !=
+            hipSuccess)
+            return MOE_ERROR_LAUNCH;
+        moe_status_t r = expert_compute_impl(s, plan, x, row_src, offsets, wgu, wd, h, y, st);
+        if (r != MOE_SUCCESS) return r;
+    }
     if (s.T == 0) return MOE_SUCCESS;
     return launched(moe::launch_combine(s, y, token_row, w, ntok, out, st));
 }

@@ -97,39 +97,15 @@ __global__ __launch_bounds__(kDispatchThreads) void dispatch_scatter_kernel(
             int v = ids[a];
             if (v >= 0 && v < E) e = v;
         }
-        int rank = 0;
-        unsigned long long rem = __ballot(e >= 0);
-        while (rem) {
-            const int leader = __ffsll((long long)rem) - 1;
-            const int ve = __shfl(e, leader, 64);
-            const unsigned long long m = __ballot(e == ve);
-            if (e == ve) rank = __popcll(m & ((1ull << lane) - 1ull));
-            if (lane == leader) s_wcnt[wave * E + ve] = __popcll(m);
-            rem &= ~m;
-        }
-        __syncthreads();
-        for (int x = tid; x < E; x += blockDim.x) {  // counts -> bases, wave order
-            int run = s_base[x];
-            for (int w = 0; w < kWaves; ++w) {
-                int c = s_wcnt[w * E + x];
-                s_wcnt[w * E + x] = run;
-                run += c;
-            }
-            s_base[x] = run;
-        }
-        __syncthreads();
+        const int r = moe_stable_rows(e, E, s_wcnt, s_base);
         if (in) {
-            if (e >= 0) {
-                const int r = s_wcnt[wave * E + e] + rank;
+            if (r >= 0) {
                 row_src[r] = (int)a;
                 token_row[a] = r;
             } else {
                 token_row[a] = -1;
             }
         }
-        __syncthreads();
-        for (int i = tid; i < kWaves * E; i += blockDim.x) s_wcnt[i] = 0;
-        __syncthreads();
     }
 }
 

@@ -35,7 +35,7 @@ __device__ __forceinline__ float silu_f32(float z) { return z / (1.0f + __expf(-
 
 // Tile table: s_start[e] = sum_{e' < e} ceil(M_e'/BM) * n_tiles, s_start[E] = total.
 template <int BM>
-__device__ __forceinline__ int build_tile_table(const int32_t* __restrict__ offsets, int E,
+__device__ __forceinline__ int build_tile_table(const int32_t* offsets, int E,
                                                 int n_tiles, int* s_start, int* s_wave) {
     for (int e = threadIdx.x; e < E; e += blockDim.x) {
         const int m = offsets[e + 1] - offsets[e];
@@ -58,30 +58,35 @@ __device__ __forceinline__ int find_expert(const int* s_start, int E, int tile) 
 
 // ---------------------------------------------------------------------------
 // Skinny kernel: weight-streaming regime (a handful of rows per expert).
-// Tile = 16 weight rows x 16 token rows x the whole K, split over the 4 waves
-// of the workgroup (contiguous k ranges), reduced through LDS in wave order.
-// gated: the 16 weight rows are 8 gate rows and the 8 matching up rows, so a
-// tile produces 8 output columns; plain: 16 output columns.  Each wave keeps
-// two blocks of 8 k-steps (16 KB of weights) in flight: the next block is
-// loaded while the current one is multiplied.  Token rows past the expert's
-// valid rows load a valid row and are zeroed in registers (no branches).
+// Tile = 16*RB weight rows x 16 token rows x the whole K, split over the 4
+// waves of the workgroup (contiguous k ranges), reduced through LDS in wave
+// order.  gated (RB = 1): the 16 weight rows are 8 gate rows and the 8
+// matching up rows, so a tile produces 8 output columns; plain: 16*RB output
+// columns (the down GEMM uses RB = 2 so that one token's tiles fill the
+// resident workgroups in one round).  Each wave keeps two blocks of weights
+// (16 KB) in flight: the next block is loaded while the current one is
+// multiplied.  Token rows past the expert's valid rows load a valid row and
+// are zeroed in registers (no branches).
 // ---------------------------------------------------------------------------
-constexpr int kSkU = 8;   // k-steps (of 32) per block
-
 // Plain loads: measured on the device, marking these one-use weight loads
 // non-temporal made the decode workloads 8-20% slower.
 __device__ __forceinline__ moe_bf16x8 stream_load(const moe_bf16x8* p) { return *p; }
 
-template <bool GATED>
-__global__ __launch_bounds__(256) void gemm_skinny_kernel(
-    const uint16_t* __restrict__ A, const int32_t* __restrict__ row_src, int topk,
-    const int32_t* __restrict__ offsets, const uint16_t* __restrict__ W,
-    uint16_t* __restrict__ C, int E, int Kd, int N) {
+// RB = 16-row weight blocks per tile (1 or 2; gated tiles use 1).  Blocks of
+// U k-steps keep RB * U KB of weights in flight per wave and per buffer.
+// offsets and rows may point to global memory or LDS; s_red is
+// [4 waves][16*RB rows][17].
+template <bool GATED, int RB>
+__device__ __forceinline__ void skinny_tiles(const uint16_t* __restrict__ A, const int32_t* rows,
+                                             int topk, const int32_t* offsets,
+                                             const uint16_t* __restrict__ W,
+                                             uint16_t* __restrict__ C, int E, int Kd, int N,
+                                             int* s_start, int* s_wave, float* s_red) {
+    static_assert(RB == 1 || (RB == 2 && !GATED), "tile rows");
     constexpr int BM = 16;
-    constexpr int COLS = GATED ? 8 : 16;
-    __shared__ int s_start[kMaxExperts + 1];
-    __shared__ int s_wave[4];
-    __shared__ float s_red[4][16][17];
+    constexpr int U = 8 / RB;                      // k-steps (of 32) per block
+    constexpr int COLS = GATED ? 8 : 16 * RB;
+    constexpr int RED_ROWS = 16 * RB;
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int li = lane & 15, lg = lane >> 4;
@@ -91,7 +96,7 @@ __global__ __launch_bounds__(256) void gemm_skinny_kernel(
 
     const int ksteps = Kd / 32;
     const int ks0 = (wave * ksteps) / 4, ks1 = ((wave + 1) * ksteps) / 4;
-    const int nblk = (ks1 - ks0) / kSkU;             // full blocks; the rest is a tail
+    const int nblk = (ks1 - ks0) / U;              // full blocks; the rest is a tail
     const moe_bf16x8 zero = {};
 
     for (int tile = blockIdx.x; tile < total; tile += gridDim.x) {
@@ -104,39 +109,46 @@ __global__ __launch_bounds__(256) void gemm_skinny_kernel(
         const int r0 = row0 + m_tile * BM;
         const int mrows = (me - m_tile * BM) < BM ? (me - m_tile * BM) : BM;
 
-        int wrow;
-        if (GATED) wrow = (li < 8) ? (n_tile * 8 + li) : (N + n_tile * 8 + (li - 8));
-        else wrow = n_tile * 16 + li;
-        const moe_bf16x8* wp = reinterpret_cast<const moe_bf16x8*>(
-            W + ((size_t)e * w_rows + wrow) * (size_t)Kd + (size_t)ks0 * 32 + lg * 8);
-
-        moe_bf16x8 wa[kSkU], wb[kSkU], xa[kSkU], xb[kSkU];
-        // first weight block before the (dependent) row_src lookup
-        if (nblk > 0) {
+        const moe_bf16x8* wp[RB];
 #pragma unroll
-            for (int u = 0; u < kSkU; ++u) wa[u] = stream_load(wp + u * 4);
+        for (int rb = 0; rb < RB; ++rb) {
+            int wrow;
+            if (GATED) wrow = (li < 8) ? (n_tile * 8 + li) : (N + n_tile * 8 + (li - 8));
+            else wrow = n_tile * COLS + rb * 16 + li;
+            wp[rb] = reinterpret_cast<const moe_bf16x8*>(
+                W + ((size_t)e * w_rows + wrow) * (size_t)Kd + (size_t)ks0 * 32 + lg * 8);
         }
+
+        moe_bf16x8 wa[RB][U], wb[RB][U], xa[U], xb[U];
+        auto load_w = [&](moe_bf16x8 (*wv)[U], int b) {
+#pragma unroll
+            for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+                for (int u = 0; u < U; ++u) wv[rb][u] = stream_load(wp[rb] + (b * U + u) * 4);
+        };
+        // first weight block before the (dependent) row lookup
+        if (nblk > 0) load_w(wa, 0);
         const bool mvalid = li < mrows;
         const int rr = r0 + (mvalid ? li : 0);
-        const long long arow = row_src ? (long long)(row_src[rr] / topk) : (long long)rr;
+        const long long arow = rows ? (long long)(rows[rr] / topk) : (long long)rr;
         const moe_bf16x8* ap = reinterpret_cast<const moe_bf16x8*>(
             A + (size_t)arow * Kd + (size_t)ks0 * 32 + lg * 8);
         auto load_x = [&](moe_bf16x8* xv, int b) {
 #pragma unroll
-            for (int u = 0; u < kSkU; ++u) {
-                const moe_bf16x8 v = ap[(b * kSkU + u) * 4];
+            for (int u = 0; u < U; ++u) {
+                const moe_bf16x8 v = ap[(b * U + u) * 4];
                 xv[u] = mvalid ? v : zero;
             }
         };
-        auto load_w = [&](moe_bf16x8* wv, int b) {
+        moe_f32x4 acc[RB];
 #pragma unroll
-            for (int u = 0; u < kSkU; ++u) wv[u] = stream_load(wp + (b * kSkU + u) * 4);
-        };
-        moe_f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-        auto mma = [&](const moe_bf16x8* wv, const moe_bf16x8* xv) {
+        for (int rb = 0; rb < RB; ++rb) acc[rb] = (moe_f32x4){0.f, 0.f, 0.f, 0.f};
+        auto mma = [&](moe_bf16x8 (*wv)[U], const moe_bf16x8* xv) {
 #pragma unroll
-            for (int u = 0; u < kSkU; ++u)
-                acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wv[u], xv[u], acc, 0, 0, 0);
+            for (int u = 0; u < U; ++u)
+#pragma unroll
+                for (int rb = 0; rb < RB; ++rb)
+                    acc[rb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wv[rb][u], xv[u], acc[rb], 0, 0, 0);
         };
         if (nblk > 0) load_x(xa, 0);
         int b = 0;
@@ -151,15 +163,20 @@ __global__ __launch_bounds__(256) void gemm_skinny_kernel(
             mma(wb, xb);
         }
         if (b < nblk) mma(wa, xa);
-        for (int ks = ks0 + nblk * kSkU; ks < ks1; ++ks) {   // tail k-steps
+        for (int ks = ks0 + nblk * U; ks < ks1; ++ks) {   // tail k-steps
             const int o = (ks - ks0) * 4;
             const moe_bf16x8 v = ap[o];
-            acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(stream_load(wp + o),
-                                                         mvalid ? v : zero, acc, 0, 0, 0);
+            const moe_bf16x8 xv = mvalid ? v : zero;
+#pragma unroll
+            for (int rb = 0; rb < RB; ++rb)
+                acc[rb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(stream_load(wp[rb] + o), xv, acc[rb], 0, 0, 0);
         }
 
+        auto red = [&](int w, int row, int m) -> float& { return s_red[(w * RED_ROWS + row) * 17 + m]; };
 #pragma unroll
-        for (int i = 0; i < 4; ++i) s_red[wave][4 * lg + i][li] = acc[i];
+        for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) red(wave, rb * 16 + 4 * lg + i, li) = acc[rb][i];
         __syncthreads();
         if (GATED) {
             if (tid < 128) {
@@ -167,21 +184,89 @@ __global__ __launch_bounds__(256) void gemm_skinny_kernel(
                 if (m < mrows) {
                     float g = 0.f, u = 0.f;
 #pragma unroll
-                    for (int w = 0; w < 4; ++w) { g += s_red[w][c][m]; u += s_red[w][8 + c][m]; }
+                    for (int w = 0; w < 4; ++w) { g += red(w, c, m); u += red(w, 8 + c, m); }
                     C[(size_t)(r0 + m) * N + n_tile * 8 + c] = moe_f32_to_bf16(silu_f32(g) * u);
                 }
             }
         } else {
             const int m = tid >> 4, c = tid & 15;
             if (m < mrows) {
-                float y = 0.f;
 #pragma unroll
-                for (int w = 0; w < 4; ++w) y += s_red[w][c][m];
-                C[(size_t)(r0 + m) * N + n_tile * 16 + c] = moe_f32_to_bf16(y);
+                for (int rb = 0; rb < RB; ++rb) {
+                    float y = 0.f;
+#pragma unroll
+                    for (int w = 0; w < 4; ++w) y += red(w, rb * 16 + c, m);
+                    C[(size_t)(r0 + m) * N + n_tile * COLS + rb * 16 + c] = moe_f32_to_bf16(y);
+                }
             }
         }
         __syncthreads();
     }
+}
+
+template <bool GATED, int RB>
+__global__ __launch_bounds__(256) void gemm_skinny_kernel(
+    const uint16_t* __restrict__ A, const int32_t* __restrict__ row_src, int topk,
+    const int32_t* __restrict__ offsets, const uint16_t* __restrict__ W,
+    uint16_t* __restrict__ C, int E, int Kd, int N) {
+    __shared__ int s_start[kMaxExperts + 1];
+    __shared__ int s_wave[4];
+    __shared__ float s_red[4 * 16 * RB * 17];
+    skinny_tiles<GATED, RB>(A, row_src, topk, offsets, W, C, E, Kd, N, s_start, s_wave, s_red);
+}
+
+// Gate-up GEMM of the skinny plan with the local dispatch done inside (for
+// T*K <= kFusedDispatchMax): every workgroup counts, scans and ranks the
+// assignments in LDS exactly as the dispatch kernels do, then runs its gate-up
+// tiles from that LDS copy; workgroup 0 also publishes expert_offsets, row_src
+// and token_row for the down GEMM and the combine.  This saves a launch in
+// the latency-bound small-batch regime.
+__global__ __launch_bounds__(256) void gemm_skinny_gateup_dispatch_kernel(
+    const uint16_t* __restrict__ x, const int32_t* __restrict__ ids,
+    const int32_t* __restrict__ ntok, int T, int topk, int E, int32_t* __restrict__ offsets,
+    int32_t* __restrict__ row_src, int32_t* __restrict__ token_row,
+    const uint16_t* __restrict__ W, uint16_t* __restrict__ C, int Kd, int N) {
+    __shared__ int s_off[kMaxExperts + 1];   // counts -> exclusive offsets
+    __shared__ int s_base[kMaxExperts];
+    __shared__ int s_wc[4 * kMaxExperts];
+    __shared__ int s_rows[kFusedDispatchMax];
+    __shared__ int s_start[kMaxExperts + 1];
+    __shared__ int s_wave[4];
+    __shared__ float s_red[4 * 16 * 17];
+
+    const int tid = threadIdx.x;
+    const bool publish = blockIdx.x == 0;
+    const int tv = moe_valid_tokens(ntok, T);
+    const int nvalid = tv * topk, ntotal = T * topk;
+    for (int e = tid; e < E; e += blockDim.x) s_off[e] = 0;
+    for (int i = tid; i < 4 * E; i += blockDim.x) s_wc[i] = 0;
+    __syncthreads();
+    for (int a = tid; a < nvalid; a += blockDim.x) {
+        const int e = ids[a];
+        if (e >= 0 && e < E) atomicAdd(&s_off[e], 1);  // integer counts: order-independent
+    }
+    __syncthreads();
+    moe_block_exclusive_scan(s_off, E, s_wave);
+    for (int e = tid; e < E; e += blockDim.x) s_base[e] = s_off[e];
+    if (publish)
+        for (int e = tid; e <= E; e += blockDim.x) offsets[e] = s_off[e];
+    __syncthreads();
+    for (int a0 = 0; a0 < ntotal; a0 += blockDim.x) {
+        const int a = a0 + tid;
+        int e = -1;
+        if (a < nvalid) {
+            const int v = ids[a];
+            if (v >= 0 && v < E) e = v;
+        }
+        const int r = moe_stable_rows(e, E, s_wc, s_base);
+        if (r >= 0) s_rows[r] = a;
+        if (publish && a < ntotal) {
+            token_row[a] = r;
+            if (r >= 0) row_src[r] = a;
+        }
+    }
+    __syncthreads();
+    skinny_tiles<true, 1>(x, s_rows, topk, s_off, W, C, E, Kd, N, s_start, s_wave, s_red);
 }
 
 // ---------------------------------------------------------------------------
@@ -263,7 +348,9 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_tiled_kernel(
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int wm = wave % WGM, wn = wave / WGM;
+    // token sub-tile index varies slowest across waves, so the waves that stay
+    // active on a ragged last m-tile sit on different SIMDs
+    const int wm = wave / WGN, wn = wave % WGN;
     const int n_tiles = N / COLS;
     const int w_rows = GATED ? 2 * N : N;
     const int total = build_tile_table<BM>(offsets, E, n_tiles, s_start, s_wave);
@@ -328,17 +415,18 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_tiled_kernel(
             if (GATED) return (tr < BN / 2) ? (n_tile * (BN / 2) + tr) : (N + n_tile * (BN / 2) + tr - BN / 2);
             return n_tile * BN + tr;
         };
-        auto issue = [&](int step, int buf) {
+        auto issue_one = [&](int step, int buf, int q) {
             const int ks = step < nk ? step : nk - 1;   // past the end: a harmless reload
+            const int g = wave + NW * q;
+            const uint32_t dst = ring0 + buf * STAGE + g * 1024;
+            const uint16_t* src =
+                (g < AG) ? asrc[q < TPW ? q : 0]
+                         : wbase + (size_t)wrow0(g) * Kd + ((g & 1) ? dma_chunk_odd : dma_chunk_even) * 8;
+            lds_dma16(src + (size_t)ks * kBK, dst);
+        };
+        auto issue = [&](int step, int buf) {
 #pragma unroll
-            for (int q = 0; q < GPW; ++q) {
-                const int g = wave + NW * q;
-                const uint32_t dst = ring0 + buf * STAGE + g * 1024;
-                const uint16_t* src =
-                    (g < AG) ? asrc[q < TPW ? q : 0]
-                             : wbase + (size_t)wrow0(g) * Kd + ((g & 1) ? dma_chunk_odd : dma_chunk_even) * 8;
-                lds_dma16(src + (size_t)ks * kBK, dst);
-            }
+            for (int q = 0; q < GPW; ++q) issue_one(step, buf, q);
         };
 
         moe_f32x16 acc[NS][MS];
@@ -370,12 +458,17 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_tiled_kernel(
         };
         // one step: wait until step kt+1 has landed, refill step kt's buffer
         // with step kt + kStages, multiply step kt while reading step kt+1
+        // The refill DMAs are spread between the MFMAs: issued in one burst
+        // after the barrier they would hold up every wave's first MFMA while
+        // the address unit works through them.
         auto step = [&](int kt, moe_bf16x8 (*fa_c)[MS], moe_bf16x8 (*fa_n)[MS]) {
             wait_vmcnt_barrier<GPW * (kStages - 2)>();
-            issue(kt + kStages, kt % kStages);
+            const int rbuf = kt % kStages;
             if (active) {
-                const bool more = kt + 1 < nk;
-                if (more) read_a(kt + 1, fa_n);
+                // step kt+1's fragments; on the last step this reads the ring's
+                // harmless reload and the values are never used (no branches
+                // between the MFMAs)
+                read_a(kt + 1, fa_n);
 #pragma unroll
                 for (int sk = 0; sk < 2; ++sk)
 #pragma unroll
@@ -383,8 +476,18 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_tiled_kernel(
 #pragma unroll
                         for (int j = 0; j < MS; ++j)
                             acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fw[sk][i], fa_c[sk][j], acc[i][j], 0, 0, 0);
-                        if (more) read_w(kt + 1, sk, i);
+                        read_w(kt + 1, sk, i);
+                        constexpr int SLOTS = 2 * NS;
+                        const int slot = sk * NS + i;
+                        // spread the GPW refills over the SLOTS MFMA groups
+                        if (GPW >= SLOTS || (slot * GPW) / SLOTS != ((slot + 1) * GPW) / SLOTS) {
+#pragma unroll
+                            for (int q = (slot * GPW) / SLOTS; q < ((slot + 1) * GPW) / SLOTS; ++q)
+                                issue_one(kt + kStages, rbuf, q);
+                        }
                     }
+            } else {
+                issue(kt + kStages, rbuf);
             }
         };
 
@@ -456,6 +559,16 @@ hipError_t launch_tiled(int grid, const uint16_t* A, const int32_t* row_src, int
 
 }  // namespace
 
+hipError_t launch_gateup_fused_dispatch(const Shape& s, const GemmPlan& plan, const uint16_t* x,
+                                        const int32_t* ids, const int32_t* ntok,
+                                        int32_t* offsets, int32_t* row_src, int32_t* token_row,
+                                        const uint16_t* W, uint16_t* h, hipStream_t st) {
+    hipLaunchKernelGGL(gemm_skinny_gateup_dispatch_kernel, dim3(plan.grid_gateup), dim3(256), 0,
+                       st, x, ids, ntok, s.T, s.K, s.E, offsets, row_src, token_row, W, h, s.H,
+                       s.I);
+    return hipGetLastError();
+}
+
 GemmPlan choose_plan(const Shape& s, int hint) {
     GemmPlan p{};
     int kind = hint;
@@ -501,10 +614,13 @@ hipError_t launch_grouped_gemm(const Shape& s, const GemmPlan& plan, bool gated,
     switch (plan.kind) {
         case kSkinny:
             if (gated)
-                hipLaunchKernelGGL(gemm_skinny_kernel<true>, dim3(grid), dim3(256), 0, st, A,
+                hipLaunchKernelGGL((gemm_skinny_kernel<true, 1>), dim3(grid), dim3(256), 0, st, A,
+                                   row_src, topk, offsets, W, C, s.E, Kd, N);
+            else if (N % 32 == 0)
+                hipLaunchKernelGGL((gemm_skinny_kernel<false, 2>), dim3(grid), dim3(256), 0, st, A,
                                    row_src, topk, offsets, W, C, s.E, Kd, N);
             else
-                hipLaunchKernelGGL(gemm_skinny_kernel<false>, dim3(grid), dim3(256), 0, st, A,
+                hipLaunchKernelGGL((gemm_skinny_kernel<false, 1>), dim3(grid), dim3(256), 0, st, A,
                                    row_src, topk, offsets, W, C, s.E, Kd, N);
             return hipGetLastError();
         case kTiled64:

@@ -13,6 +13,7 @@ constexpr int kDispatchThreads = 1024;
 constexpr int kDispatchChunk = 4096;     // assignments per block, multi-block dispatch
 constexpr int kDispatchSingleMax = 8192; // up to this many assignments: one block does it all
 constexpr int kNumCUs = 256;
+constexpr int kFusedDispatchMax = 1024;  // T*K up to this: the skinny gate-up kernel dispatches
 
 struct Shape {
     int T, K, E, H, I, cap;
@@ -48,6 +49,13 @@ hipError_t launch_grouped_gemm(const Shape& s, const GemmPlan& plan, bool gated,
                                const uint16_t* A, const int32_t* row_src, int topk,
                                const int32_t* offsets, const uint16_t* W, uint16_t* C,
                                int Kd, int N, hipStream_t st);
+// Gate-up GEMM of the skinny plan with the local dispatch done inside: every
+// workgroup builds the dispatch of the T*K (<= kFusedDispatchMax) assignments
+// in LDS; workgroup 0 also writes expert_offsets, row_src and token_row.
+hipError_t launch_gateup_fused_dispatch(const Shape& s, const GemmPlan& plan, const uint16_t* x,
+                                        const int32_t* ids, const int32_t* ntok,
+                                        int32_t* offsets, int32_t* row_src, int32_t* token_row,
+                                        const uint16_t* W, uint16_t* h, hipStream_t st);
 hipError_t launch_combine(const Shape& s, const uint16_t* y, const int32_t* token_row,
                           const float* w, const int32_t* ntok, uint16_t* out, hipStream_t st);
 
@@ -107,5 +115,43 @@ __device__ __forceinline__ void moe_block_exclusive_scan(int* s, int n, int* s_w
     }
     if (tid == nt - 1) s[n] = run;
     __syncthreads();
+}
+
+// Stable ranks of one chunk of assignments, one per thread of the block
+// (e = expert id, or -1 for an invalid assignment).  Within each wave the
+// lanes that share an expert are ranked with ballots (each round takes the
+// expert of the lowest remaining lane); per-wave counts are then turned into
+// bases in wave order, on top of the running per-expert bases s_base[E].
+// Returns the thread's row, or -1.  s_wc (nwaves x E) must be zero on entry
+// and is zero again on return; every thread of the block must call.
+__device__ __forceinline__ int moe_stable_rows(int e, int E, int* s_wc, int* s_base) {
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int nwaves = blockDim.x >> 6;
+    int rank = 0;
+    unsigned long long rem = __ballot(e >= 0);
+    while (rem) {
+        const int leader = __ffsll((long long)rem) - 1;
+        const int ve = __shfl(e, leader, 64);
+        const unsigned long long m = __ballot(e == ve);
+        if (e == ve) rank = __popcll(m & ((1ull << lane) - 1ull));
+        if (lane == leader) s_wc[wave * E + ve] = __popcll(m);
+        rem &= ~m;
+    }
+    __syncthreads();
+    for (int x = tid; x < E; x += blockDim.x) {   // counts -> bases, wave order
+        int run = s_base[x];
+        for (int w = 0; w < nwaves; ++w) {
+            const int c = s_wc[w * E + x];
+            s_wc[w * E + x] = run;
+            run += c;
+        }
+        s_base[x] = run;
+    }
+    __syncthreads();
+    const int r = e >= 0 ? s_wc[wave * E + e] + rank : -1;
+    __syncthreads();
+    for (int i = tid; i < nwaves * E; i += blockDim.x) s_wc[i] = 0;
+    __syncthreads();
+    return r;
 }
 #endif

@@ -378,3 +378,34 @@ def test_zero_tokens():
     out, off = ops.forward(p, x, ids, w, wgu, wd)
     assert out.shape == (0, 256)
     assert bool((off == 0).all())
+
+
+@pytest.mark.parametrize("T,K,E,H,I,lo,hi,tv", [
+    (1, 6, 96, 512, 256, 0, 384, None),      # one token, most ids non-local
+    (37, 6, 16, 256, 192, -1, 20, None),
+    (170, 6, 8, 128, 128, 0, 8, 101),        # T*K = 1020, device-side T_v
+    (5, 2, 4, 64, 64, 7, 9, None),           # no valid assignment at all
+])
+def test_small_batch_forward_composes(T, K, E, H, I, lo, hi, tv):
+    """moe_forward on a small batch (T*K <= 1024, skinny plan: the gate-up
+    kernel does the dispatch itself) equals the staged calls bit for bit and
+    the oracle to tolerance."""
+    inp = rand_case(T, K, E, H, I, seed=31, lo=lo, hi=hi)
+    d = to_dev(inp)
+    p = moe.problem(T, K, E, H, I, 0, 1)
+    nt = None if tv is None else torch.tensor([tv], dtype=torch.int32, device=DEV)
+    out = torch.zeros((T, H), dtype=torch.bfloat16, device=DEV)
+    out, off = ops.forward(p, d["x"], d["topk_ids"], d["topk_weights"], d["w_gateup"], d["w_down"],
+                           num_tokens_dev=nt, out=out)
+    x_disp, off2, rs, tr = ops.dispatch(p, d["x"], d["topk_ids"], num_tokens_dev=nt)
+    y = ops.expert_compute(p, x_disp, off2, d["w_gateup"], d["w_down"])
+    out2 = torch.zeros((T, H), dtype=torch.bfloat16, device=DEV)
+    ops.combine(p, y, tr, d["topk_weights"], num_tokens_dev=nt, out=out2)
+    assert torch.equal(off, off2)
+    assert torch.equal(out.view(torch.int16), out2.view(torch.int16))
+    tvv = T if tv is None else tv
+    ref = oracle.forward(bits(inp["x"]), inp["topk_ids"].numpy(), inp["topk_weights"].numpy(),
+                         bits(inp["w_gateup"]), bits(inp["w_down"]), num_valid_tokens=tvv)
+    _, o_off, _, _ = oracle.dispatch(inp["topk_ids"].numpy(), E, tvv)
+    assert np.array_equal(off.cpu().numpy(), o_off)
+    check_close(f64(out)[:tvv], ref[:tvv], f"small batch T={T}")
