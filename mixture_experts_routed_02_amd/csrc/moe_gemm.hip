@@ -31,7 +31,9 @@ __device__ __forceinline__ moe_bf16x8 load16(const uint16_t* p) {
     return *reinterpret_cast<const moe_bf16x8*>(p);
 }
 
-__device__ __forceinline__ float silu_f32(float z) { return z / (1.0f + __expf(-z)); }
+// silu(z) = z / (1 + exp(-z)), with the hardware reciprocal (about 1 ulp of
+// fp32, far below the bf16 rounding that follows) in place of an IEEE divide
+__device__ __forceinline__ float silu_f32(float z) { return z * __builtin_amdgcn_rcpf(1.0f + __expf(-z)); }
 
 // Tile table: s_start[e] = sum_{e' < e} ceil(M_e'/BM) * n_tiles, s_start[E] = total.
 template <int BM>
@@ -270,21 +272,34 @@ __global__ __launch_bounds__(256) void gemm_skinny_gateup_dispatch_kernel(
 }
 
 // ---------------------------------------------------------------------------
-// Tiled kernel: BM token rows x BN weight rows per tile, operands streamed
-// through a kStages-deep LDS ring, BK = 32 per stage, filled by direct
-// global->LDS loads (global_load_lds_dwordx4: no staging registers), so
-// kStages-1 stages of loads are in flight while one stage is multiplied.
-// The product runs on v_mfma_f32_32x32x16_bf16: measured on the device, it
-// sustains ~2.2 PFLOP/s where the 16x16x32 form stops near 1.3.
+// Tiled kernel: BM token rows x BN weight rows per tile.  Operands stream
+// through an S-slot LDS ring, 64 k-values (128 bytes of every row) per stage,
+// filled by direct global->LDS loads (global_load_lds_dwordx4: no staging
+// registers).  A 128-byte row segment is one cache line; measured on the
+// device, 1 KiB DMA instructions that cover 8 rows x 128 B move ~1.7x more
+// data per CU through the address unit than 16 rows x 64 B, and at this
+// kernel's ~128 FLOP per staged byte the address unit is what runs out first.
+// The product runs on v_mfma_f32_32x32x16_bf16.
 //
-// Stage layout: 16-row groups of 1 KiB, token groups first, then weight
-// groups; row r of a stage holds its 32-element k-slice as four 16-byte
-// chunks, chunk c stored in slot c ^ f(r), f(r) = 2*bit2(r) + bit4(r).  A DMA
-// instruction fills one group (lane L -> row L/4, slot L%4); a 32x32x16
-// fragment read takes 32 rows x one chunk.  A ds_read_b128 pass on gfx950
-// serves lanes {0-7,16-23}, {8-15,24-31}, ...; with f those sixteen lanes hit
-// sixteen distinct 16-byte bank groups, so neither the DMA writes nor the
-// fragment reads have bank conflicts.
+// Stage layout: 8-row groups of 1 KiB, token rows first, then weight rows.
+// Row r holds its 64-element k-slice as eight 16-byte chunks, chunk c stored
+// in slot c ^ f(r % 32), f(r) = ((r >> 1) & 3) | ((r >> 2) & 4).  A DMA
+// instruction fills one group (lane L writes row L/8, slot L%8, so it fetches
+// chunk (L%8) ^ f); a 32x32x16 fragment read takes 32 rows x one chunk.  A
+// ds_read_b128 pass on gfx950 serves lanes {0-7,16-23}, {8-15,24-31}, ...:
+// rows of one parity among r..r+7 differ in bits 0-1 of f, rows r and r+16 in
+// bit 2, so the sixteen lanes of a pass hit sixteen distinct 16-byte bank
+// groups and the fragment reads are conflict-free.
+//
+// Pipeline.  Stage d sits in slot d % S and is multiplied as two 32-wide
+// halves 2d and 2d+1; the fragments of half h+1 are read from LDS while half h
+// runs its MFMAs (token fragments into a second register set, each weight
+// fragment into its own registers right after its last MFMA of half h).  So
+// every read of stage d is done by the start of half 2d+1.  There, each wave
+// waits for its own loads of stage d+1, one barrier tells every wave that
+// stage d+1 has landed everywhere and that nobody reads slot d % S any more,
+// and the wave refills that slot with stage d+S, its loads spread between the
+// MFMAs of the half.  Even halves wait for nothing.
 //
 // WGM x WGN waves; each wave owns (BM/WGM) token rows x (BN/WGN) weight rows
 // of the tile as 32x32 MFMA sub-tiles (weights = MFMA rows, tokens = MFMA
@@ -294,8 +309,15 @@ __global__ __launch_bounds__(256) void gemm_skinny_gateup_dispatch_kernel(
 // are explicit (vmcnt + s_barrier): a full __syncthreads() would also drain
 // the loads that are meant to stay in flight.
 // ---------------------------------------------------------------------------
-constexpr int kBK = 32;
-constexpr int kStages = 4;
+constexpr int kBK = 64;   // k-values per stage
+
+// ring slots: as many stages as fit (at most 4) in 152 KiB when one
+// workgroup of 8 waves fills a CU, in 76 KiB when two 4-wave ones share it
+constexpr int ring_slots(int stage_bytes, int waves) {
+    const int budget = (waves == 8 ? 152 : 76) * 1024;
+    const int s = budget / stage_bytes;
+    return s > 4 ? 4 : s;
+}
 
 typedef __attribute__((address_space(3))) unsigned char lds_u8;
 
@@ -303,7 +325,8 @@ typedef __attribute__((address_space(3))) unsigned char lds_u8;
 // wave-uniform).  Written as inline asm so that the compiler does not treat
 // the pending LDS writes as aliasing every later LDS read (it would then drain
 // the whole ring with vmcnt(0) before each read); the ring's own explicit
-// vmcnt waits and barriers order these writes against the reads.
+// vmcnt waits and barriers order these writes against the reads.  m0 is
+// written here only; the kernels below use it for nothing else.
 __device__ __forceinline__ void lds_dma16(const uint16_t* g, uint32_t lds_base) {
     asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off"
                  :: "v"(g), "s"(lds_base) : "memory", "m0");
@@ -314,15 +337,27 @@ __device__ __forceinline__ uint32_t lds_addr(const unsigned char* p) {
 }
 
 template <int N>
-__device__ __forceinline__ void wait_vmcnt_barrier() {
+__device__ __forceinline__ void wait_vmcnt() {
     static_assert(N >= 0 && N < 64, "vmcnt range");
     asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+
+template <int N>
+__device__ __forceinline__ void wait_vmcnt_barrier() {
+    wait_vmcnt<N>();
     __builtin_amdgcn_s_barrier();
     asm volatile("" ::: "memory");
 }
 
-// slot swizzle of stage row r (see above)
-__device__ __forceinline__ int ring_swz(int r) { return (((r >> 2) & 1) << 1) | ((r >> 4) & 1); }
+// LDS writes of this wave done, then a workgroup barrier (no vmcnt drain)
+__device__ __forceinline__ void lds_barrier() {
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+}
+
+// chunk swizzle of row r (see above)
+__device__ __forceinline__ int ring_swz(int r) { return ((r >> 1) & 3) | ((r >> 2) & 4); }
 
 template <int BM, int BN, int WGM, int WGN, bool GATED>
 __global__ __launch_bounds__(64 * WGM * WGN) void gemm_tiled_kernel(
@@ -333,18 +368,22 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_tiled_kernel(
     constexpr int WM = BM / WGM, WN = BN / WGN;       // per-wave extent
     constexpr int MS = WM / 32, NS = WN / 32;         // 32x32 sub-tiles per wave
     constexpr int COLS = GATED ? BN / 2 : BN;         // output columns per tile
-    constexpr int AG = BM / 16;                       // token groups per stage
-    constexpr int GROUPS = (BM + BN) / 16;            // 1 KiB groups per stage
+    constexpr int AG = BM / 8;                        // token groups per stage
+    constexpr int GROUPS = (BM + BN) / 8;             // 1 KiB groups per stage
     constexpr int GPW = GROUPS / NW;                  // DMA instructions per wave per stage
     constexpr int TPW = (AG + NW - 1) / NW;           // token groups per wave (upper bound)
     constexpr int STAGE = GROUPS * 1024;              // bytes per stage
+    constexpr int S = ring_slots(STAGE, NW);          // ring slots
     static_assert(WM % 32 == 0 && WN % 32 == 0 && GROUPS % NW == 0, "tile shape");
+    static_assert(NW % 4 == 0, "a wave's DMA groups share one row-swizzle phase");
     static_assert(!GATED || NS % 2 == 0, "gated tiles pair gate and up sub-tiles");
-    static_assert(GPW * (kStages - 2) < 64, "vmcnt range");
+    static_assert(S >= 2 && GPW * (S - 1) < 64, "ring depth");
+    constexpr int OP = 2 * COLS + 8;                  // epilogue staging pitch, bytes
+    constexpr int RING = (S * STAGE > BM * OP) ? S * STAGE : BM * OP;
 
     __shared__ int s_start[kMaxExperts + 1];
     __shared__ int s_wave[NW];
-    __shared__ __attribute__((aligned(1024))) unsigned char s_ring[kStages * STAGE];
+    __shared__ __attribute__((aligned(1024))) unsigned char s_ring[RING];
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -363,27 +402,27 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_tiled_kernel(
     const int lb = (G % 8 == 0) ? ((int)(blockIdx.x % 8) * (G / 8) + (int)(blockIdx.x / 8))
                                 : (int)blockIdx.x;
 
-    // DMA role of this lane: row lane/4 of a group, slot lane%4
-    const int dma_row = lane >> 2;
-    const int dma_chunk_even = (lane & 3) ^ ring_swz(dma_row);        // groups with even index
-    const int dma_chunk_odd = (lane & 3) ^ ring_swz(dma_row + 16);    // odd index (row bit 4 set)
-    // fragment-read offsets of this lane inside a 32-row block, for the two
-    // 16-wide k halves: row l%32, chunk 2*s + l/32
+    // DMA role of this lane: row lane/8 of a group, slot lane%8.  Group g holds
+    // rows 8g..8g+7, i.e. rows 8*(g%4).. of its 32-row block, and g % 4 is
+    // wave % 4 for every group this wave fills.
+    const int dma_row = lane >> 3;
+    const int dma_chunk = (lane & 7) ^ ring_swz((wave & 3) * 8 + dma_row);
+    // fragment-read offsets of this lane inside a 32-row block for the four
+    // 16-wide k steps of a stage: row l%32, chunk 2*s + l/32
     const int fr = lane & 31, fh = lane >> 5;
-    int rd_off[2];
+    int rd_off[4];
 #pragma unroll
-    for (int sk = 0; sk < 2; ++sk)
-        rd_off[sk] = (fr >> 4) * 1024 + (fr & 15) * 64 + (((2 * sk + fh) ^ ring_swz(fr)) << 4);
-    int ga[MS], gw[NS];   // 32-row blocks, in units of 1 KiB groups
+    for (int s = 0; s < 4; ++s) rd_off[s] = fr * 128 + (((2 * s + fh) ^ ring_swz(fr)) << 4);
+    int ga[MS], gw[NS];   // byte offsets of this wave's 32-row blocks in a stage
 #pragma unroll
-    for (int j = 0; j < MS; ++j) ga[j] = (wm * WM + j * 32) / 16;
+    for (int j = 0; j < MS; ++j) ga[j] = (wm * WM + j * 32) * 128;
 #pragma unroll
     for (int i = 0; i < NS; ++i) {
         int trow;
         if (GATED) trow = (i < NS / 2) ? (wn * (WN / 2) + i * 32)
                                        : (BN / 2 + wn * (WN / 2) + (i - NS / 2) * 32);
         else trow = wn * WN + i * 32;
-        gw[i] = AG + trow / 16;
+        gw[i] = (BM + trow) * 128;
     }
 
     for (int tile = lb; tile < total; tile += G) {
@@ -398,35 +437,29 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_tiled_kernel(
         // a wave whose token rows all lie past the valid rows skips its MFMAs
         const bool active = wm * WM < mrows;
 
-        // global source of each group this wave fills (k-step 0): token groups
-        // gather rows through row_src; weight rows are affine in the group
+        // global source of each group this wave fills (stage 0): token groups
+        // gather rows through row_src (rows past the valid ones repeat the
+        // last valid row); weight rows are affine in the group
         const uint16_t* asrc[TPW];
 #pragma unroll
         for (int q = 0; q < TPW; ++q) {
             const int g = wave + NW * q;
-            const int tr = (g < AG ? g : 0) * 16 + dma_row;
+            const int tr = (g < AG ? g : 0) * 8 + dma_row;
             const int rr = r0 + (tr < mrows ? tr : mrows - 1);
             const long long arow = row_src ? (long long)(row_src[rr] / topk) : (long long)rr;
-            asrc[q] = A + (size_t)arow * Kd + ((g & 1) ? dma_chunk_odd : dma_chunk_even) * 8;
+            asrc[q] = A + (size_t)arow * Kd + dma_chunk * 8;
         }
-        const uint16_t* wbase = W + (size_t)e * w_rows * Kd + (size_t)dma_row * Kd;
+        const uint16_t* wbase = W + (size_t)e * w_rows * Kd + (size_t)dma_row * Kd + dma_chunk * 8;
         auto wrow0 = [&](int g) {   // first weight row of weight group g (wave-uniform)
-            const int tr = (g - AG) * 16;
+            const int tr = (g - AG) * 8;
             if (GATED) return (tr < BN / 2) ? (n_tile * (BN / 2) + tr) : (N + n_tile * (BN / 2) + tr - BN / 2);
             return n_tile * BN + tr;
         };
-        auto issue_one = [&](int step, int buf, int q) {
-            const int ks = step < nk ? step : nk - 1;   // past the end: a harmless reload
+        auto issue_one = [&](int stage, int q) {
             const int g = wave + NW * q;
-            const uint32_t dst = ring0 + buf * STAGE + g * 1024;
-            const uint16_t* src =
-                (g < AG) ? asrc[q < TPW ? q : 0]
-                         : wbase + (size_t)wrow0(g) * Kd + ((g & 1) ? dma_chunk_odd : dma_chunk_even) * 8;
-            lds_dma16(src + (size_t)ks * kBK, dst);
-        };
-        auto issue = [&](int step, int buf) {
-#pragma unroll
-            for (int q = 0; q < GPW; ++q) issue_one(step, buf, q);
+            const uint32_t dst = ring0 + (stage % S) * STAGE + g * 1024;
+            const uint16_t* src = (g < AG) ? asrc[q < TPW ? q : 0] : wbase + (size_t)wrow0(g) * Kd;
+            lds_dma16(src + (size_t)stage * kBK, dst);
         };
 
         moe_f32x16 acc[NS][MS];
@@ -437,38 +470,26 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_tiled_kernel(
 #pragma unroll
                 for (int q = 0; q < 16; ++q) acc[i][j][q] = 0.f;
 
-        // Software pipeline over k-steps: when step kt is multiplied its
-        // fragments are already in registers, and step kt+1's fragments are
-        // read from LDS in the shadow of those MFMAs (token fragments into a
-        // second register set, each weight fragment into its own registers
-        // right after its last MFMA of step kt).  The LDS buffer of step kt is
-        // refilled with step kt + kStages once every wave has read it.
         moe_bf16x8 fw[2][NS];
-        auto read_a = [&](int step, moe_bf16x8 (*fa)[MS]) {
-            const unsigned char* st = s_ring + (step % kStages) * STAGE;
+        // fragments of half h (stage h/2, k steps 2*(h%2) and 2*(h%2)+1)
+        auto read_a = [&](int h, moe_bf16x8 (*fa)[MS]) {
+            const unsigned char* st = s_ring + ((h >> 1) % S) * STAGE;
 #pragma unroll
             for (int sk = 0; sk < 2; ++sk)
 #pragma unroll
                 for (int j = 0; j < MS; ++j)
-                    fa[sk][j] = *reinterpret_cast<const moe_bf16x8*>(st + ga[j] * 1024 + rd_off[sk]);
+                    fa[sk][j] = *reinterpret_cast<const moe_bf16x8*>(st + ga[j] + rd_off[2 * (h & 1) + sk]);
         };
-        auto read_w = [&](int step, int sk, int i) {
-            const unsigned char* st = s_ring + (step % kStages) * STAGE;
-            fw[sk][i] = *reinterpret_cast<const moe_bf16x8*>(st + gw[i] * 1024 + rd_off[sk]);
+        auto read_w = [&](int h, int sk, int i) {
+            const unsigned char* st = s_ring + ((h >> 1) % S) * STAGE;
+            fw[sk][i] = *reinterpret_cast<const moe_bf16x8*>(st + gw[i] + rd_off[2 * (h & 1) + sk]);
         };
-        // one step: wait until step kt+1 has landed, refill step kt's buffer
-        // with step kt + kStages, multiply step kt while reading step kt+1
-        // The refill DMAs are spread between the MFMAs: issued in one burst
-        // after the barrier they would hold up every wave's first MFMA while
-        // the address unit works through them.
-        auto step = [&](int kt, moe_bf16x8 (*fa_c)[MS], moe_bf16x8 (*fa_n)[MS]) {
-            wait_vmcnt_barrier<GPW * (kStages - 2)>();
-            const int rbuf = kt % kStages;
+        // half h: multiply it from registers while reading half h+1; when
+        // REFILL, load stage `refill` into its slot between the MFMA groups
+        auto half = [&](int h, moe_bf16x8 (*fa_c)[MS], moe_bf16x8 (*fa_n)[MS], bool refill,
+                        int stage) {
             if (active) {
-                // step kt+1's fragments; on the last step this reads the ring's
-                // harmless reload and the values are never used (no branches
-                // between the MFMAs)
-                read_a(kt + 1, fa_n);
+                read_a(h + 1, fa_n);
 #pragma unroll
                 for (int sk = 0; sk < 2; ++sk)
 #pragma unroll
@@ -476,25 +497,29 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_tiled_kernel(
 #pragma unroll
                         for (int j = 0; j < MS; ++j)
                             acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fw[sk][i], fa_c[sk][j], acc[i][j], 0, 0, 0);
-                        read_w(kt + 1, sk, i);
+                        read_w(h + 1, sk, i);
                         constexpr int SLOTS = 2 * NS;
                         const int slot = sk * NS + i;
-                        // spread the GPW refills over the SLOTS MFMA groups
-                        if (GPW >= SLOTS || (slot * GPW) / SLOTS != ((slot + 1) * GPW) / SLOTS) {
+                        if (refill && (GPW >= SLOTS || (slot * GPW) / SLOTS != ((slot + 1) * GPW) / SLOTS)) {
 #pragma unroll
                             for (int q = (slot * GPW) / SLOTS; q < ((slot + 1) * GPW) / SLOTS; ++q)
-                                issue_one(kt + kStages, rbuf, q);
+                                issue_one(stage, q);
                         }
                     }
-            } else {
-                issue(kt + kStages, rbuf);
+            } else if (refill) {
+#pragma unroll
+                for (int q = 0; q < GPW; ++q) issue_one(stage, q);
             }
         };
 
+        // prologue: stages 0..S-1 (or fewer) in flight, wait for stage 0
+        const int pre = nk < S ? nk : S;
+        for (int s2 = 0; s2 < pre; ++s2)
 #pragma unroll
-        for (int s = 0; s < kStages; ++s) issue(s, s);
+            for (int q = 0; q < GPW; ++q) issue_one(s2, q);
+        if (pre == S) wait_vmcnt_barrier<GPW * (S - 1)>();
+        else wait_vmcnt_barrier<0>();
         moe_bf16x8 fa0[2][MS], fa1[2][MS];
-        wait_vmcnt_barrier<GPW * (kStages - 1)>();
         if (active) {
             read_a(0, fa0);
 #pragma unroll
@@ -502,49 +527,72 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_tiled_kernel(
 #pragma unroll
                 for (int i = 0; i < NS; ++i) read_w(0, sk, i);
         }
-        int kt = 0;
-        for (; kt + 2 <= nk; kt += 2) {
-            step(kt, fa0, fa1);
-            step(kt + 1, fa1, fa0);
+        for (int d = 0; d < nk; ++d) {
+            half(2 * d, fa0, fa1, false, 0);
+            // stage d+1 landed everywhere and slot d % S is free (see above;
+            // the wave's own reads of it have returned before the barrier);
+            // on the last stage the read-ahead takes stale but valid LDS data
+            // that is never used
+            asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+            if (d + S - 1 < nk) wait_vmcnt_barrier<GPW * (S - 2)>();
+            else wait_vmcnt_barrier<0>();
+            half(2 * d + 1, fa1, fa0, d + S < nk, d + S);
         }
-        if (kt < nk) step(kt, fa0, fa1);
         // drain the ring before the next tile refills it
         wait_vmcnt_barrier<0>();
 
-        // epilogue: lane holds D[n = 8*p + 4*fh + u][m = fr] in acc[..][16p..] : q = 4p + u
+        // epilogue, staged through the idle ring so that the global stores are
+        // whole 16-byte pieces of contiguous output rows (written straight
+        // from the MFMA layout, every store would touch 32 rows with 8 bytes
+        // each).  Lane (fr, fh) holds D[n = 8p + 4fh + u][m = fr] of sub-tile
+        // (i, j) in acc[i][j][4p + u] and writes those four values (8 bytes)
+        // to LDS row m at pitch OP = 2*COLS + 8 bytes, so the 32 rows of one
+        // write fall on 32 distinct 8-byte bank slots.
+        constexpr int CPR = COLS / 8;                    // 16-byte pieces per row
+        if (active) {
 #pragma unroll
-        for (int j = 0; j < MS; ++j) {
-            const int m = wm * WM + j * 32 + fr;
-            if (m >= mrows) continue;
-            uint16_t* crow = C + (size_t)(r0 + m) * N;
-            if (GATED) {
+            for (int j = 0; j < MS; ++j) {
+                unsigned char* orow = s_ring + (wm * WM + j * 32 + fr) * OP;
+                if (GATED) {
 #pragma unroll
-                for (int i = 0; i < NS / 2; ++i)
+                    for (int i = 0; i < NS / 2; ++i)
 #pragma unroll
-                    for (int p = 0; p < 4; ++p) {
-                        const int col = n_tile * COLS + wn * (WN / 2) + i * 32 + p * 8 + fh * 4;
-                        uint16_t hv[4];
+                        for (int p = 0; p < 4; ++p) {
+                            const int col = wn * (WN / 2) + i * 32 + p * 8 + fh * 4;
+                            float hv[4];
 #pragma unroll
-                        for (int u = 0; u < 4; ++u)
-                            hv[u] = moe_f32_to_bf16(silu_f32(acc[i][j][4 * p + u]) * acc[i + NS / 2][j][4 * p + u]);
-                        uint2 pk;
-                        pk.x = (uint32_t)hv[0] | ((uint32_t)hv[1] << 16);
-                        pk.y = (uint32_t)hv[2] | ((uint32_t)hv[3] << 16);
-                        *reinterpret_cast<uint2*>(crow + col) = pk;
-                    }
-            } else {
+                            for (int u = 0; u < 4; ++u)
+                                hv[u] = silu_f32(acc[i][j][4 * p + u]) * acc[i + NS / 2][j][4 * p + u];
+                            uint2 pk;
+                            pk.x = moe_f32x2_to_bf16x2(hv[0], hv[1]);
+                            pk.y = moe_f32x2_to_bf16x2(hv[2], hv[3]);
+                            *reinterpret_cast<uint2*>(orow + col * 2) = pk;
+                        }
+                } else {
 #pragma unroll
-                for (int i = 0; i < NS; ++i)
+                    for (int i = 0; i < NS; ++i)
 #pragma unroll
-                    for (int p = 0; p < 4; ++p) {
-                        const int col = n_tile * COLS + wn * WN + i * 32 + p * 8 + fh * 4;
-                        uint2 pk;
-                        pk.x = (uint32_t)moe_f32_to_bf16(acc[i][j][4 * p]) | ((uint32_t)moe_f32_to_bf16(acc[i][j][4 * p + 1]) << 16);
-                        pk.y = (uint32_t)moe_f32_to_bf16(acc[i][j][4 * p + 2]) | ((uint32_t)moe_f32_to_bf16(acc[i][j][4 * p + 3]) << 16);
-                        *reinterpret_cast<uint2*>(crow + col) = pk;
-                    }
+                        for (int p = 0; p < 4; ++p) {
+                            const int col = wn * WN + i * 32 + p * 8 + fh * 4;
+                            uint2 pk;
+                            pk.x = moe_f32x2_to_bf16x2(acc[i][j][4 * p], acc[i][j][4 * p + 1]);
+                            pk.y = moe_f32x2_to_bf16x2(acc[i][j][4 * p + 2], acc[i][j][4 * p + 3]);
+                            *reinterpret_cast<uint2*>(orow + col * 2) = pk;
+                        }
+                }
             }
         }
+        lds_barrier();
+        uint16_t* cbase = C + (size_t)r0 * N + n_tile * COLS;
+        for (int idx = tid; idx < mrows * CPR; idx += NT) {
+            const int r = idx / CPR, c = idx % CPR;
+            const unsigned char* src = s_ring + r * OP + c * 16;
+            const uint2 lo = *reinterpret_cast<const uint2*>(src);
+            const uint2 hi = *reinterpret_cast<const uint2*>(src + 8);
+            *reinterpret_cast<uint4*>(cbase + (size_t)r * N + c * 8) = make_uint4(lo.x, lo.y, hi.x, hi.y);
+        }
+        // every read of the staged rows is done before the ring is refilled
+        lds_barrier();
     }
 }
 

@@ -73,12 +73,20 @@ __device__ __forceinline__ float moe_bf16_to_f32(uint16_t b) {
     return __uint_as_float(((uint32_t)b) << 16);
 }
 
-// fp32 -> bf16, round to nearest even; NaN stays a quiet NaN.
+// fp32 -> bf16, round to nearest even; NaN stays a quiet NaN.  gfx950's
+// v_cvt_pk_bf16_f32 rounds this way (checked bit for bit on the device against
+// the integer form u + 0x7fff + ((u >> 16) & 1) over rounding ties,
+// subnormals, overflow and NaN).
 __device__ __forceinline__ uint16_t moe_f32_to_bf16(float f) {
-    uint32_t u = __float_as_uint(f);
-    if ((u & 0x7fffffffu) > 0x7f800000u) return (uint16_t)((u >> 16) | 0x40u);
-    u += 0x7fffu + ((u >> 16) & 1u);
-    return (uint16_t)(u >> 16);
+    return __builtin_bit_cast(uint16_t, (__bf16)f);
+}
+
+// two values at once, lo in bits 0-15 (one v_cvt_pk_bf16_f32)
+__device__ __forceinline__ uint32_t moe_f32x2_to_bf16x2(float lo, float hi) {
+    typedef float f32x2 __attribute__((ext_vector_type(2)));
+    typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+    const f32x2 v = {lo, hi};
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2));
 }
 
 __device__ __forceinline__ int moe_valid_tokens(const int32_t* ntok, int T) {
