@@ -273,50 +273,61 @@ __global__ __launch_bounds__(256) void gemm_skinny_gateup_dispatch_kernel(
 
 // ---------------------------------------------------------------------------
 // Tiled kernel: BM token rows x BN weight rows per tile.  Operands stream
-// through an S-slot LDS ring, 64 k-values (128 bytes of every row) per stage,
-// filled by direct global->LDS loads (global_load_lds_dwordx4: no staging
-// registers).  A 128-byte row segment is one cache line; measured on the
+// through LDS rings, 64 k-values (128 bytes of every row) per stage, filled
+// by direct global->LDS loads (global_load_lds_dwordx4: no staging
+// registers).  A 128-byte row segment is one cache line: measured on the
 // device, 1 KiB DMA instructions that cover 8 rows x 128 B move ~1.7x more
 // data per CU through the address unit than 16 rows x 64 B, and at this
 // kernel's ~128 FLOP per staged byte the address unit is what runs out first.
 // The product runs on v_mfma_f32_32x32x16_bf16.
 //
-// Stage layout: 8-row groups of 1 KiB, token rows first, then weight rows.
-// Row r holds its 64-element k-slice as eight 16-byte chunks, chunk c stored
-// in slot c ^ f(r % 32), f(r) = ((r >> 1) & 3) | ((r >> 2) & 4).  A DMA
-// instruction fills one group (lane L writes row L/8, slot L%8, so it fetches
-// chunk (L%8) ^ f); a 32x32x16 fragment read takes 32 rows x one chunk.  A
-// ds_read_b128 pass on gfx950 serves lanes {0-7,16-23}, {8-15,24-31}, ...:
-// rows of one parity among r..r+7 differ in bits 0-1 of f, rows r and r+16 in
-// bit 2, so the sixteen lanes of a pass hit sixteen distinct 16-byte bank
-// groups and the fragment reads are conflict-free.
+// Stage layout: 8-row groups of 1 KiB.  Row r holds its 64-element k-slice
+// as eight 16-byte chunks, chunk c stored in slot c ^ f(r % 32),
+// f(r) = ((r >> 1) & 3) | ((r >> 2) & 4).  A DMA instruction fills one group
+// (lane L writes row L/8, slot L%8, so it fetches chunk (L%8) ^ f); a
+// 32x32x16 fragment read takes 32 rows x one chunk.  A ds_read_b128 pass on
+// gfx950 serves lanes {0-7,16-23}, {8-15,24-31}, ...: rows of one parity
+// among r..r+7 differ in bits 0-1 of f, rows r and r+16 in bit 2, so the
+// sixteen lanes of a pass hit sixteen distinct 16-byte bank groups and the
+// fragment reads are conflict-free.
 //
-// Pipeline.  Stage d sits in slot d % S and is multiplied as two 32-wide
-// halves 2d and 2d+1; the fragments of half h+1 are read from LDS while half h
-// runs its MFMAs (token fragments into a second register set, each weight
-// fragment into its own registers right after its last MFMA of half h).  So
-// every read of stage d is done by the start of half 2d+1.  There, each wave
-// waits for its own loads of stage d+1, one barrier tells every wave that
-// stage d+1 has landed everywhere and that nobody reads slot d % S any more,
-// and the wave refills that slot with stage d+S, its loads spread between the
-// MFMAs of the half.  Even halves wait for nothing.
+// Two rings: token stages (SA slots) and weight stages (SW >= SA slots), so
+// the weights, which miss L2 more often, are requested further ahead.  LDS
+// holds nothing else; the tile table lives in registers.
+//
+// Pipeline.  Stage d is multiplied as two 32-wide halves 2d and 2d+1; the
+// fragments of half h+1 are read from LDS while half h runs its MFMAs (each
+// fragment into its own registers right after its last MFMA of half h), so
+// every read of stage d is done by the start of half 2d+1.  There, each wave waits for its own
+// loads of stage d+1, one barrier tells every wave that stage d+1 has landed
+// everywhere and that nobody reads stage d's slots any more, and the wave
+// refills them: tokens of stage d+SA, then weights of stage d+SW, spread
+// between the MFMAs of the half.  Even halves wait for nothing.  Issue order
+// per wave: weights 0..SW-SA-1, then the pairs (tokens s, weights s+SW-SA)
+// for s < SA, then one such pair per odd half; the vmcnt of each wait counts
+// the loads issued after the ones it needs.
 //
 // WGM x WGN waves; each wave owns (BM/WGM) token rows x (BN/WGN) weight rows
 // of the tile as 32x32 MFMA sub-tiles (weights = MFMA rows, tokens = MFMA
 // columns).  gated: tile rows [0, BN/2) are gate columns n0.. and [BN/2, BN)
 // the matching up columns; each wave takes the same column range from both
-// halves so gate and up of one output meet in one lane.  Waits on the ring
+// halves so gate and up of one output meet in one lane.  Waits on the rings
 // are explicit (vmcnt + s_barrier): a full __syncthreads() would also drain
 // the loads that are meant to stay in flight.
 // ---------------------------------------------------------------------------
 constexpr int kBK = 64;   // k-values per stage
 
-// ring slots: as many stages as fit (at most 4) in 152 KiB when one
-// workgroup of 8 waves fills a CU, in 76 KiB when two 4-wave ones share it
-constexpr int ring_slots(int stage_bytes, int waves) {
-    const int budget = (waves == 8 ? 152 : 76) * 1024;
-    const int s = budget / stage_bytes;
-    return s > 4 ? 4 : s;
+// LDS per workgroup: all of it when one 8-wave workgroup fills a CU, half
+// when two 4-wave ones share it
+constexpr int ring_budget(int waves) { return (waves == 8 ? 160 : 80) * 1024; }
+// token slots: 3 if both rings can have 3, else 2
+constexpr int ring_sa(int a_bytes, int w_bytes, int budget) {
+    return 3 * (a_bytes + w_bytes) <= budget ? 3 : 2;
+}
+// weight slots: what is left, at most 5
+constexpr int ring_sw(int a_bytes, int w_bytes, int budget) {
+    const int s = (budget - ring_sa(a_bytes, w_bytes, budget) * a_bytes) / w_bytes;
+    return s > 5 ? 5 : s;
 }
 
 typedef __attribute__((address_space(3))) unsigned char lds_u8;
@@ -329,7 +340,7 @@ typedef __attribute__((address_space(3))) unsigned char lds_u8;
 // written here only; the kernels below use it for nothing else.
 __device__ __forceinline__ void lds_dma16(const uint16_t* g, uint32_t lds_base) {
     asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off"
-                 :: "v"(g), "s"(lds_base) : "memory", "m0");
+                 :: "v"(g), "s"(__builtin_amdgcn_readfirstlane(lds_base)) : "memory", "m0");
 }
 
 __device__ __forceinline__ uint32_t lds_addr(const unsigned char* p) {
@@ -359,6 +370,41 @@ __device__ __forceinline__ void lds_barrier() {
 // chunk swizzle of row r (see above)
 __device__ __forceinline__ int ring_swz(int r) { return ((r >> 1) & 3) | ((r >> 2) & 4); }
 
+// Tile table of the tiled kernel, recomputed by each wave from expert_offsets
+// when it needs it (no LDS): expert e owns ceil(M_e / BM) * n_tiles logical
+// tiles, in expert order.  Lane l looks after experts 64*c + l; a wave scan
+// gives each expert's first tile.  Returns the total and, for `tile` < total,
+// the owning expert (the largest e whose first tile is <= tile: first tiles
+// are non-decreasing, so that is the count of such e, minus one) and its
+// first tile.
+template <int BM>
+__device__ __forceinline__ int wave_tile_lookup(const int32_t* offsets, int E, int n_tiles,
+                                                int lane, int tile, int& expert, int& first) {
+    int carry = 0, cnt_le = 0, first_v = 0;
+    for (int c = 0; c * 64 < E; ++c) {
+        const int e = c * 64 + lane;
+        int cnt = 0;
+        if (e < E) {
+            const int m = offsets[e + 1] - offsets[e];
+            cnt = ((m + BM - 1) / BM) * n_tiles;
+        }
+        int v = cnt;   // inclusive scan over the wave
+#pragma unroll
+        for (int o = 1; o < 64; o <<= 1) {
+            const int t = __shfl_up(v, o);
+            if (lane >= o) v += t;
+        }
+        const int start = carry + v - cnt;
+        const unsigned long long le = __ballot(e < E && start <= tile);
+        cnt_le += __popcll(le);
+        if (le) first_v = __shfl(start, 63 - __clzll(le));   // last expert so far with start <= tile
+        carry += __shfl(v, 63);
+    }
+    expert = __builtin_amdgcn_readfirstlane(cnt_le - 1);
+    first = __builtin_amdgcn_readfirstlane(first_v);
+    return __builtin_amdgcn_readfirstlane(carry);
+}
+
 template <int BM, int BN, int WGM, int WGN, bool GATED>
 __global__ __launch_bounds__(64 * WGM * WGN) void gemm_tiled_kernel(
     const uint16_t* __restrict__ A, const int32_t* __restrict__ row_src, int topk,
@@ -368,22 +414,28 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_tiled_kernel(
     constexpr int WM = BM / WGM, WN = BN / WGN;       // per-wave extent
     constexpr int MS = WM / 32, NS = WN / 32;         // 32x32 sub-tiles per wave
     constexpr int COLS = GATED ? BN / 2 : BN;         // output columns per tile
-    constexpr int AG = BM / 8;                        // token groups per stage
-    constexpr int GROUPS = (BM + BN) / 8;             // 1 KiB groups per stage
-    constexpr int GPW = GROUPS / NW;                  // DMA instructions per wave per stage
-    constexpr int TPW = (AG + NW - 1) / NW;           // token groups per wave (upper bound)
-    constexpr int STAGE = GROUPS * 1024;              // bytes per stage
-    constexpr int S = ring_slots(STAGE, NW);          // ring slots
-    static_assert(WM % 32 == 0 && WN % 32 == 0 && GROUPS % NW == 0, "tile shape");
+    constexpr int AG = BM / 8, WG = BN / 8;           // 1 KiB groups per stage
+    constexpr int GA = AG / NW, GW = WG / NW;         // DMA instructions per wave per stage
+    constexpr int A_STAGE = AG * 1024, W_STAGE = WG * 1024;
+    constexpr int BUDGET = ring_budget(NW);
+    constexpr int SA = ring_sa(A_STAGE, W_STAGE, BUDGET);
+    constexpr int SW = ring_sw(A_STAGE, W_STAGE, BUDGET);
+    constexpr int OP = 2 * COLS + 8;                  // epilogue staging pitch, bytes
+    constexpr int RINGS = SA * A_STAGE + SW * W_STAGE;
+    constexpr int LDS = RINGS > BM * OP ? RINGS : BM * OP;
+    // loads issued after the ones a wait needs: at an odd half (stage d+1),
+    // and in the prologue (stage 0)
+    constexpr int N_STEADY = (SW > SA ? GW : 0) + (SA - 2) * (GA + GW);
+    constexpr int N_FIRST = (SW > SA ? GW : 0) + (SA - 1) * (GA + GW);
+    static_assert(WM % 32 == 0 && WN % 32 == 0 && AG % NW == 0 && WG % NW == 0, "tile shape");
     static_assert(NW % 4 == 0, "a wave's DMA groups share one row-swizzle phase");
     static_assert(!GATED || NS % 2 == 0, "gated tiles pair gate and up sub-tiles");
-    static_assert(S >= 2 && GPW * (S - 1) < 64, "ring depth");
-    constexpr int OP = 2 * COLS + 8;                  // epilogue staging pitch, bytes
-    constexpr int RING = (S * STAGE > BM * OP) ? S * STAGE : BM * OP;
+    static_assert(SA >= 2 && SW >= SA && LDS <= BUDGET, "ring sizes");
+    static_assert(N_FIRST < 64 && N_STEADY < 64, "vmcnt range");
 
-    __shared__ int s_start[kMaxExperts + 1];
-    __shared__ int s_wave[NW];
-    __shared__ __attribute__((aligned(1024))) unsigned char s_ring[RING];
+    __shared__ __attribute__((aligned(1024))) unsigned char s_lds[LDS];
+    unsigned char* const s_ringA = s_lds;
+    unsigned char* const s_ringW = s_lds + SA * A_STAGE;
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -392,9 +444,10 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_tiled_kernel(
     const int wm = wave / WGN, wn = wave % WGN;
     const int n_tiles = N / COLS;
     const int w_rows = GATED ? 2 * N : N;
-    const int total = build_tile_table<BM>(offsets, E, n_tiles, s_start, s_wave);
+    int e_unused, f_unused;
+    const int total = wave_tile_lookup<BM>(offsets, E, n_tiles, lane, 0, e_unused, f_unused);
     const int nk = Kd / kBK;
-    const uint32_t ring0 = lds_addr(s_ring);
+    const uint32_t ringA0 = lds_addr(s_ringA), ringW0 = lds_addr(s_ringW);
 
     // XCD-aware order: workgroup b runs on XCD b % 8; give each XCD a
     // contiguous run of logical tiles so neighbouring m-tiles share its L2.
@@ -404,7 +457,7 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_tiled_kernel(
 
     // DMA role of this lane: row lane/8 of a group, slot lane%8.  Group g holds
     // rows 8g..8g+7, i.e. rows 8*(g%4).. of its 32-row block, and g % 4 is
-    // wave % 4 for every group this wave fills.
+    // wave % 4 for every group this wave fills (g = wave + NW*q).
     const int dma_row = lane >> 3;
     const int dma_chunk = (lane & 7) ^ ring_swz((wave & 3) * 8 + dma_row);
     // fragment-read offsets of this lane inside a 32-row block for the four
@@ -422,15 +475,16 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_tiled_kernel(
         if (GATED) trow = (i < NS / 2) ? (wn * (WN / 2) + i * 32)
                                        : (BN / 2 + wn * (WN / 2) + (i - NS / 2) * 32);
         else trow = wn * WN + i * 32;
-        gw[i] = (BM + trow) * 128;
+        gw[i] = trow * 128;
     }
 
     for (int tile = lb; tile < total; tile += G) {
-        const int e = find_expert(s_start, E, tile);
+        int e, first;
+        wave_tile_lookup<BM>(offsets, E, n_tiles, lane, tile, e, first);
         const int row0 = offsets[e];
         const int me = offsets[e + 1] - row0;
         const int mt = (me + BM - 1) / BM;
-        const int local = tile - s_start[e];
+        const int local = tile - first;
         const int m_tile = local % mt, n_tile = local / mt;
         const int r0 = row0 + m_tile * BM;
         const int mrows = (me - m_tile * BM) < BM ? (me - m_tile * BM) : BM;
@@ -440,26 +494,30 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_tiled_kernel(
         // global source of each group this wave fills (stage 0): token groups
         // gather rows through row_src (rows past the valid ones repeat the
         // last valid row); weight rows are affine in the group
-        const uint16_t* asrc[TPW];
+        const uint16_t* asrc[GA];
 #pragma unroll
-        for (int q = 0; q < TPW; ++q) {
-            const int g = wave + NW * q;
-            const int tr = (g < AG ? g : 0) * 8 + dma_row;
+        for (int q = 0; q < GA; ++q) {
+            const int tr = (wave + NW * q) * 8 + dma_row;
             const int rr = r0 + (tr < mrows ? tr : mrows - 1);
             const long long arow = row_src ? (long long)(row_src[rr] / topk) : (long long)rr;
             asrc[q] = A + (size_t)arow * Kd + dma_chunk * 8;
         }
         const uint16_t* wbase = W + (size_t)e * w_rows * Kd + (size_t)dma_row * Kd + dma_chunk * 8;
-        auto wrow0 = [&](int g) {   // first weight row of weight group g (wave-uniform)
-            const int tr = (g - AG) * 8;
+        auto wrow0 = [&](int q) {   // first weight row of this wave's weight group q
+            const int tr = (wave + NW * q) * 8;
             if (GATED) return (tr < BN / 2) ? (n_tile * (BN / 2) + tr) : (N + n_tile * (BN / 2) + tr - BN / 2);
             return n_tile * BN + tr;
         };
-        auto issue_one = [&](int stage, int q) {
-            const int g = wave + NW * q;
-            const uint32_t dst = ring0 + (stage % S) * STAGE + g * 1024;
-            const uint16_t* src = (g < AG) ? asrc[q < TPW ? q : 0] : wbase + (size_t)wrow0(g) * Kd;
-            lds_dma16(src + (size_t)stage * kBK, dst);
+        // DMA number q of a refill pair: tokens first (q < GA), then weights
+        auto issue_one = [&](int sa, int sw, int q) {
+            if (q < GA) {
+                lds_dma16(asrc[q < GA ? q : 0] + (size_t)sa * kBK,
+                          ringA0 + (sa % SA) * A_STAGE + (wave + NW * q) * 1024);
+            } else {
+                const int qw = q - GA;
+                lds_dma16(wbase + (size_t)wrow0(qw) * Kd + (size_t)sw * kBK,
+                          ringW0 + (sw % SW) * W_STAGE + (wave + NW * qw) * 1024);
+            }
         };
 
         moe_f32x16 acc[NS][MS];
@@ -470,75 +528,97 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_tiled_kernel(
 #pragma unroll
                 for (int q = 0; q < 16; ++q) acc[i][j][q] = 0.f;
 
-        moe_bf16x8 fw[2][NS];
+        moe_bf16x8 fw[2][NS], fa[2][MS];
         // fragments of half h (stage h/2, k steps 2*(h%2) and 2*(h%2)+1)
-        auto read_a = [&](int h, moe_bf16x8 (*fa)[MS]) {
-            const unsigned char* st = s_ring + ((h >> 1) % S) * STAGE;
-#pragma unroll
-            for (int sk = 0; sk < 2; ++sk)
-#pragma unroll
-                for (int j = 0; j < MS; ++j)
-                    fa[sk][j] = *reinterpret_cast<const moe_bf16x8*>(st + ga[j] + rd_off[2 * (h & 1) + sk]);
+        auto read_a = [&](int h, int sk, int j) {
+            const unsigned char* st = s_ringA + ((h >> 1) % SA) * A_STAGE;
+            fa[sk][j] = *reinterpret_cast<const moe_bf16x8*>(st + ga[j] + rd_off[2 * (h & 1) + sk]);
         };
         auto read_w = [&](int h, int sk, int i) {
-            const unsigned char* st = s_ring + ((h >> 1) % S) * STAGE;
+            const unsigned char* st = s_ringW + ((h >> 1) % SW) * W_STAGE;
             fw[sk][i] = *reinterpret_cast<const moe_bf16x8*>(st + gw[i] + rd_off[2 * (h & 1) + sk]);
         };
-        // half h: multiply it from registers while reading half h+1; when
-        // REFILL, load stage `refill` into its slot between the MFMA groups
-        auto half = [&](int h, moe_bf16x8 (*fa_c)[MS], moe_bf16x8 (*fa_n)[MS], bool refill,
-                        int stage) {
+        // half h: multiply it from registers while reading half h+1 into the
+        // same registers (each fragment right after its last MFMA of half h),
+        // and load tokens of stage sa (if RA and ra) and weights of stage sw
+        // (if RW) between the MFMA groups
+        auto half = [&](int h, auto RA, auto RW, bool ra, int sa, int sw) {
+            constexpr bool kRA = decltype(RA)::value, kRW = decltype(RW)::value;
+            constexpr int GP = GA + GW;
             if (active) {
-                read_a(h + 1, fa_n);
 #pragma unroll
                 for (int sk = 0; sk < 2; ++sk)
 #pragma unroll
                     for (int i = 0; i < NS; ++i) {
 #pragma unroll
-                        for (int j = 0; j < MS; ++j)
-                            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fw[sk][i], fa_c[sk][j], acc[i][j], 0, 0, 0);
+                        for (int j = 0; j < MS; ++j) {
+                            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fw[sk][i], fa[sk][j], acc[i][j], 0, 0, 0);
+                            if (i == NS - 1) read_a(h + 1, sk, j);
+                        }
                         read_w(h + 1, sk, i);
                         constexpr int SLOTS = 2 * NS;
                         const int slot = sk * NS + i;
-                        if (refill && (GPW >= SLOTS || (slot * GPW) / SLOTS != ((slot + 1) * GPW) / SLOTS)) {
+                        if (GP >= SLOTS || (slot * GP) / SLOTS != ((slot + 1) * GP) / SLOTS) {
 #pragma unroll
-                            for (int q = (slot * GPW) / SLOTS; q < ((slot + 1) * GPW) / SLOTS; ++q)
-                                issue_one(stage, q);
+                            for (int q = (slot * GP) / SLOTS; q < ((slot + 1) * GP) / SLOTS; ++q)
+                                if (q < GA ? (kRA && ra) : kRW) issue_one(sa, sw, q);
                         }
                     }
-            } else if (refill) {
+            } else {
 #pragma unroll
-                for (int q = 0; q < GPW; ++q) issue_one(stage, q);
+                for (int q = 0; q < GP; ++q)
+                    if (q < GA ? (kRA && ra) : kRW) issue_one(sa, sw, q);
             }
         };
+        const std::true_type yes{};
+        const std::false_type no{};
 
-        // prologue: stages 0..S-1 (or fewer) in flight, wait for stage 0
-        const int pre = nk < S ? nk : S;
-        for (int s2 = 0; s2 < pre; ++s2)
+        // prologue in the steady-state order: weights 0..SW-SA-1, then pairs
+        // (tokens s, weights s+SW-SA) for s < SA; wait for stage 0
 #pragma unroll
-            for (int q = 0; q < GPW; ++q) issue_one(s2, q);
-        if (pre == S) wait_vmcnt_barrier<GPW * (S - 1)>();
+        for (int s2 = 0; s2 < SW - SA; ++s2)
+            if (s2 < nk)
+#pragma unroll
+                for (int q = GA; q < GA + GW; ++q) issue_one(0, s2, q);
+#pragma unroll
+        for (int s2 = 0; s2 < SA; ++s2) {
+            const int sw2 = s2 + SW - SA;
+#pragma unroll
+            for (int q = 0; q < GA + GW; ++q)
+                if (q < GA ? s2 < nk : sw2 < nk) issue_one(s2, sw2, q);
+        }
+        if (SW - 1 < nk) wait_vmcnt_barrier<N_FIRST>();
         else wait_vmcnt_barrier<0>();
-        moe_bf16x8 fa0[2][MS], fa1[2][MS];
         if (active) {
-            read_a(0, fa0);
 #pragma unroll
-            for (int sk = 0; sk < 2; ++sk)
+            for (int sk = 0; sk < 2; ++sk) {
+#pragma unroll
+                for (int j = 0; j < MS; ++j) read_a(0, sk, j);
 #pragma unroll
                 for (int i = 0; i < NS; ++i) read_w(0, sk, i);
+            }
         }
-        for (int d = 0; d < nk; ++d) {
-            half(2 * d, fa0, fa1, false, 0);
-            // stage d+1 landed everywhere and slot d % S is free (see above;
-            // the wave's own reads of it have returned before the barrier);
-            // on the last stage the read-ahead takes stale but valid LDS data
-            // that is never used
+        // steady state: both refills due (d + SW < nk)
+        int d = 0;
+        for (; d + SW < nk; ++d) {
+            half(2 * d, no, no, false, 0, 0);
+            // stage d+1 landed everywhere and stage d's slots are free (see
+            // above; the wave's own reads of them have returned before the
+            // barrier)
             asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-            if (d + S - 1 < nk) wait_vmcnt_barrier<GPW * (S - 2)>();
-            else wait_vmcnt_barrier<0>();
-            half(2 * d + 1, fa1, fa0, d + S < nk, d + S);
+            wait_vmcnt_barrier<N_STEADY>();
+            half(2 * d + 1, yes, yes, true, d + SA, d + SW);
         }
-        // drain the ring before the next tile refills it
+        // last SW stages: no weight refills, token refills while d + SA < nk,
+        // full waits.  On the last stage the read-ahead takes stale but valid
+        // LDS data that is never used.
+        for (; d < nk; ++d) {
+            half(2 * d, no, no, false, 0, 0);
+            asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+            wait_vmcnt_barrier<0>();
+            half(2 * d + 1, yes, no, d + SA < nk, d + SA, 0);
+        }
+        // drain the rings before the epilogue reuses them
         wait_vmcnt_barrier<0>();
 
         // epilogue, staged through the idle ring so that the global stores are
@@ -552,7 +632,7 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_tiled_kernel(
         if (active) {
 #pragma unroll
             for (int j = 0; j < MS; ++j) {
-                unsigned char* orow = s_ring + (wm * WM + j * 32 + fr) * OP;
+                unsigned char* orow = s_lds + (wm * WM + j * 32 + fr) * OP;
                 if (GATED) {
 #pragma unroll
                     for (int i = 0; i < NS / 2; ++i)
@@ -586,7 +666,7 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_tiled_kernel(
         uint16_t* cbase = C + (size_t)r0 * N + n_tile * COLS;
         for (int idx = tid; idx < mrows * CPR; idx += NT) {
             const int r = idx / CPR, c = idx % CPR;
-            const unsigned char* src = s_ring + r * OP + c * 16;
+            const unsigned char* src = s_lds + r * OP + c * 16;
             const uint2 lo = *reinterpret_cast<const uint2*>(src);
             const uint2 hi = *reinterpret_cast<const uint2*>(src + 8);
             *reinterpret_cast<uint4*>(cbase + (size_t)r * N + c * 8) = make_uint4(lo.x, lo.y, hi.x, hi.y);
