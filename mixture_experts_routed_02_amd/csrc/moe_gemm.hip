@@ -300,12 +300,12 @@ __global__ __launch_bounds__(256) void gemm_skinny_gateup_dispatch_kernel(
 // fragment into its own registers right after its last MFMA of half h), so
 // every read of stage d is done by the start of half 2d+1.  There, each wave waits for its own
 // loads of stage d+1, one barrier tells every wave that stage d+1 has landed
-// everywhere and that nobody reads stage d's slots any more, and the wave
-// refills them: tokens of stage d+SA, then weights of stage d+SW, spread
-// between the MFMAs of the half.  Even halves wait for nothing.  Issue order
-// per wave: weights 0..SW-SA-1, then the pairs (tokens s, weights s+SW-SA)
-// for s < SA, then one such pair per odd half; the vmcnt of each wait counts
-// the loads issued after the ones it needs.
+// everywhere and that nobody reads stage d's slots any more; the wave refills
+// the token slot with stage d+SA during half 2d+1 and the weight slot with
+// stage d+SW during half 2d+2, each refill spread between the MFMAs of its
+// half, so that the loads of the eight waves do not arrive at the address
+// unit in one burst.  Even halves wait for nothing.  The vmcnt of each wait
+// counts the loads this wave issued after the ones it needs.
 //
 // WGM x WGN waves; each wave owns (BM/WGM) token rows x (BN/WGN) weight rows
 // of the tile as 32x32 MFMA sub-tiles (weights = MFMA rows, tokens = MFMA
@@ -425,8 +425,8 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_tiled_kernel(
     constexpr int LDS = RINGS > BM * OP ? RINGS : BM * OP;
     // loads issued after the ones a wait needs: at an odd half (stage d+1),
     // and in the prologue (stage 0)
-    constexpr int N_STEADY = (SW > SA ? GW : 0) + (SA - 2) * (GA + GW);
-    constexpr int N_FIRST = (SW > SA ? GW : 0) + (SA - 1) * (GA + GW);
+    constexpr int N_STEADY = SW > SA ? (SA - 1) * GW + (SA - 2) * GA : (SA - 2) * (GA + GW);
+    constexpr int N_FIRST = SW > SA ? (SA - 1) * (GA + GW) : (SA - 1) * GA + (SA - 2) * GW;
     static_assert(WM % 32 == 0 && WN % 32 == 0 && AG % NW == 0 && WG % NW == 0, "tile shape");
     static_assert(NW % 4 == 0, "a wave's DMA groups share one row-swizzle phase");
     static_assert(!GATED || NS % 2 == 0, "gated tiles pair gate and up sub-tiles");
@@ -540,11 +540,15 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_tiled_kernel(
         };
         // half h: multiply it from registers while reading half h+1 into the
         // same registers (each fragment right after its last MFMA of half h),
-        // and load tokens of stage sa (if RA and ra) and weights of stage sw
-        // (if RW) between the MFMA groups
-        auto half = [&](int h, auto RA, auto RW, bool ra, int sa, int sw) {
-            constexpr bool kRA = decltype(RA)::value, kRW = decltype(RW)::value;
-            constexpr int GP = GA + GW;
+        // and, if rf, spread the loads of one refill between the MFMA groups:
+        // tokens of stage `stage` (KIND 1) or weights of stage `stage` (KIND 2)
+        auto half = [&](int h, auto KIND, bool rf, int stage) {
+            constexpr int kKind = decltype(KIND)::value;
+            constexpr int GP = kKind == 1 ? GA : (kKind == 2 ? GW : 0);
+            auto issue = [&](int q) {
+                if (kKind == 1) issue_one(stage, 0, q);
+                else issue_one(0, stage, GA + q);
+            };
             if (active) {
 #pragma unroll
                 for (int sk = 0; sk < 2; ++sk)
@@ -558,36 +562,38 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_tiled_kernel(
                         read_w(h + 1, sk, i);
                         constexpr int SLOTS = 2 * NS;
                         const int slot = sk * NS + i;
-                        if (GP >= SLOTS || (slot * GP) / SLOTS != ((slot + 1) * GP) / SLOTS) {
+                        if (GP > 0 && (GP >= SLOTS || (slot * GP) / SLOTS != ((slot + 1) * GP) / SLOTS)) {
 #pragma unroll
                             for (int q = (slot * GP) / SLOTS; q < ((slot + 1) * GP) / SLOTS; ++q)
-                                if (q < GA ? (kRA && ra) : kRW) issue_one(sa, sw, q);
+                                if (rf) issue(q);
                         }
                     }
-            } else {
+            } else if (rf) {
 #pragma unroll
-                for (int q = 0; q < GP; ++q)
-                    if (q < GA ? (kRA && ra) : kRW) issue_one(sa, sw, q);
+                for (int q = 0; q < GP; ++q) issue(q);
             }
         };
-        const std::true_type yes{};
-        const std::false_type no{};
+        const std::integral_constant<int, 1> tokens{};
+        const std::integral_constant<int, 2> weights{};
 
-        // prologue in the steady-state order: weights 0..SW-SA-1, then pairs
-        // (tokens s, weights s+SW-SA) for s < SA; wait for stage 0
+        // prologue: the loads the k loop would have issued in earlier halves,
+        // in that order (weights s in half 2(s-SW+1), tokens s in half
+        // 2(s-SA)+1); then wait for stage 0
 #pragma unroll
-        for (int s2 = 0; s2 < SW - SA; ++s2)
-            if (s2 < nk)
+        for (int v = (2 - 2 * SW < 1 - 2 * SA ? 2 - 2 * SW : 1 - 2 * SA); v < 0; ++v) {
+            if ((v & 1) == 0) {
+                const int s2 = v / 2 + SW - 1;
+                if (s2 >= 0 && s2 < nk)
 #pragma unroll
-                for (int q = GA; q < GA + GW; ++q) issue_one(0, s2, q);
+                    for (int q = 0; q < GW; ++q) issue_one(0, s2, GA + q);
+            } else {
+                const int s2 = (v - 1) / 2 + SA;
+                if (s2 >= 0 && s2 < nk)
 #pragma unroll
-        for (int s2 = 0; s2 < SA; ++s2) {
-            const int sw2 = s2 + SW - SA;
-#pragma unroll
-            for (int q = 0; q < GA + GW; ++q)
-                if (q < GA ? s2 < nk : sw2 < nk) issue_one(s2, sw2, q);
+                    for (int q = 0; q < GA; ++q) issue_one(s2, 0, q);
+            }
         }
-        if (SW - 1 < nk) wait_vmcnt_barrier<N_FIRST>();
+        if (SW - 2 < nk && SA - 1 < nk) wait_vmcnt_barrier<N_FIRST>();
         else wait_vmcnt_barrier<0>();
         if (active) {
 #pragma unroll
@@ -598,25 +604,27 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_tiled_kernel(
                 for (int i = 0; i < NS; ++i) read_w(0, sk, i);
             }
         }
-        // steady state: both refills due (d + SW < nk)
+        // Stage d: half 2d refills weights of stage d+SW-1 (slot of stage d-1,
+        // whose reads were done at the barrier of half 2d-1); half 2d+1 waits
+        // for stage d+1, then refills tokens of stage d+SA.
         int d = 0;
         for (; d + SW < nk; ++d) {
-            half(2 * d, no, no, false, 0, 0);
+            half(2 * d, weights, true, d + SW - 1);
             // stage d+1 landed everywhere and stage d's slots are free (see
             // above; the wave's own reads of them have returned before the
             // barrier)
             asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
             wait_vmcnt_barrier<N_STEADY>();
-            half(2 * d + 1, yes, yes, true, d + SA, d + SW);
+            half(2 * d + 1, tokens, true, d + SA);
         }
-        // last SW stages: no weight refills, token refills while d + SA < nk,
-        // full waits.  On the last stage the read-ahead takes stale but valid
-        // LDS data that is never used.
+        // last SW stages: refills only while below nk, full waits.  On the
+        // last stage the read-ahead takes stale but valid LDS data that is
+        // never used.
         for (; d < nk; ++d) {
-            half(2 * d, no, no, false, 0, 0);
+            half(2 * d, weights, d + SW - 1 < nk, d + SW - 1);
             asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
             wait_vmcnt_barrier<0>();
-            half(2 * d + 1, yes, no, d + SA < nk, d + SA, 0);
+            half(2 * d + 1, tokens, d + SA < nk, d + SA);
         }
         // drain the rings before the epilogue reuses them
         wait_vmcnt_barrier<0>();
