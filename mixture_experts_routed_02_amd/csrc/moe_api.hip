@@ -125,6 +125,9 @@ moe_status_t forward_impl(const Shape& s, int hint, const uint16_t* x, const int
         if (moe::launch_gateup_fused_dispatch(s, plan, x, ids, ntok, offsets, row_src, token_row,
                                               wgu, h, st) != hipSuccess)
             return MOE_ERROR_LAUNCH;
+        if (moe::tiny_down_ok(s))   // tiny batch: the down kernel also combines
+            return launched(moe::launch_down_combine_tiny(s, h, offsets, wd, token_row, w, ntok,
+                                                          out, st));
         if (moe::launch_grouped_gemm(s, plan, false, h, nullptr, 1, offsets, wd, y, s.I, s.H, st) !=
             hipSuccess)
             return MOE_ERROR_LAUNCH;

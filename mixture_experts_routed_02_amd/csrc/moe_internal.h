@@ -56,6 +56,16 @@ hipError_t launch_gateup_fused_dispatch(const Shape& s, const GemmPlan& plan, co
                                         const int32_t* ids, const int32_t* ntok,
                                         int32_t* offsets, int32_t* row_src, int32_t* token_row,
                                         const uint16_t* W, uint16_t* h, hipStream_t st);
+// Down GEMM + weighted combine in one launch for tiny batches: usable when
+// T*K <= kTinyRows and I % 512 == 0 (tiny_down_ok); needs the expert_offsets
+// and token_row of the fused gate-up kernel.
+constexpr int kTinyRows = 16;
+inline bool tiny_down_ok(const Shape& s) {
+    return (long long)s.T * s.K <= kTinyRows && s.I % 512 == 0 && s.H % 16 == 0;
+}
+hipError_t launch_down_combine_tiny(const Shape& s, const uint16_t* h, const int32_t* offsets,
+                                    const uint16_t* W, const int32_t* token_row, const float* w,
+                                    const int32_t* ntok, uint16_t* out, hipStream_t st);
 hipError_t launch_combine(const Shape& s, const uint16_t* y, const int32_t* token_row,
                           const float* w, const int32_t* ntok, uint16_t* out, hipStream_t st);
 

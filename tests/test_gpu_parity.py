@@ -389,20 +389,28 @@ def test_zero_tokens():
 def test_small_batch_forward_composes(T, K, E, H, I, lo, hi, tv):
     """moe_forward on a small batch (T*K <= 1024, skinny plan: the gate-up
     kernel does the dispatch itself) equals the staged calls bit for bit and
-    the oracle to tolerance."""
+    the oracle to tolerance, on two calls in a row with one workspace.
+    Outputs start as a NaN sentinel: rows t < T_v must be written (zero rows
+    when nothing is valid), rows t >= T_v are left alone by both paths."""
     inp = rand_case(T, K, E, H, I, seed=31, lo=lo, hi=hi)
     d = to_dev(inp)
     p = moe.problem(T, K, E, H, I, 0, 1)
     nt = None if tv is None else torch.tensor([tv], dtype=torch.int32, device=DEV)
-    out = torch.zeros((T, H), dtype=torch.bfloat16, device=DEV)
-    out, off = ops.forward(p, d["x"], d["topk_ids"], d["topk_weights"], d["w_gateup"], d["w_down"],
-                           num_tokens_dev=nt, out=out)
+
+    def sentinel():
+        o = torch.empty((T, H), dtype=torch.bfloat16, device=DEV)
+        o.view(torch.int16).fill_(0x7FC1)
+        return o
+
     x_disp, off2, rs, tr = ops.dispatch(p, d["x"], d["topk_ids"], num_tokens_dev=nt)
     y = ops.expert_compute(p, x_disp, off2, d["w_gateup"], d["w_down"])
-    out2 = torch.zeros((T, H), dtype=torch.bfloat16, device=DEV)
-    ops.combine(p, y, tr, d["topk_weights"], num_tokens_dev=nt, out=out2)
-    assert torch.equal(off, off2)
-    assert torch.equal(out.view(torch.int16), out2.view(torch.int16))
+    out2 = ops.combine(p, y, tr, d["topk_weights"], num_tokens_dev=nt, out=sentinel())
+    ws = ops.make_workspace(p, DEV)
+    for call in range(2):
+        out, off = ops.forward(p, d["x"], d["topk_ids"], d["topk_weights"], d["w_gateup"],
+                               d["w_down"], num_tokens_dev=nt, out=sentinel(), workspace=ws)
+        assert torch.equal(off, off2), f"call {call}"
+        assert torch.equal(out.view(torch.int16), out2.view(torch.int16)), f"call {call}"
     tvv = T if tv is None else tv
     ref = oracle.forward(bits(inp["x"]), inp["topk_ids"].numpy(), inp["topk_weights"].numpy(),
                          bits(inp["w_gateup"]), bits(inp["w_down"]), num_valid_tokens=tvv)
