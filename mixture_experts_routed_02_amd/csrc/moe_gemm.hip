@@ -231,14 +231,14 @@ __global__ __launch_bounds__(256) void gemm_skinny_kernel(
 // out[t, cols] for every valid token with the combine kernel's arithmetic.
 // The result is bit-identical to the down GEMM followed by the combine, with
 // one launch fewer and no y rows through memory.  Needs the per-wave k range
-// to be whole blocks (I % 512 == 0).
+// to be whole blocks of 8 k-steps (I % 1024 == 0).
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(256) void down_combine_tiny_kernel(
     const uint16_t* __restrict__ A, const int32_t* __restrict__ offsets,
     const uint16_t* __restrict__ W, int E, int Kd, int N,
     const int32_t* __restrict__ token_row, const float* __restrict__ wts,
     const int32_t* __restrict__ ntok, int T, int topk, uint16_t* __restrict__ out) {
-    constexpr int U = 4;
+    constexpr int U = 8;   // 16 KB of weights in flight per wave
     __shared__ int s_e[kTinyRows], s_r0[kTinyRows], s_m[kTinyRows];
     __shared__ int s_ne;
     __shared__ float s_part[kTinyRows][4][16][17];   // [expert slot][wave][weight row][token row]

@@ -57,11 +57,11 @@ hipError_t launch_gateup_fused_dispatch(const Shape& s, const GemmPlan& plan, co
                                         int32_t* offsets, int32_t* row_src, int32_t* token_row,
                                         const uint16_t* W, uint16_t* h, hipStream_t st);
 // Down GEMM + weighted combine in one launch for tiny batches: usable when
-// T*K <= kTinyRows and I % 512 == 0 (tiny_down_ok); needs the expert_offsets
+// T*K <= kTinyRows and I % 1024 == 0 (tiny_down_ok); needs the expert_offsets
 // and token_row of the fused gate-up kernel.
-constexpr int kTinyRows = 16;
+constexpr int kTinyRows = 8;
 inline bool tiny_down_ok(const Shape& s) {
-    return (long long)s.T * s.K <= kTinyRows && s.I % 512 == 0 && s.H % 16 == 0;
+    return (long long)s.T * s.K <= kTinyRows && s.I % 1024 == 0 && s.H % 16 == 0;
 }
 hipError_t launch_down_combine_tiny(const Shape& s, const uint16_t* h, const int32_t* offsets,
                                     const uint16_t* W, const int32_t* token_row, const float* w,

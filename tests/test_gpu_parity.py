@@ -385,6 +385,11 @@ def test_zero_tokens():
     (37, 6, 16, 256, 192, -1, 20, None),
     (170, 6, 8, 128, 128, 0, 8, 101),        # T*K = 1020, device-side T_v
     (5, 2, 4, 64, 64, 7, 9, None),           # no valid assignment at all
+    # T*K <= 8 and I % 1024 == 0: the down kernel also does the combine
+    (1, 6, 96, 256, 1024, 0, 384, None),
+    (2, 4, 8, 128, 1024, 0, 8, None),        # duplicates likely: 8 rows over 8 experts
+    (4, 2, 8, 64, 1024, 0, 8, 3),            # device-side T_v
+    (1, 6, 8, 64, 1024, 9, 12, None),        # every id dropped: a zero row
 ])
 def test_small_batch_forward_composes(T, K, E, H, I, lo, hi, tv):
     """moe_forward on a small batch (T*K <= 1024, skinny plan: the gate-up
