@@ -4,19 +4,22 @@
 // pointwise op, then a down grouped GEMM; one column mapping and one
 // epilogue serve every row policy).
 //
-// Both kernels are persistent and fixed-grid.  Each workgroup first turns the
-// GPU-resident expert_offsets into an LDS table of per-expert tile starts
-// (tiles = ceil(M_e / BM) * n_tiles), so the valid-row count bounds all the
-// work on the device and the same launch serves every T_v (graph replay).
-// Tiles of one expert are numbered m-fastest, so the m-tiles that reuse one
-// weight tile run at the same time and share it through L2 / MALL.
+// Every kernel here is persistent and fixed-grid.  The tile schedule comes
+// from the GPU-resident expert_offsets (tiles = ceil(M_e / BM) * n_tiles per
+// expert; an LDS table in the skinny kernels, a per-wave scan in the tiled
+// one), so the valid-row count bounds all the work on the device and the same
+// launch serves every T_v (graph replay).  Tiles of one expert are numbered
+// m-fastest, so the m-tiles that reuse one weight tile run at the same time
+// and share it through L2 / MALL.
 //
 // MFMA operands are "swapped": the weight rows are the A operand (MFMA rows)
 // and the dispatched token rows the B operand (MFMA columns), so an
-// accumulator lane holds 4 consecutive output columns of one token row.
-// v_mfma_f32_16x16x32_bf16 lane layout (gfx950): lane l supplies A row l%16
-// and B column l%16 with 8 k-values each; lane groups l/16 = 0..3 cover k
-// blocks of 8; D[4*(l/16)+i][l%16] lands in accumulator i.
+// accumulator lane holds consecutive output columns of one token row.
+// v_mfma_f32_16x16x32_bf16 lane layout (gfx950, checked on the device): lane
+// l supplies A row l%16 and B column l%16 with 8 k-values each; lane groups
+// l/16 = 0..3 cover k blocks of 8; D[4*(l/16)+i][l%16] lands in accumulator
+// i.  v_mfma_f32_32x32x16_bf16 (tiled kernel): lane l supplies row l%32 with
+// k group l/32; D[(q/4)*8 + (l/32)*4 + q%4][l%32] lands in accumulator q.
 //
 // gated: W = [E, 2N, Kd] (rows [0,N) gate, [N,2N) up), C = bf16(silu(g)*u) [cap, N]
 // plain: W = [E, N, Kd],                                 C = bf16(acc)      [cap, N]
@@ -26,10 +29,6 @@
 
 namespace moe {
 namespace {
-
-__device__ __forceinline__ moe_bf16x8 load16(const uint16_t* p) {
-    return *reinterpret_cast<const moe_bf16x8*>(p);
-}
 
 // silu(z) = z / (1 + exp(-z)), with the hardware reciprocal (about 1 ulp of
 // fp32, far below the bf16 rounding that follows) in place of an IEEE divide
