@@ -1,0 +1,84 @@
+"""GPU parity at the edges of the supported range: the largest top-k and
+expert count, capacity above T*K, the single/multi-block dispatch boundary,
+and experts whose row counts fall exactly on (or one past) tile sizes.  Each
+case runs moe_forward under every plan, checks it against the float64 oracle
+(tolerances of the contract) and checks that the staged calls reproduce it
+bit for bit."""
+import numpy as np
+import pytest
+import torch
+
+import mixture_experts_routed_02_amd as moe
+import oracle
+from mixture_experts_routed_02_amd import ops
+
+from helpers import bits, check_close, f64
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda:0"
+
+
+def case_inputs(T, K, E, H, I, ids, seed):
+    g = torch.Generator().manual_seed(seed)
+    x = torch.randn((T, H), generator=g).to(torch.bfloat16)
+    wgu = (torch.randn((E, 2 * I, H), generator=g) * H ** -0.5).to(torch.bfloat16)
+    wd = (torch.randn((E, H, I), generator=g) * I ** -0.5).to(torch.bfloat16)
+    w = torch.softmax(torch.randn((T, K), generator=g), dim=1)
+    return {"x": x, "topk_ids": ids, "topk_weights": w, "w_gateup": wgu, "w_down": wd}
+
+
+def exact_rows_ids(counts, K):
+    """ids giving expert e exactly counts[e] rows (T*K = sum(counts)), shuffled."""
+    flat = np.concatenate([np.full(c, e, dtype=np.int32) for e, c in enumerate(counts)])
+    rng = np.random.default_rng(7)
+    rng.shuffle(flat)
+    return torch.from_numpy(flat.reshape(-1, K))
+
+
+def random_ids(T, K, lo, hi, seed):
+    g = torch.Generator().manual_seed(seed)
+    return torch.randint(lo, hi, (T, K), generator=g, dtype=torch.int32)
+
+
+CASES = {
+    # name: (T, K, E, H, I, capacity, ids)
+    "top_k_64": (24, 64, 80, 128, 128, 0, lambda: random_ids(24, 64, -3, 90, 1)),
+    "experts_512": (300, 4, 512, 128, 192, 0, lambda: random_ids(300, 4, 0, 512, 2)),
+    "capacity_above_TK": (100, 4, 8, 192, 128, 1000, lambda: random_ids(100, 4, 0, 9, 3)),
+    "dispatch_single_block_max": (1024, 8, 16, 64, 64, 0, lambda: random_ids(1024, 8, 0, 16, 4)),
+    "dispatch_multi_block_min": (8193, 1, 16, 64, 64, 0, lambda: random_ids(8193, 1, 0, 16, 5)),
+    # rows exactly a 256-, 128- and 64-row tile, one row past, one row, none
+    "tile_edges": (1, 1, 7, 128, 128, 0, None),
+}
+TILE_EDGE_COUNTS = [256, 257, 128, 129, 64, 1, 0]
+
+
+def build(name):
+    T, K, E, H, I, cap, mk = CASES[name]
+    if name == "tile_edges":
+        ids = exact_rows_ids(TILE_EDGE_COUNTS, 1)
+        T = ids.shape[0]
+    else:
+        ids = mk()
+    return T, K, E, H, I, cap, case_inputs(T, K, E, H, I, ids, seed=sum(map(ord, name)))
+
+
+@pytest.mark.parametrize("name", list(CASES))
+@pytest.mark.parametrize("hint", [0, 1, 2, 3, 4])
+def test_forward_limits(name, hint):
+    T, K, E, H, I, cap, inp = build(name)
+    d = {k: v.to(DEV) for k, v in inp.items()}
+    p = moe.problem(T, K, E, H, I, cap, hint)
+    out, off = ops.forward(p, d["x"], d["topk_ids"], d["topk_weights"], d["w_gateup"],
+                           d["w_down"])
+    ids_np = inp["topk_ids"].numpy()
+    _, o_off, _, _ = oracle.dispatch(ids_np, E, T)
+    assert np.array_equal(off.cpu().numpy(), o_off)
+    ref = oracle.forward(bits(inp["x"]), ids_np, inp["topk_weights"].numpy(),
+                         bits(inp["w_gateup"]), bits(inp["w_down"]))
+    check_close(f64(out), ref, f"{name}/hint{hint}")
+    # the staged calls give the same bits
+    x_disp, off2, _, tr = ops.dispatch(p, d["x"], d["topk_ids"])
+    y = ops.expert_compute(p, x_disp, off2, d["w_gateup"], d["w_down"])
+    out2 = ops.combine(p, y, tr, d["topk_weights"])
+    assert torch.equal(out.view(torch.int16), out2.view(torch.int16)), f"{name}/hint{hint}"
