@@ -272,7 +272,7 @@ def main():
     if not args.no_cpu_baseline:
         budget = args.cpu_tokens
         if budget is None:
-            budget = {"mixtral": 256, "tiny": 64}.get(cfg.name, max(16, min(T, 64)))
+            budget = {"mixtral": T, "tiny": 64}.get(cfg.name, max(16, min(T, 64)))
         result["cpu_baseline"] = cpu_baseline({"x": x_h, "topk_ids": ids_h, "topk_weights": w_h},
                                               wgu, wd, cfg, budget)
     print(json.dumps(result), flush=True)
