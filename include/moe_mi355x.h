@@ -67,7 +67,8 @@ typedef struct moe_problem {
     int32_t capacity;      /* rows of the dispatched buffers; 0 => T*K; must be >= T*K */
     int32_t kernel_hint;   /* grouped-GEMM plan: 0 auto (chosen from T*K/E on the host),
                               1 skinny (16-row tiles, in-workgroup split-K),
-                              2 tiled 64-row, 3 tiled 128-row, 4 tiled 256-row        */
+                              2 tiled 64-row, 3 tiled 128-row, 4 tiled large (192-row
+                              tiles; 256-row when I is not a multiple of 128)         */
 } moe_problem_t;
 
 typedef enum moe_status {

@@ -24,7 +24,7 @@ moe_status_t check_problem(const moe_problem_t* p, Shape* s) {
         return MOE_ERROR_INVALID_VALUE;
     if (p->top_k > 64 || p->num_experts > moe::kMaxExperts) return MOE_ERROR_NOT_SUPPORTED;
     if (p->hidden % 64 != 0 || p->intermediate % 64 != 0) return MOE_ERROR_NOT_SUPPORTED;
-    if (p->kernel_hint < 0 || p->kernel_hint > moe::kTiled256) return MOE_ERROR_INVALID_VALUE;
+    if (p->kernel_hint < 0 || p->kernel_hint > moe::kTiledLarge) return MOE_ERROR_INVALID_VALUE;
     const long long tk = (long long)p->num_tokens * p->top_k;
     if (tk > (1ll << 28)) return MOE_ERROR_NOT_SUPPORTED;
     const long long cap = p->capacity ? p->capacity : tk;

@@ -9,10 +9,11 @@
 // Larger ones run two fixed grids: a per-block histogram into the workspace,
 // then a scatter pass in which every block rebuilds its own prefix from those
 // histograms (no atomics across blocks, nothing to reset between calls).
-// Within a block, ranks among equal experts come from wave64 ballots: each
-// round takes the expert of the lowest remaining lane, ballots the lanes that
-// share it, and gives each such lane the popcount of the matching lanes below
-// it; per-wave counts are then scanned across waves in LDS.
+// Within a block, ranks among equal experts come from wave64 ballots: one
+// ballot per bit of the expert id gives each lane the mask of lanes holding
+// its expert, and the lane's rank is the popcount of that mask below it plus
+// the count of that expert earlier in the wave's slice; per-wave counts are
+// then scanned across waves in LDS.
 #include "moe_internal.h"
 
 namespace moe {
@@ -40,13 +41,24 @@ __global__ __launch_bounds__(kDispatchThreads) void dispatch_count_kernel(
 // SINGLE: one block handles all T*K assignments and builds its own histogram.
 // Otherwise block b handles assignments [b*chunk, (b+1)*chunk) and reads every
 // block's histogram from blk_counts.
+//
+// Wave w of the block owns the contiguous slice of kPer*64 assignments that
+// starts at a0 + w*kPer*64 and walks it 64 at a time in increasing order, so
+// a wave-local running count per expert gives every assignment its rank among
+// the earlier ones of the same expert in that slice.  One pass over the
+// per-wave counts (wave order) then turns them into per-wave bases; the rank
+// stays in a register until the final write.  The block needs four barriers
+// however many rounds it takes.
 template <bool SINGLE>
 __global__ __launch_bounds__(kDispatchThreads) void dispatch_scatter_kernel(
     const int32_t* __restrict__ ids, const int32_t* __restrict__ ntok, int T, int K, int E,
     const int32_t* __restrict__ blk_counts, int nblk, int32_t* __restrict__ offsets,
     int32_t* __restrict__ row_src, int32_t* __restrict__ token_row) {
     constexpr int kWaves = kDispatchThreads / 64;
-    __shared__ int s_base[kMaxExperts];            // next row of each expert in this block
+    constexpr int kPer = (SINGLE ? kDispatchSingleMax : kDispatchChunk) / kDispatchThreads;
+    static_assert(kPer * kDispatchThreads == (SINGLE ? kDispatchSingleMax : kDispatchChunk),
+                  "whole rounds");
+    __shared__ int s_base[kMaxExperts];            // this block's start inside each expert
     __shared__ int s_scan[kMaxExperts + 1];        // totals -> exclusive offsets
     __shared__ int s_wcnt[kWaves * kMaxExperts];   // per-wave counts -> per-wave bases
     __shared__ int s_wave[kWaves];
@@ -57,20 +69,51 @@ __global__ __launch_bounds__(kDispatchThreads) void dispatch_scatter_kernel(
     const long long ntotal = (long long)T * K;
     const long long a0 = SINGLE ? 0 : (long long)blockIdx.x * kDispatchChunk;
     const long long a1 = SINGLE ? ntotal : ((a0 + kDispatchChunk < ntotal) ? a0 + kDispatchChunk : ntotal);
+    const long long aw = a0 + (long long)wave * kPer * 64 + lane;   // round k adds 64*k
 
-    // 1. per-expert totals and this block's start inside each expert
-    if (SINGLE) {
-        for (int e = tid; e < E; e += blockDim.x) { s_base[e] = 0; s_scan[e] = 0; }
-        __syncthreads();
-        for (long long a = tid; a < nvalid; a += blockDim.x) {
-            int e = ids[a];
-            if (e >= 0 && e < E) atomicAdd(&s_scan[e], 1);
+    // expert of each owned assignment, -1 when dropped or past the end
+    int my_e[kPer];
+#pragma unroll
+    for (int k = 0; k < kPer; ++k) {
+        const long long a = aw + 64 * k;
+        int e = -1;
+        if (a < a1 && a < nvalid) {
+            const int v = ids[a];
+            if (v >= 0 && v < E) e = v;
         }
-    } else {
-        for (int e = tid; e < E; e += blockDim.x) {
+        my_e[k] = e;
+    }
+    for (int i = tid; i < kWaves * E; i += blockDim.x) s_wcnt[i] = 0;
+    __syncthreads();
+
+    // 1. wave-local ranks and per-wave counts; each wave touches only its own
+    //    row of s_wcnt, and a wave's LDS accesses take effect in program order
+    int my_rank[kPer];
+    int* wc = s_wcnt + wave * E;
+    const int nbits = moe_expert_bits(E);
+    const unsigned long long below = (1ull << lane) - 1ull;
+#pragma unroll
+    for (int k = 0; k < kPer; ++k) {
+        const int e = my_e[k];
+        const unsigned long long m = moe_match_mask(e, nbits);
+        const int before = __popcll(m & below);
+        const int run = e >= 0 ? wc[e] : 0;
+        my_rank[k] = run + before;
+        if (e >= 0 && before == 0) wc[e] = run + __popcll(m);   // lowest lane of its expert
+    }
+    __syncthreads();
+
+    // 2. per-expert totals and this block's start inside each expert
+    for (int e = tid; e < E; e += blockDim.x) {
+        if (SINGLE) {
+            int tot = 0;
+            for (int w = 0; w < kWaves; ++w) tot += s_wcnt[w * E + e];
+            s_base[e] = 0;
+            s_scan[e] = tot;
+        } else {
             int pre = 0, tot = 0;
             for (int b = 0; b < nblk; ++b) {
-                int c = blk_counts[(long long)b * E + e];
+                const int c = blk_counts[(long long)b * E + e];
                 tot += c;
                 pre += (b < (int)blockIdx.x) ? c : 0;
             }
@@ -78,28 +121,31 @@ __global__ __launch_bounds__(kDispatchThreads) void dispatch_scatter_kernel(
             s_scan[e] = tot;
         }
     }
-    for (int i = tid; i < kWaves * E; i += blockDim.x) s_wcnt[i] = 0;
     __syncthreads();
 
-    // 2. exclusive scan of the totals -> expert_offsets
+    // 3. exclusive scan of the totals -> expert_offsets; per-wave counts ->
+    //    per-wave first rows, in wave order
     moe_block_exclusive_scan(s_scan, E, s_wave);
     if (blockIdx.x == 0)
         for (int e = tid; e <= E; e += blockDim.x) offsets[e] = s_scan[e];
-    for (int e = tid; e < E; e += blockDim.x) s_base[e] += s_scan[e];
+    for (int e = tid; e < E; e += blockDim.x) {
+        int run = s_scan[e] + s_base[e];
+        for (int w = 0; w < kWaves; ++w) {
+            const int c = s_wcnt[w * E + e];
+            s_wcnt[w * E + e] = run;
+            run += c;
+        }
+    }
     __syncthreads();
 
-    // 3. stable scatter, blockDim assignments at a time
-    for (long long sb = a0; sb < a1; sb += blockDim.x) {
-        const long long a = sb + tid;
-        const bool in = a < a1;
-        int e = -1;
-        if (in && a < nvalid) {
-            int v = ids[a];
-            if (v >= 0 && v < E) e = v;
-        }
-        const int r = moe_stable_rows(e, E, s_wcnt, s_base);
-        if (in) {
-            if (r >= 0) {
+    // 4. scatter
+#pragma unroll
+    for (int k = 0; k < kPer; ++k) {
+        const long long a = aw + 64 * k;
+        if (a < a1) {
+            const int e = my_e[k];
+            if (e >= 0) {
+                const int r = wc[e] + my_rank[k];
                 row_src[r] = (int)a;
                 token_row[a] = r;
             } else {

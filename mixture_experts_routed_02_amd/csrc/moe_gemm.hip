@@ -844,22 +844,23 @@ hipError_t launch_down_combine_tiny(const Shape& s, const uint16_t* h, const int
 GemmPlan choose_plan(const Shape& s, int hint) {
     GemmPlan p{};
     int kind = hint;
-    if (kind < kSkinny || kind > kTiled256) {
+    if (kind < kSkinny || kind > kTiledLarge) {
         const double rows_per_expert = (double)s.T * s.K / (double)s.E;
         kind = rows_per_expert <= 24.0 ? kSkinny
-             : rows_per_expert <= 96.0 ? kTiled64 : kTiled256;
+             : rows_per_expert <= 96.0 ? kTiled64 : kTiledLarge;
     }
     p.kind = kind;
     if (kind == kSkinny) {
         p.grid_gateup = p.grid_down = 4 * kNumCUs;   // 4 workgroups fit per CU
         p.bn_gateup = p.bn_down = 16;
-    } else if (kind == kTiled256) {
-        // gate-up: 128 gate + 128 up rows; down: 256 or 128 weight rows,
-        // whichever fills the last round of tiles better
+    } else if (kind == kTiledLarge) {
+        // 192 token rows per tile.  gate-up: 128 gate + 128 up rows (256-row
+        // token tiles with 64 + 64 when I is not a multiple of 128); down: 256
+        // or 128 weight rows, whichever fills the last round of tiles better
         p.bn_gateup = (s.I % 128 == 0) ? 256 : 128;
         p.bn_down = (s.H % 128 == 0) ? 128 : 64;
         if (s.H % 256 == 0) {
-            const double m_tiles = s.E * std::ceil((double)s.T * s.K / s.E / 256.0);
+            const double m_tiles = s.E * std::ceil((double)s.T * s.K / s.E / 192.0);
             auto fill = [&](int bn) {
                 const double t = m_tiles * (s.H / bn);
                 return t / (std::ceil(t / kNumCUs) * kNumCUs);
@@ -902,9 +903,10 @@ hipError_t launch_grouped_gemm(const Shape& s, const GemmPlan& plan, bool gated,
             if (gated) return MOE_TILED(128, 128, 2, 2, true);
             return bn == 128 ? MOE_TILED(128, 128, 2, 2, false) : MOE_TILED(128, 64, 2, 2, false);
         default:
-            if (gated) return bn == 256 ? MOE_TILED(256, 256, 4, 2, true) : MOE_TILED(256, 128, 4, 2, true);
-            return bn == 256 ? MOE_TILED(256, 256, 4, 2, false)
-                 : bn == 128 ? MOE_TILED(256, 128, 4, 2, false) : MOE_TILED(128, 64, 2, 2, false);
+            // 192 = 2 x 96 token rows: a wave holds 3 x 2 sub-tiles of 32 x 32
+            if (gated) return bn == 256 ? MOE_TILED(192, 256, 2, 4, true) : MOE_TILED(256, 128, 4, 2, true);
+            return bn == 256 ? MOE_TILED(192, 256, 2, 4, false)
+                 : bn == 128 ? MOE_TILED(192, 128, 2, 4, false) : MOE_TILED(128, 64, 2, 2, false);
     }
 #undef MOE_TILED
 }

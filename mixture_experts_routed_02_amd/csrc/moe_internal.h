@@ -20,7 +20,7 @@ struct Shape {
 };
 
 // Grouped-GEMM plan, chosen on the host from host-known sizes only.
-enum GemmKind { kSkinny = 1, kTiled64 = 2, kTiled128 = 3, kTiled256 = 4 };
+enum GemmKind { kSkinny = 1, kTiled64 = 2, kTiled128 = 3, kTiledLarge = 4 };
 struct GemmPlan {
     int kind;
     int grid_gateup, grid_down;
@@ -135,26 +135,37 @@ __device__ __forceinline__ void moe_block_exclusive_scan(int* s, int n, int* s_w
     __syncthreads();
 }
 
+// Bits needed to tell the expert ids 0..E-1 apart.
+__device__ __forceinline__ int moe_expert_bits(int E) { return E <= 1 ? 0 : 32 - __clz(E - 1); }
+
+// The lanes of this wave that hold the same expert id as this lane, as a
+// 64-bit lane mask (meaningful for e >= 0; lanes with e < 0 are in no mask).
+// One ballot per bit of the id: a valid lane matches when it agrees on every
+// one of the nbits low bits, and ids are below 1 << nbits.  The cost is fixed
+// however many distinct experts the wave holds.
+__device__ __forceinline__ unsigned long long moe_match_mask(int e, int nbits) {
+    unsigned long long m = __ballot(e >= 0);
+    for (int b = 0; b < nbits; ++b) {
+        const int bit = (e >> b) & 1;
+        const unsigned long long v = __ballot(bit);
+        m &= bit ? v : ~v;
+    }
+    return m;
+}
+
 // Stable ranks of one chunk of assignments, one per thread of the block
 // (e = expert id, or -1 for an invalid assignment).  Within each wave the
-// lanes that share an expert are ranked with ballots (each round takes the
-// expert of the lowest remaining lane); per-wave counts are then turned into
-// bases in wave order, on top of the running per-expert bases s_base[E].
-// Returns the thread's row, or -1.  s_wc (nwaves x E) must be zero on entry
-// and is zero again on return; every thread of the block must call.
+// lanes that share an expert are ranked by the matching lanes below them;
+// per-wave counts are then turned into bases in wave order, on top of the
+// running per-expert bases s_base[E].  Returns the thread's row, or -1.
+// s_wc (nwaves x E) must be zero on entry and is zero again on return;
+// every thread of the block must call.
 __device__ __forceinline__ int moe_stable_rows(int e, int E, int* s_wc, int* s_base) {
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int nwaves = blockDim.x >> 6;
-    int rank = 0;
-    unsigned long long rem = __ballot(e >= 0);
-    while (rem) {
-        const int leader = __ffsll((long long)rem) - 1;
-        const int ve = __shfl(e, leader, 64);
-        const unsigned long long m = __ballot(e == ve);
-        if (e == ve) rank = __popcll(m & ((1ull << lane) - 1ull));
-        if (lane == leader) s_wc[wave * E + ve] = __popcll(m);
-        rem &= ~m;
-    }
+    const unsigned long long m = moe_match_mask(e, moe_expert_bits(E));
+    const int rank = __popcll(m & ((1ull << lane) - 1ull));
+    if (e >= 0 && rank == 0) s_wc[wave * E + e] = __popcll(m);   // lowest lane of its expert
     __syncthreads();
     for (int x = tid; x < E; x += blockDim.x) {   // counts -> bases, wave order
         int run = s_base[x];

@@ -49,14 +49,18 @@ CASES = {
     "dispatch_multi_block_min": (8193, 1, 16, 64, 64, 0, lambda: random_ids(8193, 1, 0, 16, 5)),
     # rows exactly a 256-, 128- and 64-row tile, one row past, one row, none
     "tile_edges": (1, 1, 7, 128, 128, 0, None),
+    # the 192-row tiles of the large plan: one short, exact, one past, two
+    # tiles (+1), and the 96-row half a wave pair covers (+1)
+    "tile_edges_192": (1, 1, 9, 256, 256, 0, None),
 }
-TILE_EDGE_COUNTS = [256, 257, 128, 129, 64, 1, 0]
+TILE_EDGE_COUNTS = {"tile_edges": [256, 257, 128, 129, 64, 1, 0],
+                    "tile_edges_192": [191, 192, 193, 384, 385, 96, 97, 1, 0]}
 
 
 def build(name):
     T, K, E, H, I, cap, mk = CASES[name]
-    if name == "tile_edges":
-        ids = exact_rows_ids(TILE_EDGE_COUNTS, 1)
+    if name in TILE_EDGE_COUNTS:
+        ids = exact_rows_ids(TILE_EDGE_COUNTS[name], 1)
         T = ids.shape[0]
     else:
         ids = mk()
