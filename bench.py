@@ -122,7 +122,7 @@ def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawTextHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--config", default="mixtral")
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--hint", type=int, default=0, help="grouped-GEMM plan (0 auto, 1-4 forced)")
