@@ -22,16 +22,23 @@ namespace {
 __global__ __launch_bounds__(kDispatchThreads) void dispatch_count_kernel(
     const int32_t* __restrict__ ids, const int32_t* __restrict__ ntok, int T, int K, int E,
     int32_t* __restrict__ blk_counts) {
+    constexpr int kPer = kDispatchChunk / kDispatchThreads;
     __shared__ int s_hist[kMaxExperts];
-    const int tv = moe_valid_tokens(ntok, T);
-    const long long nvalid = (long long)tv * K;
+    const long long ntotal = (long long)T * K;
+    const long long a0 = (long long)blockIdx.x * kDispatchChunk + threadIdx.x;
+    int v[kPer];   // requested together with the valid-token count
+#pragma unroll
+    for (int k = 0; k < kPer; ++k) {
+        const long long a = a0 + (long long)k * kDispatchThreads;
+        v[k] = a < ntotal ? ids[a] : -1;
+    }
+    const long long nvalid = (long long)moe_valid_tokens(ntok, T) * K;
     for (int e = threadIdx.x; e < E; e += blockDim.x) s_hist[e] = 0;
     __syncthreads();
-    const long long a0 = (long long)blockIdx.x * kDispatchChunk;
-    const long long a1 = (a0 + kDispatchChunk < nvalid) ? a0 + kDispatchChunk : nvalid;
-    for (long long a = a0 + threadIdx.x; a < a1; a += blockDim.x) {
-        int e = ids[a];
-        if (e >= 0 && e < E) atomicAdd(&s_hist[e], 1);  // integer: order-independent
+#pragma unroll
+    for (int k = 0; k < kPer; ++k) {
+        const long long a = a0 + (long long)k * kDispatchThreads;
+        if (a < nvalid && v[k] >= 0 && v[k] < E) atomicAdd(&s_hist[v[k]], 1);  // integer: order-independent
     }
     __syncthreads();
     for (int e = threadIdx.x; e < E; e += blockDim.x)
@@ -64,24 +71,24 @@ __global__ __launch_bounds__(kDispatchThreads) void dispatch_scatter_kernel(
     __shared__ int s_wave[kWaves];
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int tv = moe_valid_tokens(ntok, T);
-    const long long nvalid = (long long)tv * K;
     const long long ntotal = (long long)T * K;
     const long long a0 = SINGLE ? 0 : (long long)blockIdx.x * kDispatchChunk;
     const long long a1 = SINGLE ? ntotal : ((a0 + kDispatchChunk < ntotal) ? a0 + kDispatchChunk : ntotal);
     const long long aw = a0 + (long long)wave * kPer * 64 + lane;   // round k adds 64*k
 
-    // expert of each owned assignment, -1 when dropped or past the end
+    // expert of each owned assignment, -1 when dropped or past the end; the
+    // ids are requested together with the valid-token count, not after it
     int my_e[kPer];
 #pragma unroll
     for (int k = 0; k < kPer; ++k) {
         const long long a = aw + 64 * k;
-        int e = -1;
-        if (a < a1 && a < nvalid) {
-            const int v = ids[a];
-            if (v >= 0 && v < E) e = v;
-        }
-        my_e[k] = e;
+        my_e[k] = a < a1 ? ids[a] : -1;
+    }
+    const long long nvalid = (long long)moe_valid_tokens(ntok, T) * K;
+#pragma unroll
+    for (int k = 0; k < kPer; ++k) {
+        const long long a = aw + 64 * k;
+        if (!(a < nvalid && my_e[k] >= 0 && my_e[k] < E)) my_e[k] = -1;
     }
     for (int i = tid; i < kWaves * E; i += blockDim.x) s_wcnt[i] = 0;
     __syncthreads();

@@ -347,52 +347,95 @@ __global__ __launch_bounds__(256) void down_combine_tiny_kernel(
 
 // Gate-up GEMM of the skinny plan with the local dispatch done inside (for
 // T*K <= kFusedDispatchMax): every workgroup counts, scans and ranks the
-// assignments in LDS exactly as the dispatch kernels do, then runs its gate-up
-// tiles from that LDS copy; workgroup 0 also publishes expert_offsets, row_src
-// and token_row for the down GEMM and the combine.  This saves a launch in
-// the latency-bound small-batch regime.
+// assignments in LDS with the same stable order as the dispatch kernels, then
+// runs its gate-up tiles from that LDS copy; workgroup 0 also publishes
+// expert_offsets, row_src and token_row for the down GEMM and the combine.
+// This saves a launch in the latency-bound small-batch regime.  The ids are
+// read once, into registers, together with the valid-token count (not after
+// it); wave w ranks the contiguous slice of 256 assignments starting at 256*w
+// with per-bit ballot masks and a wave-local running count per expert, and
+// the per-wave counts double as the histogram.
 __global__ __launch_bounds__(256) void gemm_skinny_gateup_dispatch_kernel(
     const uint16_t* __restrict__ x, const int32_t* __restrict__ ids,
     const int32_t* __restrict__ ntok, int T, int topk, int E, int32_t* __restrict__ offsets,
     int32_t* __restrict__ row_src, int32_t* __restrict__ token_row,
     const uint16_t* __restrict__ W, uint16_t* __restrict__ C, int Kd, int N) {
-    __shared__ int s_off[kMaxExperts + 1];   // counts -> exclusive offsets
-    __shared__ int s_base[kMaxExperts];
-    __shared__ int s_wc[4 * kMaxExperts];
+    constexpr int kWaves = 4;
+    constexpr int kPer = kFusedDispatchMax / (64 * kWaves);   // assignments per lane
+    static_assert(kPer * 64 * kWaves == kFusedDispatchMax, "whole slices");
+    __shared__ int s_off[kMaxExperts + 1];        // totals -> exclusive offsets
+    __shared__ int s_wc[kWaves * kMaxExperts];    // per-wave counts -> per-wave first rows
     __shared__ int s_rows[kFusedDispatchMax];
     __shared__ int s_start[kMaxExperts + 1];
-    __shared__ int s_wave[4];
+    __shared__ int s_wave[kWaves];
     __shared__ float s_red[4 * 16 * 17];
 
-    const int tid = threadIdx.x;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const bool publish = blockIdx.x == 0;
-    const int tv = moe_valid_tokens(ntok, T);
-    const int nvalid = tv * topk, ntotal = T * topk;
-    for (int e = tid; e < E; e += blockDim.x) s_off[e] = 0;
-    for (int i = tid; i < 4 * E; i += blockDim.x) s_wc[i] = 0;
+    const int ntotal = T * topk;
+    const int aw = wave * kPer * 64 + lane;       // round k adds 64*k
+    int my_e[kPer];
+#pragma unroll
+    for (int k = 0; k < kPer; ++k) {
+        const int a = aw + 64 * k;
+        my_e[k] = a < ntotal ? ids[a] : -1;
+    }
+    const int nvalid = moe_valid_tokens(ntok, T) * topk;
+#pragma unroll
+    for (int k = 0; k < kPer; ++k) {
+        const int a = aw + 64 * k;
+        if (!(a < nvalid && my_e[k] >= 0 && my_e[k] < E)) my_e[k] = -1;
+    }
+    for (int i = tid; i < kWaves * E; i += blockDim.x) s_wc[i] = 0;
     __syncthreads();
-    for (int a = tid; a < nvalid; a += blockDim.x) {
-        const int e = ids[a];
-        if (e >= 0 && e < E) atomicAdd(&s_off[e], 1);  // integer counts: order-independent
+
+    // wave-local ranks; each wave touches only its own row of s_wc, and a
+    // wave's LDS accesses take effect in program order
+    int my_rank[kPer];
+    int* wc = s_wc + wave * E;
+    const int nbits = moe_expert_bits(E);
+    const unsigned long long below = (1ull << lane) - 1ull;
+#pragma unroll
+    for (int k = 0; k < kPer; ++k) {
+        const int e = my_e[k];
+        const unsigned long long m = moe_match_mask(e, nbits);
+        const int before = __popcll(m & below);
+        const int run = e >= 0 ? wc[e] : 0;
+        my_rank[k] = run + before;
+        if (e >= 0 && before == 0) wc[e] = run + __popcll(m);   // lowest lane of its expert
+    }
+    __syncthreads();
+    for (int e = tid; e < E; e += blockDim.x) {
+        int tot = 0;
+#pragma unroll
+        for (int w = 0; w < kWaves; ++w) tot += s_wc[w * E + e];
+        s_off[e] = tot;
     }
     __syncthreads();
     moe_block_exclusive_scan(s_off, E, s_wave);
-    for (int e = tid; e < E; e += blockDim.x) s_base[e] = s_off[e];
     if (publish)
         for (int e = tid; e <= E; e += blockDim.x) offsets[e] = s_off[e];
-    __syncthreads();
-    for (int a0 = 0; a0 < ntotal; a0 += blockDim.x) {
-        const int a = a0 + tid;
-        int e = -1;
-        if (a < nvalid) {
-            const int v = ids[a];
-            if (v >= 0 && v < E) e = v;
+    for (int e = tid; e < E; e += blockDim.x) {   // per-wave counts -> first rows, wave order
+        int run = s_off[e];
+#pragma unroll
+        for (int w = 0; w < kWaves; ++w) {
+            const int c = s_wc[w * E + e];
+            s_wc[w * E + e] = run;
+            run += c;
         }
-        const int r = moe_stable_rows(e, E, s_wc, s_base);
-        if (r >= 0) s_rows[r] = a;
-        if (publish && a < ntotal) {
-            token_row[a] = r;
-            if (r >= 0) row_src[r] = a;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int k = 0; k < kPer; ++k) {
+        const int a = aw + 64 * k;
+        if (a < ntotal) {
+            const int e = my_e[k];
+            const int r = e >= 0 ? wc[e] + my_rank[k] : -1;
+            if (r >= 0) s_rows[r] = a;
+            if (publish) {
+                token_row[a] = r;
+                if (r >= 0) row_src[r] = a;
+            }
         }
     }
     __syncthreads();

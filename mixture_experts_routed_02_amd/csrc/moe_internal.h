@@ -153,34 +153,4 @@ __device__ __forceinline__ unsigned long long moe_match_mask(int e, int nbits) {
     return m;
 }
 
-// Stable ranks of one chunk of assignments, one per thread of the block
-// (e = expert id, or -1 for an invalid assignment).  Within each wave the
-// lanes that share an expert are ranked by the matching lanes below them;
-// per-wave counts are then turned into bases in wave order, on top of the
-// running per-expert bases s_base[E].  Returns the thread's row, or -1.
-// s_wc (nwaves x E) must be zero on entry and is zero again on return;
-// every thread of the block must call.
-__device__ __forceinline__ int moe_stable_rows(int e, int E, int* s_wc, int* s_base) {
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int nwaves = blockDim.x >> 6;
-    const unsigned long long m = moe_match_mask(e, moe_expert_bits(E));
-    const int rank = __popcll(m & ((1ull << lane) - 1ull));
-    if (e >= 0 && rank == 0) s_wc[wave * E + e] = __popcll(m);   // lowest lane of its expert
-    __syncthreads();
-    for (int x = tid; x < E; x += blockDim.x) {   // counts -> bases, wave order
-        int run = s_base[x];
-        for (int w = 0; w < nwaves; ++w) {
-            const int c = s_wc[w * E + x];
-            s_wc[w * E + x] = run;
-            run += c;
-        }
-        s_base[x] = run;
-    }
-    __syncthreads();
-    const int r = e >= 0 ? s_wc[wave * E + e] + rank : -1;
-    __syncthreads();
-    for (int i = tid; i < nwaves * E; i += blockDim.x) s_wc[i] = 0;
-    __syncthreads();
-    return r;
-}
 #endif
