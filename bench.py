@@ -8,9 +8,16 @@ is already resident in HBM.  The default workload is the Mixtral-style layer
 selects another workload of the same family (see workloads.CONFIGS).
 
 Printed (one JSON line): expert-compute TFLOP/s of the layer (value), µs per
-layer, HBM GB/s, the roofline of the dominant kernel (the gate-up grouped
-GEMM, timed alone with HIP events on the stream it is launched on), and the
-CPU oracle timed on a bounded sample of the same workload.
+layer (mean, median, p10, p90), HBM GB/s, the three stages timed alone
+(stages_us: dispatch, expert compute, combine), the roofline of the dominant
+kernel (the gate-up grouped GEMM, timed alone with HIP events on the stream it
+is launched on), and the CPU oracle timed on a bounded sample of the same
+workload.  The decode workloads cycle 32 routing draws (seeds 1000..1031) one
+per step, with value and GB/s = sum of work / sum of time, so that draws that
+touch fewer experts (or none) count their time.  static_capacity adds
+`replays`: 50 HIP-graph replays, each with a device token count
+T_i ~ U{1..T}, with median/p10/p90 µs and the per-replay fraction of the
+binding roof.
 
 Algorithmic work (what the method must do, not what an implementation moves):
   F = 6*H*I*R flop, R = valid dispatched rows (2*H*2I gate-up + 2*I*H down per row)
@@ -132,6 +139,12 @@ def main():
     ap.add_argument("--graph", action="store_true",
                     help="time replays of the layer recorded as a HIP graph (moe_graph_*)")
     ap.add_argument("--kernel-reps", type=int, default=10)
+    ap.add_argument("--draws", type=int, default=None,
+                    help="routing draws cycled one per step (seeds 1000, 1001, ...; default 32 "
+                         "for the decode workloads, else 1 = the --seed routing)")
+    ap.add_argument("--replays", type=int, default=None,
+                    help="extra: HIP-graph replays with a device token count T_i ~ U{1..T} "
+                         "(default 50 for static_capacity, else 0)")
     ap.add_argument("--cpu-tokens", type=int, default=None,
                     help="tokens in the oracle's timed sample (default by workload)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -161,6 +174,12 @@ def main():
     ids_h, w_h = W.make_routing(cfg, args.seed)
     wgu, wd = W.make_weights(cfg, args.seed, dev)
     x, ids, w = x_h.to(dev), ids_h.to(dev), w_h.to(dev)
+    draws = args.draws if args.draws is not None else (32 if cfg.name.startswith("ep_decode") else 1)
+    if draws > 1:   # routing draws cycled one per step, same x and weights
+        routes_h = [W.make_routing(cfg, 1000 + d) for d in range(draws)]
+        routes = [(i_h.to(dev), w_h_.to(dev)) for i_h, w_h_ in routes_h]
+    else:
+        routes_h, routes = [(ids_h, w_h)], [(ids, w)]
     p = moe.problem(T, K, E, H, I, cfg.capacity, args.hint)
     ws = ops.make_workspace(p, dev)
     out = torch.empty((T, H), dtype=torch.bfloat16, device=dev)
@@ -176,20 +195,31 @@ def main():
     if args.graph:
         graph = ops.MoEGraph(p, x, ids, w, wgu, wd, expert_offsets=off, out=out, workspace=ws)
 
-    def step():
+    if args.graph and draws > 1:
+        raise SystemExit("--graph replays one recorded routing; use --draws 1")
+
+    def step(i=0):
         if graph is not None:
             graph.launch()
         else:
-            ops.forward(p, x, ids, w, wgu, wd, expert_offsets=off, out=out, workspace=ws)
+            ri, rw = routes[i % draws]
+            ops.forward(p, x, ri, rw, wgu, wd, expert_offsets=off, out=out, workspace=ws)
 
-    for _ in range(args.warmup):
-        step()
+    def work(ids_t, t_valid):
+        # algorithmic flop and bytes of one layer call (host copy of the routing)
+        v = ids_t[:t_valid]
+        v = v[(v >= 0) & (v < E)]
+        r = int(v.numel())
+        n_touched = int(torch.unique(v).numel()) if r else 0
+        return 6.0 * H * I * r, 6.0 * H * I * n_touched + 4.0 * H * t_valid + 8.0 * t_valid * K, r, n_touched
+
+    for i in range(args.warmup):
+        step(i)
     torch.cuda.synchronize()
-    offs = off.cpu().tolist()
-    R = offs[-1]
-    touched = sum(1 for e in range(E) if offs[e + 1] > offs[e])
-    F = 6.0 * H * I * R
-    B = 6.0 * H * I * touched + 4.0 * H * T + 8.0 * T * K
+    F, B, R, touched = work(ids_h, T)                 # the --seed routing (draw 0 if draws == 1)
+    FB = [work(i_h, T) for i_h, _ in routes_h]
+    F_steps = sum(FB[i % draws][0] for i in range(args.steps))
+    B_steps = sum(FB[i % draws][1] for i in range(args.steps))
 
     # ---- timed region: exactly `steps` layer calls ------------------------
     stream = torch.cuda.current_stream(dev)
@@ -200,13 +230,38 @@ def main():
     for i in range(args.steps):
         evict()
         ev[i][0].record(stream)
-        step()
+        step(i)
         ev[i][1].record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     per = [a.elapsed_time(b) for a, b in ev]          # ms
     ms_step = statistics.fmean(per) if args.cold else wall * 1e3 / args.steps
     sec = ms_step / 1e3
+    pct = statistics.quantiles(per, n=10, method="inclusive") if len(per) > 1 else per * 9
+
+    # ---- the three stages alone (same inputs, --seed routing) --------------
+    x_disp_s, off_s, row_src_s, token_row_s = ops.dispatch(p, x, ids, workspace=ws)
+    y_s = ops.expert_compute(p, x_disp_s, off_s, wgu, wd, workspace=ws)
+    out_s = torch.empty_like(out)
+    stage_calls = {
+        "dispatch": lambda: ops.dispatch(p, x, ids, workspace=ws,
+                                         out=(x_disp_s, off_s, row_src_s, token_row_s)),
+        "expert_compute": lambda: ops.expert_compute(p, x_disp_s, off_s, wgu, wd, workspace=ws,
+                                                     y_disp=y_s),
+        "combine": lambda: ops.combine(p, y_s, token_row_s, w, out=out_s),
+    }
+    stages_us = {}
+    for name, call in stage_calls.items():
+        sev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+               for _ in range(args.kernel_reps)]
+        torch.cuda.synchronize()
+        for a, b in sev:
+            evict()
+            a.record(stream)
+            call()
+            b.record(stream)
+        torch.cuda.synchronize()
+        stages_us[name] = statistics.fmean(a.elapsed_time(b) for a, b in sev) * 1e3
 
     # ---- dominant kernel alone: the gate-up grouped GEMM ------------------
     x_disp, off2, _, _ = ops.dispatch(p, x, ids)
@@ -241,9 +296,45 @@ def main():
     roof.update({"kernel": f"{kernel_name} (gate-up + SiLU epilogue)", "avg_launch_us": k_ms * 1e3,
                  "algorithmic_flop": F_gu, "algorithmic_bytes": B_gu})
 
+    # ---- extra: graph replays with a device token count T_i ~ U{1..T} -----
+    n_rep = args.replays if args.replays is not None else (50 if cfg.name == "static_capacity" else 0)
+    replays = None
+    if n_rep > 0:
+        ntok = torch.empty((1,), dtype=torch.int32, device=dev)
+        ntok.fill_(T)
+        g = ops.MoEGraph(p, x, ids, w, wgu, wd, num_tokens_dev=ntok, expert_offsets=off,
+                         out=out, workspace=ws)
+        gen = torch.Generator().manual_seed(args.seed)
+        t_i = torch.randint(1, T + 1, (n_rep,), generator=gen).tolist()
+        rev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+               for _ in range(n_rep)]
+        for _ in range(3):
+            g.launch()
+        torch.cuda.synchronize()
+        for (a, b), tv in zip(rev, t_i):
+            ntok.fill_(tv)        # a fill kernel on the same stream, outside the events
+            evict()
+            a.record(stream)
+            g.launch()
+            b.record(stream)
+        torch.cuda.synchronize()
+        rus = [a.elapsed_time(b) * 1e3 for a, b in rev]
+        fr = []
+        for tv, us in zip(t_i, rus):
+            f_i, b_i, _, _ = work(ids_h, tv)
+            fr.append(max(f_i / (PEAK_BF16_TFLOPS * 1e12), b_i / (PEAK_HBM_GBPS * 1e9)) / (us * 1e-6))
+        q = statistics.quantiles(rus, n=10, method="inclusive")
+        replays = {"n": n_rep, "tokens_min": min(t_i), "tokens_max": max(t_i),
+                   "us_median": statistics.median(rus), "us_p10": q[0], "us_p90": q[8],
+                   "roof_frac_median": statistics.median(fr), "roof_frac_min": min(fr),
+                   "roof_frac_max": max(fr),
+                   "note": "binding-roof fraction per replay: max(F_i/MFMA peak, B_i/HBM peak)/t_i"}
+        g.close()
+
+    total = sec * args.steps
     result = {
         "metric": METRIC,
-        "value": F / sec / 1e12,
+        "value": F_steps / total / 1e12,
         "unit": "TFLOP/s",
         "n_gpus": 1,
         "steps": args.steps,
@@ -251,10 +342,13 @@ def main():
         "ms_per_step": ms_step,
         "us_per_layer": ms_step * 1e3,
         "us_per_layer_median": statistics.median(per) * 1e3,
-        "hbm_gbps": B / sec / 1e9,
-        "layer_roofline": {"mfma_frac": F / sec / 1e12 / PEAK_BF16_TFLOPS,
-                           "hbm_frac": B / sec / 1e9 / PEAK_HBM_GBPS,
-                           "binding": "mfma" if F / max(B, 1.0) >= RIDGE else "hbm"},
+        "us_per_layer_p10": pct[0] * 1e3,
+        "us_per_layer_p90": pct[8] * 1e3,
+        "hbm_gbps": B_steps / total / 1e9,
+        "layer_roofline": {"mfma_frac": F_steps / total / 1e12 / PEAK_BF16_TFLOPS,
+                           "hbm_frac": B_steps / total / 1e9 / PEAK_HBM_GBPS,
+                           "binding": "mfma" if F_steps / max(B_steps, 1.0) >= RIDGE else "hbm"},
+        "stages_us": stages_us,
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -263,12 +357,17 @@ def main():
         "config": {"workload": describe(cfg), "tokens": T, "top_k": K, "experts": E,
                    "global_experts": cfg.pool, "hidden": H, "intermediate": I,
                    "capacity": p.capacity or T * K, "valid_rows": R, "experts_touched": touched,
+                   "routing_draws": draws,
+                   "valid_rows_mean": statistics.fmean(fb[2] for fb in FB),
+                   "experts_touched_mean": statistics.fmean(fb[3] for fb in FB),
                    "seed": args.seed, "timing": ("cold (L2/MALL evicted per step)" if args.cold
                                                  else "back-to-back")
                    + (", HIP graph replay" if args.graph else ", eager launches"),
                    "kernel_hint": args.hint},
         "roofline": roof,
     }
+    if replays is not None:
+        result["replays"] = replays
     if not args.no_cpu_baseline:
         budget = args.cpu_tokens
         if budget is None:
