@@ -120,9 +120,16 @@ def cpu_baseline(inp_host, wgu, wd, cfg, budget_tokens: int):
     dt = time.perf_counter() - t0
     rows = int(((ids[toks] >= 0) & (ids[toks] < cfg.num_experts)).sum())
     flops = 6.0 * cfg.hidden * cfg.intermediate * rows
+    model = ""
+    try:
+        with open("/proc/cpuinfo") as fh:
+            model = next((ln.split(":", 1)[1].strip() for ln in fh if ln.startswith("model name")), "")
+    except OSError:  # pragma: no cover
+        pass
     return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": cores, "kind": "oracle",
             "sample": f"first {len(toks)} tokens of the same inputs ({rows} expert rows), "
-                      f"float64 numpy, {dt:.1f} s"}
+                      f"float64 numpy, {dt:.1f} s",
+            "host": {"nproc": os.cpu_count(), "cpu_model": model}}
 
 
 def main():
