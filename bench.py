@@ -8,8 +8,9 @@ is already resident in HBM.  The default workload is the Mixtral-style layer
 selects another workload of the same family (see workloads.CONFIGS).
 
 Printed (one JSON line): expert-compute TFLOP/s of the layer (value), µs per
-layer (mean, median, p10, p90), HBM GB/s, the three stages timed alone
-(stages_us: dispatch, expert compute, combine), the roofline of the dominant
+layer (mean, median, p10, p90), HBM GB/s, the stages timed alone
+(stages_us: dispatch, expert compute, combine, and the router top-k ahead of
+dispatch for the softmax-routed workloads), the roofline of the dominant
 kernel (the gate-up grouped GEMM, timed alone with HIP events on the stream it
 is launched on), and the CPU oracle timed on a bounded sample of the same
 workload.  The decode workloads cycle 32 routing draws (seeds 1000..1031) one
@@ -246,7 +247,37 @@ def main():
     sec = ms_step / 1e3
     pct = statistics.quantiles(per, n=10, method="inclusive") if len(per) > 1 else per * 9
 
-    # ---- the three stages alone (same inputs, --seed routing) --------------
+    def timed(call):
+        """Mean event-timed ms of `call` over --kernel-reps calls (an eviction
+        read before each under --cold).  Calls shorter than the host's launch
+        latency are enqueued behind a bounded spin kernel, so that the events
+        see the GPU's time rather than the host's."""
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record(stream)
+        call()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        short = e0.elapsed_time(e1) < 0.3
+        sev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+               for _ in range(args.kernel_reps)]
+        if short:
+            torch.cuda._sleep(5_000_000)
+        for a, b in sev:
+            evict()
+            a.record(stream)
+            call()
+            b.record(stream)
+        torch.cuda.synchronize()
+        return statistics.fmean(a.elapsed_time(b) for a, b in sev)
+
+    # ---- dominant kernel alone: the gate-up grouped GEMM ------------------
+    x_disp, off2, _, _ = ops.dispatch(p, x, ids)
+    hbuf = torch.empty((p.capacity or T * K, I), dtype=torch.bfloat16, device=dev)
+    ops.gate_up(p, x_disp, off2, wgu, h=hbuf)
+    k_ms = timed(lambda: ops.gate_up(p, x_disp, off2, wgu, h=hbuf))
+
+    # ---- the stages alone (same inputs, --seed routing) -------------------
     x_disp_s, off_s, row_src_s, token_row_s = ops.dispatch(p, x, ids, workspace=ws)
     y_s = ops.expert_compute(p, x_disp_s, off_s, wgu, wd, workspace=ws)
     out_s = torch.empty_like(out)
@@ -257,33 +288,17 @@ def main():
                                                      y_disp=y_s),
         "combine": lambda: ops.combine(p, y_s, token_row_s, w, out=out_s),
     }
-    stages_us = {}
-    for name, call in stage_calls.items():
-        sev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-               for _ in range(args.kernel_reps)]
-        torch.cuda.synchronize()
-        for a, b in sev:
-            evict()
-            a.record(stream)
-            call()
-            b.record(stream)
-        torch.cuda.synchronize()
-        stages_us[name] = statistics.fmean(a.elapsed_time(b) for a, b in sev) * 1e3
+    if cfg.routing == "softmax_topk":   # the router step ahead of dispatch, on the same seed's logits
+        logits = W.make_logits(cfg, args.seed).to(dev)
+        ids_r = torch.empty_like(ids)
+        w_r = torch.empty_like(w)
+        stage_calls = {"router": lambda: ops.router_topk(p, logits, topk_ids=ids_r, topk_weights=w_r),
+                       **stage_calls}
+    # long calls first: the spin that short calls sit behind lowers the clock
+    # for a while after it
+    order = ["expert_compute", "combine", "dispatch", "router"]
+    stages_us = {name: timed(stage_calls[name]) * 1e3 for name in order if name in stage_calls}
 
-    # ---- dominant kernel alone: the gate-up grouped GEMM ------------------
-    x_disp, off2, _, _ = ops.dispatch(p, x, ids)
-    hbuf = torch.empty((p.capacity or T * K, I), dtype=torch.bfloat16, device=dev)
-    ops.gate_up(p, x_disp, off2, wgu, h=hbuf)
-    kev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-           for _ in range(args.kernel_reps)]
-    torch.cuda.synchronize()
-    for i in range(args.kernel_reps):
-        evict()
-        kev[i][0].record(stream)
-        ops.gate_up(p, x_disp, off2, wgu, h=hbuf)
-        kev[i][1].record(stream)
-    torch.cuda.synchronize()
-    k_ms = statistics.fmean(a.elapsed_time(b) for a, b in kev)
     F_gu = 4.0 * H * I * R
     B_gu = 4.0 * H * I * touched + 2.0 * H * R + 2.0 * I * R
     mfma_bound = (F_gu / max(B_gu, 1.0)) >= RIDGE
@@ -311,8 +326,7 @@ def main():
         ntok.fill_(T)
         g = ops.MoEGraph(p, x, ids, w, wgu, wd, num_tokens_dev=ntok, expert_offsets=off,
                          out=out, workspace=ws)
-        gen = torch.Generator().manual_seed(args.seed)
-        t_i = torch.randint(1, T + 1, (n_rep,), generator=gen).tolist()
+        t_i = W.make_static_token_counts(args.seed, n_rep, T)
         rev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
                for _ in range(n_rep)]
         for _ in range(3):

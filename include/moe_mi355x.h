@@ -143,6 +143,22 @@ MOE_API moe_status_t moe_combine(const moe_problem_t* p, const uint16_t* y_disp,
                          const float* topk_weights, const int32_t* num_tokens_dev,
                          uint16_t* out, void* stream);
 
+/* Router top-k, the step ahead of moe_dispatch (TileOps PR #1738, Summary:
+ * routing weights are produced outside expert compute).  For t < T_v and the
+ * E = num_experts router logits of token t:
+ *   topk_ids[t, 0..K-1]     indices of the K largest logits, in decreasing
+ *                           order; equal values in increasing index
+ *   topk_weights[t, j]      exp(l_j - l_0) / sum_{i<K} exp(l_i - l_0) over the
+ *                           selected logits l_0 >= l_1 >= ... (fp32, sum in
+ *                           increasing j)
+ *   logits fp32 [T, E] (finite values; -0 and +0 are equal), topk_ids int32
+ *   [T, K], topk_weights fp32 [T, K]; rows t >= T_v are not written.
+ * Requires K <= E.  The outputs feed moe_dispatch / moe_forward directly.
+ * hidden, intermediate and capacity are not used beyond the usual checks. */
+MOE_API moe_status_t moe_router_topk(const moe_problem_t* p, const float* logits,
+                                     const int32_t* num_tokens_dev, int32_t* topk_ids,
+                                     float* topk_weights, void* stream);
+
 /* The whole layer: dispatch, expert compute (the row gather fused into the
  * gate-up GEMM's operand loads) and combine, enqueued back to back.
  *   expert_offsets  out int32 [E+1] (the GPU-resident valid-row view)

@@ -17,11 +17,12 @@ MOE_ERROR_NOT_SUPPORTED = 2
 MOE_ERROR_LAUNCH = 3
 
 # kernel_hint values
-HINT_AUTO, HINT_SKINNY, HINT_TILED64, HINT_TILED128, HINT_TILED256 = 0, 1, 2, 3, 4
+HINT_AUTO, HINT_SKINNY, HINT_TILED64, HINT_TILED128, HINT_TILED_LARGE = 0, 1, 2, 3, 4
 
 EXPORTS = (
     "moe_status_string", "moe_workspace_size", "moe_dispatch", "moe_expert_compute",
-    "moe_gate_up", "moe_down", "moe_combine", "moe_forward", "moe_graph_create", "moe_graph_launch", "moe_graph_destroy",
+    "moe_gate_up", "moe_down", "moe_combine", "moe_router_topk", "moe_forward", "moe_graph_create",
+    "moe_graph_launch", "moe_graph_destroy",
 )
 
 
@@ -55,6 +56,7 @@ _SIGS = {
     "moe_gate_up": (ctypes.c_int, [_PP, _P, _P, _P, _P, _P]),
     "moe_down": (ctypes.c_int, [_PP, _P, _P, _P, _P, _P]),
     "moe_combine": (ctypes.c_int, [_PP, _P, _P, _P, _P, _P, _P]),
+    "moe_router_topk": (ctypes.c_int, [_PP, _P, _P, _P, _P, _P]),
     "moe_forward": (ctypes.c_int, [_PP, _P, _P, _P, _P, _P, _P, _P, _P, _P, _SZ, _P]),
     "moe_graph_create": (ctypes.c_int, [_PP, _P, _P, _P, _P, _P, _P, _P, _P, _P, _SZ,
                                         ctypes.POINTER(ctypes.c_void_p)]),

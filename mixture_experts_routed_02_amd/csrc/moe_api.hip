@@ -252,6 +252,22 @@ moe_status_t moe_combine(const moe_problem_t* p, const uint16_t* y_disp, const i
                                         static_cast<hipStream_t>(stream)));
 }
 
+moe_status_t moe_router_topk(const moe_problem_t* p, const float* logits,
+                             const int32_t* num_tokens_dev, int32_t* topk_ids,
+                             float* topk_weights, void* stream) {
+    Shape s;
+    moe_status_t st = check_problem(p, &s);
+    if (st != MOE_SUCCESS) return st;
+    if (s.K > s.E) return MOE_ERROR_INVALID_VALUE;
+    const long long tk = (long long)s.T * s.K;
+    if (bad_i32(logits, (long long)s.T * s.E) || bad_i32(topk_ids, tk) || bad_i32(topk_weights, tk))
+        return MOE_ERROR_INVALID_VALUE;
+    if (num_tokens_dev && !aligned(num_tokens_dev, 4)) return MOE_ERROR_INVALID_VALUE;
+    if (s.T == 0) return MOE_SUCCESS;
+    return launched(moe::launch_router(s, logits, num_tokens_dev, topk_ids, topk_weights,
+                                       static_cast<hipStream_t>(stream)));
+}
+
 moe_status_t moe_forward(const moe_problem_t* p, const uint16_t* x, const int32_t* topk_ids,
                          const float* topk_weights, const uint16_t* w_gateup,
                          const uint16_t* w_down, const int32_t* num_tokens_dev,

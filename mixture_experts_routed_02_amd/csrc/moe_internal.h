@@ -68,6 +68,9 @@ hipError_t launch_down_combine_tiny(const Shape& s, const uint16_t* h, const int
                                     const int32_t* ntok, uint16_t* out, hipStream_t st);
 hipError_t launch_combine(const Shape& s, const uint16_t* y, const int32_t* token_row,
                           const float* w, const int32_t* ntok, uint16_t* out, hipStream_t st);
+// router top-k: ids [T,K], weights [T,K] from logits fp32 [T,E]
+hipError_t launch_router(const Shape& s, const float* logits, const int32_t* ntok, int32_t* ids,
+                         float* wts, hipStream_t st);
 
 }  // namespace moe
 

@@ -155,6 +155,27 @@ def combine(p: MoeProblem, y_disp, token_row, topk_weights, num_tokens_dev=None,
     return out
 
 
+def router_topk(p: MoeProblem, logits, num_tokens_dev=None, topk_ids=None, topk_weights=None):
+    """Router top-k over fp32 logits [T, E]: the K largest per token (equal
+    values in increasing expert index) and the softmax over them.  Returns
+    (topk_ids int32 [T, K], topk_weights fp32 [T, K]); rows t >= T_v are left
+    as they were."""
+    T, K, E = p.num_tokens, p.top_k, p.num_experts
+    dev = logits.device
+    _need(logits, "logits", torch.float32, (T, E))
+    nt = _ntok(num_tokens_dev, dev)
+    if topk_ids is None:
+        topk_ids = torch.empty((T, K), dtype=torch.int32, device=dev)
+    if topk_weights is None:
+        topk_weights = torch.empty((T, K), dtype=torch.float32, device=dev)
+    _need(topk_ids, "topk_ids", torch.int32, (T, K), dev)
+    _need(topk_weights, "topk_weights", torch.float32, (T, K), dev)
+    check("moe_router_topk", lib().moe_router_topk(
+        ctypes.byref(p), _ptr(logits), _ptr(nt), _ptr(topk_ids), _ptr(topk_weights),
+        _stream_ptr(dev)))
+    return topk_ids, topk_weights
+
+
 def _forward_args(p, x, topk_ids, topk_weights, w_gateup, w_down, num_tokens_dev, offsets, out,
                   workspace):
     T, K, E, H, I = p.num_tokens, p.top_k, p.num_experts, p.hidden, p.intermediate

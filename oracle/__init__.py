@@ -47,7 +47,7 @@ from __future__ import annotations
 import numpy as np
 
 __all__ = [
-    "bf16_to_f64", "f64_to_bf16_bits", "dispatch", "silu", "expert_mlp",
+    "bf16_to_f64", "f64_to_bf16_bits", "router_topk", "dispatch", "silu", "expert_mlp",
     "expert_compute", "combine", "forward", "forward_tokens",
 ]
 
@@ -78,6 +78,33 @@ def f64_to_bf16_bits(v) -> np.ndarray:
 # ---------------------------------------------------------------------------
 # Local dispatch (TileOps PR #1738, Summary and Scope)
 # ---------------------------------------------------------------------------
+def router_topk(logits, top_k: int, num_valid_tokens: int | None = None):
+    """Router top-k, the step ahead of dispatch (TileOps PR #1738, Summary:
+    the routing weights are produced outside expert compute and carried next
+    to the ids).  Reading of the routing the workloads describe: for each
+    token t < T_v, the top_k largest of its E logits in decreasing order, equal
+    values in increasing expert index, and the softmax over those selected
+    values, w_j = exp(l_j - l_0) / sum_i exp(l_i - l_0).
+
+    logits: fp32 [T, E] (widened exactly to float64, so the selection compares
+    the very values the GPU compares).  Returns (ids int32 [T_v, K],
+    weights float64 [T_v, K])."""
+    lg = np.asarray(logits, dtype=np.float64)
+    T, E = lg.shape
+    tv = T if num_valid_tokens is None else max(0, min(T, int(num_valid_tokens)))
+    ids = np.empty((tv, top_k), dtype=np.int32)
+    w = np.empty((tv, top_k), dtype=np.float64)
+    index = np.arange(E)
+    for t in range(tv):
+        # lexsort: the last key is the primary one -- value descending, then index
+        sel = np.lexsort((index, -lg[t]))[:top_k]
+        v = lg[t, sel]
+        ex = np.exp(v - v[0])
+        ids[t] = sel
+        w[t] = ex / ex.sum()
+    return ids, w
+
+
 def dispatch(topk_ids, num_experts: int, num_valid_tokens: int | None = None):
     """Stable counting sort of the routed assignments into a tight,
     expert-major batch.

@@ -25,7 +25,7 @@ def declared_functions():
 
 def test_exports_every_declared_symbol():
     names = declared_functions()
-    assert len(names) == 11, names
+    assert len(names) == 12, names
     L = moe.lib()
     for n in names:
         assert hasattr(L, n), n
@@ -94,6 +94,15 @@ def test_bad_pointers_rejected():
     assert L.moe_dispatch(ctypes.byref(p), A16, None, None, A16, A4, A4, A4, A16, ws, None) == 1
     assert L.moe_expert_compute(ctypes.byref(p), A16, A4, A16, A16, A16, A16, ws - 256, None) == 1
     assert L.moe_combine(ctypes.byref(p), A16, A4, A4, None, A16 + 8, None) == 1
+    # router: K > E, null and misaligned pointers, all before any launch
+    pk = moe.problem(64, 9, 8, 256, 512)
+    assert L.moe_router_topk(ctypes.byref(pk), A4, None, A4, A4, None) == 1
+    assert L.moe_router_topk(ctypes.byref(p), None, None, A4, A4, None) == 1
+    assert L.moe_router_topk(ctypes.byref(p), A4, None, None, A4, None) == 1
+    assert L.moe_router_topk(ctypes.byref(p), A4, None, A4, A4 + 1, None) == 1
+    assert L.moe_router_topk(ctypes.byref(p), A4, A4 + 2, A4, A4, None) == 1
+    assert L.moe_router_topk(ctypes.byref(moe.problem(0, 2, 8, 256, 512)), None, None, None, None,
+                             None) == 0   # T = 0: nothing to do
     assert L.moe_graph_launch(None, None) == 1
     assert L.moe_graph_destroy(None) == 1
     h = ctypes.c_void_p()

@@ -283,3 +283,70 @@ def test_stages_compose_to_forward():
         np.testing.assert_allclose(out, ref, rtol=1e-13, atol=1e-15)
         sub = oracle.expert_compute(x_disp, off, wgub, wdb, rows=np.arange(0, int(off[-1]), 3))
         np.testing.assert_allclose(sub, y[::3], rtol=1e-13, atol=1e-15)
+
+
+# ---------------------------------------------------------------------------
+# Router top-k
+# ---------------------------------------------------------------------------
+def _check_router_order(lg, ids, K):
+    """Each selected expert beats every unselected one (larger value, or the
+    same value and a lower index), the picks are distinct and in decreasing
+    order with the same tie rule."""
+    T, E = lg.shape
+    for t in range(ids.shape[0]):
+        sel = [int(e) for e in ids[t]]
+        assert len(set(sel)) == K and all(0 <= e < E for e in sel)
+        for a, b in zip(sel, sel[1:]):
+            assert lg[t, a] > lg[t, b] or (lg[t, a] == lg[t, b] and a < b)
+        last = sel[-1]
+        for u in set(range(E)) - set(sel):
+            assert lg[t, last] > lg[t, u] or (lg[t, last] == lg[t, u] and last < u)
+
+
+@pytest.mark.parametrize("T,E,K,seed,ties", [(40, 8, 2, 0, False), (30, 96, 6, 1, False),
+                                             (20, 64, 64, 2, False), (25, 16, 5, 3, True),
+                                             (10, 512, 17, 4, True), (12, 1, 1, 5, False)])
+def test_router_order_and_weights(T, E, K, seed, ties):
+    rng = np.random.default_rng(seed)
+    lg = rng.standard_normal((T, E)).astype(np.float32)
+    if ties:                        # many equal values: the index decides
+        lg = np.round(lg * 2).astype(np.float32)
+    ids, w = oracle.router_topk(lg, K)
+    _check_router_order(lg, ids, K)
+    # weights: positive, sum to one, ratios exp(l_j - l_0)
+    assert np.all(w > 0)
+    assert np.allclose(w.sum(axis=1), 1.0, rtol=0, atol=1e-12)
+    l64 = lg.astype(np.float64)
+    for t in range(T):
+        v = l64[t, ids[t]]
+        assert np.allclose(w[t] / w[t, 0], np.exp(v - v[0]), rtol=1e-12, atol=0)
+
+
+def test_router_closed_forms_and_ties():
+    # K = 1: weight exactly 1; K = 2: the logistic of the logit gap
+    lg = np.array([[0.5, 2.0, -1.0, 2.0], [-0.0, 0.0, -3.0, -3.0]], dtype=np.float32)
+    ids, w = oracle.router_topk(lg, 1)
+    assert ids.tolist() == [[1], [0]] and np.all(w == 1.0)   # ties: lower index; -0 == +0
+    ids, w = oracle.router_topk(lg, 2)
+    assert ids.tolist() == [[1, 3], [0, 1]]
+    assert np.allclose(w, 0.5, rtol=0, atol=0)
+    lg = np.array([[1.0, 3.0, 2.0]], dtype=np.float32)
+    ids, w = oracle.router_topk(lg, 2)
+    assert ids.tolist() == [[1, 2]]
+    assert abs(w[0, 1] - 1.0 / (1.0 + math.exp(1.0))) < 1e-15
+    # valid-token bound
+    ids, w = oracle.router_topk(np.zeros((5, 4), np.float32), 3, num_valid_tokens=2)
+    assert ids.shape == (2, 3) and ids.tolist() == [[0, 1, 2], [0, 1, 2]]
+
+
+def test_router_matches_generator():
+    """The Mixtral-style workload draws its routing as torch.argsort of the
+    negated logits (stable) and a torch softmax over the selected ones."""
+    import workloads as W
+    for name in ("tiny", "mixtral"):
+        cfg = W.CONFIGS[name]
+        lg = W.make_logits(cfg, 3)
+        ids_g, w_g = W.make_routing(cfg, 3)
+        ids, w = oracle.router_topk(lg.numpy(), cfg.top_k)
+        assert np.array_equal(ids, ids_g.numpy())
+        assert np.abs(w - w_g.numpy().astype(np.float64)).max() < 1e-6

@@ -160,6 +160,17 @@ def make_routing(cfg: MoEConfig, seed: int, num_tokens: Optional[int] = None):
     return ids.to(torch.int32).contiguous(), w.contiguous()
 
 
+def make_logits(cfg: MoEConfig, seed: int, num_tokens: Optional[int] = None):
+    """Router logits fp32 [T, E] of a softmax_topk workload: the very values
+    make_routing draws (same generator stream), so that a router applied to
+    them must give make_routing's ids and weights."""
+    if cfg.routing != "softmax_topk":
+        raise ValueError(f"{cfg.name} has no router logits (routing {cfg.routing!r})")
+    T = cfg.num_tokens if num_tokens is None else num_tokens
+    g = _gen(seed, _S_ROUTE)
+    return torch.randn((T, cfg.pool), generator=g, dtype=torch.float32)
+
+
 def make_static_token_counts(seed: int, replays: int = STATIC_REPLAYS, max_tokens: int = 2048) -> list:
     """T_v for each graph replay of the static-capacity workload, ~ U{1..max_tokens}."""
     g = _gen(seed, _S_TV)
