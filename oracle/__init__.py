@@ -48,7 +48,10 @@ import numpy as np
 
 __all__ = [
     "bf16_to_f64", "f64_to_bf16_bits", "router_topk", "dispatch", "silu", "expert_mlp",
+    "expert_mlp_f64",
     "expert_compute", "combine", "forward", "forward_tokens",
+    "e4m3_to_f64", "e8m0_to_f64", "mxfp8_quantize", "mxfp8_to_f64",
+    "forward_tokens_mxfp8", "forward_mxfp8",
 ]
 
 
@@ -167,10 +170,14 @@ def expert_mlp(x_rows, w_gateup_e, w_down_e):
     x_rows: float64 [M, H]; w_gateup_e: bf16 bits [2I, H] (gate rows [0,I),
     up rows [I,2I)); w_down_e: bf16 bits [H, I].  Returns float64 [M, H].
     The three matrix products are library matmuls in float64."""
-    wgu = bf16_to_f64(w_gateup_e)
+    return expert_mlp_f64(x_rows, bf16_to_f64(w_gateup_e), bf16_to_f64(w_down_e))
+
+
+def expert_mlp_f64(x_rows, wgu, w_down):
+    """expert_mlp on weights already widened to float64 (wgu [2I, H], gate
+    rows first; w_down [H, I])."""
     I = wgu.shape[0] // 2
     w_gate, w_up = wgu[:I], wgu[I:]
-    w_down = bf16_to_f64(w_down_e)
     x = np.asarray(x_rows, dtype=np.float64)
     g = x @ w_gate.T                              # [M, I]
     u = x @ w_up.T                                # [M, I]
@@ -235,10 +242,18 @@ def forward_tokens(x, topk_ids, topk_weights, w_gateup, w_down, tokens,
     w[t,j] * y(ids[t,j], x[t]).  x: bf16 bits [T, H]; w_gateup: bf16 bits
     [E, 2I, H]; w_down: bf16 bits [E, H, I] (any object indexable by expert
     that yields such arrays)."""
+    return _forward_tokens_widened(
+        x, topk_ids, topk_weights, len(w_gateup),
+        lambda e: (bf16_to_f64(np.asarray(w_gateup[e])), bf16_to_f64(np.asarray(w_down[e]))),
+        tokens, num_valid_tokens)
+
+
+def _forward_tokens_widened(x, topk_ids, topk_weights, E, widen, tokens, num_valid_tokens):
+    """forward_tokens with the expert weights supplied as float64 by
+    widen(e) -> (W_gateup[e] [2I, H], W_down[e] [H, I])."""
     ids = np.asarray(topk_ids, dtype=np.int64)
     wts = np.asarray(topk_weights, dtype=np.float32).astype(np.float64)
     T, K = ids.shape
-    E = len(w_gateup)
     tv = T if num_valid_tokens is None else max(0, min(int(num_valid_tokens), T))
     toks = np.asarray(tokens, dtype=np.int64)
     H = np.asarray(x).shape[1]
@@ -255,7 +270,7 @@ def forward_tokens(x, topk_ids, topk_weights, w_gateup, w_down, tokens,
                 pairs.setdefault(int(e), []).append((i, int(t), j))
     for e, lst in sorted(pairs.items()):
         xr = bf16_to_f64(np.asarray(x)[[t for _, t, _ in lst]])
-        y = expert_mlp(xr, np.asarray(w_gateup[e]), np.asarray(w_down[e]))
+        y = expert_mlp_f64(xr, *widen(e))
         for (i, t, j), yrow in zip(lst, y):
             out[i] += wts[t, j] * yrow
     return out
@@ -266,3 +281,121 @@ def forward(x, topk_ids, topk_weights, w_gateup, w_down, num_valid_tokens: int |
     T = np.asarray(topk_ids).shape[0]
     return forward_tokens(x, topk_ids, topk_weights, w_gateup, w_down, np.arange(T),
                           num_valid_tokens)
+
+
+# ---------------------------------------------------------------------------
+# MXFP8 expert weights (FlashInfer PR #3980: the MXFP8 MegaMoE backend, and
+# the commit notes on the quantized combine wire, whose 'mxfp8' format is
+# blocks of 32 e4m3 values sharing one e8m0 scale).  TileOps PR #1738 Scope
+# leaves FP8 outside the BF16 path; this is the low-precision weight variant
+# of the same layer.
+#
+# Readings (the pages name the format, not the recipe):
+#   * e4m3 is the OCP FP8 E4M3 ("fn") encoding: sign, 4 exponent bits with
+#     bias 7, 3 mantissa bits; exponent field 0 holds subnormals m/8 * 2^-6;
+#     S.1111.111 is NaN; there are no infinities; the largest value is 448.
+#   * e8m0 is a bare biased exponent: code s means 2^(s - 127) (255 = NaN).
+#   * one scale per 32 consecutive values along K (the contraction axis) of
+#     every weight row.
+#   * the scale of a block is 2^(floor(log2(amax)) - 8), 8 being the exponent
+#     of e4m3's largest binade (the OCP MX recipe), with the code clamped to
+#     [0, 254]; an all-zero block takes code 0.
+#   * elements are v / scale rounded to the nearest e4m3 value, ties to even
+#     mantissa, magnitudes above 448 saturated to 448; the sign bit of the
+#     code is the sign bit of the input (so -0 stays -0).
+#   * the layer computes with the dequantized weights q * scale (exact in
+#     float64); the activations stay bf16.
+# ---------------------------------------------------------------------------
+E4M3_MAX = 448.0
+MX_BLOCK = 32
+
+
+def e4m3_to_f64(codes) -> np.ndarray:
+    """Value of OCP FP8 E4M3 codes (uint8) as float64."""
+    c = np.asarray(codes, dtype=np.uint8).astype(np.int64)
+    sign = (c >> 7) & 1
+    ex = (c >> 3) & 15
+    man = c & 7
+    mag = np.where(ex == 0, man / 8.0 * 2.0 ** -6, (1.0 + man / 8.0) * np.exp2(ex - 7.0))
+    v = np.where(sign == 1, -mag, mag)
+    return np.where((ex == 15) & (man == 7), np.nan, v)
+
+
+def e8m0_to_f64(codes) -> np.ndarray:
+    """Value of E8M0 scale codes (uint8): 2^(s - 127), NaN for 255."""
+    c = np.asarray(codes, dtype=np.uint8).astype(np.float64)
+    return np.where(c == 255, np.nan, np.exp2(c - 127.0))
+
+
+def _round_to_e4m3(y: np.ndarray) -> np.ndarray:
+    """Nearest e4m3 magnitude to |y| (float64, exact), ties to even mantissa,
+    saturated at 448.  Normal binades [2^E, 2^(E+1)) hold 8 values spaced
+    2^(E-3); below 2^-6 the spacing is the subnormal step 2^-9."""
+    a = np.abs(y)
+    _, ex = np.frexp(a)                     # a = f * 2^ex, f in [0.5, 1)
+    binade = np.maximum(ex - 1, -6)         # floor(log2 a), subnormals share -6's step
+    step = np.exp2(binade - 3.0)
+    q = np.round(a / step) * step           # np.round: half to even
+    return np.minimum(q, E4M3_MAX)
+
+
+def _encode_e4m3(mag: np.ndarray, sign: np.ndarray) -> np.ndarray:
+    """Code of an exactly representable e4m3 magnitude (<= 448) and a sign."""
+    code = np.zeros(mag.shape, dtype=np.int64)
+    sub = mag < 2.0 ** -6
+    code[sub] = np.rint(mag[sub] / 2.0 ** -9).astype(np.int64)        # exponent field 0
+    f, ex = np.frexp(mag[~sub])
+    e_field = (ex - 1) + 7
+    m_field = np.rint((f * 2.0 - 1.0) * 8.0).astype(np.int64)
+    code[~sub] = (e_field << 3) | m_field
+    return (code | (sign.astype(np.int64) << 7)).astype(np.uint8)
+
+
+def mxfp8_quantize(w_bits):
+    """MXFP8 quantization of bf16 weights along their last axis.
+
+    w_bits: bf16 bits (uint16) [..., K], K a multiple of 32.  Returns
+    (codes uint8 [..., K], scales uint8 [..., K // 32]) with
+    value(codes[..., k]) * 2^(scales[..., k // 32] - 127) the dequantized
+    weight."""
+    b = np.ascontiguousarray(w_bits, dtype=np.uint16)
+    K = b.shape[-1]
+    if K % MX_BLOCK:
+        raise ValueError("K must be a multiple of 32")
+    v = bf16_to_f64(b).reshape(b.shape[:-1] + (K // MX_BLOCK, MX_BLOCK))
+    amax = np.abs(v).max(axis=-1)
+    _, ex = np.frexp(amax)                                   # amax = f * 2^ex
+    s_code = np.where(amax > 0, np.clip((ex - 1) - 8 + 127, 0, 254), 0).astype(np.int64)
+    y = v / np.exp2(s_code - 127.0)[..., None]               # exact: power-of-two scale
+    mag = _round_to_e4m3(y)
+    sign = (b.reshape(v.shape) >> np.uint16(15)).astype(np.int64)
+    codes = _encode_e4m3(mag, sign).reshape(b.shape)
+    return codes, s_code.astype(np.uint8)
+
+
+def mxfp8_to_f64(codes, scales) -> np.ndarray:
+    """Dequantized MXFP8 weights: e4m3 value times its block's e8m0 scale."""
+    c = np.asarray(codes, dtype=np.uint8)
+    s = np.asarray(scales, dtype=np.uint8)
+    K = c.shape[-1]
+    return e4m3_to_f64(c) * np.repeat(e8m0_to_f64(s), MX_BLOCK, axis=-1)[..., :K]
+
+
+def forward_tokens_mxfp8(x, topk_ids, topk_weights, wgu_codes, wgu_scales, wd_codes, wd_scales,
+                         tokens, num_valid_tokens: int | None = None):
+    """forward_tokens with MXFP8 expert weights: codes [E, 2I, H] / scales
+    [E, 2I, H/32] for W_gateup, codes [E, H, I] / scales [E, H, I/32] for
+    W_down (any objects indexable by expert), dequantized exactly to float64
+    and then the same layer definition."""
+    return _forward_tokens_widened(
+        x, topk_ids, topk_weights, len(wgu_codes),
+        lambda e: (mxfp8_to_f64(wgu_codes[e], wgu_scales[e]), mxfp8_to_f64(wd_codes[e], wd_scales[e])),
+        tokens, num_valid_tokens)
+
+
+def forward_mxfp8(x, topk_ids, topk_weights, wgu_codes, wgu_scales, wd_codes, wd_scales,
+                  num_valid_tokens: int | None = None):
+    """The whole MXFP8-weight layer for every token: float64 [T, H]."""
+    T = np.asarray(topk_ids).shape[0]
+    return forward_tokens_mxfp8(x, topk_ids, topk_weights, wgu_codes, wgu_scales, wd_codes,
+                                wd_scales, np.arange(T), num_valid_tokens)
