@@ -186,6 +186,63 @@ MOE_API moe_status_t moe_graph_create(const moe_problem_t* p, const uint16_t* x,
 MOE_API moe_status_t moe_graph_launch(void* graph, void* stream);
 MOE_API moe_status_t moe_graph_destroy(void* graph);
 
+/* ---------------------------------------------------------------------------
+ * MXFP8 expert weights (FlashInfer PR #3980: the MXFP8 MegaMoE backend; its
+ * combine-wire notes name the format, 32 e4m3 values sharing one e8m0 scale).
+ * TileOps PR #1738, Scope, leaves FP8 outside its BF16 path; this is the
+ * low-precision weight variant of the same layer, for the weight-streaming
+ * regime: about half the weight bytes of bf16.
+ *
+ * Format of a weight matrix with K-contiguous rows [rows, K], K % 32 == 0:
+ *   codes   uint8 [rows, K]: OCP FP8 E4M3 ("fn": bias 7, subnormals, no
+ *           infinities, 0x7F / 0xFF NaN, largest value 448)
+ *   scales  uint8 [rows, K/32]: e8m0, code s means 2^(s - 127), one per 32
+ *           consecutive values of a row
+ *   value(r, k) = e4m3(codes[r, k]) * 2^(scales[r, k/32] - 127)
+ * For the layer: W_gateup codes [E, 2I, H] + scales [E, 2I, H/32] (gate rows
+ * first), W_down codes [E, H, I] + scales [E, H, I/32].  codes 16-byte
+ * aligned, scales 2-byte aligned.
+ * ------------------------------------------------------------------------- */
+
+/* Quantize bf16 rows w [rows, k] (16-byte aligned) to MXFP8: per block of 32
+ * the scale is 2^(floor(log2(amax)) - 8), its code clamped to [0, 254] (0 for
+ * an all-zero block); each code is the nearest e4m3 value to v / scale, ties
+ * to even, magnitudes above 448 saturated to 448, sign bit = the input's.
+ * Exact integer arithmetic (the result is bit-reproducible).  Finite inputs
+ * only.  rows >= 0, k a positive multiple of 32; rows * k <= 2^40. */
+MOE_API moe_status_t moe_mxfp8_quantize(const uint16_t* w, int64_t rows, int32_t k,
+                                        uint8_t* codes, uint8_t* scales, void* stream);
+
+/* Dequantize MXFP8 rows to bf16 w [rows, k] with the conversion the expert
+ * kernels use (v_cvt_scalef32_pk_bf16_fp8).  Exact for scale codes whose
+ * results stay in bf16's normal range (every code the quantizer gives for
+ * weights between 2^-117 and 2^119 in magnitude). */
+MOE_API moe_status_t moe_mxfp8_dequantize(const uint8_t* codes, const uint8_t* scales,
+                                          int64_t rows, int32_t k, uint16_t* w, void* stream);
+
+/* moe_gate_up on MXFP8 gate-up weights: h = bf16(silu(x_disp W_gate^T) *
+ * (x_disp W_up^T)) with the weights dequantized exactly in registers and fp32
+ * accumulation.  kernel_hint must be 0 or 1 (the 16-row skinny tiles serve
+ * every batch size on this path); MOE_ERROR_NOT_SUPPORTED otherwise. */
+MOE_API moe_status_t moe_gate_up_mxfp8(const moe_problem_t* p, const uint16_t* x_disp,
+                                       const int32_t* expert_offsets,
+                                       const uint8_t* w_gateup_codes,
+                                       const uint8_t* w_gateup_scales, uint16_t* h,
+                                       void* stream);
+
+/* moe_forward on MXFP8 expert weights: the same layer, dispatch, combine,
+ * workspace, T_v handling and output contract, with W_gateup and W_down given
+ * as codes + scales (above).  x, h, y and out stay bf16.  kernel_hint 0 or 1. */
+MOE_API moe_status_t moe_forward_mxfp8(const moe_problem_t* p, const uint16_t* x,
+                                       const int32_t* topk_ids, const float* topk_weights,
+                                       const uint8_t* w_gateup_codes,
+                                       const uint8_t* w_gateup_scales,
+                                       const uint8_t* w_down_codes,
+                                       const uint8_t* w_down_scales,
+                                       const int32_t* num_tokens_dev, int32_t* expert_offsets,
+                                       uint16_t* out, void* workspace, size_t ws_bytes,
+                                       void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -22,7 +22,8 @@ HINT_AUTO, HINT_SKINNY, HINT_TILED64, HINT_TILED128, HINT_TILED_LARGE = 0, 1, 2,
 EXPORTS = (
     "moe_status_string", "moe_workspace_size", "moe_dispatch", "moe_expert_compute",
     "moe_gate_up", "moe_down", "moe_combine", "moe_router_topk", "moe_forward", "moe_graph_create",
-    "moe_graph_launch", "moe_graph_destroy",
+    "moe_graph_launch", "moe_graph_destroy", "moe_mxfp8_quantize", "moe_mxfp8_dequantize",
+    "moe_gate_up_mxfp8", "moe_forward_mxfp8",
 )
 
 
@@ -61,6 +62,10 @@ _SIGS = {
     "moe_graph_create": (ctypes.c_int, [_PP, _P, _P, _P, _P, _P, _P, _P, _P, _P, _SZ,
                                         ctypes.POINTER(ctypes.c_void_p)]),
     "moe_graph_launch": (ctypes.c_int, [_P, _P]),
+    "moe_mxfp8_quantize": (ctypes.c_int, [_P, ctypes.c_int64, ctypes.c_int32, _P, _P, _P]),
+    "moe_mxfp8_dequantize": (ctypes.c_int, [_P, _P, ctypes.c_int64, ctypes.c_int32, _P, _P]),
+    "moe_gate_up_mxfp8": (ctypes.c_int, [_PP, _P, _P, _P, _P, _P, _P]),
+    "moe_forward_mxfp8": (ctypes.c_int, [_PP, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _SZ, _P]),
     "moe_graph_destroy": (ctypes.c_int, [_P]),
 }
 

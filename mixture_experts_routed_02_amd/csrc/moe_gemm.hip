@@ -76,6 +76,50 @@ __device__ __forceinline__ int find_expert(const int* s_start, int E, int tile) 
 // non-temporal made the decode workloads 8-20% slower.
 __device__ __forceinline__ moe_bf16x8 stream_load(const moe_bf16x8* p) { return *p; }
 
+// Tile epilogue of the skinny kernels: the four waves' partial sums of the
+// tile (accumulator i of lane l = weight row 4*(l/16)+i, token row l%16) are
+// added in wave order through LDS; gated tiles write bf16(silu(g) * u) for
+// their 8 columns, plain tiles bf16(y) for their 16*RB columns.  Ends with a
+// barrier, so s_red is free again.
+template <bool GATED, int RB>
+__device__ __forceinline__ void skinny_epilogue(const moe_f32x4 (&acc)[RB], float* s_red,
+                                                uint16_t* __restrict__ C, int N, int r0,
+                                                int mrows, int n_tile) {
+    constexpr int COLS = GATED ? 8 : 16 * RB;
+    constexpr int RED_ROWS = 16 * RB;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int li = lane & 15, lg = lane >> 4;
+    auto red = [&](int w, int row, int m) -> float& { return s_red[(w * RED_ROWS + row) * 17 + m]; };
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) red(wave, rb * 16 + 4 * lg + i, li) = acc[rb][i];
+    __syncthreads();
+    if (GATED) {
+        if (tid < 128) {
+            const int m = tid >> 3, c = tid & 7;
+            if (m < mrows) {
+                float g = 0.f, u = 0.f;
+#pragma unroll
+                for (int w = 0; w < 4; ++w) { g += red(w, c, m); u += red(w, 8 + c, m); }
+                C[(size_t)(r0 + m) * N + n_tile * 8 + c] = moe_f32_to_bf16(silu_f32(g) * u);
+            }
+        }
+    } else {
+        const int m = tid >> 4, c = tid & 15;
+        if (m < mrows) {
+#pragma unroll
+            for (int rb = 0; rb < RB; ++rb) {
+                float y = 0.f;
+#pragma unroll
+                for (int w = 0; w < 4; ++w) y += red(w, rb * 16 + c, m);
+                C[(size_t)(r0 + m) * N + n_tile * COLS + rb * 16 + c] = moe_f32_to_bf16(y);
+            }
+        }
+    }
+    __syncthreads();
+}
+
 // RB = 16-row weight blocks per tile (1 or 2; gated tiles use 1).  Blocks of
 // U k-steps keep RB * U KB of weights in flight per wave and per buffer.
 // offsets and rows may point to global memory or LDS; s_red is
@@ -90,7 +134,6 @@ __device__ __forceinline__ void skinny_tiles(const uint16_t* __restrict__ A, con
     constexpr int BM = 16;
     constexpr int U = 4 / RB;                      // k-steps (of 32) per block
     constexpr int COLS = GATED ? 8 : 16 * RB;
-    constexpr int RED_ROWS = 16 * RB;
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int li = lane & 15, lg = lane >> 4;
@@ -176,35 +219,7 @@ __device__ __forceinline__ void skinny_tiles(const uint16_t* __restrict__ A, con
                 acc[rb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(stream_load(wp[rb] + o), xv, acc[rb], 0, 0, 0);
         }
 
-        auto red = [&](int w, int row, int m) -> float& { return s_red[(w * RED_ROWS + row) * 17 + m]; };
-#pragma unroll
-        for (int rb = 0; rb < RB; ++rb)
-#pragma unroll
-            for (int i = 0; i < 4; ++i) red(wave, rb * 16 + 4 * lg + i, li) = acc[rb][i];
-        __syncthreads();
-        if (GATED) {
-            if (tid < 128) {
-                const int m = tid >> 3, c = tid & 7;
-                if (m < mrows) {
-                    float g = 0.f, u = 0.f;
-#pragma unroll
-                    for (int w = 0; w < 4; ++w) { g += red(w, c, m); u += red(w, 8 + c, m); }
-                    C[(size_t)(r0 + m) * N + n_tile * 8 + c] = moe_f32_to_bf16(silu_f32(g) * u);
-                }
-            }
-        } else {
-            const int m = tid >> 4, c = tid & 15;
-            if (m < mrows) {
-#pragma unroll
-                for (int rb = 0; rb < RB; ++rb) {
-                    float y = 0.f;
-#pragma unroll
-                    for (int w = 0; w < 4; ++w) y += red(w, rb * 16 + c, m);
-                    C[(size_t)(r0 + m) * N + n_tile * COLS + rb * 16 + c] = moe_f32_to_bf16(y);
-                }
-            }
-        }
-        __syncthreads();
+        skinny_epilogue<GATED, RB>(acc, s_red, C, N, r0, mrows, n_tile);
     }
 }
 
@@ -217,6 +232,66 @@ __global__ __launch_bounds__(256) void gemm_skinny_kernel(
     __shared__ int s_wave[4];
     __shared__ float s_red[4 * 16 * RB * 17];
     skinny_tiles<GATED, RB>(A, row_src, topk, offsets, W, C, E, Kd, N, s_start, s_wave, s_red);
+}
+
+// Expert slots of the tiny down kernels: the experts that hold rows, in
+// expert order (at most kTinyRows of them): s_e = expert, s_r0 = first row,
+// s_m = rows; *s_ne = their number.  Ends with a barrier.
+__device__ __forceinline__ void tiny_expert_slots(const int32_t* __restrict__ offsets, int E,
+                                                  int* s_e, int* s_r0, int* s_m, int* s_ne) {
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    if (wave == 0) {
+        int base = 0;
+        for (int c = 0; c * 64 < E; ++c) {
+            const int e = c * 64 + lane;
+            const int m = e < E ? offsets[e + 1] - offsets[e] : 0;
+            const unsigned long long has = __ballot(m > 0);
+            const int slot = base + __popcll(has & ((1ull << lane) - 1ull));
+            if (m > 0 && slot < kTinyRows) {
+                s_e[slot] = e;
+                s_r0[slot] = offsets[e];
+                s_m[slot] = m;
+            }
+            base += __popcll(has);
+        }
+        if (lane == 0) *s_ne = base < kTinyRows ? base : kTinyRows;
+    }
+    __syncthreads();
+}
+
+// End of the tiny down kernels, after every wave stored its partial sums in
+// s_part [slot][wave][weight row][17]: y = the four partials added in wave
+// order, rounded to bf16 into s_y [slot][token row][16]; then
+// out[t, n0 + c] = bf16( sum_j w[t,j] * y[token_row[t*K+j]][c] ), j increasing
+// (the combine kernel's arithmetic).
+__device__ __forceinline__ void tiny_combine(int ne, const int* s_r0, const float* s_part,
+                                             uint16_t* s_y, const int32_t* __restrict__ token_row,
+                                             const float* __restrict__ wts,
+                                             const int32_t* __restrict__ ntok, int T, int topk,
+                                             int N, int n0, uint16_t* __restrict__ out) {
+    const int tid = threadIdx.x;
+    for (int idx = tid; idx < ne * 256; idx += 256) {
+        const int i = idx >> 8, c = (idx >> 4) & 15, m = idx & 15;
+        float y = 0.f;
+#pragma unroll
+        for (int w = 0; w < 4; ++w) y += s_part[((i * 4 + w) * 16 + c) * 17 + m];
+        s_y[(i * 16 + m) * 16 + c] = moe_f32_to_bf16(y);
+    }
+    __syncthreads();
+    const int tv = moe_valid_tokens(ntok, T);
+    for (int idx = tid; idx < tv * 16; idx += 256) {
+        const int t = idx >> 4, c = idx & 15;
+        float acc1 = 0.f;
+        for (int j = 0; j < topk; ++j) {
+            const int r = token_row[(size_t)t * topk + j];
+            if (r < 0) continue;
+            int i = 0;
+            while (i + 1 < ne && r >= s_r0[i + 1]) ++i;
+            const float yv = moe_bf16_to_f32(s_y[(i * 16 + (r - s_r0[i])) * 16 + c]);
+            acc1 = fmaf(wts[(size_t)t * topk + j], yv, acc1);
+        }
+        out[(size_t)t * N + n0 + c] = moe_f32_to_bf16(acc1);
+    }
 }
 
 // ---------------------------------------------------------------------------
@@ -247,24 +322,7 @@ __global__ __launch_bounds__(256) void down_combine_tiny_kernel(
     const int li = lane & 15, lg = lane >> 4;
     const int n0 = blockIdx.x * 16;
 
-    // experts with rows, in expert order
-    if (wave == 0) {
-        int base = 0;
-        for (int c = 0; c * 64 < E; ++c) {
-            const int e = c * 64 + lane;
-            const int m = e < E ? offsets[e + 1] - offsets[e] : 0;
-            const unsigned long long has = __ballot(m > 0);
-            const int slot = base + __popcll(has & ((1ull << lane) - 1ull));
-            if (m > 0 && slot < kTinyRows) {
-                s_e[slot] = e;
-                s_r0[slot] = offsets[e];
-                s_m[slot] = m;
-            }
-            base += __popcll(has);
-        }
-        if (lane == 0) s_ne = base < kTinyRows ? base : kTinyRows;
-    }
-    __syncthreads();
+    tiny_expert_slots(offsets, E, s_e, s_r0, s_m, &s_ne);
     const int ne = s_ne;
 
     const int ksteps = Kd / 32;
@@ -317,59 +375,26 @@ __global__ __launch_bounds__(256) void down_combine_tiny_kernel(
     }
     if (b < total) step(wa, xa, b);
     __syncthreads();
-
-    // y = sum of the four partials in wave order, rounded to bf16
-    for (int idx = tid; idx < ne * 256; idx += 256) {
-        const int i = idx >> 8, c = (idx >> 4) & 15, m = idx & 15;
-        float y = 0.f;
-#pragma unroll
-        for (int w = 0; w < 4; ++w) y += s_part[i][w][c][m];
-        s_y[i][m][c] = moe_f32_to_bf16(y);
-    }
-    __syncthreads();
-
-    // out[t, n0 + c] = bf16( sum_j w[t,j] * y[token_row[t*K+j]][c] ), j increasing
-    const int tv = moe_valid_tokens(ntok, T);
-    for (int idx = tid; idx < tv * 16; idx += 256) {
-        const int t = idx >> 4, c = idx & 15;
-        float acc1 = 0.f;
-        for (int j = 0; j < topk; ++j) {
-            const int r = token_row[(size_t)t * topk + j];
-            if (r < 0) continue;
-            int i = 0;
-            while (i + 1 < ne && r >= s_r0[i + 1]) ++i;
-            const float yv = moe_bf16_to_f32(s_y[i][r - s_r0[i]][c]);
-            acc1 = fmaf(wts[(size_t)t * topk + j], yv, acc1);
-        }
-        out[(size_t)t * N + n0 + c] = moe_f32_to_bf16(acc1);
-    }
+    tiny_combine(ne, s_r0, &s_part[0][0][0][0], &s_y[0][0][0], token_row, wts, ntok, T, topk, N, n0, out);
 }
 
-// Gate-up GEMM of the skinny plan with the local dispatch done inside (for
-// T*K <= kFusedDispatchMax): every workgroup counts, scans and ranks the
-// assignments in LDS with the same stable order as the dispatch kernels, then
-// runs its gate-up tiles from that LDS copy; workgroup 0 also publishes
-// expert_offsets, row_src and token_row for the down GEMM and the combine.
-// This saves a launch in the latency-bound small-batch regime.  The ids are
-// read once, into registers, together with the valid-token count (not after
-// it); wave w ranks the contiguous slice of 256 assignments starting at 256*w
-// with per-bit ballot masks and a wave-local running count per expert, and
-// the per-wave counts double as the histogram.
-__global__ __launch_bounds__(256) void gemm_skinny_gateup_dispatch_kernel(
-    const uint16_t* __restrict__ x, const int32_t* __restrict__ ids,
-    const int32_t* __restrict__ ntok, int T, int topk, int E, int32_t* __restrict__ offsets,
-    int32_t* __restrict__ row_src, int32_t* __restrict__ token_row,
-    const uint16_t* __restrict__ W, uint16_t* __restrict__ C, int Kd, int N) {
+// The dispatch of the fused kernels: counts, scans and ranks the T*K (<=
+// kFusedDispatchMax) assignments in LDS (s_off: exclusive expert offsets,
+// s_off[E] = valid rows; s_rows: row -> assignment); workgroup 0 also
+// publishes expert_offsets, row_src and token_row.  The ids are read once,
+// into registers, together with the valid-token count; wave w ranks the
+// contiguous slice of 256 assignments starting at 256*w with per-bit ballot
+// masks and a wave-local running count per expert, and the per-wave counts
+// double as the histogram.  Ends with a barrier.
+__device__ __forceinline__ void fused_dispatch(const int32_t* __restrict__ ids,
+                                               const int32_t* __restrict__ ntok, int T, int topk,
+                                               int E, int32_t* __restrict__ offsets,
+                                               int32_t* __restrict__ row_src,
+                                               int32_t* __restrict__ token_row, int* s_off,
+                                               int* s_wc, int* s_rows, int* s_wave) {
     constexpr int kWaves = 4;
     constexpr int kPer = kFusedDispatchMax / (64 * kWaves);   // assignments per lane
     static_assert(kPer * 64 * kWaves == kFusedDispatchMax, "whole slices");
-    __shared__ int s_off[kMaxExperts + 1];        // totals -> exclusive offsets
-    __shared__ int s_wc[kWaves * kMaxExperts];    // per-wave counts -> per-wave first rows
-    __shared__ int s_rows[kFusedDispatchMax];
-    __shared__ int s_start[kMaxExperts + 1];
-    __shared__ int s_wave[kWaves];
-    __shared__ float s_red[4 * 16 * 17];
-
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const bool publish = blockIdx.x == 0;
     const int ntotal = T * topk;
@@ -439,7 +464,375 @@ __global__ __launch_bounds__(256) void gemm_skinny_gateup_dispatch_kernel(
         }
     }
     __syncthreads();
+}
+
+// Gate-up GEMM of the skinny plan with the local dispatch done inside (for
+// T*K <= kFusedDispatchMax): every workgroup runs fused_dispatch, then its
+// gate-up tiles from that LDS copy.  This saves a launch in the
+// latency-bound small-batch regime.
+__global__ __launch_bounds__(256) void gemm_skinny_gateup_dispatch_kernel(
+    const uint16_t* __restrict__ x, const int32_t* __restrict__ ids,
+    const int32_t* __restrict__ ntok, int T, int topk, int E, int32_t* __restrict__ offsets,
+    int32_t* __restrict__ row_src, int32_t* __restrict__ token_row,
+    const uint16_t* __restrict__ W, uint16_t* __restrict__ C, int Kd, int N) {
+    __shared__ int s_off[kMaxExperts + 1];        // totals -> exclusive offsets
+    __shared__ int s_wc[4 * kMaxExperts];         // per-wave counts -> per-wave first rows
+    __shared__ int s_rows[kFusedDispatchMax];
+    __shared__ int s_start[kMaxExperts + 1];
+    __shared__ int s_wave[4];
+    __shared__ float s_red[4 * 16 * 17];
+    fused_dispatch(ids, ntok, T, topk, E, offsets, row_src, token_row, s_off, s_wc, s_rows, s_wave);
     skinny_tiles<true, 1>(x, s_rows, topk, s_off, W, C, E, Kd, N, s_start, s_wave, s_red);
+}
+
+// ---------------------------------------------------------------------------
+// MXFP8 weights (FlashInfer PR #3980: the MXFP8 MegaMoE backend; its combine
+// wire names the format, 32 e4m3 values sharing one e8m0 scale).  The skinny
+// kernels again, streaming 1-byte OCP e4m3 codes plus one scale byte per 32
+// k-values of a weight row, i.e. about half the bytes of bf16 weights, and
+// dequantizing in registers: v_cvt_scalef32_pk_bf16_fp8 turns two codes into
+// two bf16 values times 2^(s - 127), which is exact for the scales the
+// quantizer produces (the product of a 4-bit-significand value and a power
+// of two inside bf16's range), so the MFMA sees the dequantized weights
+// exactly and accumulates in fp32 as the bf16 path does.
+//
+// k order.  A lane loads 16 consecutive codes of its weight row, k = 64*seg +
+// 16*lg + (0..15), and the matching 16 token values as two 16-byte pieces.
+// MFMA step s of the segment takes codes 8s..8s+7 of every lane group, so an
+// instruction sums over k = 64*seg + 16*g + 8*s + (0..7), g = 0..3: both
+// operands use the same map, and every k of the segment is summed once.  The
+// scale of lane group lg is the one of 32-block 2*seg + lg/2; one 16-bit load
+// per segment brings both of the segment's scales.
+// ---------------------------------------------------------------------------
+typedef uint32_t moe_u32x4 __attribute__((ext_vector_type(4)));
+
+// Scale operand of v_cvt_scalef32_*: an fp32 whose exponent field holds the
+// e8m0 code (gfx950 reads the scale from those bits).
+__device__ __forceinline__ float mx_scale_operand(uint32_t code) { return __uint_as_float(code << 23); }
+
+// 8 e4m3 codes (w0: codes 0-3, w1: codes 4-7, lowest byte first) -> 8 bf16
+__device__ __forceinline__ moe_bf16x8 mx_dequant8(uint32_t w0, uint32_t w1, float scale) {
+    typedef __bf16 bf16x2 __attribute__((__vector_size__(2 * sizeof(__bf16))));
+    union {
+        bf16x2 p[4];
+        moe_bf16x8 v;
+    } r;
+    r.p[0] = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w0, scale, false);
+    r.p[1] = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w0, scale, true);
+    r.p[2] = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w1, scale, false);
+    r.p[3] = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w1, scale, true);
+    return r.v;
+}
+
+// Skinny tiles on MXFP8 weights: codes Wq [E, rows, Kd], scales Ws [E, rows,
+// Kd/32].  Same tiles, tile order, k split over the waves (in 64-k
+// segments), double-buffered blocks and epilogue as skinny_tiles; a block is
+// US segments (2 KB of codes per wave for either RB).
+template <bool GATED, int RB>
+__device__ __forceinline__ void skinny_tiles_mx(const uint16_t* __restrict__ A, const int32_t* rows,
+                                                int topk, const int32_t* offsets,
+                                                const uint8_t* __restrict__ Wq,
+                                                const uint8_t* __restrict__ Ws,
+                                                uint16_t* __restrict__ C, int E, int Kd, int N,
+                                                int* s_start, int* s_wave, float* s_red) {
+    static_assert(RB == 1 || (RB == 2 && !GATED), "tile rows");
+    constexpr int BM = 16;
+    constexpr int US = 2 / RB;                     // 64-k segments per block
+    constexpr int COLS = GATED ? 8 : 16 * RB;
+
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int li = lane & 15, lg = lane >> 4;
+    const int n_tiles = N / COLS;
+    const int w_rows = GATED ? 2 * N : N;
+    const int total = build_tile_table<BM>(offsets, E, n_tiles, s_start, s_wave);
+
+    const int nseg = Kd / 64;
+    const int sg0 = (wave * nseg) / 4, sg1 = ((wave + 1) * nseg) / 4;
+    const int nblk = (sg1 - sg0) / US;             // full blocks; the rest is a tail
+    const int sshift = 8 * (lg >> 1);              // this lane group's scale byte
+    const moe_bf16x8 zero = {};
+
+    for (int tile = blockIdx.x; tile < total; tile += gridDim.x) {
+        const int e = find_expert(s_start, E, tile);
+        const int row0 = offsets[e];
+        const int me = offsets[e + 1] - row0;
+        const int mt = (me + BM - 1) / BM;
+        const int local = tile - s_start[e];
+        const int m_tile = local % mt, n_tile = local / mt;
+        const int r0 = row0 + m_tile * BM;
+        const int mrows = (me - m_tile * BM) < BM ? (me - m_tile * BM) : BM;
+
+        const moe_u32x4* wq[RB];
+        const uint16_t* wsc[RB];
+#pragma unroll
+        for (int rb = 0; rb < RB; ++rb) {
+            int wrow;
+            if (GATED) wrow = (li < 8) ? (n_tile * 8 + li) : (N + n_tile * 8 + (li - 8));
+            else wrow = n_tile * COLS + rb * 16 + li;
+            const size_t grow = (size_t)e * w_rows + wrow;
+            wq[rb] = reinterpret_cast<const moe_u32x4*>(Wq + grow * (size_t)Kd + (size_t)sg0 * 64 + lg * 16);
+            wsc[rb] = reinterpret_cast<const uint16_t*>(Ws + grow * (size_t)(Kd / 32)) + sg0;
+        }
+
+        moe_u32x4 qa[RB][US], qb[RB][US];
+        uint32_t sa[RB][US], sb[RB][US];
+        moe_bf16x8 xa[US][2], xb[US][2];
+        auto load_w = [&](moe_u32x4 (*q)[US], uint32_t (*sc)[US], int b) {
+#pragma unroll
+            for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+                for (int u = 0; u < US; ++u) {
+                    q[rb][u] = wq[rb][(b * US + u) * 4];
+                    sc[rb][u] = wsc[rb][b * US + u];
+                }
+        };
+        if (nblk > 0) load_w(qa, sa, 0);
+        const bool mvalid = li < mrows;
+        const int rr = r0 + (mvalid ? li : 0);
+        const long long arow = rows ? (long long)(rows[rr] / topk) : (long long)rr;
+        const moe_bf16x8* ap = reinterpret_cast<const moe_bf16x8*>(
+            A + (size_t)arow * Kd + (size_t)sg0 * 64 + lg * 16);
+        auto load_x = [&](moe_bf16x8 (*xv)[2], int b) {
+#pragma unroll
+            for (int u = 0; u < US; ++u)
+#pragma unroll
+                for (int h = 0; h < 2; ++h) {
+                    const moe_bf16x8 v = ap[(b * US + u) * 8 + h];
+                    xv[u][h] = mvalid ? v : zero;
+                }
+        };
+        moe_f32x4 acc[RB];
+#pragma unroll
+        for (int rb = 0; rb < RB; ++rb) acc[rb] = (moe_f32x4){0.f, 0.f, 0.f, 0.f};
+        auto seg_mma = [&](const moe_u32x4& q, uint32_t sc, const moe_bf16x8 (&xv)[2], moe_f32x4& a) {
+            const float scale = mx_scale_operand((sc >> sshift) & 0xffu);
+            a = __builtin_amdgcn_mfma_f32_16x16x32_bf16(mx_dequant8(q[0], q[1], scale), xv[0], a, 0, 0, 0);
+            a = __builtin_amdgcn_mfma_f32_16x16x32_bf16(mx_dequant8(q[2], q[3], scale), xv[1], a, 0, 0, 0);
+        };
+        auto mma = [&](moe_u32x4 (*q)[US], uint32_t (*sc)[US], moe_bf16x8 (*xv)[2]) {
+#pragma unroll
+            for (int u = 0; u < US; ++u)
+#pragma unroll
+                for (int rb = 0; rb < RB; ++rb) seg_mma(q[rb][u], sc[rb][u], xv[u], acc[rb]);
+        };
+        if (nblk > 0) load_x(xa, 0);
+        int b = 0;
+        for (; b + 2 <= nblk; b += 2) {
+            load_w(qb, sb, b + 1);
+            load_x(xb, b + 1);
+            mma(qa, sa, xa);
+            if (b + 2 < nblk) {
+                load_w(qa, sa, b + 2);
+                load_x(xa, b + 2);
+            }
+            mma(qb, sb, xb);
+        }
+        if (b < nblk) mma(qa, sa, xa);
+        for (int sg = sg0 + nblk * US; sg < sg1; ++sg) {   // tail segments
+            const int o = sg - sg0;
+            moe_bf16x8 xv[2];
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+                const moe_bf16x8 v = ap[o * 8 + h];
+                xv[h] = mvalid ? v : zero;
+            }
+#pragma unroll
+            for (int rb = 0; rb < RB; ++rb) seg_mma(wq[rb][o * 4], wsc[rb][o], xv, acc[rb]);
+        }
+        skinny_epilogue<GATED, RB>(acc, s_red, C, N, r0, mrows, n_tile);
+    }
+}
+
+template <bool GATED, int RB>
+__global__ __launch_bounds__(256) void gemm_skinny_mx_kernel(
+    const uint16_t* __restrict__ A, const int32_t* __restrict__ row_src, int topk,
+    const int32_t* __restrict__ offsets, const uint8_t* __restrict__ Wq,
+    const uint8_t* __restrict__ Ws, uint16_t* __restrict__ C, int E, int Kd, int N) {
+    __shared__ int s_start[kMaxExperts + 1];
+    __shared__ int s_wave[4];
+    __shared__ float s_red[4 * 16 * RB * 17];
+    skinny_tiles_mx<GATED, RB>(A, row_src, topk, offsets, Wq, Ws, C, E, Kd, N, s_start, s_wave, s_red);
+}
+
+// Gate-up on MXFP8 weights with the dispatch inside (T*K <= kFusedDispatchMax).
+__global__ __launch_bounds__(256) void gemm_skinny_gateup_dispatch_mx_kernel(
+    const uint16_t* __restrict__ x, const int32_t* __restrict__ ids,
+    const int32_t* __restrict__ ntok, int T, int topk, int E, int32_t* __restrict__ offsets,
+    int32_t* __restrict__ row_src, int32_t* __restrict__ token_row,
+    const uint8_t* __restrict__ Wq, const uint8_t* __restrict__ Ws, uint16_t* __restrict__ C,
+    int Kd, int N) {
+    __shared__ int s_off[kMaxExperts + 1];
+    __shared__ int s_wc[4 * kMaxExperts];
+    __shared__ int s_rows[kFusedDispatchMax];
+    __shared__ int s_start[kMaxExperts + 1];
+    __shared__ int s_wave[4];
+    __shared__ float s_red[4 * 16 * 17];
+    fused_dispatch(ids, ntok, T, topk, E, offsets, row_src, token_row, s_off, s_wc, s_rows, s_wave);
+    skinny_tiles_mx<true, 1>(x, s_rows, topk, s_off, Wq, Ws, C, E, Kd, N, s_start, s_wave, s_red);
+}
+
+// Down GEMM + combine for tiny batches on MXFP8 weights: down_combine_tiny_kernel
+// with blocks of 4 segments (4 KB of codes per wave and buffer); needs whole
+// blocks per wave (I % 1024 == 0).
+__global__ __launch_bounds__(256) void down_combine_tiny_mx_kernel(
+    const uint16_t* __restrict__ A, const int32_t* __restrict__ offsets,
+    const uint8_t* __restrict__ Wq, const uint8_t* __restrict__ Ws, int E, int Kd, int N,
+    const int32_t* __restrict__ token_row, const float* __restrict__ wts,
+    const int32_t* __restrict__ ntok, int T, int topk, uint16_t* __restrict__ out) {
+    constexpr int US = 4;
+    __shared__ int s_e[kTinyRows], s_r0[kTinyRows], s_m[kTinyRows];
+    __shared__ int s_ne;
+    __shared__ float s_part[kTinyRows][4][16][17];
+    __shared__ uint16_t s_y[kTinyRows][16][16];
+
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int li = lane & 15, lg = lane >> 4;
+    const int n0 = blockIdx.x * 16;
+    tiny_expert_slots(offsets, E, s_e, s_r0, s_m, &s_ne);
+    const int ne = s_ne;
+
+    const int nseg = Kd / 64;
+    const int sg0 = (wave * nseg) / 4;
+    const int nblk = (((wave + 1) * nseg) / 4 - sg0) / US;   // whole blocks (checked on the host)
+    const int total = ne * nblk;
+    const int sshift = 8 * (lg >> 1);
+    const moe_bf16x8 zero = {};
+
+    moe_u32x4 qa[US], qb[US];
+    uint32_t sa[US], sb[US];
+    moe_bf16x8 xa[US][2], xb[US][2];
+    auto load = [&](moe_u32x4* q, uint32_t* sc, moe_bf16x8 (*xv)[2], int b) {
+        const int i = b / nblk, kb = b - i * nblk;
+        const size_t grow = (size_t)s_e[i] * N + n0 + li;
+        const moe_u32x4* wp = reinterpret_cast<const moe_u32x4*>(Wq + grow * (size_t)Kd + (size_t)sg0 * 64 + lg * 16);
+        const uint16_t* sp = reinterpret_cast<const uint16_t*>(Ws + grow * (size_t)(Kd / 32)) + sg0;
+        const bool mvalid = li < s_m[i];
+        const int rr = s_r0[i] + (mvalid ? li : 0);
+        const moe_bf16x8* ap = reinterpret_cast<const moe_bf16x8*>(A + (size_t)rr * Kd + (size_t)sg0 * 64 + lg * 16);
+#pragma unroll
+        for (int u = 0; u < US; ++u) {
+            q[u] = wp[(kb * US + u) * 4];
+            sc[u] = sp[kb * US + u];
+        }
+#pragma unroll
+        for (int u = 0; u < US; ++u)
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+                const moe_bf16x8 v = ap[(kb * US + u) * 8 + h];
+                xv[u][h] = mvalid ? v : zero;
+            }
+    };
+    moe_f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+    auto step = [&](const moe_u32x4* q, const uint32_t* sc, moe_bf16x8 (*xv)[2], int b) {
+#pragma unroll
+        for (int u = 0; u < US; ++u) {
+            const float scale = mx_scale_operand((sc[u] >> sshift) & 0xffu);
+            acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(mx_dequant8(q[u][0], q[u][1], scale), xv[u][0], acc, 0, 0, 0);
+            acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(mx_dequant8(q[u][2], q[u][3], scale), xv[u][1], acc, 0, 0, 0);
+        }
+        if ((b + 1) % nblk == 0) {   // last block of expert slot b / nblk
+            const int i = b / nblk;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) s_part[i][wave][4 * lg + r][li] = acc[r];
+            acc = (moe_f32x4){0.f, 0.f, 0.f, 0.f};
+        }
+    };
+    if (total > 0) load(qa, sa, xa, 0);
+    int b = 0;
+    for (; b + 2 <= total; b += 2) {
+        load(qb, sb, xb, b + 1);
+        step(qa, sa, xa, b);
+        if (b + 2 < total) load(qa, sa, xa, b + 2);
+        step(qb, sb, xb, b + 1);
+    }
+    if (b < total) step(qa, sa, xa, b);
+    __syncthreads();
+    tiny_combine(ne, s_r0, &s_part[0][0][0][0], &s_y[0][0][0], token_row, wts, ntok, T, topk, N, n0, out);
+}
+
+// ---------------------------------------------------------------------------
+// MXFP8 quantization and dequantization of weight rows (OCP MX recipe: the
+// block scale is 2^(floor(log2(amax)) - 8), 8 being the exponent of e4m3's
+// largest binade; codes are v / scale rounded to the nearest e4m3 value, ties
+// to even, saturated at 448; the code's sign bit is the input's).  Exact
+// integer arithmetic on the bf16 bit patterns; one thread per 32-value block.
+// ---------------------------------------------------------------------------
+// e4m3 code of sig * 2^t (sig >= 0 an integer below 2^8), sign in bit 7
+__device__ __forceinline__ uint32_t mx_e4m3_code(uint32_t sig, int t, uint32_t sign) {
+    if (sig == 0) return sign << 7;
+    const int msb = 31 - __clz((int)sig);
+    const int L = msb + t;                               // floor(log2(value))
+    const int qe = (L > -6 ? L : -6) - 3;                // exponent of the code spacing
+    const int sh = qe - t;                               // value / 2^qe = sig * 2^-sh
+    uint32_t n;
+    if (sh <= 0) {
+        n = sig << (-sh);
+    } else if (sh >= 31) {
+        n = 0;
+    } else {
+        n = sig >> sh;
+        const uint32_t rem = sig & ((1u << sh) - 1u), half = 1u << (sh - 1);
+        if (rem > half || (rem == half && (n & 1u))) ++n;   // nearest, ties to even
+    }
+    uint32_t code = L >= -6 ? (uint32_t)(((L + 7) << 3) + (int)n - 8) : n;
+    if (L >= -6 && code > 0x7Eu) code = 0x7Eu;           // saturate at 448
+    return code | (sign << 7);
+}
+
+__global__ __launch_bounds__(256) void mxfp8_quantize_kernel(const uint16_t* __restrict__ w,
+                                                             long long nblocks,
+                                                             uint8_t* __restrict__ codes,
+                                                             uint8_t* __restrict__ scales) {
+    const long long blk = (long long)blockIdx.x * blockDim.x + threadIdx.x;
+    if (blk >= nblocks) return;
+    typedef uint16_t u16x8 __attribute__((ext_vector_type(8)));
+    const u16x8* src = reinterpret_cast<const u16x8*>(w + blk * 32);
+    uint16_t v[32];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const u16x8 p = src[i];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) v[8 * i + j] = p[j];
+    }
+    uint32_t amax = 0;   // magnitude bit patterns order like the magnitudes
+#pragma unroll
+    for (int i = 0; i < 32; ++i) amax = max(amax, (uint32_t)(v[i] & 0x7FFFu));
+    int sc = 0;
+    if (amax != 0) {
+        const int eb = (int)(amax >> 7);
+        const int lg2 = eb ? eb - 127 : (31 - __clz((int)amax)) - 133;   // floor(log2(amax))
+        sc = lg2 - 8 + 127;
+        sc = sc < 0 ? 0 : (sc > 254 ? 254 : sc);
+    }
+    uint32_t out[8] = {};
+#pragma unroll
+    for (int i = 0; i < 32; ++i) {
+        const uint32_t m = v[i] & 0x7FFFu, eb = m >> 7, mb = m & 0x7Fu;
+        const uint32_t sig = eb ? (128u + mb) : mb;
+        const int t = (int)(eb ? eb : 1u) - sc - 7;      // |v| / 2^(sc - 127) = sig * 2^t
+        out[i >> 2] |= mx_e4m3_code(sig, t, v[i] >> 15) << (8 * (i & 3));
+    }
+    moe_u32x4* dst = reinterpret_cast<moe_u32x4*>(codes + blk * 32);
+    dst[0] = (moe_u32x4){out[0], out[1], out[2], out[3]};
+    dst[1] = (moe_u32x4){out[4], out[5], out[6], out[7]};
+    scales[blk] = (uint8_t)sc;
+}
+
+__global__ __launch_bounds__(256) void mxfp8_dequantize_kernel(const uint8_t* __restrict__ codes,
+                                                               const uint8_t* __restrict__ scales,
+                                                               long long nblocks,
+                                                               uint16_t* __restrict__ w) {
+    const long long blk = (long long)blockIdx.x * blockDim.x + threadIdx.x;
+    if (blk >= nblocks) return;
+    const moe_u32x4* src = reinterpret_cast<const moe_u32x4*>(codes + blk * 32);
+    const float scale = mx_scale_operand(scales[blk]);
+    moe_bf16x8* dst = reinterpret_cast<moe_bf16x8*>(w + blk * 32);
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+        const moe_u32x4 q = src[i];
+        dst[2 * i] = mx_dequant8(q[0], q[1], scale);
+        dst[2 * i + 1] = mx_dequant8(q[2], q[3], scale);
+    }
 }
 
 // ---------------------------------------------------------------------------
@@ -881,6 +1274,59 @@ hipError_t launch_down_combine_tiny(const Shape& s, const uint16_t* h, const int
                                     const int32_t* ntok, uint16_t* out, hipStream_t st) {
     hipLaunchKernelGGL(down_combine_tiny_kernel, dim3(s.H / 16), dim3(256), 0, st, h, offsets, W,
                        s.E, s.I, s.H, token_row, w, ntok, s.T, s.K, out);
+    return hipGetLastError();
+}
+
+hipError_t launch_gateup_fused_dispatch_mx(const Shape& s, const uint16_t* x, const int32_t* ids,
+                                           const int32_t* ntok, int32_t* offsets,
+                                           int32_t* row_src, int32_t* token_row,
+                                           const uint8_t* Wq, const uint8_t* Ws, uint16_t* h,
+                                           hipStream_t st) {
+    hipLaunchKernelGGL(gemm_skinny_gateup_dispatch_mx_kernel, dim3(4 * kNumCUs), dim3(256), 0, st,
+                       x, ids, ntok, s.T, s.K, s.E, offsets, row_src, token_row, Wq, Ws, h, s.H,
+                       s.I);
+    return hipGetLastError();
+}
+
+hipError_t launch_down_combine_tiny_mx(const Shape& s, const uint16_t* h, const int32_t* offsets,
+                                       const uint8_t* Wq, const uint8_t* Ws,
+                                       const int32_t* token_row, const float* w,
+                                       const int32_t* ntok, uint16_t* out, hipStream_t st) {
+    hipLaunchKernelGGL(down_combine_tiny_mx_kernel, dim3(s.H / 16), dim3(256), 0, st, h, offsets,
+                       Wq, Ws, s.E, s.I, s.H, token_row, w, ntok, s.T, s.K, out);
+    return hipGetLastError();
+}
+
+hipError_t launch_grouped_gemm_mx(const Shape& s, bool gated, const uint16_t* A,
+                                  const int32_t* row_src, int topk, const int32_t* offsets,
+                                  const uint8_t* Wq, const uint8_t* Ws, uint16_t* C, int Kd, int N,
+                                  hipStream_t st) {
+    const dim3 grid(4 * kNumCUs), block(256);
+    if (gated)
+        hipLaunchKernelGGL((gemm_skinny_mx_kernel<true, 1>), grid, block, 0, st, A, row_src, topk,
+                           offsets, Wq, Ws, C, s.E, Kd, N);
+    else if (N % 32 == 0)
+        hipLaunchKernelGGL((gemm_skinny_mx_kernel<false, 2>), grid, block, 0, st, A, row_src, topk,
+                           offsets, Wq, Ws, C, s.E, Kd, N);
+    else
+        hipLaunchKernelGGL((gemm_skinny_mx_kernel<false, 1>), grid, block, 0, st, A, row_src, topk,
+                           offsets, Wq, Ws, C, s.E, Kd, N);
+    return hipGetLastError();
+}
+
+hipError_t launch_mxfp8_quantize(const uint16_t* w, long long nblocks, uint8_t* codes,
+                                 uint8_t* scales, hipStream_t st) {
+    if (nblocks == 0) return hipSuccess;
+    hipLaunchKernelGGL(mxfp8_quantize_kernel, dim3((unsigned)((nblocks + 255) / 256)), dim3(256), 0,
+                       st, w, nblocks, codes, scales);
+    return hipGetLastError();
+}
+
+hipError_t launch_mxfp8_dequantize(const uint8_t* codes, const uint8_t* scales, long long nblocks,
+                                   uint16_t* w, hipStream_t st) {
+    if (nblocks == 0) return hipSuccess;
+    hipLaunchKernelGGL(mxfp8_dequantize_kernel, dim3((unsigned)((nblocks + 255) / 256)), dim3(256),
+                       0, st, codes, scales, nblocks, w);
     return hipGetLastError();
 }
 

@@ -310,15 +310,24 @@ E4M3_MAX = 448.0
 MX_BLOCK = 32
 
 
-def e4m3_to_f64(codes) -> np.ndarray:
-    """Value of OCP FP8 E4M3 codes (uint8) as float64."""
-    c = np.asarray(codes, dtype=np.uint8).astype(np.int64)
+def _e4m3_value(c: np.ndarray) -> np.ndarray:
+    """The E4M3 encoding written out: sign, exponent field, mantissa field."""
+    c = c.astype(np.int64)
     sign = (c >> 7) & 1
     ex = (c >> 3) & 15
     man = c & 7
     mag = np.where(ex == 0, man / 8.0 * 2.0 ** -6, (1.0 + man / 8.0) * np.exp2(ex - 7.0))
     v = np.where(sign == 1, -mag, mag)
     return np.where((ex == 15) & (man == 7), np.nan, v)
+
+
+_E4M3_VALUES = _e4m3_value(np.arange(256))
+
+
+def e4m3_to_f64(codes) -> np.ndarray:
+    """Value of OCP FP8 E4M3 codes (uint8) as float64 (the 256 values of the
+    encoding, looked up by code)."""
+    return _E4M3_VALUES[np.asarray(codes, dtype=np.uint8)]
 
 
 def e8m0_to_f64(codes) -> np.ndarray:

@@ -25,7 +25,7 @@ def declared_functions():
 
 def test_exports_every_declared_symbol():
     names = declared_functions()
-    assert len(names) == 12, names
+    assert len(names) == 16, names
     L = moe.lib()
     for n in names:
         assert hasattr(L, n), n
@@ -109,3 +109,39 @@ def test_bad_pointers_rejected():
     assert L.moe_graph_create(ctypes.byref(p), A16, A4, A4, A16, A16, None, A4, A16, A16, 16,
                               ctypes.byref(h)) == 1
     assert h.value is None
+
+
+def test_mxfp8_entry_points_fail_closed():
+    L = moe.lib()
+    p = moe.problem(64, 2, 8, 256, 512)
+    ws = moe.workspace_size(p)
+    fwd = lambda q, *a: L.moe_forward_mxfp8(ctypes.byref(q), *a)
+    good = [A16, A4, A4, A16, A16 + 2, A16, A16 + 2, None, A4, A16, A16, ws, None]
+    for i in (0, 1, 2, 3, 4, 5, 6, 8, 9, 10):   # each required pointer nulled
+        args = list(good)
+        args[i] = None
+        assert fwd(p, *args) == _lib.MOE_ERROR_INVALID_VALUE, i
+    for i, bad in ((3, A16 + 1), (5, A16 + 8), (4, A16 + 1), (6, A16 + 3), (0, A16 + 2)):
+        args = list(good)                       # codes 16-B, scales 2-B, x 16-B aligned
+        args[i] = bad
+        assert fwd(p, *args) == _lib.MOE_ERROR_INVALID_VALUE, i
+    args = list(good)
+    args[11] = ws - 1
+    assert fwd(p, *args) == _lib.MOE_ERROR_INVALID_VALUE
+    for hint in (2, 3, 4):                      # only the skinny plan serves MXFP8 weights
+        q = moe.problem(64, 2, 8, 256, 512, kernel_hint=hint)
+        assert fwd(q, *good) == _lib.MOE_ERROR_NOT_SUPPORTED
+        assert L.moe_gate_up_mxfp8(ctypes.byref(q), A16, A4, A16, A16, A16, None) == 2
+    assert L.moe_gate_up_mxfp8(ctypes.byref(p), A16, A4, A16, A16 + 1, A16, None) == 1
+    # quantize / dequantize: k a positive multiple of 32, aligned buffers
+    assert L.moe_mxfp8_quantize(A16, 4, 48, A16, A16, None) == 1
+    assert L.moe_mxfp8_quantize(A16, 4, 0, A16, A16, None) == 1
+    assert L.moe_mxfp8_quantize(A16, -1, 32, A16, A16, None) == 1
+    assert L.moe_mxfp8_quantize(A16 + 2, 4, 32, A16, A16, None) == 1
+    assert L.moe_mxfp8_quantize(A16, 4, 32, A16 + 4, A16, None) == 1
+    assert L.moe_mxfp8_quantize(A16, 4, 32, A16, None, None) == 1
+    assert L.moe_mxfp8_quantize(None, 0, 32, None, None, None) == 0     # nothing to do
+    assert L.moe_mxfp8_quantize(A16, 1 << 36, 1 << 12, A16, A16, None) == 2
+    assert L.moe_mxfp8_dequantize(A16 + 1, A16, 4, 32, A16, None) == 1
+    assert L.moe_mxfp8_dequantize(A16, A16, 4, 32, A16 + 2, None) == 1
+    assert L.moe_mxfp8_dequantize(A16, A16, 4, 33, A16, None) == 1
