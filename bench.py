@@ -85,8 +85,9 @@ def kernel_src_hash() -> str:
     return h.hexdigest()
 
 
-def cpu_baseline(inp_host, wgu, wd, cfg, budget_tokens: int):
-    """The oracle, as it stands, on the first `budget_tokens` tokens."""
+def cpu_baseline(inp_host, wgu, wd, cfg, budget_tokens: int, mx=None):
+    """The oracle, as it stands, on the first `budget_tokens` tokens (with
+    mx = (codes_gu, scales_gu, codes_d, scales_d) on the MXFP8 weights)."""
     import numpy as np
     import torch
 
@@ -106,7 +107,8 @@ def cpu_baseline(inp_host, wgu, wd, cfg, budget_tokens: int):
 
     class Experts:
         def __init__(self, w):
-            self.host = {e: bits(w[e].cpu()) for e in used}
+            self.host = {e: (w[e].cpu().numpy() if w.dtype == torch.uint8 else bits(w[e].cpu()))
+                         for e in used}
             self.n = w.shape[0]
 
         def __len__(self):
@@ -115,9 +117,15 @@ def cpu_baseline(inp_host, wgu, wd, cfg, budget_tokens: int):
         def __getitem__(self, e):
             return self.host[int(e)]
 
-    xg, wug, wdg = bits(inp_host["x"]), Experts(wgu), Experts(wd)
-    t0 = time.perf_counter()
-    oracle.forward_tokens(xg, ids, inp_host["topk_weights"].numpy(), wug, wdg, toks)
+    xg = bits(inp_host["x"])
+    if mx is None:
+        wug, wdg = Experts(wgu), Experts(wd)
+        t0 = time.perf_counter()
+        oracle.forward_tokens(xg, ids, inp_host["topk_weights"].numpy(), wug, wdg, toks)
+    else:
+        qs = [Experts(t) for t in mx]
+        t0 = time.perf_counter()
+        oracle.forward_tokens_mxfp8(xg, ids, inp_host["topk_weights"].numpy(), *qs, toks)
     dt = time.perf_counter() - t0
     rows = int(((ids[toks] >= 0) & (ids[toks] < cfg.num_experts)).sum())
     flops = 6.0 * cfg.hidden * cfg.intermediate * rows
@@ -155,6 +163,9 @@ def main():
                          "(default 50 for static_capacity, else 0)")
     ap.add_argument("--cpu-tokens", type=int, default=None,
                     help="tokens in the oracle's timed sample (default by workload)")
+    ap.add_argument("--weights", choices=("bf16", "mxfp8"), default="bf16",
+                    help="expert weight format: bf16, or MXFP8 (e4m3 codes + one e8m0 scale per "
+                         "32 values, quantized on the device before timing)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     args = ap.parse_args()
 
@@ -182,6 +193,15 @@ def main():
     ids_h, w_h = W.make_routing(cfg, args.seed)
     wgu, wd = W.make_weights(cfg, args.seed, dev)
     x, ids, w = x_h.to(dev), ids_h.to(dev), w_h.to(dev)
+    mx = args.weights == "mxfp8"
+    if mx:
+        if args.graph or args.replays:
+            raise SystemExit("--graph / --replays record the bf16 layer; use --weights bf16")
+        qgu, sgu = ops.mxfp8_quantize(wgu)
+        qd, sd = ops.mxfp8_quantize(wd)
+        torch.cuda.synchronize()
+    # HBM bytes per weight value: bf16, or an e4m3 code plus 1/32 of a scale byte
+    wbytes = 1.0 + 1.0 / 32.0 if mx else 2.0
     draws = args.draws if args.draws is not None else (32 if cfg.name.startswith("ep_decode") else 1)
     if draws > 1:   # routing draws cycled one per step, same x and weights
         routes_h = [W.make_routing(cfg, 1000 + d) for d in range(draws)]
@@ -211,7 +231,11 @@ def main():
             graph.launch()
         else:
             ri, rw = routes[i % draws]
-            ops.forward(p, x, ri, rw, wgu, wd, expert_offsets=off, out=out, workspace=ws)
+            if mx:
+                ops.forward_mxfp8(p, x, ri, rw, qgu, sgu, qd, sd, expert_offsets=off, out=out,
+                                  workspace=ws)
+            else:
+                ops.forward(p, x, ri, rw, wgu, wd, expert_offsets=off, out=out, workspace=ws)
 
     def work(ids_t, t_valid):
         # algorithmic flop and bytes of one layer call (host copy of the routing)
@@ -219,7 +243,8 @@ def main():
         v = v[(v >= 0) & (v < E)]
         r = int(v.numel())
         n_touched = int(torch.unique(v).numel()) if r else 0
-        return 6.0 * H * I * r, 6.0 * H * I * n_touched + 4.0 * H * t_valid + 8.0 * t_valid * K, r, n_touched
+        return (6.0 * H * I * r, 3.0 * wbytes * H * I * n_touched + 4.0 * H * t_valid + 8.0 * t_valid * K,
+                r, n_touched)
 
     for i in range(args.warmup):
         step(i)
@@ -274,8 +299,12 @@ def main():
     # ---- dominant kernel alone: the gate-up grouped GEMM ------------------
     x_disp, off2, _, _ = ops.dispatch(p, x, ids)
     hbuf = torch.empty((p.capacity or T * K, I), dtype=torch.bfloat16, device=dev)
-    ops.gate_up(p, x_disp, off2, wgu, h=hbuf)
-    k_ms = timed(lambda: ops.gate_up(p, x_disp, off2, wgu, h=hbuf))
+    if mx:
+        gu_call = lambda: ops.gate_up_mxfp8(p, x_disp, off2, qgu, sgu, h=hbuf)
+    else:
+        gu_call = lambda: ops.gate_up(p, x_disp, off2, wgu, h=hbuf)
+    gu_call()
+    k_ms = timed(gu_call)
 
     # ---- the stages alone (same inputs, --seed routing) -------------------
     x_disp_s, off_s, row_src_s, token_row_s = ops.dispatch(p, x, ids, workspace=ws)
@@ -288,6 +317,9 @@ def main():
                                                      y_disp=y_s),
         "combine": lambda: ops.combine(p, y_s, token_row_s, w, out=out_s),
     }
+    if mx:   # the staged MXFP8 calls: the gate-up grouped GEMM alone
+        del stage_calls["expert_compute"]
+        stage_calls["gate_up"] = gu_call
     if cfg.routing == "softmax_topk":   # the router step ahead of dispatch, on the same seed's logits
         logits = W.make_logits(cfg, args.seed).to(dev)
         ids_r = torch.empty_like(ids)
@@ -296,16 +328,18 @@ def main():
                        **stage_calls}
     # long calls first: the spin that short calls sit behind lowers the clock
     # for a while after it
-    order = ["expert_compute", "combine", "dispatch", "router"]
+    order = ["expert_compute", "gate_up", "combine", "dispatch", "router"]
     stages_us = {name: timed(stage_calls[name]) * 1e3 for name in order if name in stage_calls}
 
     F_gu = 4.0 * H * I * R
-    B_gu = 4.0 * H * I * touched + 2.0 * H * R + 2.0 * I * R
+    B_gu = 2.0 * wbytes * H * I * touched + 2.0 * H * R + 2.0 * I * R
     mfma_bound = (F_gu / max(B_gu, 1.0)) >= RIDGE
     # the host plan rule of the library: forced hint, else rows per expert T*K/E
     rpe = T * K / E
     kind = args.hint if args.hint in (1, 2, 3, 4) else (1 if rpe <= 24 else 2 if rpe <= 96 else 4)
     kernel_name = "gemm_skinny_kernel" if kind == 1 else "gemm_tiled_kernel"
+    if mx:
+        kernel_name = "gemm_skinny_mx_kernel"
     traffic = pmc_traffic(f"{kernel_name}<gated>@{cfg.name}", kernel_src_hash(), 1)
     if mfma_bound:
         ach = F_gu / (k_ms / 1e3) / 1e12
@@ -319,7 +353,8 @@ def main():
                  "algorithmic_flop": F_gu, "algorithmic_bytes": B_gu})
 
     # ---- extra: graph replays with a device token count T_i ~ U{1..T} -----
-    n_rep = args.replays if args.replays is not None else (50 if cfg.name == "static_capacity" else 0)
+    n_rep = args.replays if args.replays is not None else (
+        50 if cfg.name == "static_capacity" and not mx else 0)
     replays = None
     if n_rep > 0:
         ntok = torch.empty((1,), dtype=torch.int32, device=dev)
@@ -384,7 +419,9 @@ def main():
                    "seed": args.seed, "timing": ("cold (L2/MALL evicted per step)" if args.cold
                                                  else "back-to-back")
                    + (", HIP graph replay" if args.graph else ", eager launches"),
-                   "kernel_hint": args.hint},
+                   "kernel_hint": args.hint,
+                   "weights": ("mxfp8: e4m3 codes + one e8m0 scale per 32 values along K"
+                               if mx else "bf16")},
         "roofline": roof,
     }
     if replays is not None:
@@ -394,7 +431,8 @@ def main():
         if budget is None:
             budget = {"mixtral": T, "tiny": 64}.get(cfg.name, max(16, min(T, 64)))
         result["cpu_baseline"] = cpu_baseline({"x": x_h, "topk_ids": ids_h, "topk_weights": w_h},
-                                              wgu, wd, cfg, budget)
+                                              wgu, wd, cfg, budget,
+                                              (qgu, sgu, qd, sd) if mx else None)
     print(json.dumps(result), flush=True)
 
 

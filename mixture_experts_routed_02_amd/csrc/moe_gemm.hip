@@ -61,10 +61,12 @@ __device__ __forceinline__ int find_expert(const int* s_start, int E, int tile) 
 // Skinny kernel: weight-streaming regime (a handful of rows per expert).
 // Tile = 16*RB weight rows x 16 token rows x the whole K, split over the 4
 // waves of the workgroup (contiguous k ranges), reduced through LDS in wave
-// order.  gated (RB = 1): the 16 weight rows are 8 gate rows and the 8
-// matching up rows, so a tile produces 8 output columns; plain: 16*RB output
-// columns (the down GEMM uses RB = 2 so that one token's tiles fill the
-// resident workgroups in one round).  Each wave keeps two blocks of weights
+// order.  gated: the 16*RB weight rows are 8*RB gate rows and the 8*RB
+// matching up rows, so a tile produces 8*RB output columns (the gate-up GEMM
+// uses RB = 1: 32-row gated tiles, which halve the token-row loads per weight
+// byte, measured no faster); plain: 16*RB output columns (the down GEMM uses
+// RB = 2 so that one token's tiles fill the resident workgroups in one
+// round).  Each wave keeps two blocks of weights
 // (8 KB) in flight: the next block is loaded while the current one is
 // multiplied.  Blocks of 4 k-steps (rather than 8) keep the kernel under 128
 // VGPRs, so 4 workgroups fit per CU: measured 2-3% faster on the decode
@@ -85,7 +87,7 @@ template <bool GATED, int RB>
 __device__ __forceinline__ void skinny_epilogue(const moe_f32x4 (&acc)[RB], float* s_red,
                                                 uint16_t* __restrict__ C, int N, int r0,
                                                 int mrows, int n_tile) {
-    constexpr int COLS = GATED ? 8 : 16 * RB;
+    constexpr int COLS = GATED ? 8 * RB : 16 * RB;
     constexpr int RED_ROWS = 16 * RB;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int li = lane & 15, lg = lane >> 4;
@@ -95,14 +97,14 @@ __device__ __forceinline__ void skinny_epilogue(const moe_f32x4 (&acc)[RB], floa
 #pragma unroll
         for (int i = 0; i < 4; ++i) red(wave, rb * 16 + 4 * lg + i, li) = acc[rb][i];
     __syncthreads();
-    if (GATED) {
-        if (tid < 128) {
-            const int m = tid >> 3, c = tid & 7;
+    if (GATED) {   // tile rows [0, COLS) gate, [COLS, 2 COLS) the matching up rows
+        if (tid < 16 * COLS) {
+            const int m = tid / COLS, c = tid % COLS;
             if (m < mrows) {
                 float g = 0.f, u = 0.f;
 #pragma unroll
-                for (int w = 0; w < 4; ++w) { g += red(w, c, m); u += red(w, 8 + c, m); }
-                C[(size_t)(r0 + m) * N + n_tile * 8 + c] = moe_f32_to_bf16(silu_f32(g) * u);
+                for (int w = 0; w < 4; ++w) { g += red(w, c, m); u += red(w, COLS + c, m); }
+                C[(size_t)(r0 + m) * N + n_tile * COLS + c] = moe_f32_to_bf16(silu_f32(g) * u);
             }
         }
     } else {
@@ -130,10 +132,10 @@ __device__ __forceinline__ void skinny_tiles(const uint16_t* __restrict__ A, con
                                              const uint16_t* __restrict__ W,
                                              uint16_t* __restrict__ C, int E, int Kd, int N,
                                              int* s_start, int* s_wave, float* s_red) {
-    static_assert(RB == 1 || (RB == 2 && !GATED), "tile rows");
+    static_assert(RB == 1 || RB == 2, "tile rows");
     constexpr int BM = 16;
     constexpr int U = 4 / RB;                      // k-steps (of 32) per block
-    constexpr int COLS = GATED ? 8 : 16 * RB;
+    constexpr int COLS = GATED ? 8 * RB : 16 * RB;
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int li = lane & 15, lg = lane >> 4;
@@ -159,9 +161,9 @@ __device__ __forceinline__ void skinny_tiles(const uint16_t* __restrict__ A, con
         const moe_bf16x8* wp[RB];
 #pragma unroll
         for (int rb = 0; rb < RB; ++rb) {
-            int wrow;
-            if (GATED) wrow = (li < 8) ? (n_tile * 8 + li) : (N + n_tile * 8 + (li - 8));
-            else wrow = n_tile * COLS + rb * 16 + li;
+            const int tr = rb * 16 + li;   // gated: rows [0, COLS) gate, then the matching up rows
+            const int wrow = !GATED ? n_tile * COLS + tr
+                           : tr < COLS ? n_tile * COLS + tr : N + n_tile * COLS + (tr - COLS);
             wp[rb] = reinterpret_cast<const moe_bf16x8*>(
                 W + ((size_t)e * w_rows + wrow) * (size_t)Kd + (size_t)ks0 * 32 + lg * 8);
         }
@@ -506,6 +508,16 @@ __global__ __launch_bounds__(256) void gemm_skinny_gateup_dispatch_kernel(
 // ---------------------------------------------------------------------------
 typedef uint32_t moe_u32x4 __attribute__((ext_vector_type(4)));
 
+// Block size and grid of the MXFP8 skinny kernels.  Blocks of 4 segments (4 KB
+// of codes per wave and buffer, 8 KB in flight, as the bf16 kernel keeps)
+// need ~148 VGPRs, so 3 workgroups fit per CU and the grid is 3 x CUs.
+// Measured against 2-segment blocks at 4 x CUs: 12-14% faster on the 96-expert
+// decode shapes (T = 8 .. 128), 7% at T = 1; 6-segment blocks at 2 x CUs and
+// 32-weight-row gated tiles (half the token-row loads per weight byte) were no
+// faster.
+constexpr int kMxSegs = 4;
+constexpr int kMxGrid = 3;
+
 // Scale operand of v_cvt_scalef32_*: an fp32 whose exponent field holds the
 // e8m0 code (gfx950 reads the scale from those bits).
 __device__ __forceinline__ float mx_scale_operand(uint32_t code) { return __uint_as_float(code << 23); }
@@ -535,10 +547,10 @@ __device__ __forceinline__ void skinny_tiles_mx(const uint16_t* __restrict__ A, 
                                                 const uint8_t* __restrict__ Ws,
                                                 uint16_t* __restrict__ C, int E, int Kd, int N,
                                                 int* s_start, int* s_wave, float* s_red) {
-    static_assert(RB == 1 || (RB == 2 && !GATED), "tile rows");
+    static_assert(RB == 1 || RB == 2, "tile rows");
     constexpr int BM = 16;
-    constexpr int US = 2 / RB;                     // 64-k segments per block
-    constexpr int COLS = GATED ? 8 : 16 * RB;
+    constexpr int US = kMxSegs / RB;               // 64-k segments per block
+    constexpr int COLS = GATED ? 8 * RB : 16 * RB;
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int li = lane & 15, lg = lane >> 4;
@@ -566,9 +578,9 @@ __device__ __forceinline__ void skinny_tiles_mx(const uint16_t* __restrict__ A, 
         const uint16_t* wsc[RB];
 #pragma unroll
         for (int rb = 0; rb < RB; ++rb) {
-            int wrow;
-            if (GATED) wrow = (li < 8) ? (n_tile * 8 + li) : (N + n_tile * 8 + (li - 8));
-            else wrow = n_tile * COLS + rb * 16 + li;
+            const int tr = rb * 16 + li;   // gated: rows [0, COLS) gate, then the matching up rows
+            const int wrow = !GATED ? n_tile * COLS + tr
+                           : tr < COLS ? n_tile * COLS + tr : N + n_tile * COLS + (tr - COLS);
             const size_t grow = (size_t)e * w_rows + wrow;
             wq[rb] = reinterpret_cast<const moe_u32x4*>(Wq + grow * (size_t)Kd + (size_t)sg0 * 64 + lg * 16);
             wsc[rb] = reinterpret_cast<const uint16_t*>(Ws + grow * (size_t)(Kd / 32)) + sg0;
@@ -1282,7 +1294,7 @@ hipError_t launch_gateup_fused_dispatch_mx(const Shape& s, const uint16_t* x, co
                                            int32_t* row_src, int32_t* token_row,
                                            const uint8_t* Wq, const uint8_t* Ws, uint16_t* h,
                                            hipStream_t st) {
-    hipLaunchKernelGGL(gemm_skinny_gateup_dispatch_mx_kernel, dim3(4 * kNumCUs), dim3(256), 0, st,
+    hipLaunchKernelGGL(gemm_skinny_gateup_dispatch_mx_kernel, dim3(kMxGrid * kNumCUs), dim3(256), 0, st,
                        x, ids, ntok, s.T, s.K, s.E, offsets, row_src, token_row, Wq, Ws, h, s.H,
                        s.I);
     return hipGetLastError();
@@ -1301,7 +1313,7 @@ hipError_t launch_grouped_gemm_mx(const Shape& s, bool gated, const uint16_t* A,
                                   const int32_t* row_src, int topk, const int32_t* offsets,
                                   const uint8_t* Wq, const uint8_t* Ws, uint16_t* C, int Kd, int N,
                                   hipStream_t st) {
-    const dim3 grid(4 * kNumCUs), block(256);
+    const dim3 grid(kMxGrid * kNumCUs), block(256);
     if (gated)
         hipLaunchKernelGGL((gemm_skinny_mx_kernel<true, 1>), grid, block, 0, st, A, row_src, topk,
                            offsets, Wq, Ws, C, s.E, Kd, N);
