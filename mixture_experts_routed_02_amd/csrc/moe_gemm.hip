@@ -71,8 +71,10 @@ __device__ __forceinline__ int find_expert(const int* s_start, int E, int tile) 
 // multiplied.  Blocks of 4 k-steps (rather than 8) keep the kernel under 128
 // VGPRs, so 4 workgroups fit per CU: measured 2-3% faster on the decode
 // workloads than 3 workgroups with twice the bytes in flight each.  Token rows
-// past the expert's valid rows load a valid row and are zeroed in registers
-// (no branches).
+// past the expert's valid rows load a valid row (no branches) and are left as
+// they are: MFMA output column j depends on token row j alone, and the
+// epilogues write only the valid rows (zeroing them in registers made the
+// loads wait early; 1-2% slower on the MXFP8 decode shapes).
 // ---------------------------------------------------------------------------
 // Plain loads: measured on the device, marking these one-use weight loads
 // non-temporal made the decode workloads 8-20% slower.
@@ -146,7 +148,6 @@ __device__ __forceinline__ void skinny_tiles(const uint16_t* __restrict__ A, con
     const int ksteps = Kd / 32;
     const int ks0 = (wave * ksteps) / 4, ks1 = ((wave + 1) * ksteps) / 4;
     const int nblk = (ks1 - ks0) / U;              // full blocks; the rest is a tail
-    const moe_bf16x8 zero = {};
 
     for (int tile = blockIdx.x; tile < total; tile += gridDim.x) {
         const int e = find_expert(s_start, E, tile);
@@ -186,7 +187,7 @@ __device__ __forceinline__ void skinny_tiles(const uint16_t* __restrict__ A, con
 #pragma unroll
             for (int u = 0; u < U; ++u) {
                 const moe_bf16x8 v = ap[(b * U + u) * 4];
-                xv[u] = mvalid ? v : zero;
+                xv[u] = v;
             }
         };
         moe_f32x4 acc[RB];
@@ -215,7 +216,7 @@ __device__ __forceinline__ void skinny_tiles(const uint16_t* __restrict__ A, con
         for (int ks = ks0 + nblk * U; ks < ks1; ++ks) {   // tail k-steps
             const int o = (ks - ks0) * 4;
             const moe_bf16x8 v = ap[o];
-            const moe_bf16x8 xv = mvalid ? v : zero;
+            const moe_bf16x8 xv = v;
 #pragma unroll
             for (int rb = 0; rb < RB; ++rb)
                 acc[rb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(stream_load(wp[rb] + o), xv, acc[rb], 0, 0, 0);
@@ -332,7 +333,6 @@ __global__ __launch_bounds__(256) void down_combine_tiny_kernel(
     const int nb = ((wave + 1) * ksteps) / 4 - ks0;
     const int nblk = nb / U;                       // whole blocks (checked on the host)
     const int total = ne * nblk;
-    const moe_bf16x8 zero = {};
 
     auto wptr = [&](int i) {
         return reinterpret_cast<const moe_bf16x8*>(
@@ -347,13 +347,12 @@ __global__ __launch_bounds__(256) void down_combine_tiny_kernel(
         const int i = b / nblk, kb = b - i * nblk;
         const moe_bf16x8* wp = wptr(i);
         const moe_bf16x8* ap = xptr(i);
-        const bool mvalid = li < s_m[i];
 #pragma unroll
         for (int u = 0; u < U; ++u) wv[u] = stream_load(wp + (kb * U + u) * 4);
 #pragma unroll
         for (int u = 0; u < U; ++u) {
             const moe_bf16x8 v = ap[(kb * U + u) * 4];
-            xv[u] = mvalid ? v : zero;
+            xv[u] = v;
         }
     };
     moe_f32x4 acc = {0.f, 0.f, 0.f, 0.f};
@@ -562,7 +561,6 @@ __device__ __forceinline__ void skinny_tiles_mx(const uint16_t* __restrict__ A, 
     const int sg0 = (wave * nseg) / 4, sg1 = ((wave + 1) * nseg) / 4;
     const int nblk = (sg1 - sg0) / US;             // full blocks; the rest is a tail
     const int sshift = 8 * (lg >> 1);              // this lane group's scale byte
-    const moe_bf16x8 zero = {};
 
     for (int tile = blockIdx.x; tile < total; tile += gridDim.x) {
         const int e = find_expert(s_start, E, tile);
@@ -610,7 +608,7 @@ __device__ __forceinline__ void skinny_tiles_mx(const uint16_t* __restrict__ A, 
 #pragma unroll
                 for (int h = 0; h < 2; ++h) {
                     const moe_bf16x8 v = ap[(b * US + u) * 8 + h];
-                    xv[u][h] = mvalid ? v : zero;
+                    xv[u][h] = v;
                 }
         };
         moe_f32x4 acc[RB];
@@ -646,7 +644,7 @@ __device__ __forceinline__ void skinny_tiles_mx(const uint16_t* __restrict__ A, 
 #pragma unroll
             for (int h = 0; h < 2; ++h) {
                 const moe_bf16x8 v = ap[o * 8 + h];
-                xv[h] = mvalid ? v : zero;
+                xv[h] = v;
             }
 #pragma unroll
             for (int rb = 0; rb < RB; ++rb) seg_mma(wq[rb][o * 4], wsc[rb][o], xv, acc[rb]);
@@ -708,7 +706,6 @@ __global__ __launch_bounds__(256) void down_combine_tiny_mx_kernel(
     const int nblk = (((wave + 1) * nseg) / 4 - sg0) / US;   // whole blocks (checked on the host)
     const int total = ne * nblk;
     const int sshift = 8 * (lg >> 1);
-    const moe_bf16x8 zero = {};
 
     moe_u32x4 qa[US], qb[US];
     uint32_t sa[US], sb[US];
@@ -731,7 +728,7 @@ __global__ __launch_bounds__(256) void down_combine_tiny_mx_kernel(
 #pragma unroll
             for (int h = 0; h < 2; ++h) {
                 const moe_bf16x8 v = ap[(kb * US + u) * 8 + h];
-                xv[u][h] = mvalid ? v : zero;
+                xv[u][h] = v;
             }
     };
     moe_f32x4 acc = {0.f, 0.f, 0.f, 0.f};
