@@ -51,7 +51,8 @@ __all__ = [
     "expert_mlp_f64",
     "expert_compute", "combine", "forward", "forward_tokens",
     "e4m3_to_f64", "e8m0_to_f64", "mxfp8_quantize", "mxfp8_to_f64",
-    "forward_tokens_mxfp8", "forward_mxfp8",
+    "forward_tokens_mxfp8", "forward_mxfp8", "e2m1_to_f64", "mxfp4_quantize", "mxfp4_to_f64",
+    "forward_tokens_mxfp4", "forward_mxfp4",
 ]
 
 
@@ -407,4 +408,112 @@ def forward_mxfp8(x, topk_ids, topk_weights, wgu_codes, wgu_scales, wd_codes, wd
     """The whole MXFP8-weight layer for every token: float64 [T, H]."""
     T = np.asarray(topk_ids).shape[0]
     return forward_tokens_mxfp8(x, topk_ids, topk_weights, wgu_codes, wgu_scales, wd_codes,
+                                wd_scales, np.arange(T), num_valid_tokens)
+
+
+# ---------------------------------------------------------------------------
+# MXFP4 expert weights: blocks of 32 e2m1 values sharing one e8m0 scale (the
+# 4-bit member of the same family: FlashInfer PR #3980 pairs its MXFP8 backend
+# with 4-bit NVFP4 weights, and DeepGEMM PR #394 streams FP4 weight packets).
+#
+# Readings: e2m1 is the OCP FP4 encoding -- sign, 2 exponent bits with bias 1,
+# 1 mantissa bit; exponent field 0 holds the subnormal m/2; no infinities or
+# NaN; the values are 0, 0.5, 1, 1.5, 2, 3, 4, 6.  Two codes per byte, the
+# even-indexed value of a pair in the low nibble.  The block scale follows the
+# OCP MX recipe with e2m1's top-binade exponent 2: 2^(floor(log2(amax)) - 2),
+# code clamped to [0, 254], 0 for an all-zero block; elements are v / scale
+# rounded to the nearest e2m1 value, ties to even mantissa, magnitudes above 6
+# saturated to 6; the sign bit is the input's.
+# ---------------------------------------------------------------------------
+E2M1_MAX = 6.0
+
+
+def _e2m1_value(c: np.ndarray) -> np.ndarray:
+    """The E2M1 encoding written out: sign, exponent field, mantissa field."""
+    c = c.astype(np.int64)
+    sign = (c >> 3) & 1
+    ex = (c >> 1) & 3
+    man = c & 1
+    mag = np.where(ex == 0, man * 0.5, (1.0 + man / 2.0) * np.exp2(ex - 1.0))
+    return np.where(sign == 1, -mag, mag)
+
+
+_E2M1_VALUES = _e2m1_value(np.arange(16))
+
+
+def e2m1_to_f64(codes) -> np.ndarray:
+    """Value of 4-bit E2M1 codes (0..15, one per array element) as float64."""
+    return _E2M1_VALUES[np.asarray(codes, dtype=np.uint8) & 15]
+
+
+def _round_to_e2m1(y: np.ndarray) -> np.ndarray:
+    """Nearest e2m1 magnitude to |y|, ties to even mantissa, saturated at 6.
+    Binade [2^E, 2^(E+1)), E >= 0, holds 2 values spaced 2^(E-1); below 1 the
+    spacing is the subnormal step 1/2."""
+    a = np.abs(y)
+    _, ex = np.frexp(a)
+    binade = np.maximum(ex - 1, 0)
+    step = np.exp2(binade - 1.0)
+    q = np.round(a / step) * step
+    return np.minimum(q, E2M1_MAX)
+
+
+def _encode_e2m1(mag: np.ndarray, sign: np.ndarray) -> np.ndarray:
+    """Code (0..15) of an exactly representable e2m1 magnitude and a sign."""
+    code = np.zeros(mag.shape, dtype=np.int64)
+    sub = mag < 1.0
+    code[sub] = np.rint(mag[sub] * 2.0).astype(np.int64)              # 0 or 1: field 0
+    f, ex = np.frexp(mag[~sub])
+    code[~sub] = (((ex - 1) + 1) << 1) | np.rint((f * 2.0 - 1.0) * 2.0).astype(np.int64)
+    return code | (sign.astype(np.int64) << 3)
+
+
+def mxfp4_quantize(w_bits):
+    """MXFP4 quantization of bf16 weights along their last axis.
+
+    w_bits: bf16 bits (uint16) [..., K], K a multiple of 32.  Returns
+    (packed uint8 [..., K // 2], scales uint8 [..., K // 32]): byte i of a row
+    holds the codes of values 2i (low nibble) and 2i + 1 (high nibble)."""
+    b = np.ascontiguousarray(w_bits, dtype=np.uint16)
+    K = b.shape[-1]
+    if K % MX_BLOCK:
+        raise ValueError("K must be a multiple of 32")
+    v = bf16_to_f64(b).reshape(b.shape[:-1] + (K // MX_BLOCK, MX_BLOCK))
+    amax = np.abs(v).max(axis=-1)
+    _, ex = np.frexp(amax)
+    s_code = np.where(amax > 0, np.clip((ex - 1) - 2 + 127, 0, 254), 0).astype(np.int64)
+    y = v / np.exp2(s_code - 127.0)[..., None]
+    mag = _round_to_e2m1(y)
+    sign = (b.reshape(v.shape) >> np.uint16(15)).astype(np.int64)
+    codes = _encode_e2m1(mag, sign).reshape(b.shape)
+    packed = (codes[..., 0::2] | (codes[..., 1::2] << 4)).astype(np.uint8)
+    return packed, s_code.astype(np.uint8)
+
+
+def mxfp4_to_f64(packed, scales) -> np.ndarray:
+    """Dequantized MXFP4 weights [..., K]: e2m1 value times its block's scale."""
+    p = np.asarray(packed, dtype=np.uint8)
+    codes = np.empty(p.shape[:-1] + (2 * p.shape[-1],), dtype=np.uint8)
+    codes[..., 0::2] = p & 15
+    codes[..., 1::2] = p >> 4
+    s = np.asarray(scales, dtype=np.uint8)
+    return e2m1_to_f64(codes) * np.repeat(e8m0_to_f64(s), MX_BLOCK, axis=-1)
+
+
+def forward_tokens_mxfp4(x, topk_ids, topk_weights, wgu_packed, wgu_scales, wd_packed, wd_scales,
+                         tokens, num_valid_tokens: int | None = None):
+    """forward_tokens with MXFP4 expert weights (packed codes [E, 2I, H/2] /
+    scales [E, 2I, H/32], packed codes [E, H, I/2] / scales [E, H, I/32]),
+    dequantized exactly to float64, then the same layer definition."""
+    return _forward_tokens_widened(
+        x, topk_ids, topk_weights, len(wgu_packed),
+        lambda e: (mxfp4_to_f64(wgu_packed[e], wgu_scales[e]), mxfp4_to_f64(wd_packed[e], wd_scales[e])),
+        tokens, num_valid_tokens)
+
+
+def forward_mxfp4(x, topk_ids, topk_weights, wgu_packed, wgu_scales, wd_packed, wd_scales,
+                  num_valid_tokens: int | None = None):
+    """The whole MXFP4-weight layer for every token: float64 [T, H]."""
+    T = np.asarray(topk_ids).shape[0]
+    return forward_tokens_mxfp4(x, topk_ids, topk_weights, wgu_packed, wgu_scales, wd_packed,
                                 wd_scales, np.arange(T), num_valid_tokens)
