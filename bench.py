@@ -85,9 +85,9 @@ def kernel_src_hash() -> str:
     return h.hexdigest()
 
 
-def cpu_baseline(inp_host, wgu, wd, cfg, budget_tokens: int, mx=None):
+def cpu_baseline(inp_host, wgu, wd, cfg, budget_tokens: int, mx=None, fmt="bf16"):
     """The oracle, as it stands, on the first `budget_tokens` tokens (with
-    mx = (codes_gu, scales_gu, codes_d, scales_d) on the MXFP8 weights)."""
+    mx = (codes_gu, scales_gu, codes_d, scales_d) on the MX weights of fmt)."""
     import numpy as np
     import torch
 
@@ -125,7 +125,8 @@ def cpu_baseline(inp_host, wgu, wd, cfg, budget_tokens: int, mx=None):
     else:
         qs = [Experts(t) for t in mx]
         t0 = time.perf_counter()
-        oracle.forward_tokens_mxfp8(xg, ids, inp_host["topk_weights"].numpy(), *qs, toks)
+        fwd = oracle.forward_tokens_mxfp8 if fmt == "mxfp8" else oracle.forward_tokens_mxfp4
+        fwd(xg, ids, inp_host["topk_weights"].numpy(), *qs, toks)
     dt = time.perf_counter() - t0
     rows = int(((ids[toks] >= 0) & (ids[toks] < cfg.num_experts)).sum())
     flops = 6.0 * cfg.hidden * cfg.intermediate * rows
@@ -163,9 +164,10 @@ def main():
                          "(default 50 for static_capacity, else 0)")
     ap.add_argument("--cpu-tokens", type=int, default=None,
                     help="tokens in the oracle's timed sample (default by workload)")
-    ap.add_argument("--weights", choices=("bf16", "mxfp8"), default="bf16",
-                    help="expert weight format: bf16, or MXFP8 (e4m3 codes + one e8m0 scale per "
-                         "32 values, quantized on the device before timing)")
+    ap.add_argument("--weights", choices=("bf16", "mxfp8", "mxfp4"), default="bf16",
+                    help="expert weight format: bf16, MXFP8 (e4m3 codes + one e8m0 scale per 32 "
+                         "values) or MXFP4 (e2m1 codes, two per byte, same scales), quantized on "
+                         "the device before timing")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     args = ap.parse_args()
 
@@ -193,15 +195,15 @@ def main():
     ids_h, w_h = W.make_routing(cfg, args.seed)
     wgu, wd = W.make_weights(cfg, args.seed, dev)
     x, ids, w = x_h.to(dev), ids_h.to(dev), w_h.to(dev)
-    mx = args.weights == "mxfp8"
+    mx = args.weights != "bf16"
     if mx:
         if args.graph or args.replays:
             raise SystemExit("--graph / --replays record the bf16 layer; use --weights bf16")
-        qgu, sgu = ops.mxfp8_quantize(wgu)
-        qd, sd = ops.mxfp8_quantize(wd)
+        qgu, sgu = ops.mx_quantize(wgu, args.weights)
+        qd, sd = ops.mx_quantize(wd, args.weights)
         torch.cuda.synchronize()
-    # HBM bytes per weight value: bf16, or an e4m3 code plus 1/32 of a scale byte
-    wbytes = 1.0 + 1.0 / 32.0 if mx else 2.0
+    # HBM bytes per weight value: bf16, or a code (1 or 1/2 byte) plus 1/32 of a scale byte
+    wbytes = {"bf16": 2.0, "mxfp8": 1.0 + 1.0 / 32.0, "mxfp4": 0.5 + 1.0 / 32.0}[args.weights]
     draws = args.draws if args.draws is not None else (32 if cfg.name.startswith("ep_decode") else 1)
     if draws > 1:   # routing draws cycled one per step, same x and weights
         routes_h = [W.make_routing(cfg, 1000 + d) for d in range(draws)]
@@ -232,8 +234,8 @@ def main():
         else:
             ri, rw = routes[i % draws]
             if mx:
-                ops.forward_mxfp8(p, x, ri, rw, qgu, sgu, qd, sd, expert_offsets=off, out=out,
-                                  workspace=ws)
+                ops.forward_mx(p, x, ri, rw, qgu, sgu, qd, sd, args.weights, expert_offsets=off,
+                               out=out, workspace=ws)
             else:
                 ops.forward(p, x, ri, rw, wgu, wd, expert_offsets=off, out=out, workspace=ws)
 
@@ -300,7 +302,7 @@ def main():
     x_disp, off2, _, _ = ops.dispatch(p, x, ids)
     hbuf = torch.empty((p.capacity or T * K, I), dtype=torch.bfloat16, device=dev)
     if mx:
-        gu_call = lambda: ops.gate_up_mxfp8(p, x_disp, off2, qgu, sgu, h=hbuf)
+        gu_call = lambda: ops.gate_up_mx(p, x_disp, off2, qgu, sgu, args.weights, h=hbuf)
     else:
         gu_call = lambda: ops.gate_up(p, x_disp, off2, wgu, h=hbuf)
     gu_call()
@@ -317,7 +319,7 @@ def main():
                                                      y_disp=y_s),
         "combine": lambda: ops.combine(p, y_s, token_row_s, w, out=out_s),
     }
-    if mx:   # the staged MXFP8 calls: the gate-up grouped GEMM alone
+    if mx:   # the staged MX calls: the gate-up grouped GEMM alone
         del stage_calls["expert_compute"]
         stage_calls["gate_up"] = gu_call
     if cfg.routing == "softmax_topk":   # the router step ahead of dispatch, on the same seed's logits
@@ -339,7 +341,7 @@ def main():
     kind = args.hint if args.hint in (1, 2, 3, 4) else (1 if rpe <= 24 else 2 if rpe <= 96 else 4)
     kernel_name = "gemm_skinny_kernel" if kind == 1 else "gemm_tiled_kernel"
     if mx:
-        kernel_name = "gemm_skinny_mx_kernel"
+        kernel_name = f"gemm_skinny_mx_kernel<{8 if args.weights == 'mxfp8' else 4}>"
     traffic = pmc_traffic(f"{kernel_name}<gated>@{cfg.name}", kernel_src_hash(), 1)
     if mfma_bound:
         ach = F_gu / (k_ms / 1e3) / 1e12
@@ -420,8 +422,10 @@ def main():
                                                  else "back-to-back")
                    + (", HIP graph replay" if args.graph else ", eager launches"),
                    "kernel_hint": args.hint,
-                   "weights": ("mxfp8: e4m3 codes + one e8m0 scale per 32 values along K"
-                               if mx else "bf16")},
+                   "weights": {"bf16": "bf16",
+                               "mxfp8": "mxfp8: e4m3 codes + one e8m0 scale per 32 values along K",
+                               "mxfp4": "mxfp4: e2m1 codes (two per byte) + one e8m0 scale per "
+                                        "32 values along K"}[args.weights]},
         "roofline": roof,
     }
     if replays is not None:
@@ -432,7 +436,7 @@ def main():
             budget = {"mixtral": T, "tiny": 64}.get(cfg.name, max(16, min(T, 64)))
         result["cpu_baseline"] = cpu_baseline({"x": x_h, "topk_ids": ids_h, "topk_weights": w_h},
                                               wgu, wd, cfg, budget,
-                                              (qgu, sgu, qd, sd) if mx else None)
+                                              (qgu, sgu, qd, sd) if mx else None, args.weights)
     print(json.dumps(result), flush=True)
 
 

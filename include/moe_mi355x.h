@@ -243,6 +243,53 @@ MOE_API moe_status_t moe_forward_mxfp8(const moe_problem_t* p, const uint16_t* x
                                        uint16_t* out, void* workspace, size_t ws_bytes,
                                        void* stream);
 
+/* ---------------------------------------------------------------------------
+ * MXFP4 expert weights: the 4-bit member of the same family (FlashInfer PR
+ * #3980 pairs its MXFP8 backend with 4-bit NVFP4 weights; DeepGEMM PR #394,
+ * Summary, streams FP4 expert weights), a quarter of the bf16 weight bytes.
+ *
+ * Format of a weight matrix with K-contiguous rows [rows, K], K % 32 == 0:
+ *   codes   uint8 [rows, K/2]: OCP FP4 E2M1 codes (sign, 2 exponent bits with
+ *           bias 1, 1 mantissa bit: 0, 0.5, 1, 1.5, 2, 3, 4, 6; no infinities
+ *           or NaN), two per byte, value 2i in the low nibble of byte i
+ *   scales  uint8 [rows, K/32]: e8m0, one per 32 consecutive values of a row
+ *   value(r, k) = e2m1(code(r, k)) * 2^(scales[r, k/32] - 127)
+ * For the layer: W_gateup codes [E, 2I, H/2] + scales [E, 2I, H/32], W_down
+ * codes [E, H, I/2] + scales [E, H, I/32].  codes 16-byte aligned, scales
+ * 4-byte aligned; H and I multiples of 128 (MOE_ERROR_NOT_SUPPORTED
+ * otherwise).
+ * ------------------------------------------------------------------------- */
+
+/* Quantize bf16 rows w [rows, k] to MXFP4: per block of 32 the scale is
+ * 2^(floor(log2(amax)) - 2), its code clamped to [0, 254] (0 for an all-zero
+ * block); each code is the nearest e2m1 value to v / scale, ties to even,
+ * magnitudes above 6 saturated to 6, sign bit = the input's.  Exact integer
+ * arithmetic.  Same argument rules as moe_mxfp8_quantize. */
+MOE_API moe_status_t moe_mxfp4_quantize(const uint16_t* w, int64_t rows, int32_t k,
+                                        uint8_t* codes, uint8_t* scales, void* stream);
+
+/* Dequantize MXFP4 rows to bf16 w [rows, k] with the conversion the expert
+ * kernels use (v_cvt_scalef32_pk_bf16_fp4); exact whenever the result is a
+ * normal bf16 value. */
+MOE_API moe_status_t moe_mxfp4_dequantize(const uint8_t* codes, const uint8_t* scales,
+                                          int64_t rows, int32_t k, uint16_t* w, void* stream);
+
+/* moe_gate_up_mxfp8 / moe_forward_mxfp8 with MXFP4 weights (same contracts). */
+MOE_API moe_status_t moe_gate_up_mxfp4(const moe_problem_t* p, const uint16_t* x_disp,
+                                       const int32_t* expert_offsets,
+                                       const uint8_t* w_gateup_codes,
+                                       const uint8_t* w_gateup_scales, uint16_t* h,
+                                       void* stream);
+MOE_API moe_status_t moe_forward_mxfp4(const moe_problem_t* p, const uint16_t* x,
+                                       const int32_t* topk_ids, const float* topk_weights,
+                                       const uint8_t* w_gateup_codes,
+                                       const uint8_t* w_gateup_scales,
+                                       const uint8_t* w_down_codes,
+                                       const uint8_t* w_down_scales,
+                                       const int32_t* num_tokens_dev, int32_t* expert_offsets,
+                                       uint16_t* out, void* workspace, size_t ws_bytes,
+                                       void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -142,18 +142,20 @@ moe_status_t forward_impl(const Shape& s, int hint, const uint16_t* x, const int
     return launched(moe::launch_combine(s, y, token_row, w, ntok, out, st));
 }
 
-// MXFP8 expert weights: the skinny kernels for every batch size.
+// MX expert weights (fmt 8 = MXFP8, 4 = MXFP4): the skinny kernels for every
+// batch size.
 bool bad_codes(const void* p) { return !p || !aligned(p, 16); }
-bool bad_scales(const void* p) { return !p || !aligned(p, 2); }
+bool bad_scales(const void* p, int fmt) { return !p || !aligned(p, fmt == 8 ? 2 : 4); }
 
-moe_status_t check_mx_problem(const moe_problem_t* p, Shape* s) {
+moe_status_t check_mx_problem(const moe_problem_t* p, int fmt, Shape* s) {
     moe_status_t st = check_problem(p, s);
     if (st != MOE_SUCCESS) return st;
     if (p->kernel_hint != 0 && p->kernel_hint != moe::kSkinny) return MOE_ERROR_NOT_SUPPORTED;
+    if (fmt == 4 && (s->H % 128 != 0 || s->I % 128 != 0)) return MOE_ERROR_NOT_SUPPORTED;
     return MOE_SUCCESS;
 }
 
-moe_status_t forward_mx_impl(const Shape& s, const uint16_t* x, const int32_t* ids,
+moe_status_t forward_mx_impl(const Shape& s, int fmt, const uint16_t* x, const int32_t* ids,
                              const float* w, const uint8_t* qgu, const uint8_t* sgu,
                              const uint8_t* qd, const uint8_t* sd, const int32_t* ntok,
                              int32_t* offsets, uint16_t* out, void* ws, hipStream_t st) {
@@ -164,22 +166,22 @@ moe_status_t forward_mx_impl(const Shape& s, const uint16_t* x, const int32_t* i
     uint16_t* h = at<uint16_t>(ws, L.h);
     uint16_t* y = at<uint16_t>(ws, L.y);
     if ((long long)s.T * s.K <= moe::kFusedDispatchMax) {
-        if (moe::launch_gateup_fused_dispatch_mx(s, x, ids, ntok, offsets, row_src, token_row, qgu,
-                                                 sgu, h, st) != hipSuccess)
+        if (moe::launch_gateup_fused_dispatch_mx(s, fmt, x, ids, ntok, offsets, row_src, token_row,
+                                                 qgu, sgu, h, st) != hipSuccess)
             return MOE_ERROR_LAUNCH;
         if (moe::tiny_down_ok(s))
-            return launched(moe::launch_down_combine_tiny_mx(s, h, offsets, qd, sd, token_row, w,
-                                                             ntok, out, st));
+            return launched(moe::launch_down_combine_tiny_mx(s, fmt, h, offsets, qd, sd, token_row,
+                                                             w, ntok, out, st));
     } else {
         if (moe::launch_dispatch(s, ids, ntok, offsets, row_src, token_row, counts, st) !=
             hipSuccess)
             return MOE_ERROR_LAUNCH;
-        if (moe::launch_grouped_gemm_mx(s, true, x, row_src, s.K, offsets, qgu, sgu, h, s.H, s.I,
-                                        st) != hipSuccess)
+        if (moe::launch_grouped_gemm_mx(s, fmt, true, x, row_src, s.K, offsets, qgu, sgu, h, s.H,
+                                        s.I, st) != hipSuccess)
             return MOE_ERROR_LAUNCH;
     }
-    if (moe::launch_grouped_gemm_mx(s, false, h, nullptr, 1, offsets, qd, sd, y, s.I, s.H, st) !=
-        hipSuccess)
+    if (moe::launch_grouped_gemm_mx(s, fmt, false, h, nullptr, 1, offsets, qd, sd, y, s.I, s.H,
+                                    st) != hipSuccess)
         return MOE_ERROR_LAUNCH;
     if (s.T == 0) return MOE_SUCCESS;
     return launched(moe::launch_combine(s, y, token_row, w, ntok, out, st));
@@ -191,6 +193,59 @@ moe_status_t check_mx_rows(const void* a, const void* b, int64_t rows, int32_t k
     if (rows == 0) return MOE_SUCCESS;
     if (!a || !b || !aligned(a, 16)) return MOE_ERROR_INVALID_VALUE;
     return MOE_SUCCESS;
+}
+
+moe_status_t mx_quantize(int fmt, const uint16_t* w, int64_t rows, int32_t k, uint8_t* codes,
+                         uint8_t* scales, void* stream) {
+    moe_status_t st = check_mx_rows(w, scales, rows, k);
+    if (st != MOE_SUCCESS) return st;
+    if (rows == 0) return MOE_SUCCESS;
+    if (!codes || !aligned(codes, 16)) return MOE_ERROR_INVALID_VALUE;
+    return launched(moe::launch_mx_quantize(fmt, w, rows * (k / 32), codes, scales,
+                                            static_cast<hipStream_t>(stream)));
+}
+
+moe_status_t mx_dequantize(int fmt, const uint8_t* codes, const uint8_t* scales, int64_t rows,
+                           int32_t k, uint16_t* w, void* stream) {
+    moe_status_t st = check_mx_rows(codes, scales, rows, k);
+    if (st != MOE_SUCCESS) return st;
+    if (rows == 0) return MOE_SUCCESS;
+    if (!w || !aligned(w, 16)) return MOE_ERROR_INVALID_VALUE;
+    return launched(moe::launch_mx_dequantize(fmt, codes, scales, rows * (k / 32), w,
+                                              static_cast<hipStream_t>(stream)));
+}
+
+moe_status_t gate_up_mx(int fmt, const moe_problem_t* p, const uint16_t* x_disp,
+                        const int32_t* expert_offsets, const uint8_t* codes, const uint8_t* scales,
+                        uint16_t* h, void* stream) {
+    Shape s;
+    moe_status_t st = check_mx_problem(p, fmt, &s);
+    if (st != MOE_SUCCESS) return st;
+    if (bad_bf16(x_disp, s.cap) || bad_i32(expert_offsets) || bad_codes(codes) ||
+        bad_scales(scales, fmt) || bad_bf16(h, s.cap))
+        return MOE_ERROR_INVALID_VALUE;
+    return launched(moe::launch_grouped_gemm_mx(s, fmt, true, x_disp, nullptr, s.K,
+                                                expert_offsets, codes, scales, h, s.H, s.I,
+                                                static_cast<hipStream_t>(stream)));
+}
+
+moe_status_t forward_mx(int fmt, const moe_problem_t* p, const uint16_t* x,
+                        const int32_t* topk_ids, const float* topk_weights, const uint8_t* qgu,
+                        const uint8_t* sgu, const uint8_t* qd, const uint8_t* sd,
+                        const int32_t* num_tokens_dev, int32_t* expert_offsets, uint16_t* out,
+                        void* workspace, size_t ws_bytes, void* stream) {
+    Shape s;
+    moe_status_t st = check_mx_problem(p, fmt, &s);
+    if (st != MOE_SUCCESS) return st;
+    const long long tk = (long long)s.T * s.K;
+    if (bad_bf16(x, s.T) || bad_i32(topk_ids, tk) || bad_i32(topk_weights, tk) ||
+        bad_codes(qgu) || bad_scales(sgu, fmt) || bad_codes(qd) || bad_scales(sd, fmt) ||
+        bad_i32(expert_offsets) || bad_bf16(out, s.T))
+        return MOE_ERROR_INVALID_VALUE;
+    if (num_tokens_dev && !aligned(num_tokens_dev, 4)) return MOE_ERROR_INVALID_VALUE;
+    if ((st = check_ws(s, workspace, ws_bytes)) != MOE_SUCCESS) return st;
+    return forward_mx_impl(s, fmt, x, topk_ids, topk_weights, qgu, sgu, qd, sd, num_tokens_dev,
+                           expert_offsets, out, workspace, static_cast<hipStream_t>(stream));
 }
 
 struct GraphHandle {
@@ -335,36 +390,18 @@ moe_status_t moe_forward(const moe_problem_t* p, const uint16_t* x, const int32_
 
 moe_status_t moe_mxfp8_quantize(const uint16_t* w, int64_t rows, int32_t k, uint8_t* codes,
                                 uint8_t* scales, void* stream) {
-    moe_status_t st = check_mx_rows(w, scales, rows, k);
-    if (st != MOE_SUCCESS) return st;
-    if (rows == 0) return MOE_SUCCESS;
-    if (!codes || !aligned(codes, 16)) return MOE_ERROR_INVALID_VALUE;
-    return launched(moe::launch_mxfp8_quantize(w, rows * (k / 32), codes, scales,
-                                               static_cast<hipStream_t>(stream)));
+    return mx_quantize(8, w, rows, k, codes, scales, stream);
 }
 
 moe_status_t moe_mxfp8_dequantize(const uint8_t* codes, const uint8_t* scales, int64_t rows,
                                   int32_t k, uint16_t* w, void* stream) {
-    moe_status_t st = check_mx_rows(codes, scales, rows, k);
-    if (st != MOE_SUCCESS) return st;
-    if (rows == 0) return MOE_SUCCESS;
-    if (!w || !aligned(w, 16)) return MOE_ERROR_INVALID_VALUE;
-    return launched(moe::launch_mxfp8_dequantize(codes, scales, rows * (k / 32), w,
-                                                 static_cast<hipStream_t>(stream)));
+    return mx_dequantize(8, codes, scales, rows, k, w, stream);
 }
 
 moe_status_t moe_gate_up_mxfp8(const moe_problem_t* p, const uint16_t* x_disp,
                                const int32_t* expert_offsets, const uint8_t* w_gateup_codes,
                                const uint8_t* w_gateup_scales, uint16_t* h, void* stream) {
-    Shape s;
-    moe_status_t st = check_mx_problem(p, &s);
-    if (st != MOE_SUCCESS) return st;
-    if (bad_bf16(x_disp, s.cap) || bad_i32(expert_offsets) || bad_codes(w_gateup_codes) ||
-        bad_scales(w_gateup_scales) || bad_bf16(h, s.cap))
-        return MOE_ERROR_INVALID_VALUE;
-    return launched(moe::launch_grouped_gemm_mx(s, true, x_disp, nullptr, s.K, expert_offsets,
-                                                w_gateup_codes, w_gateup_scales, h, s.H, s.I,
-                                                static_cast<hipStream_t>(stream)));
+    return gate_up_mx(8, p, x_disp, expert_offsets, w_gateup_codes, w_gateup_scales, h, stream);
 }
 
 moe_status_t moe_forward_mxfp8(const moe_problem_t* p, const uint16_t* x, const int32_t* topk_ids,
@@ -373,19 +410,36 @@ moe_status_t moe_forward_mxfp8(const moe_problem_t* p, const uint16_t* x, const 
                                const uint8_t* w_down_scales, const int32_t* num_tokens_dev,
                                int32_t* expert_offsets, uint16_t* out, void* workspace,
                                size_t ws_bytes, void* stream) {
-    Shape s;
-    moe_status_t st = check_mx_problem(p, &s);
-    if (st != MOE_SUCCESS) return st;
-    const long long tk = (long long)s.T * s.K;
-    if (bad_bf16(x, s.T) || bad_i32(topk_ids, tk) || bad_i32(topk_weights, tk) ||
-        bad_codes(w_gateup_codes) || bad_scales(w_gateup_scales) || bad_codes(w_down_codes) ||
-        bad_scales(w_down_scales) || bad_i32(expert_offsets) || bad_bf16(out, s.T))
-        return MOE_ERROR_INVALID_VALUE;
-    if (num_tokens_dev && !aligned(num_tokens_dev, 4)) return MOE_ERROR_INVALID_VALUE;
-    if ((st = check_ws(s, workspace, ws_bytes)) != MOE_SUCCESS) return st;
-    return forward_mx_impl(s, x, topk_ids, topk_weights, w_gateup_codes, w_gateup_scales,
-                           w_down_codes, w_down_scales, num_tokens_dev, expert_offsets, out,
-                           workspace, static_cast<hipStream_t>(stream));
+    return forward_mx(8, p, x, topk_ids, topk_weights, w_gateup_codes, w_gateup_scales,
+                      w_down_codes, w_down_scales, num_tokens_dev, expert_offsets, out, workspace,
+                      ws_bytes, stream);
+}
+
+moe_status_t moe_mxfp4_quantize(const uint16_t* w, int64_t rows, int32_t k, uint8_t* codes,
+                                uint8_t* scales, void* stream) {
+    return mx_quantize(4, w, rows, k, codes, scales, stream);
+}
+
+moe_status_t moe_mxfp4_dequantize(const uint8_t* codes, const uint8_t* scales, int64_t rows,
+                                  int32_t k, uint16_t* w, void* stream) {
+    return mx_dequantize(4, codes, scales, rows, k, w, stream);
+}
+
+moe_status_t moe_gate_up_mxfp4(const moe_problem_t* p, const uint16_t* x_disp,
+                               const int32_t* expert_offsets, const uint8_t* w_gateup_codes,
+                               const uint8_t* w_gateup_scales, uint16_t* h, void* stream) {
+    return gate_up_mx(4, p, x_disp, expert_offsets, w_gateup_codes, w_gateup_scales, h, stream);
+}
+
+moe_status_t moe_forward_mxfp4(const moe_problem_t* p, const uint16_t* x, const int32_t* topk_ids,
+                               const float* topk_weights, const uint8_t* w_gateup_codes,
+                               const uint8_t* w_gateup_scales, const uint8_t* w_down_codes,
+                               const uint8_t* w_down_scales, const int32_t* num_tokens_dev,
+                               int32_t* expert_offsets, uint16_t* out, void* workspace,
+                               size_t ws_bytes, void* stream) {
+    return forward_mx(4, p, x, topk_ids, topk_weights, w_gateup_codes, w_gateup_scales,
+                      w_down_codes, w_down_scales, num_tokens_dev, expert_offsets, out, workspace,
+                      ws_bytes, stream);
 }
 
 moe_status_t moe_graph_create(const moe_problem_t* p, const uint16_t* x, const int32_t* topk_ids,

@@ -185,10 +185,7 @@ __device__ __forceinline__ void skinny_tiles(const uint16_t* __restrict__ A, con
             A + (size_t)arow * Kd + (size_t)ks0 * 32 + lg * 8);
         auto load_x = [&](moe_bf16x8* xv, int b) {
 #pragma unroll
-            for (int u = 0; u < U; ++u) {
-                const moe_bf16x8 v = ap[(b * U + u) * 4];
-                xv[u] = v;
-            }
+            for (int u = 0; u < U; ++u) xv[u] = ap[(b * U + u) * 4];
         };
         moe_f32x4 acc[RB];
 #pragma unroll
@@ -215,8 +212,7 @@ __device__ __forceinline__ void skinny_tiles(const uint16_t* __restrict__ A, con
         if (b < nblk) mma(wa, xa);
         for (int ks = ks0 + nblk * U; ks < ks1; ++ks) {   // tail k-steps
             const int o = (ks - ks0) * 4;
-            const moe_bf16x8 v = ap[o];
-            const moe_bf16x8 xv = v;
+            const moe_bf16x8 xv = ap[o];
 #pragma unroll
             for (int rb = 0; rb < RB; ++rb)
                 acc[rb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(stream_load(wp[rb] + o), xv, acc[rb], 0, 0, 0);
@@ -506,16 +502,7 @@ __global__ __launch_bounds__(256) void gemm_skinny_gateup_dispatch_kernel(
 // per segment brings both of the segment's scales.
 // ---------------------------------------------------------------------------
 typedef uint32_t moe_u32x4 __attribute__((ext_vector_type(4)));
-
-// Block size and grid of the MXFP8 skinny kernels.  Blocks of 4 segments (4 KB
-// of codes per wave and buffer, 8 KB in flight, as the bf16 kernel keeps)
-// need ~148 VGPRs, so 3 workgroups fit per CU and the grid is 3 x CUs.
-// Measured against 2-segment blocks at 4 x CUs: 12-14% faster on the 96-expert
-// decode shapes (T = 8 .. 128), 7% at T = 1; 6-segment blocks at 2 x CUs and
-// 32-weight-row gated tiles (half the token-row loads per weight byte) were no
-// faster.
-constexpr int kMxSegs = 4;
-constexpr int kMxGrid = 3;
+typedef __bf16 moe_bf16x2 __attribute__((__vector_size__(2 * sizeof(__bf16))));
 
 // Scale operand of v_cvt_scalef32_*: an fp32 whose exponent field holds the
 // e8m0 code (gfx950 reads the scale from those bits).
@@ -523,9 +510,8 @@ __device__ __forceinline__ float mx_scale_operand(uint32_t code) { return __uint
 
 // 8 e4m3 codes (w0: codes 0-3, w1: codes 4-7, lowest byte first) -> 8 bf16
 __device__ __forceinline__ moe_bf16x8 mx_dequant8(uint32_t w0, uint32_t w1, float scale) {
-    typedef __bf16 bf16x2 __attribute__((__vector_size__(2 * sizeof(__bf16))));
     union {
-        bf16x2 p[4];
+        moe_bf16x2 p[4];
         moe_bf16x8 v;
     } r;
     r.p[0] = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w0, scale, false);
@@ -535,11 +521,72 @@ __device__ __forceinline__ moe_bf16x8 mx_dequant8(uint32_t w0, uint32_t w1, floa
     return r.v;
 }
 
-// Skinny tiles on MXFP8 weights: codes Wq [E, rows, Kd], scales Ws [E, rows,
-// Kd/32].  Same tiles, tile order, k split over the waves (in 64-k
+// 8 e2m1 codes (4 bytes, the lower nibble of a byte first) -> 8 bf16
+__device__ __forceinline__ moe_bf16x8 mx_dequant8_fp4(uint32_t w, float scale) {
+    union {
+        moe_bf16x2 p[4];
+        moe_bf16x8 v;
+    } r;
+    r.p[0] = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, scale, 0);
+    r.p[1] = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, scale, 1);
+    r.p[2] = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, scale, 2);
+    r.p[3] = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, scale, 3);
+    return r.v;
+}
+
+// The two code formats of the MX skinny kernels.  Either way a lane loads 16
+// bytes of codes per segment and a wave 64 bytes of every weight row, so the
+// code addressing is the same; what differs is how many k-values those bytes
+// hold (G per lane, SEG per wave), the MFMA steps they feed, and which of the
+// segment's scale bytes belongs to the lane.
+//   FMT 8 (e4m3):  G = 16, SEG = 64,  2 steps; scales of a segment: 2 bytes
+//                  (one 16-bit load), lane group lg takes byte lg / 2
+//   FMT 4 (e2m1):  G = 32, SEG = 128, 4 steps; scales of a segment: 4 bytes
+//                  (one 32-bit load), lane group lg takes byte lg
+// Step s of a segment takes the lane's codes 8s..8s+7, so an MFMA sums over
+// k = SEG*seg + G*g + 8*s + (0..7), g = 0..3, and the token operand is loaded
+// in the same k order (G/8 16-byte pieces per lane and segment).
+template <int FMT>
+struct MxFmt;
+template <>
+struct MxFmt<8> {
+    static constexpr int G = 16, SEG = 64, STEPS = 2, SCALES = 2;
+    typedef uint16_t scale_t;
+    __device__ static int scale_shift(int lg) { return 8 * (lg >> 1); }
+    __device__ static moe_bf16x8 dequant(const moe_u32x4& q, int s, float scale) {
+        return s == 0 ? mx_dequant8(q[0], q[1], scale) : mx_dequant8(q[2], q[3], scale);
+    }
+};
+template <>
+struct MxFmt<4> {
+    static constexpr int G = 32, SEG = 128, STEPS = 4, SCALES = 4;
+    typedef uint32_t scale_t;
+    __device__ static int scale_shift(int lg) { return 8 * lg; }
+    __device__ static moe_bf16x8 dequant(const moe_u32x4& q, int s, float scale) {
+        return mx_dequant8_fp4(q[s], scale);
+    }
+};
+
+// Block size (segments) and grid of the MX skinny kernels.  MXFP8: blocks of 4
+// segments (4 KB of codes per wave and buffer, 8 KB in flight, as the bf16
+// kernel keeps) need ~148 VGPRs, so 3 workgroups fit per CU and the grid is
+// 3 x CUs.  Measured against 2-segment blocks at 4 x CUs: 12-14% faster on the
+// 96-expert decode shapes (T = 8 .. 128), 7% at T = 1; 6-segment blocks at 2 x
+// CUs and 32-weight-row gated tiles (half the token-row loads per weight byte)
+// were no faster.  MXFP4: a segment carries twice the token values, so 2
+// segments keep the token registers, and the VGPR count, of MXFP8's 4 (4
+// segments at 2 x CUs: within 2%).  Loading the token operand only in the
+// lanes that hold valid rows (exec-masked) was 0-2% slower on all three
+// formats.
+template <int FMT>
+constexpr int mx_segs() { return FMT == 8 ? 4 : 2; }
+constexpr int kMxGrid = 3;
+
+// Skinny tiles on MX weights: codes Wq [E, rows, Kd * FMT / 8 bytes], scales
+// Ws [E, rows, Kd / 32].  Same tiles, tile order, k split over the waves (in
 // segments), double-buffered blocks and epilogue as skinny_tiles; a block is
-// US segments (2 KB of codes per wave for either RB).
-template <bool GATED, int RB>
+// US segments.
+template <int FMT, bool GATED, int RB>
 __device__ __forceinline__ void skinny_tiles_mx(const uint16_t* __restrict__ A, const int32_t* rows,
                                                 int topk, const int32_t* offsets,
                                                 const uint8_t* __restrict__ Wq,
@@ -547,8 +594,11 @@ __device__ __forceinline__ void skinny_tiles_mx(const uint16_t* __restrict__ A, 
                                                 uint16_t* __restrict__ C, int E, int Kd, int N,
                                                 int* s_start, int* s_wave, float* s_red) {
     static_assert(RB == 1 || RB == 2, "tile rows");
+    typedef MxFmt<FMT> F;
+    typedef typename F::scale_t scale_t;
     constexpr int BM = 16;
-    constexpr int US = kMxSegs / RB;               // 64-k segments per block
+    constexpr int US = mx_segs<FMT>() / RB;        // segments per block
+    constexpr int XS = F::G / 8;                   // 16-byte token pieces per lane and segment
     constexpr int COLS = GATED ? 8 * RB : 16 * RB;
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -557,10 +607,11 @@ __device__ __forceinline__ void skinny_tiles_mx(const uint16_t* __restrict__ A, 
     const int w_rows = GATED ? 2 * N : N;
     const int total = build_tile_table<BM>(offsets, E, n_tiles, s_start, s_wave);
 
-    const int nseg = Kd / 64;
+    const int nseg = Kd / F::SEG;
+    const size_t row_bytes = (size_t)Kd * FMT / 8;
     const int sg0 = (wave * nseg) / 4, sg1 = ((wave + 1) * nseg) / 4;
     const int nblk = (sg1 - sg0) / US;             // full blocks; the rest is a tail
-    const int sshift = 8 * (lg >> 1);              // this lane group's scale byte
+    const int sshift = F::scale_shift(lg);         // this lane group's scale byte
 
     for (int tile = blockIdx.x; tile < total; tile += gridDim.x) {
         const int e = find_expert(s_start, E, tile);
@@ -573,20 +624,20 @@ __device__ __forceinline__ void skinny_tiles_mx(const uint16_t* __restrict__ A, 
         const int mrows = (me - m_tile * BM) < BM ? (me - m_tile * BM) : BM;
 
         const moe_u32x4* wq[RB];
-        const uint16_t* wsc[RB];
+        const scale_t* wsc[RB];
 #pragma unroll
         for (int rb = 0; rb < RB; ++rb) {
             const int tr = rb * 16 + li;   // gated: rows [0, COLS) gate, then the matching up rows
             const int wrow = !GATED ? n_tile * COLS + tr
                            : tr < COLS ? n_tile * COLS + tr : N + n_tile * COLS + (tr - COLS);
             const size_t grow = (size_t)e * w_rows + wrow;
-            wq[rb] = reinterpret_cast<const moe_u32x4*>(Wq + grow * (size_t)Kd + (size_t)sg0 * 64 + lg * 16);
-            wsc[rb] = reinterpret_cast<const uint16_t*>(Ws + grow * (size_t)(Kd / 32)) + sg0;
+            wq[rb] = reinterpret_cast<const moe_u32x4*>(Wq + grow * row_bytes + (size_t)sg0 * 64 + lg * 16);
+            wsc[rb] = reinterpret_cast<const scale_t*>(Ws + grow * (size_t)(Kd / 32)) + sg0;
         }
 
         moe_u32x4 qa[RB][US], qb[RB][US];
         uint32_t sa[RB][US], sb[RB][US];
-        moe_bf16x8 xa[US][2], xb[US][2];
+        moe_bf16x8 xa[US][XS], xb[US][XS];
         auto load_w = [&](moe_u32x4 (*q)[US], uint32_t (*sc)[US], int b) {
 #pragma unroll
             for (int rb = 0; rb < RB; ++rb)
@@ -597,29 +648,26 @@ __device__ __forceinline__ void skinny_tiles_mx(const uint16_t* __restrict__ A, 
                 }
         };
         if (nblk > 0) load_w(qa, sa, 0);
-        const bool mvalid = li < mrows;
-        const int rr = r0 + (mvalid ? li : 0);
+        const int rr = r0 + (li < mrows ? li : 0);
         const long long arow = rows ? (long long)(rows[rr] / topk) : (long long)rr;
         const moe_bf16x8* ap = reinterpret_cast<const moe_bf16x8*>(
-            A + (size_t)arow * Kd + (size_t)sg0 * 64 + lg * 16);
-        auto load_x = [&](moe_bf16x8 (*xv)[2], int b) {
+            A + (size_t)arow * Kd + (size_t)sg0 * F::SEG + lg * F::G);
+        auto load_x = [&](moe_bf16x8 (*xv)[XS], int b) {
 #pragma unroll
             for (int u = 0; u < US; ++u)
 #pragma unroll
-                for (int h = 0; h < 2; ++h) {
-                    const moe_bf16x8 v = ap[(b * US + u) * 8 + h];
-                    xv[u][h] = v;
-                }
+                for (int h = 0; h < XS; ++h) xv[u][h] = ap[(b * US + u) * (F::SEG / 8) + h];
         };
         moe_f32x4 acc[RB];
 #pragma unroll
         for (int rb = 0; rb < RB; ++rb) acc[rb] = (moe_f32x4){0.f, 0.f, 0.f, 0.f};
-        auto seg_mma = [&](const moe_u32x4& q, uint32_t sc, const moe_bf16x8 (&xv)[2], moe_f32x4& a) {
+        auto seg_mma = [&](const moe_u32x4& q, uint32_t sc, const moe_bf16x8 (&xv)[XS], moe_f32x4& a) {
             const float scale = mx_scale_operand((sc >> sshift) & 0xffu);
-            a = __builtin_amdgcn_mfma_f32_16x16x32_bf16(mx_dequant8(q[0], q[1], scale), xv[0], a, 0, 0, 0);
-            a = __builtin_amdgcn_mfma_f32_16x16x32_bf16(mx_dequant8(q[2], q[3], scale), xv[1], a, 0, 0, 0);
+#pragma unroll
+            for (int st = 0; st < F::STEPS; ++st)
+                a = __builtin_amdgcn_mfma_f32_16x16x32_bf16(F::dequant(q, st, scale), xv[st], a, 0, 0, 0);
         };
-        auto mma = [&](moe_u32x4 (*q)[US], uint32_t (*sc)[US], moe_bf16x8 (*xv)[2]) {
+        auto mma = [&](moe_u32x4 (*q)[US], uint32_t (*sc)[US], moe_bf16x8 (*xv)[XS]) {
 #pragma unroll
             for (int u = 0; u < US; ++u)
 #pragma unroll
@@ -640,12 +688,9 @@ __device__ __forceinline__ void skinny_tiles_mx(const uint16_t* __restrict__ A, 
         if (b < nblk) mma(qa, sa, xa);
         for (int sg = sg0 + nblk * US; sg < sg1; ++sg) {   // tail segments
             const int o = sg - sg0;
-            moe_bf16x8 xv[2];
+            moe_bf16x8 xv[XS];
 #pragma unroll
-            for (int h = 0; h < 2; ++h) {
-                const moe_bf16x8 v = ap[o * 8 + h];
-                xv[h] = v;
-            }
+            for (int h = 0; h < XS; ++h) xv[h] = ap[o * (F::SEG / 8) + h];
 #pragma unroll
             for (int rb = 0; rb < RB; ++rb) seg_mma(wq[rb][o * 4], wsc[rb][o], xv, acc[rb]);
         }
@@ -653,7 +698,7 @@ __device__ __forceinline__ void skinny_tiles_mx(const uint16_t* __restrict__ A, 
     }
 }
 
-template <bool GATED, int RB>
+template <int FMT, bool GATED, int RB>
 __global__ __launch_bounds__(256) void gemm_skinny_mx_kernel(
     const uint16_t* __restrict__ A, const int32_t* __restrict__ row_src, int topk,
     const int32_t* __restrict__ offsets, const uint8_t* __restrict__ Wq,
@@ -661,10 +706,12 @@ __global__ __launch_bounds__(256) void gemm_skinny_mx_kernel(
     __shared__ int s_start[kMaxExperts + 1];
     __shared__ int s_wave[4];
     __shared__ float s_red[4 * 16 * RB * 17];
-    skinny_tiles_mx<GATED, RB>(A, row_src, topk, offsets, Wq, Ws, C, E, Kd, N, s_start, s_wave, s_red);
+    skinny_tiles_mx<FMT, GATED, RB>(A, row_src, topk, offsets, Wq, Ws, C, E, Kd, N, s_start,
+                                    s_wave, s_red);
 }
 
-// Gate-up on MXFP8 weights with the dispatch inside (T*K <= kFusedDispatchMax).
+// Gate-up on MX weights with the dispatch inside (T*K <= kFusedDispatchMax).
+template <int FMT>
 __global__ __launch_bounds__(256) void gemm_skinny_gateup_dispatch_mx_kernel(
     const uint16_t* __restrict__ x, const int32_t* __restrict__ ids,
     const int32_t* __restrict__ ntok, int T, int topk, int E, int32_t* __restrict__ offsets,
@@ -678,18 +725,23 @@ __global__ __launch_bounds__(256) void gemm_skinny_gateup_dispatch_mx_kernel(
     __shared__ int s_wave[4];
     __shared__ float s_red[4 * 16 * 17];
     fused_dispatch(ids, ntok, T, topk, E, offsets, row_src, token_row, s_off, s_wc, s_rows, s_wave);
-    skinny_tiles_mx<true, 1>(x, s_rows, topk, s_off, Wq, Ws, C, E, Kd, N, s_start, s_wave, s_red);
+    skinny_tiles_mx<FMT, true, 1>(x, s_rows, topk, s_off, Wq, Ws, C, E, Kd, N, s_start, s_wave,
+                                  s_red);
 }
 
-// Down GEMM + combine for tiny batches on MXFP8 weights: down_combine_tiny_kernel
-// with blocks of 4 segments (4 KB of codes per wave and buffer); needs whole
-// blocks per wave (I % 1024 == 0).
+// Down GEMM + combine for tiny batches on MX weights: down_combine_tiny_kernel
+// with blocks of 256 k-values per wave (4 MXFP8 segments, 4 KB of codes, or 2
+// MXFP4 segments, 2 KB); needs whole blocks per wave (I % 1024 == 0).
+template <int FMT>
 __global__ __launch_bounds__(256) void down_combine_tiny_mx_kernel(
     const uint16_t* __restrict__ A, const int32_t* __restrict__ offsets,
     const uint8_t* __restrict__ Wq, const uint8_t* __restrict__ Ws, int E, int Kd, int N,
     const int32_t* __restrict__ token_row, const float* __restrict__ wts,
     const int32_t* __restrict__ ntok, int T, int topk, uint16_t* __restrict__ out) {
-    constexpr int US = 4;
+    typedef MxFmt<FMT> F;
+    typedef typename F::scale_t scale_t;
+    constexpr int US = FMT == 8 ? 4 : 2;
+    constexpr int XS = F::G / 8;
     __shared__ int s_e[kTinyRows], s_r0[kTinyRows], s_m[kTinyRows];
     __shared__ int s_ne;
     __shared__ float s_part[kTinyRows][4][16][17];
@@ -701,23 +753,24 @@ __global__ __launch_bounds__(256) void down_combine_tiny_mx_kernel(
     tiny_expert_slots(offsets, E, s_e, s_r0, s_m, &s_ne);
     const int ne = s_ne;
 
-    const int nseg = Kd / 64;
+    const int nseg = Kd / F::SEG;
+    const size_t row_bytes = (size_t)Kd * FMT / 8;
     const int sg0 = (wave * nseg) / 4;
     const int nblk = (((wave + 1) * nseg) / 4 - sg0) / US;   // whole blocks (checked on the host)
     const int total = ne * nblk;
-    const int sshift = 8 * (lg >> 1);
+    const int sshift = F::scale_shift(lg);
 
     moe_u32x4 qa[US], qb[US];
     uint32_t sa[US], sb[US];
-    moe_bf16x8 xa[US][2], xb[US][2];
-    auto load = [&](moe_u32x4* q, uint32_t* sc, moe_bf16x8 (*xv)[2], int b) {
+    moe_bf16x8 xa[US][XS], xb[US][XS];
+    auto load = [&](moe_u32x4* q, uint32_t* sc, moe_bf16x8 (*xv)[XS], int b) {
         const int i = b / nblk, kb = b - i * nblk;
         const size_t grow = (size_t)s_e[i] * N + n0 + li;
-        const moe_u32x4* wp = reinterpret_cast<const moe_u32x4*>(Wq + grow * (size_t)Kd + (size_t)sg0 * 64 + lg * 16);
-        const uint16_t* sp = reinterpret_cast<const uint16_t*>(Ws + grow * (size_t)(Kd / 32)) + sg0;
-        const bool mvalid = li < s_m[i];
-        const int rr = s_r0[i] + (mvalid ? li : 0);
-        const moe_bf16x8* ap = reinterpret_cast<const moe_bf16x8*>(A + (size_t)rr * Kd + (size_t)sg0 * 64 + lg * 16);
+        const moe_u32x4* wp = reinterpret_cast<const moe_u32x4*>(Wq + grow * row_bytes + (size_t)sg0 * 64 + lg * 16);
+        const scale_t* sp = reinterpret_cast<const scale_t*>(Ws + grow * (size_t)(Kd / 32)) + sg0;
+        const int rr = s_r0[i] + (li < s_m[i] ? li : 0);
+        const moe_bf16x8* ap = reinterpret_cast<const moe_bf16x8*>(
+            A + (size_t)rr * Kd + (size_t)sg0 * F::SEG + lg * F::G);
 #pragma unroll
         for (int u = 0; u < US; ++u) {
             q[u] = wp[(kb * US + u) * 4];
@@ -726,18 +779,16 @@ __global__ __launch_bounds__(256) void down_combine_tiny_mx_kernel(
 #pragma unroll
         for (int u = 0; u < US; ++u)
 #pragma unroll
-            for (int h = 0; h < 2; ++h) {
-                const moe_bf16x8 v = ap[(kb * US + u) * 8 + h];
-                xv[u][h] = v;
-            }
+            for (int h = 0; h < XS; ++h) xv[u][h] = ap[(kb * US + u) * (F::SEG / 8) + h];
     };
     moe_f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-    auto step = [&](const moe_u32x4* q, const uint32_t* sc, moe_bf16x8 (*xv)[2], int b) {
+    auto step = [&](const moe_u32x4* q, const uint32_t* sc, moe_bf16x8 (*xv)[XS], int b) {
 #pragma unroll
         for (int u = 0; u < US; ++u) {
             const float scale = mx_scale_operand((sc[u] >> sshift) & 0xffu);
-            acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(mx_dequant8(q[u][0], q[u][1], scale), xv[u][0], acc, 0, 0, 0);
-            acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(mx_dequant8(q[u][2], q[u][3], scale), xv[u][1], acc, 0, 0, 0);
+#pragma unroll
+            for (int st = 0; st < F::STEPS; ++st)
+                acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(F::dequant(q[u], st, scale), xv[u][st], acc, 0, 0, 0);
         }
         if ((b + 1) % nblk == 0) {   // last block of expert slot b / nblk
             const int i = b / nblk;
@@ -760,18 +811,23 @@ __global__ __launch_bounds__(256) void down_combine_tiny_mx_kernel(
 }
 
 // ---------------------------------------------------------------------------
-// MXFP8 quantization and dequantization of weight rows (OCP MX recipe: the
-// block scale is 2^(floor(log2(amax)) - 8), 8 being the exponent of e4m3's
-// largest binade; codes are v / scale rounded to the nearest e4m3 value, ties
-// to even, saturated at 448; the code's sign bit is the input's).  Exact
-// integer arithmetic on the bf16 bit patterns; one thread per 32-value block.
+// MX quantization and dequantization of weight rows (OCP MX recipe: the block
+// scale is 2^(floor(log2(amax)) - emax), emax being the exponent of the code
+// format's largest binade, 8 for e4m3 and 2 for e2m1; codes are v / scale
+// rounded to the nearest code value, ties to even, saturated at the largest
+// value (448, 6); the code's sign bit is the input's).  Exact integer
+// arithmetic on the bf16 bit patterns; one thread per 32-value block.
 // ---------------------------------------------------------------------------
-// e4m3 code of sig * 2^t (sig >= 0 an integer below 2^8), sign in bit 7
-__device__ __forceinline__ uint32_t mx_e4m3_code(uint32_t sig, int t, uint32_t sign) {
-    if (sig == 0) return sign << 7;
+// Code of sig * 2^t (sig >= 0 an integer below 2^8) in a format with MB
+// mantissa bits, exponent bias BIAS (smallest normal binade 1 - BIAS) and
+// largest code MAXC; the sign goes to bit SB.
+template <int MB, int BIAS, uint32_t MAXC, int SB>
+__device__ __forceinline__ uint32_t mx_code(uint32_t sig, int t, uint32_t sign) {
+    if (sig == 0) return sign << SB;
     const int msb = 31 - __clz((int)sig);
     const int L = msb + t;                               // floor(log2(value))
-    const int qe = (L > -6 ? L : -6) - 3;                // exponent of the code spacing
+    const int Lmin = 1 - BIAS;                           // smallest normal binade
+    const int qe = (L > Lmin ? L : Lmin) - MB;           // exponent of the code spacing
     const int sh = qe - t;                               // value / 2^qe = sig * 2^-sh
     uint32_t n;
     if (sh <= 0) {
@@ -783,15 +839,20 @@ __device__ __forceinline__ uint32_t mx_e4m3_code(uint32_t sig, int t, uint32_t s
         const uint32_t rem = sig & ((1u << sh) - 1u), half = 1u << (sh - 1);
         if (rem > half || (rem == half && (n & 1u))) ++n;   // nearest, ties to even
     }
-    uint32_t code = L >= -6 ? (uint32_t)(((L + 7) << 3) + (int)n - 8) : n;
-    if (L >= -6 && code > 0x7Eu) code = 0x7Eu;           // saturate at 448
-    return code | (sign << 7);
+    // normal: n in [2^MB, 2^(MB+1)] -> exponent field L + BIAS, mantissa n - 2^MB
+    // (n = 2^(MB+1) carries into the next binade); subnormal: the code is n
+    uint32_t code = L >= Lmin ? (uint32_t)(((L + BIAS) << MB) + (int)n - (1 << MB)) : n;
+    if (L >= Lmin && code > MAXC) code = MAXC;           // saturate
+    return code | (sign << SB);
 }
 
-__global__ __launch_bounds__(256) void mxfp8_quantize_kernel(const uint16_t* __restrict__ w,
-                                                             long long nblocks,
-                                                             uint8_t* __restrict__ codes,
-                                                             uint8_t* __restrict__ scales) {
+// bf16 bits -> (significand, exponent) with |v| = sig * 2^(max(eb, 1) - 134)
+template <int FMT>
+__global__ __launch_bounds__(256) void mx_quantize_kernel(const uint16_t* __restrict__ w,
+                                                          long long nblocks,
+                                                          uint8_t* __restrict__ codes,
+                                                          uint8_t* __restrict__ scales) {
+    constexpr int EMAX = FMT == 8 ? 8 : 2;
     const long long blk = (long long)blockIdx.x * blockDim.x + threadIdx.x;
     if (blk >= nblocks) return;
     typedef uint16_t u16x8 __attribute__((ext_vector_type(8)));
@@ -810,37 +871,55 @@ __global__ __launch_bounds__(256) void mxfp8_quantize_kernel(const uint16_t* __r
     if (amax != 0) {
         const int eb = (int)(amax >> 7);
         const int lg2 = eb ? eb - 127 : (31 - __clz((int)amax)) - 133;   // floor(log2(amax))
-        sc = lg2 - 8 + 127;
+        sc = lg2 - EMAX + 127;
         sc = sc < 0 ? 0 : (sc > 254 ? 254 : sc);
     }
-    uint32_t out[8] = {};
+    uint32_t c[32];
 #pragma unroll
     for (int i = 0; i < 32; ++i) {
         const uint32_t m = v[i] & 0x7FFFu, eb = m >> 7, mb = m & 0x7Fu;
         const uint32_t sig = eb ? (128u + mb) : mb;
         const int t = (int)(eb ? eb : 1u) - sc - 7;      // |v| / 2^(sc - 127) = sig * 2^t
-        out[i >> 2] |= mx_e4m3_code(sig, t, v[i] >> 15) << (8 * (i & 3));
+        c[i] = FMT == 8 ? mx_code<3, 7, 0x7Eu, 7>(sig, t, v[i] >> 15)
+                        : mx_code<1, 1, 0x7u, 3>(sig, t, v[i] >> 15);
     }
-    moe_u32x4* dst = reinterpret_cast<moe_u32x4*>(codes + blk * 32);
-    dst[0] = (moe_u32x4){out[0], out[1], out[2], out[3]};
-    dst[1] = (moe_u32x4){out[4], out[5], out[6], out[7]};
+    if (FMT == 8) {
+        uint32_t out[8] = {};
+#pragma unroll
+        for (int i = 0; i < 32; ++i) out[i >> 2] |= c[i] << (8 * (i & 3));
+        moe_u32x4* dst = reinterpret_cast<moe_u32x4*>(codes + blk * 32);
+        dst[0] = (moe_u32x4){out[0], out[1], out[2], out[3]};
+        dst[1] = (moe_u32x4){out[4], out[5], out[6], out[7]};
+    } else {
+        uint32_t out[4] = {};   // value 2i in the low nibble of byte i
+#pragma unroll
+        for (int i = 0; i < 32; ++i) out[i >> 3] |= c[i] << (4 * (i & 7));
+        *reinterpret_cast<moe_u32x4*>(codes + blk * 16) = (moe_u32x4){out[0], out[1], out[2], out[3]};
+    }
     scales[blk] = (uint8_t)sc;
 }
 
-__global__ __launch_bounds__(256) void mxfp8_dequantize_kernel(const uint8_t* __restrict__ codes,
-                                                               const uint8_t* __restrict__ scales,
-                                                               long long nblocks,
-                                                               uint16_t* __restrict__ w) {
+template <int FMT>
+__global__ __launch_bounds__(256) void mx_dequantize_kernel(const uint8_t* __restrict__ codes,
+                                                            const uint8_t* __restrict__ scales,
+                                                            long long nblocks,
+                                                            uint16_t* __restrict__ w) {
     const long long blk = (long long)blockIdx.x * blockDim.x + threadIdx.x;
     if (blk >= nblocks) return;
-    const moe_u32x4* src = reinterpret_cast<const moe_u32x4*>(codes + blk * 32);
     const float scale = mx_scale_operand(scales[blk]);
     moe_bf16x8* dst = reinterpret_cast<moe_bf16x8*>(w + blk * 32);
+    if (FMT == 8) {
+        const moe_u32x4* src = reinterpret_cast<const moe_u32x4*>(codes + blk * 32);
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
-        const moe_u32x4 q = src[i];
-        dst[2 * i] = mx_dequant8(q[0], q[1], scale);
-        dst[2 * i + 1] = mx_dequant8(q[2], q[3], scale);
+        for (int i = 0; i < 2; ++i) {
+            const moe_u32x4 q = src[i];
+            dst[2 * i] = mx_dequant8(q[0], q[1], scale);
+            dst[2 * i + 1] = mx_dequant8(q[2], q[3], scale);
+        }
+    } else {
+        const moe_u32x4 q = *reinterpret_cast<const moe_u32x4*>(codes + blk * 16);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) dst[i] = mx_dequant8_fp4(q[i], scale);
     }
 }
 
@@ -1286,56 +1365,82 @@ hipError_t launch_down_combine_tiny(const Shape& s, const uint16_t* h, const int
     return hipGetLastError();
 }
 
-hipError_t launch_gateup_fused_dispatch_mx(const Shape& s, const uint16_t* x, const int32_t* ids,
-                                           const int32_t* ntok, int32_t* offsets,
-                                           int32_t* row_src, int32_t* token_row,
+hipError_t launch_gateup_fused_dispatch_mx(const Shape& s, int fmt, const uint16_t* x,
+                                           const int32_t* ids, const int32_t* ntok,
+                                           int32_t* offsets, int32_t* row_src, int32_t* token_row,
                                            const uint8_t* Wq, const uint8_t* Ws, uint16_t* h,
                                            hipStream_t st) {
-    hipLaunchKernelGGL(gemm_skinny_gateup_dispatch_mx_kernel, dim3(kMxGrid * kNumCUs), dim3(256), 0, st,
-                       x, ids, ntok, s.T, s.K, s.E, offsets, row_src, token_row, Wq, Ws, h, s.H,
-                       s.I);
+    const dim3 grid(kMxGrid * kNumCUs), block(256);
+    if (fmt == 8)
+        hipLaunchKernelGGL(gemm_skinny_gateup_dispatch_mx_kernel<8>, grid, block, 0, st, x, ids,
+                           ntok, s.T, s.K, s.E, offsets, row_src, token_row, Wq, Ws, h, s.H, s.I);
+    else
+        hipLaunchKernelGGL(gemm_skinny_gateup_dispatch_mx_kernel<4>, grid, block, 0, st, x, ids,
+                           ntok, s.T, s.K, s.E, offsets, row_src, token_row, Wq, Ws, h, s.H, s.I);
     return hipGetLastError();
 }
 
-hipError_t launch_down_combine_tiny_mx(const Shape& s, const uint16_t* h, const int32_t* offsets,
-                                       const uint8_t* Wq, const uint8_t* Ws,
-                                       const int32_t* token_row, const float* w,
+hipError_t launch_down_combine_tiny_mx(const Shape& s, int fmt, const uint16_t* h,
+                                       const int32_t* offsets, const uint8_t* Wq,
+                                       const uint8_t* Ws, const int32_t* token_row, const float* w,
                                        const int32_t* ntok, uint16_t* out, hipStream_t st) {
-    hipLaunchKernelGGL(down_combine_tiny_mx_kernel, dim3(s.H / 16), dim3(256), 0, st, h, offsets,
-                       Wq, Ws, s.E, s.I, s.H, token_row, w, ntok, s.T, s.K, out);
+    if (fmt == 8)
+        hipLaunchKernelGGL(down_combine_tiny_mx_kernel<8>, dim3(s.H / 16), dim3(256), 0, st, h,
+                           offsets, Wq, Ws, s.E, s.I, s.H, token_row, w, ntok, s.T, s.K, out);
+    else
+        hipLaunchKernelGGL(down_combine_tiny_mx_kernel<4>, dim3(s.H / 16), dim3(256), 0, st, h,
+                           offsets, Wq, Ws, s.E, s.I, s.H, token_row, w, ntok, s.T, s.K, out);
     return hipGetLastError();
 }
 
-hipError_t launch_grouped_gemm_mx(const Shape& s, bool gated, const uint16_t* A,
+template <int FMT>
+static void launch_skinny_mx(bool gated, int grid, const uint16_t* A, const int32_t* row_src,
+                             int topk, const int32_t* offsets, const uint8_t* Wq,
+                             const uint8_t* Ws, uint16_t* C, int E, int Kd, int N,
+                             hipStream_t st) {
+    if (gated)
+        hipLaunchKernelGGL((gemm_skinny_mx_kernel<FMT, true, 1>), dim3(grid), dim3(256), 0, st, A,
+                           row_src, topk, offsets, Wq, Ws, C, E, Kd, N);
+    else if (N % 32 == 0)
+        hipLaunchKernelGGL((gemm_skinny_mx_kernel<FMT, false, 2>), dim3(grid), dim3(256), 0, st, A,
+                           row_src, topk, offsets, Wq, Ws, C, E, Kd, N);
+    else
+        hipLaunchKernelGGL((gemm_skinny_mx_kernel<FMT, false, 1>), dim3(grid), dim3(256), 0, st, A,
+                           row_src, topk, offsets, Wq, Ws, C, E, Kd, N);
+}
+
+hipError_t launch_grouped_gemm_mx(const Shape& s, int fmt, bool gated, const uint16_t* A,
                                   const int32_t* row_src, int topk, const int32_t* offsets,
                                   const uint8_t* Wq, const uint8_t* Ws, uint16_t* C, int Kd, int N,
                                   hipStream_t st) {
-    const dim3 grid(kMxGrid * kNumCUs), block(256);
-    if (gated)
-        hipLaunchKernelGGL((gemm_skinny_mx_kernel<true, 1>), grid, block, 0, st, A, row_src, topk,
-                           offsets, Wq, Ws, C, s.E, Kd, N);
-    else if (N % 32 == 0)
-        hipLaunchKernelGGL((gemm_skinny_mx_kernel<false, 2>), grid, block, 0, st, A, row_src, topk,
-                           offsets, Wq, Ws, C, s.E, Kd, N);
+    if (fmt == 8)
+        launch_skinny_mx<8>(gated, kMxGrid * kNumCUs, A, row_src, topk, offsets, Wq, Ws, C, s.E,
+                            Kd, N, st);
     else
-        hipLaunchKernelGGL((gemm_skinny_mx_kernel<false, 1>), grid, block, 0, st, A, row_src, topk,
-                           offsets, Wq, Ws, C, s.E, Kd, N);
+        launch_skinny_mx<4>(gated, kMxGrid * kNumCUs, A, row_src, topk, offsets, Wq, Ws, C, s.E,
+                            Kd, N, st);
     return hipGetLastError();
 }
 
-hipError_t launch_mxfp8_quantize(const uint16_t* w, long long nblocks, uint8_t* codes,
-                                 uint8_t* scales, hipStream_t st) {
+hipError_t launch_mx_quantize(int fmt, const uint16_t* w, long long nblocks, uint8_t* codes,
+                              uint8_t* scales, hipStream_t st) {
     if (nblocks == 0) return hipSuccess;
-    hipLaunchKernelGGL(mxfp8_quantize_kernel, dim3((unsigned)((nblocks + 255) / 256)), dim3(256), 0,
-                       st, w, nblocks, codes, scales);
+    const dim3 grid((unsigned)((nblocks + 255) / 256)), block(256);
+    if (fmt == 8)
+        hipLaunchKernelGGL(mx_quantize_kernel<8>, grid, block, 0, st, w, nblocks, codes, scales);
+    else
+        hipLaunchKernelGGL(mx_quantize_kernel<4>, grid, block, 0, st, w, nblocks, codes, scales);
     return hipGetLastError();
 }
 
-hipError_t launch_mxfp8_dequantize(const uint8_t* codes, const uint8_t* scales, long long nblocks,
-                                   uint16_t* w, hipStream_t st) {
+hipError_t launch_mx_dequantize(int fmt, const uint8_t* codes, const uint8_t* scales,
+                                long long nblocks, uint16_t* w, hipStream_t st) {
     if (nblocks == 0) return hipSuccess;
-    hipLaunchKernelGGL(mxfp8_dequantize_kernel, dim3((unsigned)((nblocks + 255) / 256)), dim3(256),
-                       0, st, codes, scales, nblocks, w);
+    const dim3 grid((unsigned)((nblocks + 255) / 256)), block(256);
+    if (fmt == 8)
+        hipLaunchKernelGGL(mx_dequantize_kernel<8>, grid, block, 0, st, codes, scales, nblocks, w);
+    else
+        hipLaunchKernelGGL(mx_dequantize_kernel<4>, grid, block, 0, st, codes, scales, nblocks, w);
     return hipGetLastError();
 }
 

@@ -66,26 +66,29 @@ inline bool tiny_down_ok(const Shape& s) {
 hipError_t launch_down_combine_tiny(const Shape& s, const uint16_t* h, const int32_t* offsets,
                                     const uint16_t* W, const int32_t* token_row, const float* w,
                                     const int32_t* ntok, uint16_t* out, hipStream_t st);
-// ---- MXFP8 weights (codes uint8 [.., rows, Kd], scales uint8 [.., rows, Kd/32])
-// the skinny kernels on MXFP8 weights (grid 4 x CUs), same contracts as above
-hipError_t launch_gateup_fused_dispatch_mx(const Shape& s, const uint16_t* x, const int32_t* ids,
-                                           const int32_t* ntok, int32_t* offsets,
-                                           int32_t* row_src, int32_t* token_row,
+// ---- MX weights: fmt 8 = MXFP8 (e4m3 codes, one byte per value), fmt 4 =
+// MXFP4 (e2m1 codes, two per byte, low nibble first); codes uint8 [.., rows,
+// Kd * fmt / 8], scales uint8 [.., rows, Kd/32] (e8m0, one per 32 values).
+// The skinny kernels on MX weights (grid 3 x CUs), same contracts as above;
+// MXFP4 needs Kd % 128 == 0 (checked on the host).
+hipError_t launch_gateup_fused_dispatch_mx(const Shape& s, int fmt, const uint16_t* x,
+                                           const int32_t* ids, const int32_t* ntok,
+                                           int32_t* offsets, int32_t* row_src, int32_t* token_row,
                                            const uint8_t* Wq, const uint8_t* Ws, uint16_t* h,
                                            hipStream_t st);
-hipError_t launch_down_combine_tiny_mx(const Shape& s, const uint16_t* h, const int32_t* offsets,
-                                       const uint8_t* Wq, const uint8_t* Ws,
-                                       const int32_t* token_row, const float* w,
+hipError_t launch_down_combine_tiny_mx(const Shape& s, int fmt, const uint16_t* h,
+                                       const int32_t* offsets, const uint8_t* Wq,
+                                       const uint8_t* Ws, const int32_t* token_row, const float* w,
                                        const int32_t* ntok, uint16_t* out, hipStream_t st);
-hipError_t launch_grouped_gemm_mx(const Shape& s, bool gated, const uint16_t* A,
+hipError_t launch_grouped_gemm_mx(const Shape& s, int fmt, bool gated, const uint16_t* A,
                                   const int32_t* row_src, int topk, const int32_t* offsets,
                                   const uint8_t* Wq, const uint8_t* Ws, uint16_t* C, int Kd, int N,
                                   hipStream_t st);
 // nblocks blocks of 32 consecutive bf16 values <-> 32 codes + 1 scale each
-hipError_t launch_mxfp8_quantize(const uint16_t* w, long long nblocks, uint8_t* codes,
-                                 uint8_t* scales, hipStream_t st);
-hipError_t launch_mxfp8_dequantize(const uint8_t* codes, const uint8_t* scales, long long nblocks,
-                                   uint16_t* w, hipStream_t st);
+hipError_t launch_mx_quantize(int fmt, const uint16_t* w, long long nblocks, uint8_t* codes,
+                              uint8_t* scales, hipStream_t st);
+hipError_t launch_mx_dequantize(int fmt, const uint8_t* codes, const uint8_t* scales,
+                                long long nblocks, uint16_t* w, hipStream_t st);
 hipError_t launch_combine(const Shape& s, const uint16_t* y, const int32_t* token_row,
                           const float* w, const int32_t* ntok, uint16_t* out, hipStream_t st);
 // router top-k: ids [T,K], weights [T,K] from logits fp32 [T,E]

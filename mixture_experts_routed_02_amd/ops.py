@@ -18,8 +18,8 @@ from ._lib import MoeProblem, check, lib, problem, workspace_size
 __all__ = [
     "problem", "workspace_size", "make_workspace", "dispatch", "expert_compute", "gate_up",
     "down", "combine",
-    "forward", "MoEGraph", "MoeProblem", "mxfp8_quantize", "mxfp8_dequantize", "gate_up_mxfp8",
-    "forward_mxfp8",
+    "forward", "MoEGraph", "MoeProblem", "mx_quantize", "mx_dequantize", "gate_up_mx", "forward_mx",
+    "mxfp8_quantize", "mxfp8_dequantize", "gate_up_mxfp8", "forward_mxfp8",
 ]
 
 
@@ -210,11 +210,26 @@ def forward(p: MoeProblem, x, topk_ids, topk_weights, w_gateup, w_down, num_toke
 
 
 # ---------------------------------------------------------------------------
-# MXFP8 expert weights: codes uint8 [..., K] (OCP e4m3) + scales uint8
-# [..., K/32] (e8m0), as declared in include/moe_mi355x.h
+# MX expert weights (include/moe_mi355x.h): "mxfp8" = e4m3 codes uint8
+# [..., K], "mxfp4" = e2m1 codes two per byte uint8 [..., K/2]; both with e8m0
+# scales uint8 [..., K/32]
 # ---------------------------------------------------------------------------
-def mxfp8_quantize(w, codes=None, scales=None):
+_MX = {"mxfp8": (8, "mxfp8"), "mxfp4": (4, "mxfp4")}
+
+
+def _mx(fmt):
+    if fmt not in _MX:
+        raise ValueError(f"fmt must be one of {sorted(_MX)}")
+    return _MX[fmt]
+
+
+def _mx_code_cols(K, bits):
+    return K * bits // 8
+
+
+def mx_quantize(w, fmt="mxfp8", codes=None, scales=None):
     """Quantize bf16 weights [..., K] (K % 32 == 0) along K.  Returns (codes, scales)."""
+    bits_, name = _mx(fmt)
     if not isinstance(w, torch.Tensor) or w.dim() < 1:
         raise TypeError("w must be a torch.Tensor with at least one dimension")
     _need(w, "w", torch.bfloat16)
@@ -222,61 +237,82 @@ def mxfp8_quantize(w, codes=None, scales=None):
     if K % 32:
         raise ValueError("the last dimension must be a multiple of 32")
     rows = w.numel() // K if K else 0
+    cshape = tuple(w.shape[:-1]) + (_mx_code_cols(K, bits_),)
+    sshape = tuple(w.shape[:-1]) + (K // 32,)
     if codes is None:
-        codes = torch.empty(w.shape, dtype=torch.uint8, device=w.device)
+        codes = torch.empty(cshape, dtype=torch.uint8, device=w.device)
     if scales is None:
-        scales = torch.empty(tuple(w.shape[:-1]) + (K // 32,), dtype=torch.uint8, device=w.device)
-    _need(codes, "codes", torch.uint8, tuple(w.shape), w.device)
-    _need(scales, "scales", torch.uint8, tuple(w.shape[:-1]) + (K // 32,), w.device)
-    check("moe_mxfp8_quantize", lib().moe_mxfp8_quantize(
-        _ptr(w), rows, K, _ptr(codes), _ptr(scales), _stream_ptr(w.device)))
+        scales = torch.empty(sshape, dtype=torch.uint8, device=w.device)
+    _need(codes, "codes", torch.uint8, cshape, w.device)
+    _need(scales, "scales", torch.uint8, sshape, w.device)
+    fn = f"moe_{name}_quantize"
+    check(fn, getattr(lib(), fn)(_ptr(w), rows, K, _ptr(codes), _ptr(scales), _stream_ptr(w.device)))
     return codes, scales
 
 
-def mxfp8_dequantize(codes, scales, out=None):
-    """bf16 values of MXFP8 weights (the conversion the expert kernels use)."""
+def mx_dequantize(codes, scales, fmt="mxfp8", out=None):
+    """bf16 values of MX weights (the conversion the expert kernels use)."""
+    bits_, name = _mx(fmt)
     _need(codes, "codes", torch.uint8)
-    K = codes.shape[-1]
+    K = codes.shape[-1] * 8 // bits_
     _need(scales, "scales", torch.uint8, tuple(codes.shape[:-1]) + (K // 32,), codes.device)
+    oshape = tuple(codes.shape[:-1]) + (K,)
     if out is None:
-        out = torch.empty(codes.shape, dtype=torch.bfloat16, device=codes.device)
-    _need(out, "out", torch.bfloat16, tuple(codes.shape), codes.device)
-    rows = codes.numel() // K if K else 0
-    check("moe_mxfp8_dequantize", lib().moe_mxfp8_dequantize(
-        _ptr(codes), _ptr(scales), rows, K, _ptr(out), _stream_ptr(codes.device)))
+        out = torch.empty(oshape, dtype=torch.bfloat16, device=codes.device)
+    _need(out, "out", torch.bfloat16, oshape, codes.device)
+    rows = codes.numel() // codes.shape[-1] if codes.shape[-1] else 0
+    fn = f"moe_{name}_dequantize"
+    check(fn, getattr(lib(), fn)(_ptr(codes), _ptr(scales), rows, K, _ptr(out),
+                                 _stream_ptr(codes.device)))
     return out
 
 
-def gate_up_mxfp8(p: MoeProblem, x_disp, expert_offsets, w_gateup_codes, w_gateup_scales, h=None):
-    """Gate-up grouped GEMM on MXFP8 weights.  Returns h [cap, I]."""
+def mxfp8_quantize(w, codes=None, scales=None):
+    return mx_quantize(w, "mxfp8", codes, scales)
+
+
+def mxfp8_dequantize(codes, scales, out=None):
+    return mx_dequantize(codes, scales, "mxfp8", out)
+
+
+def gate_up_mx(p: MoeProblem, x_disp, expert_offsets, w_gateup_codes, w_gateup_scales,
+               fmt="mxfp8", h=None):
+    """Gate-up grouped GEMM on MX weights.  Returns h [cap, I]."""
+    bits_, name = _mx(fmt)
     E, H, I = p.num_experts, p.hidden, p.intermediate
     dev = x_disp.device
     cap = _cap(p)
     _need(x_disp, "x_disp", torch.bfloat16, (cap, H))
     _need(expert_offsets, "expert_offsets", torch.int32, (E + 1,), dev)
-    _need(w_gateup_codes, "w_gateup_codes", torch.uint8, (E, 2 * I, H), dev)
+    _need(w_gateup_codes, "w_gateup_codes", torch.uint8, (E, 2 * I, _mx_code_cols(H, bits_)), dev)
     _need(w_gateup_scales, "w_gateup_scales", torch.uint8, (E, 2 * I, H // 32), dev)
     if h is None:
         h = torch.empty((cap, I), dtype=torch.bfloat16, device=dev)
     _need(h, "h", torch.bfloat16, (cap, I), dev)
-    check("moe_gate_up_mxfp8", lib().moe_gate_up_mxfp8(
-        ctypes.byref(p), _ptr(x_disp), _ptr(expert_offsets), _ptr(w_gateup_codes),
-        _ptr(w_gateup_scales), _ptr(h), _stream_ptr(dev)))
+    fn = f"moe_gate_up_{name}"
+    check(fn, getattr(lib(), fn)(ctypes.byref(p), _ptr(x_disp), _ptr(expert_offsets),
+                                 _ptr(w_gateup_codes), _ptr(w_gateup_scales), _ptr(h),
+                                 _stream_ptr(dev)))
     return h
 
 
-def forward_mxfp8(p: MoeProblem, x, topk_ids, topk_weights, w_gateup_codes, w_gateup_scales,
-                  w_down_codes, w_down_scales, num_tokens_dev=None, expert_offsets=None, out=None,
-                  workspace=None):
-    """The routed-expert layer on MXFP8 expert weights.  Returns (out, expert_offsets)."""
+def gate_up_mxfp8(p: MoeProblem, x_disp, expert_offsets, w_gateup_codes, w_gateup_scales, h=None):
+    return gate_up_mx(p, x_disp, expert_offsets, w_gateup_codes, w_gateup_scales, "mxfp8", h)
+
+
+def forward_mx(p: MoeProblem, x, topk_ids, topk_weights, w_gateup_codes, w_gateup_scales,
+               w_down_codes, w_down_scales, fmt="mxfp8", num_tokens_dev=None,
+               expert_offsets=None, out=None, workspace=None):
+    """The routed-expert layer on MX expert weights.  Returns (out, expert_offsets)."""
+    bits_, name = _mx(fmt)
     T, K, E, H, I = p.num_tokens, p.top_k, p.num_experts, p.hidden, p.intermediate
     dev = x.device
     _need(x, "x", torch.bfloat16, (T, H))
     _need(topk_ids, "topk_ids", torch.int32, (T, K), dev)
     _need(topk_weights, "topk_weights", torch.float32, (T, K), dev)
-    _need(w_gateup_codes, "w_gateup_codes", torch.uint8, (E, 2 * I, H), dev)
+    _need(w_gateup_codes, "w_gateup_codes", torch.uint8, (E, 2 * I, _mx_code_cols(H, bits_)), dev)
     _need(w_gateup_scales, "w_gateup_scales", torch.uint8, (E, 2 * I, H // 32), dev)
-    _need(w_down_codes, "w_down_codes", torch.uint8, (E, H, I), dev)
+    _need(w_down_codes, "w_down_codes", torch.uint8, (E, H, _mx_code_cols(I, bits_)), dev)
     _need(w_down_scales, "w_down_scales", torch.uint8, (E, H, I // 32), dev)
     nt = _ntok(num_tokens_dev, dev)
     if expert_offsets is None:
@@ -286,11 +322,19 @@ def forward_mxfp8(p: MoeProblem, x, topk_ids, topk_weights, w_gateup_codes, w_ga
         out = torch.empty((T, H), dtype=torch.bfloat16, device=dev)
     _need(out, "out", torch.bfloat16, (T, H), dev)
     ws = make_workspace(p, dev) if workspace is None else workspace
-    check("moe_forward_mxfp8", lib().moe_forward_mxfp8(
+    fn = f"moe_forward_{name}"
+    check(fn, getattr(lib(), fn)(
         ctypes.byref(p), _ptr(x), _ptr(topk_ids), _ptr(topk_weights), _ptr(w_gateup_codes),
         _ptr(w_gateup_scales), _ptr(w_down_codes), _ptr(w_down_scales), _ptr(nt),
         _ptr(expert_offsets), _ptr(out), _ptr(ws), ws.numel(), _stream_ptr(dev)))
     return out, expert_offsets
+
+
+def forward_mxfp8(p: MoeProblem, x, topk_ids, topk_weights, w_gateup_codes, w_gateup_scales,
+                  w_down_codes, w_down_scales, num_tokens_dev=None, expert_offsets=None, out=None,
+                  workspace=None):
+    return forward_mx(p, x, topk_ids, topk_weights, w_gateup_codes, w_gateup_scales, w_down_codes,
+                      w_down_scales, "mxfp8", num_tokens_dev, expert_offsets, out, workspace)
 
 
 class MoEGraph:

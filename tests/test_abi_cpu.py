@@ -25,7 +25,7 @@ def declared_functions():
 
 def test_exports_every_declared_symbol():
     names = declared_functions()
-    assert len(names) == 16, names
+    assert len(names) == 20, names
     L = moe.lib()
     for n in names:
         assert hasattr(L, n), n
@@ -145,3 +145,20 @@ def test_mxfp8_entry_points_fail_closed():
     assert L.moe_mxfp8_dequantize(A16 + 1, A16, 4, 32, A16, None) == 1
     assert L.moe_mxfp8_dequantize(A16, A16, 4, 32, A16 + 2, None) == 1
     assert L.moe_mxfp8_dequantize(A16, A16, 4, 33, A16, None) == 1
+
+
+def test_mxfp4_entry_points_fail_closed():
+    L = moe.lib()
+    p = moe.problem(64, 2, 8, 256, 512)
+    ws = moe.workspace_size(p)
+    good = [A16, A4, A4, A16, A16 + 4, A16, A16 + 4, None, A4, A16, A16, ws, None]
+    assert L.moe_forward_mxfp4(ctypes.byref(moe.problem(64, 2, 8, 192, 512)), *good) == 2
+    assert L.moe_forward_mxfp4(ctypes.byref(moe.problem(64, 2, 8, 256, 320)), *good) == 2
+    for i, bad in ((4, A16 + 2), (6, A16 + 2), (3, A16 + 8)):   # scales 4-B, codes 16-B aligned
+        args = list(good)
+        args[i] = bad
+        assert L.moe_forward_mxfp4(ctypes.byref(p), *args) == _lib.MOE_ERROR_INVALID_VALUE, i
+    assert L.moe_gate_up_mxfp4(ctypes.byref(moe.problem(64, 2, 8, 256, 512, kernel_hint=4)),
+                               A16, A4, A16, A16, A16, None) == 2
+    assert L.moe_mxfp4_quantize(A16, 4, 48, A16, A16, None) == 1
+    assert L.moe_mxfp4_dequantize(A16, A16, 4, 32, A16 + 2, None) == 1

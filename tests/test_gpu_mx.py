@@ -1,14 +1,17 @@
-"""Parity of the MXFP8-weight path (through the C ABI) with the CPU oracle.
+"""Parity of the MX-weight paths (MXFP8 and MXFP4, through the C ABI) with the
+CPU oracle.
 
-* quantization: codes and scales bit for bit against oracle.mxfp8_quantize,
-  with planted rounding ties, saturating values, zeros, -0 and tiny blocks;
-* dequantization: every e4m3 code under a range of scales, bit for bit
+* quantization: codes and scales bit for bit against oracle.mxfp8_quantize /
+  oracle.mxfp4_quantize, with planted rounding ties, saturating values, zeros,
+  -0 and tiny blocks;
+* dequantization: every code byte under a range of scales, bit for bit
   against the oracle's decoding (the conversion the expert kernels use);
-* the layer: moe_forward_mxfp8 against oracle.forward_mxfp8 on the same codes
-  (to the floating-point bar of helpers.check_close), on small ragged shapes
-  through every path (fused dispatch + tiny down/combine, fused dispatch +
-  skinny down, multi-launch dispatch), the expert-parallel decode share at
-  full size (sampled tokens), a device token count and dropped ids.
+* the layer: moe_forward_mxfp8 / moe_forward_mxfp4 against the oracle's layer
+  on the same codes (to the floating-point bar of helpers.check_close), on
+  small ragged shapes through every path (fused dispatch + tiny down/combine,
+  fused dispatch + skinny down, multi-launch dispatch), the expert-parallel
+  decode share at full size (sampled tokens), a device token count and
+  dropped ids.
 """
 import numpy as np
 import pytest
@@ -25,6 +28,13 @@ if torch.cuda.is_available():
     from mixture_experts_routed_02_amd import ops
 
 DEV = "cuda:0"
+FMTS = ["mxfp8", "mxfp4"]
+ORACLE = {
+    "mxfp8": (oracle.mxfp8_quantize, oracle.mxfp8_to_f64, oracle.forward_mxfp8,
+              oracle.forward_tokens_mxfp8),
+    "mxfp4": (oracle.mxfp4_quantize, oracle.mxfp4_to_f64, oracle.forward_mxfp4,
+              oracle.forward_tokens_mxfp4),
+}
 
 
 @pytest.fixture(autouse=True)
@@ -46,29 +56,33 @@ def rand_bf16(shape, std, seed):
 # ---------------------------------------------------------------------------
 # quantize / dequantize
 # ---------------------------------------------------------------------------
+@pytest.mark.parametrize("fmt", FMTS)
 @pytest.mark.parametrize("shape,std,seed", [((64, 256), 1.0, 0), ((3, 5, 7168), 7168 ** -0.5, 1),
                                             ((128, 96), 300.0, 2), ((7, 32), 1e-38, 3)])
-def test_quantize_bitexact(shape, std, seed):
+def test_quantize_bitexact(fmt, shape, std, seed):
     w = rand_bf16(shape, std, seed).to(torch.float32)
     flat = w.view(-1)
     if flat.numel() >= 64:
         flat[:8] = torch.tensor([272.0, 464.0, 496.0, -480.0, 1.0, 1.0625, -0.0, 0.0])
+        flat[64:72] = torch.tensor([2.5, 5.0, 0.25, 1.25, 7.0, -6.5, -0.0, 3.5])
         flat[32:64] = 0.0                    # an all-zero block
         flat[40] = -0.0
     w = w.to(torch.bfloat16)
-    codes, scales = ops.mxfp8_quantize(w.to(DEV))
-    ref_c, ref_s = oracle.mxfp8_quantize(bits(w))
+    codes, scales = ops.mx_quantize(w.to(DEV), fmt)
+    ref_c, ref_s = ORACLE[fmt][0](bits(w))
     assert np.array_equal(u8(scales), ref_s)
     assert np.array_equal(u8(codes), ref_c)
 
 
+@pytest.mark.parametrize("fmt", FMTS)
 @pytest.mark.parametrize("scale", [10, 60, 100, 120, 127, 128, 200, 246])
-def test_dequantize_every_code(scale):
-    codes = np.tile(np.arange(256, dtype=np.uint8), 4).reshape(8, 128)   # 32 blocks
-    scales = np.full((8, 4), scale, dtype=np.uint8)
-    got = ops.mxfp8_dequantize(torch.from_numpy(codes).to(DEV), torch.from_numpy(scales).to(DEV))
+def test_dequantize_every_code(fmt, scale):
+    codes = np.tile(np.arange(256, dtype=np.uint8), 4).reshape(8, 128)   # every byte value
+    K = 128 if fmt == "mxfp8" else 256
+    scales = np.full((8, K // 32), scale, dtype=np.uint8)
+    got = ops.mx_dequantize(torch.from_numpy(codes).to(DEV), torch.from_numpy(scales).to(DEV), fmt)
     got = bits(got)
-    ref = oracle.mxfp8_to_f64(codes, scales)
+    ref = ORACLE[fmt][1](codes, scales)
     nan = np.isnan(ref)
     assert np.all(np.isnan(oracle.bf16_to_f64(got[nan])))
     assert np.array_equal(got[~nan], oracle.f64_to_bf16_bits(ref[~nan]))
@@ -77,22 +91,22 @@ def test_dequantize_every_code(scale):
 # ---------------------------------------------------------------------------
 # the layer
 # ---------------------------------------------------------------------------
-def quantized_case(T, K, E, H, I, seed, lo=0, hi=None):
+def quantized_case(fmt, T, K, E, H, I, seed, lo=0, hi=None):
     g = torch.Generator().manual_seed(seed)
     x = torch.randn((T, H), generator=g).to(torch.bfloat16)
     wgu = (torch.randn((E, 2 * I, H), generator=g) * H ** -0.5).to(torch.bfloat16)
     wd = (torch.randn((E, H, I), generator=g) * I ** -0.5).to(torch.bfloat16)
     ids = torch.randint(lo, E if hi is None else hi, (T, K), generator=g, dtype=torch.int32)
     w = torch.softmax(torch.randn((T, K), generator=g), dim=1)
-    qgu, sgu = oracle.mxfp8_quantize(bits(wgu))
-    qd, sd = oracle.mxfp8_quantize(bits(wd))
+    qgu, sgu = ORACLE[fmt][0](bits(wgu))
+    qd, sd = ORACLE[fmt][0](bits(wd))
     return x, ids, w, qgu, sgu, qd, sd
 
 
-def run_forward(p, x, ids, w, qgu, sgu, qd, sd, nt=None):
+def run_forward(fmt, p, x, ids, w, qgu, sgu, qd, sd, nt=None):
     t = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(DEV)
-    out, off = ops.forward_mxfp8(p, x.to(DEV), ids.to(DEV), w.to(DEV), t(qgu), t(sgu), t(qd), t(sd),
-                                 num_tokens_dev=nt)
+    out, off = ops.forward_mx(p, x.to(DEV), ids.to(DEV), w.to(DEV), t(qgu), t(sgu), t(qd), t(sd),
+                              fmt, num_tokens_dev=nt)
     return out, off
 
 
@@ -100,51 +114,56 @@ SMALL = {
     # name: (T, K, E, H, I, id_lo, id_hi) -- which launches the forward takes
     "fused_tiny_down": (1, 6, 12, 256, 1024, 0, 48),      # T*K <= 8, I % 1024 == 0
     "fused_skinny_down": (64, 2, 8, 256, 512, 0, 8),      # T*K <= 1024
-    "fused_ragged": (97, 3, 5, 192, 320, -1, 6),
+    "fused_ragged": (97, 3, 5, 384, 640, -1, 6),
     "multi_launch": (300, 4, 16, 512, 384, -1, 18),       # T*K > 1024
     "many_experts": (40, 2, 128, 256, 256, 0, 128),
 }
 
 
+@pytest.mark.parametrize("fmt", FMTS)
 @pytest.mark.parametrize("name", list(SMALL))
-def test_forward_mxfp8_small(name):
+def test_forward_mx_small(fmt, name):
     T, K, E, H, I, lo, hi = SMALL[name]
-    x, ids, w, qgu, sgu, qd, sd = quantized_case(T, K, E, H, I, 11, lo, hi)
+    x, ids, w, qgu, sgu, qd, sd = quantized_case(fmt, T, K, E, H, I, 11, lo, hi)
     p = moe.problem(T, K, E, H, I)
-    out, off = run_forward(p, x, ids, w, qgu, sgu, qd, sd)
+    out, off = run_forward(fmt, p, x, ids, w, qgu, sgu, qd, sd)
     _, ref_off, _, _ = oracle.dispatch(ids.numpy(), E)
     assert np.array_equal(off.cpu().numpy(), ref_off)
-    ref = oracle.forward_mxfp8(bits(x), ids.numpy(), w.numpy(), qgu, sgu, qd, sd)
+    ref = ORACLE[fmt][2](bits(x), ids.numpy(), w.numpy(), qgu, sgu, qd, sd)
     check_close(f64(out), ref, name)
     # the same call again gives the same bits (no state carried between calls)
-    out2, _ = run_forward(p, x, ids, w, qgu, sgu, qd, sd)
+    out2, _ = run_forward(fmt, p, x, ids, w, qgu, sgu, qd, sd)
     assert torch.equal(out.view(torch.int16), out2.view(torch.int16))
 
 
-def test_forward_mxfp8_device_token_count_and_dropped():
+@pytest.mark.parametrize("fmt", FMTS)
+def test_forward_mx_device_token_count_and_dropped(fmt):
     T, K, E, H, I = 200, 4, 16, 256, 256
-    x, ids, w, qgu, sgu, qd, sd = quantized_case(T, K, E, H, I, 12, -2, 20)
+    x, ids, w, qgu, sgu, qd, sd = quantized_case(fmt, T, K, E, H, I, 12, -2, 20)
     p = moe.problem(T, K, E, H, I)
     for tv in (0, 1, 77, 200):
         nt = torch.tensor([tv], dtype=torch.int32, device=DEV)
-        out, off = run_forward(p, x, ids, w, qgu, sgu, qd, sd, nt)
+        out, off = run_forward(fmt, p, x, ids, w, qgu, sgu, qd, sd, nt)
         _, ref_off, _, _ = oracle.dispatch(ids.numpy(), E, tv)
         assert np.array_equal(off.cpu().numpy(), ref_off)
-        ref = oracle.forward_mxfp8(bits(x), ids.numpy(), w.numpy(), qgu, sgu, qd, sd, tv)
-        check_close(f64(out)[:tv], ref[:tv], f"tv={tv}")
+        ref = ORACLE[fmt][2](bits(x), ids.numpy(), w.numpy(), qgu, sgu, qd, sd, tv)
+        check_close(f64(out[:tv]), ref[:tv], f"tv={tv}")
     # a token with no local expert gets an exact zero row
     ids0 = torch.full((1, 6), 40, dtype=torch.int32)
-    x1, _, w1, qgu1, sgu1, qd1, sd1 = quantized_case(1, 6, 12, 256, 1024, 13)
-    out, off = run_forward(moe.problem(1, 6, 12, 256, 1024), x1, ids0, w1, qgu1, sgu1, qd1, sd1)
+    x1, _, w1, qgu1, sgu1, qd1, sd1 = quantized_case(fmt, 1, 6, 12, 256, 1024, 13)
+    out, off = run_forward(fmt, moe.problem(1, 6, 12, 256, 1024), x1, ids0, w1, qgu1, sgu1, qd1,
+                           sd1)
     assert int(off[-1]) == 0 and bool((out == 0).all())
 
 
-def test_gate_up_mxfp8_staged():
-    T, K, E, H, I = 50, 2, 6, 256, 320
-    x, ids, w, qgu, sgu, qd, sd = quantized_case(T, K, E, H, I, 14)
+@pytest.mark.parametrize("fmt", FMTS)
+def test_gate_up_mx_staged(fmt):
+    T, K, E, H, I = 50, 2, 6, 256, 384
+    x, ids, w, qgu, sgu, qd, sd = quantized_case(fmt, T, K, E, H, I, 14)
     p = moe.problem(T, K, E, H, I)
     x_disp, off, rs, _ = ops.dispatch(p, x.to(DEV), ids.to(DEV))
-    h = ops.gate_up_mxfp8(p, x_disp, off, torch.from_numpy(qgu).to(DEV), torch.from_numpy(sgu).to(DEV))
+    h = ops.gate_up_mx(p, x_disp, off, torch.from_numpy(qgu).to(DEV), torch.from_numpy(sgu).to(DEV),
+                       fmt)
     o = off.cpu().numpy()
     R = int(o[-1])
     xr = oracle.bf16_to_f64(bits(x_disp)[:R])
@@ -153,14 +172,15 @@ def test_gate_up_mxfp8_staged():
         a, b = int(o[e]), int(o[e + 1])
         if a == b:
             continue
-        wgu = oracle.mxfp8_to_f64(qgu[e], sgu[e])
+        wgu = ORACLE[fmt][1](qgu[e], sgu[e])
         ref[a:b] = oracle.silu(xr[a:b] @ wgu[:I].T) * (xr[a:b] @ wgu[I:].T)
     check_close(f64(h)[:R], ref, "h")
 
 
+@pytest.mark.parametrize("fmt", FMTS)
 @pytest.mark.parametrize("name,seed", [("ep_decode_T1", 0), ("ep_decode_T8", 1),
                                        ("ep_decode_T32", 2), ("ep_decode_T128", 0)])
-def test_forward_mxfp8_ep_decode_full_size(name, seed):
+def test_forward_mx_ep_decode_full_size(fmt, name, seed):
     """The 96-of-384-expert share at full size: weights drawn and quantized on
     the device; the device quantization of one touched expert's down weights
     is checked bit for bit against the oracle, then the layer on sampled
@@ -170,11 +190,11 @@ def test_forward_mxfp8_ep_decode_full_size(name, seed):
     x = W.make_x(cfg, seed)
     ids, w = W.make_routing(cfg, seed)
     wgu, wd = W.make_weights(cfg, seed, DEV)
-    qgu, sgu = ops.mxfp8_quantize(wgu)
-    qd, sd = ops.mxfp8_quantize(wd)
+    qgu, sgu = ops.mx_quantize(wgu, fmt)
+    qd, sd = ops.mx_quantize(wd, fmt)
     del wgu, wd
     p = moe.problem(T, K, E, H, I)
-    out, off = ops.forward_mxfp8(p, x.to(DEV), ids.to(DEV), w.to(DEV), qgu, sgu, qd, sd)
+    out, off = ops.forward_mx(p, x.to(DEV), ids.to(DEV), w.to(DEV), qgu, sgu, qd, sd, fmt)
     _, ref_off, _, _ = oracle.dispatch(ids.numpy(), E)
     assert np.array_equal(off.cpu().numpy(), ref_off)
     toks = sample_tokens(T, 8 if T <= 8 else 4, seed)
@@ -197,8 +217,8 @@ def test_forward_mxfp8_ep_decode_full_size(name, seed):
     if touched:
         e = touched[0]
         wgu_e, wd_e = W.make_weights(cfg, seed, DEV)
-        c, s = oracle.mxfp8_quantize(bits(wd_e[e]))
+        c, s = ORACLE[fmt][0](bits(wd_e[e]))
         assert np.array_equal(Q[2][e], c) and np.array_equal(Q[3][e], s)
         del wgu_e, wd_e
-    ref = oracle.forward_tokens_mxfp8(bits(x), ids.numpy(), w.numpy(), *Q, toks)
+    ref = ORACLE[fmt][3](bits(x), ids.numpy(), w.numpy(), *Q, toks)
     check_close(f64(out)[toks], ref, name)
