@@ -187,6 +187,39 @@ MOE_API moe_status_t moe_graph_launch(void* graph, void* stream);
 MOE_API moe_status_t moe_graph_destroy(void* graph);
 
 /* ---------------------------------------------------------------------------
+ * Pre-packed bf16 expert weights for the weight-streaming (skinny) kernels
+ * (DeepGEMM PR #394, Summary and Motivation: expert weights laid out once, at
+ * load, in the order the kernel reads them, the row-major layout staying the
+ * reference; Correctness: the packed path checked bit for bit against it).
+ *
+ * moe_skinny_pack rewrites w [experts, rows, k] (bf16, row-major; k % 32 == 0,
+ * rows % 16 == 0) into packed [experts, rows, k] of the same size: 16-row
+ * groups, each stored as [k/32 steps][64 lanes][8 values], lane l holding row
+ * l%16 of the group and k-values 32s + 8(l/16) .. +7 of step s.  Plain
+ * (gated = 0, for W_down [E, H, I]): group g = rows 16g .. 16g+15.  Gated
+ * (gated = 1, for W_gateup [E, 2I, H]): group g = gate rows 8g .. 8g+7 and the
+ * matching up rows I+8g .. I+8g+7.  w and packed must not overlap; both
+ * 16-byte aligned.  experts * rows * k <= 2^40. */
+MOE_API moe_status_t moe_skinny_pack(const uint16_t* w, int32_t experts, int32_t rows, int32_t k,
+                                     int32_t gated, uint16_t* packed, void* stream);
+
+/* moe_gate_up / moe_forward on packed weights (W_gateup packed gated, W_down
+ * packed plain).  They run the skinny plan for every batch size (kernel_hint
+ * 0 or 1; MOE_ERROR_NOT_SUPPORTED otherwise) and are bit-identical to
+ * moe_gate_up / moe_forward with kernel_hint = 1 on the row-major weights. */
+MOE_API moe_status_t moe_gate_up_packed(const moe_problem_t* p, const uint16_t* x_disp,
+                                        const int32_t* expert_offsets,
+                                        const uint16_t* w_gateup_packed, uint16_t* h,
+                                        void* stream);
+MOE_API moe_status_t moe_forward_packed(const moe_problem_t* p, const uint16_t* x,
+                                        const int32_t* topk_ids, const float* topk_weights,
+                                        const uint16_t* w_gateup_packed,
+                                        const uint16_t* w_down_packed,
+                                        const int32_t* num_tokens_dev, int32_t* expert_offsets,
+                                        uint16_t* out, void* workspace, size_t ws_bytes,
+                                        void* stream);
+
+/* ---------------------------------------------------------------------------
  * MXFP8 expert weights (FlashInfer PR #3980: the MXFP8 MegaMoE backend; its
  * combine-wire notes name the format, 32 e4m3 values sharing one e8m0 scale).
  * TileOps PR #1738, Scope, leaves FP8 outside its BF16 path; this is the

@@ -142,6 +142,40 @@ moe_status_t forward_impl(const Shape& s, int hint, const uint16_t* x, const int
     return launched(moe::launch_combine(s, y, token_row, w, ntok, out, st));
 }
 
+// bf16 weights in the skinny pack layout: the skinny plan for every batch size.
+moe_status_t forward_packed_impl(const Shape& s, const uint16_t* x, const int32_t* ids,
+                                 const float* w, const uint16_t* wgu, const uint16_t* wd,
+                                 const int32_t* ntok, int32_t* offsets, uint16_t* out, void* ws,
+                                 hipStream_t st) {
+    const Layout L = layout(s);
+    int32_t* counts = at<int32_t>(ws, L.counts);
+    int32_t* row_src = at<int32_t>(ws, L.row_src);
+    int32_t* token_row = at<int32_t>(ws, L.token_row);
+    uint16_t* h = at<uint16_t>(ws, L.h);
+    uint16_t* y = at<uint16_t>(ws, L.y);
+    const GemmPlan plan = moe::choose_plan(s, moe::kSkinny);
+    if ((long long)s.T * s.K <= moe::kFusedDispatchMax) {
+        if (moe::launch_gateup_fused_dispatch(s, plan, x, ids, ntok, offsets, row_src, token_row,
+                                              wgu, h, st, true) != hipSuccess)
+            return MOE_ERROR_LAUNCH;
+        if (moe::tiny_down_ok(s))
+            return launched(moe::launch_down_combine_tiny(s, h, offsets, wd, token_row, w, ntok,
+                                                          out, st, true));
+    } else {
+        if (moe::launch_dispatch(s, ids, ntok, offsets, row_src, token_row, counts, st) !=
+            hipSuccess)
+            return MOE_ERROR_LAUNCH;
+        if (moe::launch_grouped_gemm_packed(s, true, x, row_src, s.K, offsets, wgu, h, s.H, s.I,
+                                            st) != hipSuccess)
+            return MOE_ERROR_LAUNCH;
+    }
+    if (moe::launch_grouped_gemm_packed(s, false, h, nullptr, 1, offsets, wd, y, s.I, s.H, st) !=
+        hipSuccess)
+        return MOE_ERROR_LAUNCH;
+    if (s.T == 0) return MOE_SUCCESS;
+    return launched(moe::launch_combine(s, y, token_row, w, ntok, out, st));
+}
+
 // MX expert weights (fmt 8 = MXFP8, 4 = MXFP4): the skinny kernels for every
 // batch size.
 bool bad_codes(const void* p) { return !p || !aligned(p, 16); }
@@ -386,6 +420,49 @@ moe_status_t moe_forward(const moe_problem_t* p, const uint16_t* x, const int32_
     return forward_impl(s, p->kernel_hint, x, topk_ids, topk_weights, w_gateup, w_down,
                         num_tokens_dev, expert_offsets, out, workspace,
                         static_cast<hipStream_t>(stream));
+}
+
+moe_status_t moe_skinny_pack(const uint16_t* w, int32_t experts, int32_t rows, int32_t k,
+                             int32_t gated, uint16_t* packed, void* stream) {
+    if (experts < 0 || rows <= 0 || k <= 0 || rows % 16 != 0 || k % 32 != 0 ||
+        (gated != 0 && gated != 1))
+        return MOE_ERROR_INVALID_VALUE;
+    if ((long long)experts * rows > (1ll << 40) / k) return MOE_ERROR_NOT_SUPPORTED;
+    if (experts == 0) return MOE_SUCCESS;
+    if (bad_bf16(w) || bad_bf16(packed) || w == packed) return MOE_ERROR_INVALID_VALUE;
+    return launched(moe::launch_skinny_pack(w, experts, rows, k, gated != 0, packed,
+                                            static_cast<hipStream_t>(stream)));
+}
+
+moe_status_t moe_gate_up_packed(const moe_problem_t* p, const uint16_t* x_disp,
+                                const int32_t* expert_offsets, const uint16_t* w_gateup_packed,
+                                uint16_t* h, void* stream) {
+    Shape s;
+    moe_status_t st = check_problem(p, &s);
+    if (st != MOE_SUCCESS) return st;
+    if (p->kernel_hint != 0 && p->kernel_hint != moe::kSkinny) return MOE_ERROR_NOT_SUPPORTED;
+    if (bad_bf16(x_disp, s.cap) || bad_i32(expert_offsets) || bad_bf16(w_gateup_packed) ||
+        bad_bf16(h, s.cap))
+        return MOE_ERROR_INVALID_VALUE;
+    return launched(moe::launch_grouped_gemm_packed(s, true, x_disp, nullptr, s.K, expert_offsets,
+                                                    w_gateup_packed, h, s.H, s.I,
+                                                    static_cast<hipStream_t>(stream)));
+}
+
+moe_status_t moe_forward_packed(const moe_problem_t* p, const uint16_t* x, const int32_t* topk_ids,
+                                const float* topk_weights, const uint16_t* w_gateup_packed,
+                                const uint16_t* w_down_packed, const int32_t* num_tokens_dev,
+                                int32_t* expert_offsets, uint16_t* out, void* workspace,
+                                size_t ws_bytes, void* stream) {
+    Shape s;
+    moe_status_t st = check_forward_args(p, &s, x, topk_ids, topk_weights, w_gateup_packed,
+                                         w_down_packed, num_tokens_dev, expert_offsets, out,
+                                         workspace, ws_bytes);
+    if (st != MOE_SUCCESS) return st;
+    if (p->kernel_hint != 0 && p->kernel_hint != moe::kSkinny) return MOE_ERROR_NOT_SUPPORTED;
+    return forward_packed_impl(s, x, topk_ids, topk_weights, w_gateup_packed, w_down_packed,
+                               num_tokens_dev, expert_offsets, out, workspace,
+                               static_cast<hipStream_t>(stream));
 }
 
 moe_status_t moe_mxfp8_quantize(const uint16_t* w, int64_t rows, int32_t k, uint8_t* codes,

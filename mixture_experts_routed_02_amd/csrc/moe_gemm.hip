@@ -127,8 +127,9 @@ __device__ __forceinline__ void skinny_epilogue(const moe_f32x4 (&acc)[RB], floa
 // RB = 16-row weight blocks per tile (1 or 2; gated tiles use 1).  Blocks of
 // U k-steps keep RB * U KB of weights in flight per wave and per buffer.
 // offsets and rows may point to global memory or LDS; s_red is
-// [4 waves][16*RB rows][17].
-template <bool GATED, int RB>
+// [4 waves][16*RB rows][17].  PACKED: W is in the skinny pack layout (see
+// skinny_pack_kernel), so a wave's load of one k-step is 1 KB contiguous.
+template <bool GATED, int RB, bool PACKED = false>
 __device__ __forceinline__ void skinny_tiles(const uint16_t* __restrict__ A, const int32_t* rows,
                                              int topk, const int32_t* offsets,
                                              const uint16_t* __restrict__ W,
@@ -148,6 +149,7 @@ __device__ __forceinline__ void skinny_tiles(const uint16_t* __restrict__ A, con
     const int ksteps = Kd / 32;
     const int ks0 = (wave * ksteps) / 4, ks1 = ((wave + 1) * ksteps) / 4;
     const int nblk = (ks1 - ks0) / U;              // full blocks; the rest is a tail
+    constexpr int WS = PACKED ? 64 : 4;            // 16-byte pieces between k-steps of a lane
 
     for (int tile = blockIdx.x; tile < total; tile += gridDim.x) {
         const int e = find_expert(s_start, E, tile);
@@ -162,11 +164,16 @@ __device__ __forceinline__ void skinny_tiles(const uint16_t* __restrict__ A, con
         const moe_bf16x8* wp[RB];
 #pragma unroll
         for (int rb = 0; rb < RB; ++rb) {
-            const int tr = rb * 16 + li;   // gated: rows [0, COLS) gate, then the matching up rows
-            const int wrow = !GATED ? n_tile * COLS + tr
-                           : tr < COLS ? n_tile * COLS + tr : N + n_tile * COLS + (tr - COLS);
-            wp[rb] = reinterpret_cast<const moe_bf16x8*>(
-                W + ((size_t)e * w_rows + wrow) * (size_t)Kd + (size_t)ks0 * 32 + lg * 8);
+            if (PACKED) {   // 16-row group n_tile (gated) or n_tile * RB + rb (plain)
+                const size_t grp = (size_t)e * (w_rows / 16) + (GATED ? n_tile : n_tile * RB + rb);
+                wp[rb] = reinterpret_cast<const moe_bf16x8*>(W) + (grp * ksteps + ks0) * 64 + lane;
+            } else {
+                const int tr = rb * 16 + li;   // gated: rows [0, COLS) gate, then the matching up rows
+                const int wrow = !GATED ? n_tile * COLS + tr
+                               : tr < COLS ? n_tile * COLS + tr : N + n_tile * COLS + (tr - COLS);
+                wp[rb] = reinterpret_cast<const moe_bf16x8*>(
+                    W + ((size_t)e * w_rows + wrow) * (size_t)Kd + (size_t)ks0 * 32 + lg * 8);
+            }
         }
 
         moe_bf16x8 wa[RB][U], wb[RB][U], xa[U], xb[U];
@@ -174,7 +181,7 @@ __device__ __forceinline__ void skinny_tiles(const uint16_t* __restrict__ A, con
 #pragma unroll
             for (int rb = 0; rb < RB; ++rb)
 #pragma unroll
-                for (int u = 0; u < U; ++u) wv[rb][u] = stream_load(wp[rb] + (b * U + u) * 4);
+                for (int u = 0; u < U; ++u) wv[rb][u] = stream_load(wp[rb] + (b * U + u) * WS);
         };
         // first weight block before the (dependent) row lookup
         if (nblk > 0) load_w(wa, 0);
@@ -215,14 +222,15 @@ __device__ __forceinline__ void skinny_tiles(const uint16_t* __restrict__ A, con
             const moe_bf16x8 xv = ap[o];
 #pragma unroll
             for (int rb = 0; rb < RB; ++rb)
-                acc[rb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(stream_load(wp[rb] + o), xv, acc[rb], 0, 0, 0);
+                acc[rb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(stream_load(wp[rb] + (ks - ks0) * WS), xv,
+                                                                  acc[rb], 0, 0, 0);
         }
 
         skinny_epilogue<GATED, RB>(acc, s_red, C, N, r0, mrows, n_tile);
     }
 }
 
-template <bool GATED, int RB>
+template <bool GATED, int RB, bool PACKED = false>
 __global__ __launch_bounds__(256) void gemm_skinny_kernel(
     const uint16_t* __restrict__ A, const int32_t* __restrict__ row_src, int topk,
     const int32_t* __restrict__ offsets, const uint16_t* __restrict__ W,
@@ -230,7 +238,8 @@ __global__ __launch_bounds__(256) void gemm_skinny_kernel(
     __shared__ int s_start[kMaxExperts + 1];
     __shared__ int s_wave[4];
     __shared__ float s_red[4 * 16 * RB * 17];
-    skinny_tiles<GATED, RB>(A, row_src, topk, offsets, W, C, E, Kd, N, s_start, s_wave, s_red);
+    skinny_tiles<GATED, RB, PACKED>(A, row_src, topk, offsets, W, C, E, Kd, N, s_start, s_wave,
+                                    s_red);
 }
 
 // Expert slots of the tiny down kernels: the experts that hold rows, in
@@ -306,6 +315,7 @@ __device__ __forceinline__ void tiny_combine(int ne, const int* s_r0, const floa
 // one launch fewer and no y rows through memory.  Needs the per-wave k range
 // to be whole blocks of 8 k-steps (I % 1024 == 0).
 // ---------------------------------------------------------------------------
+template <bool PACKED>
 __global__ __launch_bounds__(256) void down_combine_tiny_kernel(
     const uint16_t* __restrict__ A, const int32_t* __restrict__ offsets,
     const uint16_t* __restrict__ W, int E, int Kd, int N,
@@ -330,7 +340,11 @@ __global__ __launch_bounds__(256) void down_combine_tiny_kernel(
     const int nblk = nb / U;                       // whole blocks (checked on the host)
     const int total = ne * nblk;
 
+    constexpr int WS = PACKED ? 64 : 4;   // 16-byte pieces between k-steps of a lane
     auto wptr = [&](int i) {
+        if (PACKED)
+            return reinterpret_cast<const moe_bf16x8*>(W) +
+                   (((size_t)s_e[i] * (N / 16) + blockIdx.x) * ksteps + ks0) * 64 + lane;
         return reinterpret_cast<const moe_bf16x8*>(
             W + ((size_t)s_e[i] * N + n0 + li) * (size_t)Kd + (size_t)ks0 * 32 + lg * 8);
     };
@@ -344,7 +358,7 @@ __global__ __launch_bounds__(256) void down_combine_tiny_kernel(
         const moe_bf16x8* wp = wptr(i);
         const moe_bf16x8* ap = xptr(i);
 #pragma unroll
-        for (int u = 0; u < U; ++u) wv[u] = stream_load(wp + (kb * U + u) * 4);
+        for (int u = 0; u < U; ++u) wv[u] = stream_load(wp + (kb * U + u) * WS);
 #pragma unroll
         for (int u = 0; u < U; ++u) {
             const moe_bf16x8 v = ap[(kb * U + u) * 4];
@@ -467,6 +481,7 @@ __device__ __forceinline__ void fused_dispatch(const int32_t* __restrict__ ids,
 // T*K <= kFusedDispatchMax): every workgroup runs fused_dispatch, then its
 // gate-up tiles from that LDS copy.  This saves a launch in the
 // latency-bound small-batch regime.
+template <bool PACKED>
 __global__ __launch_bounds__(256) void gemm_skinny_gateup_dispatch_kernel(
     const uint16_t* __restrict__ x, const int32_t* __restrict__ ids,
     const int32_t* __restrict__ ntok, int T, int topk, int E, int32_t* __restrict__ offsets,
@@ -479,7 +494,7 @@ __global__ __launch_bounds__(256) void gemm_skinny_gateup_dispatch_kernel(
     __shared__ int s_wave[4];
     __shared__ float s_red[4 * 16 * 17];
     fused_dispatch(ids, ntok, T, topk, E, offsets, row_src, token_row, s_off, s_wc, s_rows, s_wave);
-    skinny_tiles<true, 1>(x, s_rows, topk, s_off, W, C, E, Kd, N, s_start, s_wave, s_red);
+    skinny_tiles<true, 1, PACKED>(x, s_rows, topk, s_off, W, C, E, Kd, N, s_start, s_wave, s_red);
 }
 
 // ---------------------------------------------------------------------------
@@ -924,6 +939,40 @@ __global__ __launch_bounds__(256) void mx_dequantize_kernel(const uint8_t* __res
 }
 
 // ---------------------------------------------------------------------------
+// Skinny pack layout of bf16 expert weights (DeepGEMM PR #394, Summary: expert
+// weights stored once in the order the kernel reads them; here the order of
+// the skinny kernels' MFMA operand loads).  A weight matrix [E, rows, K] is
+// cut into 16-row groups: plain matrices (W_down) take rows 16g .. 16g+15;
+// the gated W_gateup [E, 2N, K] takes gate rows 8g .. 8g+7 and the matching
+// up rows N+8g .. N+8g+7 (the rows of one gated skinny tile).  Group g of
+// expert e is stored as [K/32 k-steps][64 lanes][8 values]: lane l holds row
+// l%16 of the group and k-values 32s + 8(l/16) .. +7 of step s, exactly the
+// 16 bytes the lane loads for that MFMA step.  One wave load is then 1 KB
+// contiguous, and a wave's block of k-steps one contiguous run.  The products
+// are the same MFMAs on the same operands: the output is bit-identical.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void skinny_pack_kernel(const uint16_t* __restrict__ w,
+                                                          long long pieces, int rows, int Kd,
+                                                          int gated, uint16_t* __restrict__ out) {
+    const long long i = (long long)blockIdx.x * blockDim.x + threadIdx.x;   // output piece
+    if (i >= pieces) return;
+    const int ksteps = Kd / 32;
+    const int l = (int)(i & 63);
+    const long long t = i >> 6;
+    const int st = (int)(t % ksteps);
+    const long long eg = t / ksteps;                 // e * (rows / 16) + g
+    const int groups = rows / 16;
+    const long long e = eg / groups;
+    const int g = (int)(eg % groups);
+    const int li = l & 15, lg = l >> 4;
+    const int half = rows / 2;
+    const int r = !gated ? 16 * g + li : (li < 8 ? 8 * g + li : half + 8 * g + (li - 8));
+    const moe_bf16x8* src = reinterpret_cast<const moe_bf16x8*>(
+        w + ((size_t)e * rows + r) * (size_t)Kd + (size_t)st * 32 + lg * 8);
+    reinterpret_cast<moe_bf16x8*>(out)[i] = *src;
+}
+
+// ---------------------------------------------------------------------------
 // Tiled kernel: BM token rows x BN weight rows per tile.  Operands stream
 // through LDS rings, 64 k-values (128 bytes of every row) per stage, filled
 // by direct global->LDS loads (global_load_lds_dwordx4: no staging
@@ -1350,18 +1399,29 @@ hipError_t launch_tiled(int grid, const uint16_t* A, const int32_t* row_src, int
 hipError_t launch_gateup_fused_dispatch(const Shape& s, const GemmPlan& plan, const uint16_t* x,
                                         const int32_t* ids, const int32_t* ntok,
                                         int32_t* offsets, int32_t* row_src, int32_t* token_row,
-                                        const uint16_t* W, uint16_t* h, hipStream_t st) {
-    hipLaunchKernelGGL(gemm_skinny_gateup_dispatch_kernel, dim3(plan.grid_gateup), dim3(256), 0,
-                       st, x, ids, ntok, s.T, s.K, s.E, offsets, row_src, token_row, W, h, s.H,
-                       s.I);
+                                        const uint16_t* W, uint16_t* h, hipStream_t st,
+                                        bool packed) {
+    if (packed)
+        hipLaunchKernelGGL(gemm_skinny_gateup_dispatch_kernel<true>, dim3(plan.grid_gateup),
+                           dim3(256), 0, st, x, ids, ntok, s.T, s.K, s.E, offsets, row_src,
+                           token_row, W, h, s.H, s.I);
+    else
+        hipLaunchKernelGGL(gemm_skinny_gateup_dispatch_kernel<false>, dim3(plan.grid_gateup),
+                           dim3(256), 0, st, x, ids, ntok, s.T, s.K, s.E, offsets, row_src,
+                           token_row, W, h, s.H, s.I);
     return hipGetLastError();
 }
 
 hipError_t launch_down_combine_tiny(const Shape& s, const uint16_t* h, const int32_t* offsets,
                                     const uint16_t* W, const int32_t* token_row, const float* w,
-                                    const int32_t* ntok, uint16_t* out, hipStream_t st) {
-    hipLaunchKernelGGL(down_combine_tiny_kernel, dim3(s.H / 16), dim3(256), 0, st, h, offsets, W,
-                       s.E, s.I, s.H, token_row, w, ntok, s.T, s.K, out);
+                                    const int32_t* ntok, uint16_t* out, hipStream_t st,
+                                    bool packed) {
+    if (packed)
+        hipLaunchKernelGGL(down_combine_tiny_kernel<true>, dim3(s.H / 16), dim3(256), 0, st, h,
+                           offsets, W, s.E, s.I, s.H, token_row, w, ntok, s.T, s.K, out);
+    else
+        hipLaunchKernelGGL(down_combine_tiny_kernel<false>, dim3(s.H / 16), dim3(256), 0, st, h,
+                           offsets, W, s.E, s.I, s.H, token_row, w, ntok, s.T, s.K, out);
     return hipGetLastError();
 }
 
@@ -1441,6 +1501,32 @@ hipError_t launch_mx_dequantize(int fmt, const uint8_t* codes, const uint8_t* sc
         hipLaunchKernelGGL(mx_dequantize_kernel<8>, grid, block, 0, st, codes, scales, nblocks, w);
     else
         hipLaunchKernelGGL(mx_dequantize_kernel<4>, grid, block, 0, st, codes, scales, nblocks, w);
+    return hipGetLastError();
+}
+
+hipError_t launch_grouped_gemm_packed(const Shape& s, bool gated, const uint16_t* A,
+                                      const int32_t* row_src, int topk, const int32_t* offsets,
+                                      const uint16_t* W, uint16_t* C, int Kd, int N,
+                                      hipStream_t st) {
+    const dim3 grid(4 * kNumCUs), block(256);
+    if (gated)
+        hipLaunchKernelGGL((gemm_skinny_kernel<true, 1, true>), grid, block, 0, st, A, row_src,
+                           topk, offsets, W, C, s.E, Kd, N);
+    else if (N % 32 == 0)
+        hipLaunchKernelGGL((gemm_skinny_kernel<false, 2, true>), grid, block, 0, st, A, row_src,
+                           topk, offsets, W, C, s.E, Kd, N);
+    else
+        hipLaunchKernelGGL((gemm_skinny_kernel<false, 1, true>), grid, block, 0, st, A, row_src,
+                           topk, offsets, W, C, s.E, Kd, N);
+    return hipGetLastError();
+}
+
+hipError_t launch_skinny_pack(const uint16_t* w, int experts, int rows, int Kd, bool gated,
+                              uint16_t* out, hipStream_t st) {
+    const long long pieces = (long long)experts * rows * (Kd / 8);
+    if (pieces == 0) return hipSuccess;
+    hipLaunchKernelGGL(skinny_pack_kernel, dim3((unsigned)((pieces + 255) / 256)), dim3(256), 0,
+                       st, w, pieces, rows, Kd, gated ? 1 : 0, out);
     return hipGetLastError();
 }
 

@@ -55,7 +55,8 @@ hipError_t launch_grouped_gemm(const Shape& s, const GemmPlan& plan, bool gated,
 hipError_t launch_gateup_fused_dispatch(const Shape& s, const GemmPlan& plan, const uint16_t* x,
                                         const int32_t* ids, const int32_t* ntok,
                                         int32_t* offsets, int32_t* row_src, int32_t* token_row,
-                                        const uint16_t* W, uint16_t* h, hipStream_t st);
+                                        const uint16_t* W, uint16_t* h, hipStream_t st,
+                                        bool packed = false);
 // Down GEMM + weighted combine in one launch for tiny batches: usable when
 // T*K <= kTinyRows and I % 1024 == 0 (tiny_down_ok); needs the expert_offsets
 // and token_row of the fused gate-up kernel.
@@ -65,7 +66,17 @@ inline bool tiny_down_ok(const Shape& s) {
 }
 hipError_t launch_down_combine_tiny(const Shape& s, const uint16_t* h, const int32_t* offsets,
                                     const uint16_t* W, const int32_t* token_row, const float* w,
-                                    const int32_t* ntok, uint16_t* out, hipStream_t st);
+                                    const int32_t* ntok, uint16_t* out, hipStream_t st,
+                                    bool packed = false);
+// The skinny kernels on weights in the skinny pack layout (grid 4 x CUs).
+hipError_t launch_grouped_gemm_packed(const Shape& s, bool gated, const uint16_t* A,
+                                      const int32_t* row_src, int topk, const int32_t* offsets,
+                                      const uint16_t* W, uint16_t* C, int Kd, int N,
+                                      hipStream_t st);
+// bf16 weights [experts, rows, Kd] -> skinny pack layout (rows % 16 == 0; gated:
+// W_gateup with gate rows [0, rows/2) and up rows [rows/2, rows)).
+hipError_t launch_skinny_pack(const uint16_t* w, int experts, int rows, int Kd, bool gated,
+                              uint16_t* out, hipStream_t st);
 // ---- MX weights: fmt 8 = MXFP8 (e4m3 codes, one byte per value), fmt 4 =
 // MXFP4 (e2m1 codes, two per byte, low nibble first); codes uint8 [.., rows,
 // Kd * fmt / 8], scales uint8 [.., rows, Kd/32] (e8m0, one per 32 values).

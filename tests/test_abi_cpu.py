@@ -25,7 +25,7 @@ def declared_functions():
 
 def test_exports_every_declared_symbol():
     names = declared_functions()
-    assert len(names) == 20, names
+    assert len(names) == 23, names
     L = moe.lib()
     for n in names:
         assert hasattr(L, n), n
@@ -162,3 +162,18 @@ def test_mxfp4_entry_points_fail_closed():
                                A16, A4, A16, A16, A16, None) == 2
     assert L.moe_mxfp4_quantize(A16, 4, 48, A16, A16, None) == 1
     assert L.moe_mxfp4_dequantize(A16, A16, 4, 32, A16 + 2, None) == 1
+
+
+def test_skinny_pack_entry_points_fail_closed():
+    L = moe.lib()
+    assert L.moe_skinny_pack(A16, 2, 24, 64, 0, A16 * 2, None) == 1       # rows % 16
+    assert L.moe_skinny_pack(A16, 2, 32, 48, 0, A16 * 2, None) == 1       # k % 32
+    assert L.moe_skinny_pack(A16, 2, 32, 64, 2, A16 * 2, None) == 1       # gated is 0 or 1
+    assert L.moe_skinny_pack(A16, 2, 32, 64, 1, A16, None) == 1           # in place
+    assert L.moe_skinny_pack(A16 + 2, 2, 32, 64, 1, A16 * 2, None) == 1   # misaligned
+    assert L.moe_skinny_pack(None, 0, 32, 64, 1, None, None) == 0         # nothing to do
+    p = moe.problem(64, 2, 8, 256, 512, kernel_hint=2)
+    ws = moe.workspace_size(p)
+    assert L.moe_forward_packed(ctypes.byref(p), A16, A4, A4, A16, A16, None, A4, A16, A16, ws,
+                                None) == 2
+    assert L.moe_gate_up_packed(ctypes.byref(p), A16, A4, A16, A16, None) == 2

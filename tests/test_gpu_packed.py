@@ -1,0 +1,121 @@
+"""The skinny pack layout of bf16 expert weights (through the C ABI):
+
+* the layout itself, bit for bit, against a numpy re-layout written from its
+  definition (16-row groups, [k-steps][64 lanes][8 values], gate/up pairing
+  for W_gateup);
+* the bitwise A/B gate: moe_forward_packed and moe_gate_up_packed equal
+  moe_forward / moe_gate_up with the skinny plan on the row-major weights,
+  bit for bit, on every launch path (fused dispatch + tiny down/combine,
+  fused dispatch + skinny down, multi-launch dispatch), with a device token
+  count, and on the full-size expert-parallel decode share.  The row-major
+  path is the one checked against the oracle in test_gpu_parity.
+"""
+import numpy as np
+import pytest
+import torch
+
+import workloads as W
+from helpers import bits
+
+pytestmark = pytest.mark.gpu
+
+if torch.cuda.is_available():
+    import mixture_experts_routed_02_amd as moe
+    from mixture_experts_routed_02_amd import ops
+
+DEV = "cuda:0"
+
+
+@pytest.fixture(autouse=True)
+def _announce(request):
+    print(f"\n[case] {request.node.nodeid}", flush=True)
+    yield
+    torch.cuda.synchronize()
+
+
+def expected_pack(w_bits, gated):
+    E, rows, K = w_bits.shape
+    G, S = rows // 16, K // 32
+    l = np.arange(64)
+    li, lg = l % 16, l // 16
+    g = np.arange(G)[:, None]
+    if gated:
+        r = np.where(li[None, :] < 8, 8 * g + li[None, :], rows // 2 + 8 * g + li[None, :] - 8)
+    else:
+        r = 16 * g + li[None, :]                                   # [G, 64]
+    k0 = 32 * np.arange(S)[:, None] + 8 * lg[None, :]              # [S, 64]
+    kk = k0[:, :, None] + np.arange(8)                             # [S, 64, 8]
+    out = w_bits[:, r[:, None, :, None], kk[None, :, :, :]]        # [E, G, S, 64, 8]
+    return out.reshape(E, rows, K)
+
+
+@pytest.mark.parametrize("E,rows,K,gated", [(3, 64, 256, False), (2, 96, 192, True),
+                                            (5, 32, 512, True), (1, 2048, 64, False)])
+def test_pack_layout(E, rows, K, gated):
+    g = torch.Generator().manual_seed(E * rows + K)
+    w = torch.randn((E, rows, K), generator=g).to(torch.bfloat16)
+    got = ops.skinny_pack(w.to(DEV), gated)
+    assert np.array_equal(bits(got), expected_pack(bits(w), gated))
+
+
+def case(T, K, E, H, I, seed, lo=0, hi=None):
+    g = torch.Generator().manual_seed(seed)
+    x = torch.randn((T, H), generator=g).to(torch.bfloat16)
+    wgu = (torch.randn((E, 2 * I, H), generator=g) * H ** -0.5).to(torch.bfloat16)
+    wd = (torch.randn((E, H, I), generator=g) * I ** -0.5).to(torch.bfloat16)
+    ids = torch.randint(lo, E if hi is None else hi, (T, K), generator=g, dtype=torch.int32)
+    w = torch.softmax(torch.randn((T, K), generator=g), dim=1)
+    return [t.to(DEV) for t in (x, ids, w, wgu, wd)]
+
+
+SHAPES = {
+    "tiny_down": (1, 6, 12, 256, 1024, 0, 48),         # T*K <= 8, I % 1024 == 0
+    "fused_skinny_down": (64, 2, 8, 256, 512, 0, 8),
+    "fused_ragged": (97, 3, 5, 192, 320, -1, 6),
+    "multi_launch": (300, 4, 16, 512, 384, -1, 18),     # T*K > 1024
+    "small_hidden": (20, 2, 4, 320, 256, 0, 4),
+}
+
+
+@pytest.mark.parametrize("name", list(SHAPES))
+def test_forward_packed_bit_identical(name):
+    T, K, E, H, I, lo, hi = SHAPES[name]
+    x, ids, w, wgu, wd = case(T, K, E, H, I, 21, lo, hi)
+    p = moe.problem(T, K, E, H, I, 0, moe.HINT_SKINNY)
+    ref, ref_off = ops.forward(p, x, ids, w, wgu, wd)
+    pgu, pd = ops.skinny_pack(wgu, True), ops.skinny_pack(wd, False)
+    got, off = ops.forward_packed(p, x, ids, w, pgu, pd)
+    assert torch.equal(off, ref_off)
+    assert torch.equal(got.view(torch.int16), ref.view(torch.int16))
+    # gate-up alone
+    x_disp, o2, _, _ = ops.dispatch(p, x, ids)
+    h_ref = ops.gate_up(p, x_disp, o2, wgu)
+    h = ops.gate_up_packed(p, x_disp, o2, pgu)
+    R = int(o2[-1])
+    assert torch.equal(h[:R].view(torch.int16), h_ref[:R].view(torch.int16))
+
+
+def test_forward_packed_device_token_count():
+    T, K, E, H, I = 200, 4, 16, 256, 256
+    x, ids, w, wgu, wd = case(T, K, E, H, I, 22, -2, 20)
+    p = moe.problem(T, K, E, H, I, 0, moe.HINT_SKINNY)
+    pgu, pd = ops.skinny_pack(wgu, True), ops.skinny_pack(wd, False)
+    for tv in (0, 1, 77, 200):
+        nt = torch.tensor([tv], dtype=torch.int32, device=DEV)
+        ref, _ = ops.forward(p, x, ids, w, wgu, wd, num_tokens_dev=nt)
+        got, _ = ops.forward_packed(p, x, ids, w, pgu, pd, num_tokens_dev=nt)
+        assert torch.equal(got[:tv].view(torch.int16), ref[:tv].view(torch.int16)), tv
+
+
+@pytest.mark.parametrize("name", ["ep_decode_T1", "ep_decode_T32"])
+def test_forward_packed_ep_decode_full_size(name):
+    cfg = W.CONFIGS[name]
+    T, K, E, H, I = cfg.num_tokens, cfg.top_k, cfg.num_experts, cfg.hidden, cfg.intermediate
+    x = W.make_x(cfg, 0).to(DEV)
+    ids, w = (t.to(DEV) for t in W.make_routing(cfg, 0))
+    wgu, wd = W.make_weights(cfg, 0, DEV)
+    p = moe.problem(T, K, E, H, I)
+    ref, _ = ops.forward(p, x, ids, w, wgu, wd)
+    pgu, pd = ops.skinny_pack(wgu, True), ops.skinny_pack(wd, False)
+    got, _ = ops.forward_packed(p, x, ids, w, pgu, pd)
+    assert torch.equal(got.view(torch.int16), ref.view(torch.int16))
