@@ -164,11 +164,13 @@ def main():
                          "(default 50 for static_capacity, else 0)")
     ap.add_argument("--cpu-tokens", type=int, default=None,
                     help="tokens in the oracle's timed sample (default by workload)")
-    ap.add_argument("--weights", choices=("bf16", "bf16-packed", "mxfp8", "mxfp4"), default="bf16",
-                    help="expert weight format: bf16; bf16 in the skinny pack layout (packed on "
-                         "the device before timing, skinny plan for every batch size); MXFP8 "
-                         "(e4m3 codes + one e8m0 scale per 32 values) or MXFP4 (e2m1 codes, two "
-                         "per byte, same scales), quantized on the device before timing")
+    ap.add_argument("--weights", choices=("bf16", "mxfp8", "mxfp4"), default="bf16",
+                    help="expert weight format: bf16, MXFP8 (e4m3 codes + one e8m0 scale per 32 "
+                         "values) or MXFP4 (e2m1 codes, two per byte, same scales), quantized on "
+                         "the device before timing")
+    ap.add_argument("--packed", action="store_true",
+                    help="expert weights (bf16) or codes (MX) in the skinny pack layout, packed "
+                         "on the device before timing; the skinny plan serves every batch size")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     args = ap.parse_args()
 
@@ -196,9 +198,9 @@ def main():
     ids_h, w_h = W.make_routing(cfg, args.seed)
     wgu, wd = W.make_weights(cfg, args.seed, dev)
     x, ids, w = x_h.to(dev), ids_h.to(dev), w_h.to(dev)
-    packed = args.weights == "bf16-packed"
     mx = args.weights in ("mxfp8", "mxfp4")
-    if packed:
+    packed = args.packed
+    if packed and not mx:
         if args.graph or args.replays:
             raise SystemExit("--graph / --replays record the row-major layer; use --weights bf16")
         pgu, pd = ops.skinny_pack(wgu, True), ops.skinny_pack(wd, False)
@@ -208,10 +210,11 @@ def main():
             raise SystemExit("--graph / --replays record the bf16 layer; use --weights bf16")
         qgu, sgu = ops.mx_quantize(wgu, args.weights)
         qd, sd = ops.mx_quantize(wd, args.weights)
+        if packed:
+            qgu, qd = ops.mx_pack(qgu, True, args.weights), ops.mx_pack(qd, False, args.weights)
         torch.cuda.synchronize()
     # HBM bytes per weight value: bf16, or a code (1 or 1/2 byte) plus 1/32 of a scale byte
-    wbytes = {"bf16": 2.0, "bf16-packed": 2.0, "mxfp8": 1.0 + 1.0 / 32.0,
-              "mxfp4": 0.5 + 1.0 / 32.0}[args.weights]
+    wbytes = {"bf16": 2.0, "mxfp8": 1.0 + 1.0 / 32.0, "mxfp4": 0.5 + 1.0 / 32.0}[args.weights]
     draws = args.draws if args.draws is not None else (32 if cfg.name.startswith("ep_decode") else 1)
     if draws > 1:   # routing draws cycled one per step, same x and weights
         routes_h = [W.make_routing(cfg, 1000 + d) for d in range(draws)]
@@ -243,7 +246,7 @@ def main():
             ri, rw = routes[i % draws]
             if mx:
                 ops.forward_mx(p, x, ri, rw, qgu, sgu, qd, sd, args.weights, expert_offsets=off,
-                               out=out, workspace=ws)
+                               out=out, workspace=ws, packed=packed)
             elif packed:
                 ops.forward_packed(p, x, ri, rw, pgu, pd, expert_offsets=off, out=out,
                                    workspace=ws)
@@ -313,7 +316,8 @@ def main():
     x_disp, off2, _, _ = ops.dispatch(p, x, ids)
     hbuf = torch.empty((p.capacity or T * K, I), dtype=torch.bfloat16, device=dev)
     if mx:
-        gu_call = lambda: ops.gate_up_mx(p, x_disp, off2, qgu, sgu, args.weights, h=hbuf)
+        gu_call = lambda: ops.gate_up_mx(p, x_disp, off2, qgu, sgu, args.weights, h=hbuf,
+                                         packed=packed)
     elif packed:
         gu_call = lambda: ops.gate_up_packed(p, x_disp, off2, pgu, h=hbuf)
     else:
@@ -357,8 +361,8 @@ def main():
     kernel_name = "gemm_skinny_kernel" if kind == 1 else "gemm_tiled_kernel"
     if mx:
         kernel_name = f"gemm_skinny_mx_kernel<{8 if args.weights == 'mxfp8' else 4}>"
-    elif packed:
-        kernel_name = "gemm_skinny_kernel (packed weights)"
+    if packed:
+        kernel_name += " (packed weights)"
     traffic = pmc_traffic(f"{kernel_name}<gated>@{cfg.name}", kernel_src_hash(), 1)
     if mfma_bound:
         ach = F_gu / (k_ms / 1e3) / 1e12
@@ -439,8 +443,8 @@ def main():
                                                  else "back-to-back")
                    + (", HIP graph replay" if args.graph else ", eager launches"),
                    "kernel_hint": args.hint,
+                   "packed": packed,
                    "weights": {"bf16": "bf16",
-                               "bf16-packed": "bf16, skinny pack layout",
                                "mxfp8": "mxfp8: e4m3 codes + one e8m0 scale per 32 values along K",
                                "mxfp4": "mxfp4: e2m1 codes (two per byte) + one e8m0 scale per "
                                         "32 values along K"}[args.weights]},

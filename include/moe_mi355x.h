@@ -323,6 +323,39 @@ MOE_API moe_status_t moe_forward_mxfp4(const moe_problem_t* p, const uint16_t* x
                                        uint16_t* out, void* workspace, size_t ws_bytes,
                                        void* stream);
 
+/* ---------------------------------------------------------------------------
+ * MX codes in the skinny pack layout (the layout of moe_skinny_pack, on the
+ * code bytes): the MX decode kernels then read each wave's codes as one
+ * contiguous run.  Measured 7-17% faster than row-major codes on the decode
+ * workloads; the scales stay row-major.
+ * ------------------------------------------------------------------------- */
+
+/* Pack MX codes [experts, rows, k * bits / 8 bytes] (bits = 8: MXFP8, 4:
+ * MXFP4; k values per row) into the skinny pack layout: moe_skinny_pack on
+ * the codes viewed as 16-bit values with k' = k * bits / 16 per row (so k *
+ * bits must be a multiple of 512, rows a multiple of 16).  gated = 1 for the
+ * W_gateup codes, 0 for W_down.  Same size; no overlap; 16-byte aligned. */
+MOE_API moe_status_t moe_mx_pack(const uint8_t* codes, int32_t experts, int32_t rows, int32_t k,
+                                 int32_t bits, int32_t gated, uint8_t* packed, void* stream);
+
+/* moe_gate_up_mxfp8 / _mxfp4 and moe_forward_mxfp8 / _mxfp4 (bits = 8 / 4) on
+ * codes packed by moe_mx_pack, with the same row-major scales; bit-identical
+ * to the row-major entry points. */
+MOE_API moe_status_t moe_gate_up_mx_packed(const moe_problem_t* p, int32_t bits,
+                                           const uint16_t* x_disp, const int32_t* expert_offsets,
+                                           const uint8_t* w_gateup_codes_packed,
+                                           const uint8_t* w_gateup_scales, uint16_t* h,
+                                           void* stream);
+MOE_API moe_status_t moe_forward_mx_packed(const moe_problem_t* p, int32_t bits, const uint16_t* x,
+                                           const int32_t* topk_ids, const float* topk_weights,
+                                           const uint8_t* w_gateup_codes_packed,
+                                           const uint8_t* w_gateup_scales,
+                                           const uint8_t* w_down_codes_packed,
+                                           const uint8_t* w_down_scales,
+                                           const int32_t* num_tokens_dev, int32_t* expert_offsets,
+                                           uint16_t* out, void* workspace, size_t ws_bytes,
+                                           void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -25,7 +25,7 @@ EXPORTS = (
     "moe_graph_launch", "moe_graph_destroy", "moe_mxfp8_quantize", "moe_mxfp8_dequantize",
     "moe_gate_up_mxfp8", "moe_forward_mxfp8", "moe_mxfp4_quantize", "moe_mxfp4_dequantize",
     "moe_gate_up_mxfp4", "moe_forward_mxfp4", "moe_skinny_pack", "moe_gate_up_packed",
-    "moe_forward_packed",
+    "moe_forward_packed", "moe_mx_pack", "moe_gate_up_mx_packed", "moe_forward_mx_packed",
 )
 
 
@@ -72,6 +72,11 @@ _SIGS = {
     "moe_skinny_pack": (ctypes.c_int, [_P, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
                                        ctypes.c_int32, _P, _P]),
     "moe_gate_up_packed": (ctypes.c_int, [_PP, _P, _P, _P, _P, _P]),
+    "moe_mx_pack": (ctypes.c_int, [_P, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
+                                   ctypes.c_int32, ctypes.c_int32, _P, _P]),
+    "moe_gate_up_mx_packed": (ctypes.c_int, [_PP, ctypes.c_int32, _P, _P, _P, _P, _P, _P]),
+    "moe_forward_mx_packed": (ctypes.c_int, [_PP, ctypes.c_int32, _P, _P, _P, _P, _P, _P, _P, _P,
+                                             _P, _P, _P, _SZ, _P]),
     "moe_forward_packed": (ctypes.c_int, [_PP, _P, _P, _P, _P, _P, _P, _P, _P, _P, _SZ, _P]),
     "moe_mxfp4_dequantize": (ctypes.c_int, [_P, _P, ctypes.c_int64, ctypes.c_int32, _P, _P]),
     "moe_gate_up_mxfp4": (ctypes.c_int, [_PP, _P, _P, _P, _P, _P, _P]),

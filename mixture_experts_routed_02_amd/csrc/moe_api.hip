@@ -192,7 +192,8 @@ moe_status_t check_mx_problem(const moe_problem_t* p, int fmt, Shape* s) {
 moe_status_t forward_mx_impl(const Shape& s, int fmt, const uint16_t* x, const int32_t* ids,
                              const float* w, const uint8_t* qgu, const uint8_t* sgu,
                              const uint8_t* qd, const uint8_t* sd, const int32_t* ntok,
-                             int32_t* offsets, uint16_t* out, void* ws, hipStream_t st) {
+                             int32_t* offsets, uint16_t* out, void* ws, hipStream_t st,
+                             bool packed) {
     const Layout L = layout(s);
     int32_t* counts = at<int32_t>(ws, L.counts);
     int32_t* row_src = at<int32_t>(ws, L.row_src);
@@ -201,21 +202,21 @@ moe_status_t forward_mx_impl(const Shape& s, int fmt, const uint16_t* x, const i
     uint16_t* y = at<uint16_t>(ws, L.y);
     if ((long long)s.T * s.K <= moe::kFusedDispatchMax) {
         if (moe::launch_gateup_fused_dispatch_mx(s, fmt, x, ids, ntok, offsets, row_src, token_row,
-                                                 qgu, sgu, h, st) != hipSuccess)
+                                                 qgu, sgu, h, st, packed) != hipSuccess)
             return MOE_ERROR_LAUNCH;
         if (moe::tiny_down_ok(s))
             return launched(moe::launch_down_combine_tiny_mx(s, fmt, h, offsets, qd, sd, token_row,
-                                                             w, ntok, out, st));
+                                                             w, ntok, out, st, packed));
     } else {
         if (moe::launch_dispatch(s, ids, ntok, offsets, row_src, token_row, counts, st) !=
             hipSuccess)
             return MOE_ERROR_LAUNCH;
         if (moe::launch_grouped_gemm_mx(s, fmt, true, x, row_src, s.K, offsets, qgu, sgu, h, s.H,
-                                        s.I, st) != hipSuccess)
+                                        s.I, st, packed) != hipSuccess)
             return MOE_ERROR_LAUNCH;
     }
     if (moe::launch_grouped_gemm_mx(s, fmt, false, h, nullptr, 1, offsets, qd, sd, y, s.I, s.H,
-                                    st) != hipSuccess)
+                                    st, packed) != hipSuccess)
         return MOE_ERROR_LAUNCH;
     if (s.T == 0) return MOE_SUCCESS;
     return launched(moe::launch_combine(s, y, token_row, w, ntok, out, st));
@@ -251,7 +252,7 @@ moe_status_t mx_dequantize(int fmt, const uint8_t* codes, const uint8_t* scales,
 
 moe_status_t gate_up_mx(int fmt, const moe_problem_t* p, const uint16_t* x_disp,
                         const int32_t* expert_offsets, const uint8_t* codes, const uint8_t* scales,
-                        uint16_t* h, void* stream) {
+                        uint16_t* h, void* stream, bool packed = false) {
     Shape s;
     moe_status_t st = check_mx_problem(p, fmt, &s);
     if (st != MOE_SUCCESS) return st;
@@ -260,14 +261,14 @@ moe_status_t gate_up_mx(int fmt, const moe_problem_t* p, const uint16_t* x_disp,
         return MOE_ERROR_INVALID_VALUE;
     return launched(moe::launch_grouped_gemm_mx(s, fmt, true, x_disp, nullptr, s.K,
                                                 expert_offsets, codes, scales, h, s.H, s.I,
-                                                static_cast<hipStream_t>(stream)));
+                                                static_cast<hipStream_t>(stream), packed));
 }
 
 moe_status_t forward_mx(int fmt, const moe_problem_t* p, const uint16_t* x,
                         const int32_t* topk_ids, const float* topk_weights, const uint8_t* qgu,
                         const uint8_t* sgu, const uint8_t* qd, const uint8_t* sd,
                         const int32_t* num_tokens_dev, int32_t* expert_offsets, uint16_t* out,
-                        void* workspace, size_t ws_bytes, void* stream) {
+                        void* workspace, size_t ws_bytes, void* stream, bool packed = false) {
     Shape s;
     moe_status_t st = check_mx_problem(p, fmt, &s);
     if (st != MOE_SUCCESS) return st;
@@ -279,7 +280,8 @@ moe_status_t forward_mx(int fmt, const moe_problem_t* p, const uint16_t* x,
     if (num_tokens_dev && !aligned(num_tokens_dev, 4)) return MOE_ERROR_INVALID_VALUE;
     if ((st = check_ws(s, workspace, ws_bytes)) != MOE_SUCCESS) return st;
     return forward_mx_impl(s, fmt, x, topk_ids, topk_weights, qgu, sgu, qd, sd, num_tokens_dev,
-                           expert_offsets, out, workspace, static_cast<hipStream_t>(stream));
+                           expert_offsets, out, workspace, static_cast<hipStream_t>(stream),
+                           packed);
 }
 
 struct GraphHandle {
@@ -517,6 +519,39 @@ moe_status_t moe_forward_mxfp4(const moe_problem_t* p, const uint16_t* x, const 
     return forward_mx(4, p, x, topk_ids, topk_weights, w_gateup_codes, w_gateup_scales,
                       w_down_codes, w_down_scales, num_tokens_dev, expert_offsets, out, workspace,
                       ws_bytes, stream);
+}
+
+moe_status_t moe_mx_pack(const uint8_t* codes, int32_t experts, int32_t rows, int32_t k,
+                         int32_t bits, int32_t gated, uint8_t* packed, void* stream) {
+    if (bits != 8 && bits != 4) return MOE_ERROR_INVALID_VALUE;
+    if (k <= 0 || (long long)k * bits % 512 != 0) return MOE_ERROR_INVALID_VALUE;
+    // the byte layout of the bf16 pack, on the codes viewed as 16-bit values
+    return moe_skinny_pack(reinterpret_cast<const uint16_t*>(codes), experts, rows,
+                           (int32_t)((long long)k * bits / 16), gated,
+                           reinterpret_cast<uint16_t*>(packed), stream);
+}
+
+moe_status_t moe_gate_up_mx_packed(const moe_problem_t* p, int32_t bits, const uint16_t* x_disp,
+                                   const int32_t* expert_offsets,
+                                   const uint8_t* w_gateup_codes_packed,
+                                   const uint8_t* w_gateup_scales, uint16_t* h, void* stream) {
+    if (bits != 8 && bits != 4) return MOE_ERROR_INVALID_VALUE;
+    return gate_up_mx(bits, p, x_disp, expert_offsets, w_gateup_codes_packed, w_gateup_scales, h,
+                      stream, true);
+}
+
+moe_status_t moe_forward_mx_packed(const moe_problem_t* p, int32_t bits, const uint16_t* x,
+                                   const int32_t* topk_ids, const float* topk_weights,
+                                   const uint8_t* w_gateup_codes_packed,
+                                   const uint8_t* w_gateup_scales,
+                                   const uint8_t* w_down_codes_packed,
+                                   const uint8_t* w_down_scales, const int32_t* num_tokens_dev,
+                                   int32_t* expert_offsets, uint16_t* out, void* workspace,
+                                   size_t ws_bytes, void* stream) {
+    if (bits != 8 && bits != 4) return MOE_ERROR_INVALID_VALUE;
+    return forward_mx(bits, p, x, topk_ids, topk_weights, w_gateup_codes_packed, w_gateup_scales,
+                      w_down_codes_packed, w_down_scales, num_tokens_dev, expert_offsets, out,
+                      workspace, ws_bytes, stream, true);
 }
 
 moe_status_t moe_graph_create(const moe_problem_t* p, const uint16_t* x, const int32_t* topk_ids,

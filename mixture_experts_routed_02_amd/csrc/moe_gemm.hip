@@ -601,7 +601,7 @@ constexpr int kMxGrid = 3;
 // Ws [E, rows, Kd / 32].  Same tiles, tile order, k split over the waves (in
 // segments), double-buffered blocks and epilogue as skinny_tiles; a block is
 // US segments.
-template <int FMT, bool GATED, int RB>
+template <int FMT, bool GATED, int RB, bool PACKED = false>
 __device__ __forceinline__ void skinny_tiles_mx(const uint16_t* __restrict__ A, const int32_t* rows,
                                                 int topk, const int32_t* offsets,
                                                 const uint8_t* __restrict__ Wq,
@@ -627,6 +627,7 @@ __device__ __forceinline__ void skinny_tiles_mx(const uint16_t* __restrict__ A, 
     const int sg0 = (wave * nseg) / 4, sg1 = ((wave + 1) * nseg) / 4;
     const int nblk = (sg1 - sg0) / US;             // full blocks; the rest is a tail
     const int sshift = F::scale_shift(lg);         // this lane group's scale byte
+    constexpr int QS = PACKED ? 64 : 4;            // 16-byte pieces between segments of a lane
 
     for (int tile = blockIdx.x; tile < total; tile += gridDim.x) {
         const int e = find_expert(s_start, E, tile);
@@ -646,7 +647,12 @@ __device__ __forceinline__ void skinny_tiles_mx(const uint16_t* __restrict__ A, 
             const int wrow = !GATED ? n_tile * COLS + tr
                            : tr < COLS ? n_tile * COLS + tr : N + n_tile * COLS + (tr - COLS);
             const size_t grow = (size_t)e * w_rows + wrow;
-            wq[rb] = reinterpret_cast<const moe_u32x4*>(Wq + grow * row_bytes + (size_t)sg0 * 64 + lg * 16);
+            if (PACKED) {
+                const size_t grp = (size_t)e * (w_rows / 16) + (GATED ? n_tile : n_tile * RB + rb);
+                wq[rb] = reinterpret_cast<const moe_u32x4*>(Wq) + (grp * nseg + sg0) * 64 + lane;
+            } else {
+                wq[rb] = reinterpret_cast<const moe_u32x4*>(Wq + grow * row_bytes + (size_t)sg0 * 64 + lg * 16);
+            }
             wsc[rb] = reinterpret_cast<const scale_t*>(Ws + grow * (size_t)(Kd / 32)) + sg0;
         }
 
@@ -658,7 +664,7 @@ __device__ __forceinline__ void skinny_tiles_mx(const uint16_t* __restrict__ A, 
             for (int rb = 0; rb < RB; ++rb)
 #pragma unroll
                 for (int u = 0; u < US; ++u) {
-                    q[rb][u] = wq[rb][(b * US + u) * 4];
+                    q[rb][u] = wq[rb][(b * US + u) * QS];
                     sc[rb][u] = wsc[rb][b * US + u];
                 }
         };
@@ -707,13 +713,13 @@ __device__ __forceinline__ void skinny_tiles_mx(const uint16_t* __restrict__ A, 
 #pragma unroll
             for (int h = 0; h < XS; ++h) xv[h] = ap[o * (F::SEG / 8) + h];
 #pragma unroll
-            for (int rb = 0; rb < RB; ++rb) seg_mma(wq[rb][o * 4], wsc[rb][o], xv, acc[rb]);
+            for (int rb = 0; rb < RB; ++rb) seg_mma(wq[rb][o * QS], wsc[rb][o], xv, acc[rb]);
         }
         skinny_epilogue<GATED, RB>(acc, s_red, C, N, r0, mrows, n_tile);
     }
 }
 
-template <int FMT, bool GATED, int RB>
+template <int FMT, bool GATED, int RB, bool PACKED = false>
 __global__ __launch_bounds__(256) void gemm_skinny_mx_kernel(
     const uint16_t* __restrict__ A, const int32_t* __restrict__ row_src, int topk,
     const int32_t* __restrict__ offsets, const uint8_t* __restrict__ Wq,
@@ -721,12 +727,12 @@ __global__ __launch_bounds__(256) void gemm_skinny_mx_kernel(
     __shared__ int s_start[kMaxExperts + 1];
     __shared__ int s_wave[4];
     __shared__ float s_red[4 * 16 * RB * 17];
-    skinny_tiles_mx<FMT, GATED, RB>(A, row_src, topk, offsets, Wq, Ws, C, E, Kd, N, s_start,
-                                    s_wave, s_red);
+    skinny_tiles_mx<FMT, GATED, RB, PACKED>(A, row_src, topk, offsets, Wq, Ws, C, E, Kd, N,
+                                            s_start, s_wave, s_red);
 }
 
 // Gate-up on MX weights with the dispatch inside (T*K <= kFusedDispatchMax).
-template <int FMT>
+template <int FMT, bool PACKED = false>
 __global__ __launch_bounds__(256) void gemm_skinny_gateup_dispatch_mx_kernel(
     const uint16_t* __restrict__ x, const int32_t* __restrict__ ids,
     const int32_t* __restrict__ ntok, int T, int topk, int E, int32_t* __restrict__ offsets,
@@ -740,14 +746,14 @@ __global__ __launch_bounds__(256) void gemm_skinny_gateup_dispatch_mx_kernel(
     __shared__ int s_wave[4];
     __shared__ float s_red[4 * 16 * 17];
     fused_dispatch(ids, ntok, T, topk, E, offsets, row_src, token_row, s_off, s_wc, s_rows, s_wave);
-    skinny_tiles_mx<FMT, true, 1>(x, s_rows, topk, s_off, Wq, Ws, C, E, Kd, N, s_start, s_wave,
-                                  s_red);
+    skinny_tiles_mx<FMT, true, 1, PACKED>(x, s_rows, topk, s_off, Wq, Ws, C, E, Kd, N, s_start,
+                                          s_wave, s_red);
 }
 
 // Down GEMM + combine for tiny batches on MX weights: down_combine_tiny_kernel
 // with blocks of 256 k-values per wave (4 MXFP8 segments, 4 KB of codes, or 2
 // MXFP4 segments, 2 KB); needs whole blocks per wave (I % 1024 == 0).
-template <int FMT>
+template <int FMT, bool PACKED = false>
 __global__ __launch_bounds__(256) void down_combine_tiny_mx_kernel(
     const uint16_t* __restrict__ A, const int32_t* __restrict__ offsets,
     const uint8_t* __restrict__ Wq, const uint8_t* __restrict__ Ws, int E, int Kd, int N,
@@ -781,14 +787,17 @@ __global__ __launch_bounds__(256) void down_combine_tiny_mx_kernel(
     auto load = [&](moe_u32x4* q, uint32_t* sc, moe_bf16x8 (*xv)[XS], int b) {
         const int i = b / nblk, kb = b - i * nblk;
         const size_t grow = (size_t)s_e[i] * N + n0 + li;
-        const moe_u32x4* wp = reinterpret_cast<const moe_u32x4*>(Wq + grow * row_bytes + (size_t)sg0 * 64 + lg * 16);
+        const moe_u32x4* wp =
+            PACKED ? reinterpret_cast<const moe_u32x4*>(Wq) +
+                         (((size_t)s_e[i] * (N / 16) + blockIdx.x) * nseg + sg0) * 64 + lane
+                   : reinterpret_cast<const moe_u32x4*>(Wq + grow * row_bytes + (size_t)sg0 * 64 + lg * 16);
         const scale_t* sp = reinterpret_cast<const scale_t*>(Ws + grow * (size_t)(Kd / 32)) + sg0;
         const int rr = s_r0[i] + (li < s_m[i] ? li : 0);
         const moe_bf16x8* ap = reinterpret_cast<const moe_bf16x8*>(
             A + (size_t)rr * Kd + (size_t)sg0 * F::SEG + lg * F::G);
 #pragma unroll
         for (int u = 0; u < US; ++u) {
-            q[u] = wp[(kb * US + u) * 4];
+            q[u] = wp[(kb * US + u) * (PACKED ? 64 : 4)];
             sc[u] = sp[kb * US + u];
         }
 #pragma unroll
@@ -1425,60 +1434,77 @@ hipError_t launch_down_combine_tiny(const Shape& s, const uint16_t* h, const int
     return hipGetLastError();
 }
 
+template <int FMT, bool P>
+static void launch_fused_mx(const Shape& s, const uint16_t* x, const int32_t* ids,
+                            const int32_t* ntok, int32_t* offsets, int32_t* row_src,
+                            int32_t* token_row, const uint8_t* Wq, const uint8_t* Ws, uint16_t* h,
+                            hipStream_t st) {
+    hipLaunchKernelGGL((gemm_skinny_gateup_dispatch_mx_kernel<FMT, P>), dim3(kMxGrid * kNumCUs),
+                       dim3(256), 0, st, x, ids, ntok, s.T, s.K, s.E, offsets, row_src, token_row,
+                       Wq, Ws, h, s.H, s.I);
+}
+
 hipError_t launch_gateup_fused_dispatch_mx(const Shape& s, int fmt, const uint16_t* x,
                                            const int32_t* ids, const int32_t* ntok,
                                            int32_t* offsets, int32_t* row_src, int32_t* token_row,
                                            const uint8_t* Wq, const uint8_t* Ws, uint16_t* h,
-                                           hipStream_t st) {
-    const dim3 grid(kMxGrid * kNumCUs), block(256);
-    if (fmt == 8)
-        hipLaunchKernelGGL(gemm_skinny_gateup_dispatch_mx_kernel<8>, grid, block, 0, st, x, ids,
-                           ntok, s.T, s.K, s.E, offsets, row_src, token_row, Wq, Ws, h, s.H, s.I);
-    else
-        hipLaunchKernelGGL(gemm_skinny_gateup_dispatch_mx_kernel<4>, grid, block, 0, st, x, ids,
-                           ntok, s.T, s.K, s.E, offsets, row_src, token_row, Wq, Ws, h, s.H, s.I);
+                                           hipStream_t st, bool packed) {
+    if (fmt == 8 && packed) launch_fused_mx<8, true>(s, x, ids, ntok, offsets, row_src, token_row, Wq, Ws, h, st);
+    else if (fmt == 8) launch_fused_mx<8, false>(s, x, ids, ntok, offsets, row_src, token_row, Wq, Ws, h, st);
+    else if (packed) launch_fused_mx<4, true>(s, x, ids, ntok, offsets, row_src, token_row, Wq, Ws, h, st);
+    else launch_fused_mx<4, false>(s, x, ids, ntok, offsets, row_src, token_row, Wq, Ws, h, st);
     return hipGetLastError();
+}
+
+template <int FMT, bool P>
+static void launch_tiny_mx(const Shape& s, const uint16_t* h, const int32_t* offsets,
+                           const uint8_t* Wq, const uint8_t* Ws, const int32_t* token_row,
+                           const float* w, const int32_t* ntok, uint16_t* out, hipStream_t st) {
+    hipLaunchKernelGGL((down_combine_tiny_mx_kernel<FMT, P>), dim3(s.H / 16), dim3(256), 0, st, h,
+                       offsets, Wq, Ws, s.E, s.I, s.H, token_row, w, ntok, s.T, s.K, out);
 }
 
 hipError_t launch_down_combine_tiny_mx(const Shape& s, int fmt, const uint16_t* h,
                                        const int32_t* offsets, const uint8_t* Wq,
                                        const uint8_t* Ws, const int32_t* token_row, const float* w,
-                                       const int32_t* ntok, uint16_t* out, hipStream_t st) {
-    if (fmt == 8)
-        hipLaunchKernelGGL(down_combine_tiny_mx_kernel<8>, dim3(s.H / 16), dim3(256), 0, st, h,
-                           offsets, Wq, Ws, s.E, s.I, s.H, token_row, w, ntok, s.T, s.K, out);
-    else
-        hipLaunchKernelGGL(down_combine_tiny_mx_kernel<4>, dim3(s.H / 16), dim3(256), 0, st, h,
-                           offsets, Wq, Ws, s.E, s.I, s.H, token_row, w, ntok, s.T, s.K, out);
+                                       const int32_t* ntok, uint16_t* out, hipStream_t st,
+                                       bool packed) {
+    if (fmt == 8 && packed) launch_tiny_mx<8, true>(s, h, offsets, Wq, Ws, token_row, w, ntok, out, st);
+    else if (fmt == 8) launch_tiny_mx<8, false>(s, h, offsets, Wq, Ws, token_row, w, ntok, out, st);
+    else if (packed) launch_tiny_mx<4, true>(s, h, offsets, Wq, Ws, token_row, w, ntok, out, st);
+    else launch_tiny_mx<4, false>(s, h, offsets, Wq, Ws, token_row, w, ntok, out, st);
     return hipGetLastError();
 }
 
-template <int FMT>
+template <int FMT, bool P>
 static void launch_skinny_mx(bool gated, int grid, const uint16_t* A, const int32_t* row_src,
                              int topk, const int32_t* offsets, const uint8_t* Wq,
                              const uint8_t* Ws, uint16_t* C, int E, int Kd, int N,
                              hipStream_t st) {
     if (gated)
-        hipLaunchKernelGGL((gemm_skinny_mx_kernel<FMT, true, 1>), dim3(grid), dim3(256), 0, st, A,
-                           row_src, topk, offsets, Wq, Ws, C, E, Kd, N);
+        hipLaunchKernelGGL((gemm_skinny_mx_kernel<FMT, true, 1, P>), dim3(grid), dim3(256), 0, st,
+                           A, row_src, topk, offsets, Wq, Ws, C, E, Kd, N);
     else if (N % 32 == 0)
-        hipLaunchKernelGGL((gemm_skinny_mx_kernel<FMT, false, 2>), dim3(grid), dim3(256), 0, st, A,
-                           row_src, topk, offsets, Wq, Ws, C, E, Kd, N);
+        hipLaunchKernelGGL((gemm_skinny_mx_kernel<FMT, false, 2, P>), dim3(grid), dim3(256), 0, st,
+                           A, row_src, topk, offsets, Wq, Ws, C, E, Kd, N);
     else
-        hipLaunchKernelGGL((gemm_skinny_mx_kernel<FMT, false, 1>), dim3(grid), dim3(256), 0, st, A,
-                           row_src, topk, offsets, Wq, Ws, C, E, Kd, N);
+        hipLaunchKernelGGL((gemm_skinny_mx_kernel<FMT, false, 1, P>), dim3(grid), dim3(256), 0, st,
+                           A, row_src, topk, offsets, Wq, Ws, C, E, Kd, N);
 }
 
 hipError_t launch_grouped_gemm_mx(const Shape& s, int fmt, bool gated, const uint16_t* A,
                                   const int32_t* row_src, int topk, const int32_t* offsets,
                                   const uint8_t* Wq, const uint8_t* Ws, uint16_t* C, int Kd, int N,
-                                  hipStream_t st) {
-    if (fmt == 8)
-        launch_skinny_mx<8>(gated, kMxGrid * kNumCUs, A, row_src, topk, offsets, Wq, Ws, C, s.E,
-                            Kd, N, st);
+                                  hipStream_t st, bool packed) {
+    const int g = kMxGrid * kNumCUs;
+    if (fmt == 8 && packed)
+        launch_skinny_mx<8, true>(gated, g, A, row_src, topk, offsets, Wq, Ws, C, s.E, Kd, N, st);
+    else if (fmt == 8)
+        launch_skinny_mx<8, false>(gated, g, A, row_src, topk, offsets, Wq, Ws, C, s.E, Kd, N, st);
+    else if (packed)
+        launch_skinny_mx<4, true>(gated, g, A, row_src, topk, offsets, Wq, Ws, C, s.E, Kd, N, st);
     else
-        launch_skinny_mx<4>(gated, kMxGrid * kNumCUs, A, row_src, topk, offsets, Wq, Ws, C, s.E,
-                            Kd, N, st);
+        launch_skinny_mx<4, false>(gated, g, A, row_src, topk, offsets, Wq, Ws, C, s.E, Kd, N, st);
     return hipGetLastError();
 }
 

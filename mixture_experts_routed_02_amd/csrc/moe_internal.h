@@ -81,20 +81,23 @@ hipError_t launch_skinny_pack(const uint16_t* w, int experts, int rows, int Kd, 
 // MXFP4 (e2m1 codes, two per byte, low nibble first); codes uint8 [.., rows,
 // Kd * fmt / 8], scales uint8 [.., rows, Kd/32] (e8m0, one per 32 values).
 // The skinny kernels on MX weights (grid 3 x CUs), same contracts as above;
-// MXFP4 needs Kd % 128 == 0 (checked on the host).
+// MXFP4 needs Kd % 128 == 0 (checked on the host).  packed: the codes are in
+// the skinny pack layout (launch_skinny_pack on the codes viewed as 16-bit
+// values, k = code bytes per row / 2); the scales stay row-major.
 hipError_t launch_gateup_fused_dispatch_mx(const Shape& s, int fmt, const uint16_t* x,
                                            const int32_t* ids, const int32_t* ntok,
                                            int32_t* offsets, int32_t* row_src, int32_t* token_row,
                                            const uint8_t* Wq, const uint8_t* Ws, uint16_t* h,
-                                           hipStream_t st);
+                                           hipStream_t st, bool packed = false);
 hipError_t launch_down_combine_tiny_mx(const Shape& s, int fmt, const uint16_t* h,
                                        const int32_t* offsets, const uint8_t* Wq,
                                        const uint8_t* Ws, const int32_t* token_row, const float* w,
-                                       const int32_t* ntok, uint16_t* out, hipStream_t st);
+                                       const int32_t* ntok, uint16_t* out, hipStream_t st,
+                                       bool packed = false);
 hipError_t launch_grouped_gemm_mx(const Shape& s, int fmt, bool gated, const uint16_t* A,
                                   const int32_t* row_src, int topk, const int32_t* offsets,
                                   const uint8_t* Wq, const uint8_t* Ws, uint16_t* C, int Kd, int N,
-                                  hipStream_t st);
+                                  hipStream_t st, bool packed = false);
 // nblocks blocks of 32 consecutive bf16 values <-> 32 codes + 1 scale each
 hipError_t launch_mx_quantize(int fmt, const uint16_t* w, long long nblocks, uint8_t* codes,
                               uint8_t* scales, hipStream_t st);

@@ -20,7 +20,7 @@ __all__ = [
     "down", "combine",
     "forward", "MoEGraph", "MoeProblem", "mx_quantize", "mx_dequantize", "gate_up_mx", "forward_mx",
     "mxfp8_quantize", "mxfp8_dequantize", "gate_up_mxfp8", "forward_mxfp8", "skinny_pack",
-    "gate_up_packed", "forward_packed",
+    "gate_up_packed", "forward_packed", "mx_pack",
 ]
 
 
@@ -323,9 +323,24 @@ def mxfp8_dequantize(codes, scales, out=None):
     return mx_dequantize(codes, scales, "mxfp8", out)
 
 
+def mx_pack(codes, gated: bool, fmt="mxfp8", out=None):
+    """MX codes [E, rows, K*bits/8] -> the skinny pack layout (gated: W_gateup codes)."""
+    bits_, _ = _mx(fmt)
+    _need(codes, "codes", torch.uint8)
+    if codes.dim() != 3:
+        raise ValueError("codes must be [experts, rows, bytes]")
+    E, rows, nb = codes.shape
+    if out is None:
+        out = torch.empty_like(codes)
+    _need(out, "out", torch.uint8, tuple(codes.shape), codes.device)
+    check("moe_mx_pack", lib().moe_mx_pack(_ptr(codes), E, rows, nb * 8 // bits_, bits_,
+                                           int(bool(gated)), _ptr(out), _stream_ptr(codes.device)))
+    return out
+
+
 def gate_up_mx(p: MoeProblem, x_disp, expert_offsets, w_gateup_codes, w_gateup_scales,
-               fmt="mxfp8", h=None):
-    """Gate-up grouped GEMM on MX weights.  Returns h [cap, I]."""
+               fmt="mxfp8", h=None, packed=False):
+    """Gate-up grouped GEMM on MX weights (packed: codes from mx_pack).  Returns h [cap, I]."""
     bits_, name = _mx(fmt)
     E, H, I = p.num_experts, p.hidden, p.intermediate
     dev = x_disp.device
@@ -337,6 +352,11 @@ def gate_up_mx(p: MoeProblem, x_disp, expert_offsets, w_gateup_codes, w_gateup_s
     if h is None:
         h = torch.empty((cap, I), dtype=torch.bfloat16, device=dev)
     _need(h, "h", torch.bfloat16, (cap, I), dev)
+    if packed:
+        check("moe_gate_up_mx_packed", lib().moe_gate_up_mx_packed(
+            ctypes.byref(p), bits_, _ptr(x_disp), _ptr(expert_offsets), _ptr(w_gateup_codes),
+            _ptr(w_gateup_scales), _ptr(h), _stream_ptr(dev)))
+        return h
     fn = f"moe_gate_up_{name}"
     check(fn, getattr(lib(), fn)(ctypes.byref(p), _ptr(x_disp), _ptr(expert_offsets),
                                  _ptr(w_gateup_codes), _ptr(w_gateup_scales), _ptr(h),
@@ -350,8 +370,9 @@ def gate_up_mxfp8(p: MoeProblem, x_disp, expert_offsets, w_gateup_codes, w_gateu
 
 def forward_mx(p: MoeProblem, x, topk_ids, topk_weights, w_gateup_codes, w_gateup_scales,
                w_down_codes, w_down_scales, fmt="mxfp8", num_tokens_dev=None,
-               expert_offsets=None, out=None, workspace=None):
-    """The routed-expert layer on MX expert weights.  Returns (out, expert_offsets)."""
+               expert_offsets=None, out=None, workspace=None, packed=False):
+    """The routed-expert layer on MX expert weights (packed: codes from mx_pack).
+    Returns (out, expert_offsets)."""
     bits_, name = _mx(fmt)
     T, K, E, H, I = p.num_tokens, p.top_k, p.num_experts, p.hidden, p.intermediate
     dev = x.device
@@ -370,11 +391,14 @@ def forward_mx(p: MoeProblem, x, topk_ids, topk_weights, w_gateup_codes, w_gateu
         out = torch.empty((T, H), dtype=torch.bfloat16, device=dev)
     _need(out, "out", torch.bfloat16, (T, H), dev)
     ws = make_workspace(p, dev) if workspace is None else workspace
-    fn = f"moe_forward_{name}"
-    check(fn, getattr(lib(), fn)(
-        ctypes.byref(p), _ptr(x), _ptr(topk_ids), _ptr(topk_weights), _ptr(w_gateup_codes),
-        _ptr(w_gateup_scales), _ptr(w_down_codes), _ptr(w_down_scales), _ptr(nt),
-        _ptr(expert_offsets), _ptr(out), _ptr(ws), ws.numel(), _stream_ptr(dev)))
+    args = (_ptr(x), _ptr(topk_ids), _ptr(topk_weights), _ptr(w_gateup_codes),
+            _ptr(w_gateup_scales), _ptr(w_down_codes), _ptr(w_down_scales), _ptr(nt),
+            _ptr(expert_offsets), _ptr(out), _ptr(ws), ws.numel(), _stream_ptr(dev))
+    if packed:
+        check("moe_forward_mx_packed", lib().moe_forward_mx_packed(ctypes.byref(p), bits_, *args))
+    else:
+        fn = f"moe_forward_{name}"
+        check(fn, getattr(lib(), fn)(ctypes.byref(p), *args))
     return out, expert_offsets
 
 

@@ -25,7 +25,7 @@ def declared_functions():
 
 def test_exports_every_declared_symbol():
     names = declared_functions()
-    assert len(names) == 23, names
+    assert len(names) == 26, names
     L = moe.lib()
     for n in names:
         assert hasattr(L, n), n
@@ -177,3 +177,16 @@ def test_skinny_pack_entry_points_fail_closed():
     assert L.moe_forward_packed(ctypes.byref(p), A16, A4, A4, A16, A16, None, A4, A16, A16, ws,
                                 None) == 2
     assert L.moe_gate_up_packed(ctypes.byref(p), A16, A4, A16, A16, None) == 2
+
+
+def test_mx_pack_entry_points_fail_closed():
+    L = moe.lib()
+    assert L.moe_mx_pack(A16, 2, 32, 64, 6, 0, A16 * 2, None) == 1        # bits 8 or 4
+    assert L.moe_mx_pack(A16, 2, 32, 64, 4, 0, A16 * 2, None) == 1        # MXFP4: k % 128
+    assert L.moe_mx_pack(A16, 2, 24, 64, 8, 0, A16 * 2, None) == 1        # rows % 16
+    assert L.moe_mx_pack(None, 0, 32, 128, 4, 1, None, None) == 0         # nothing to do
+    p = moe.problem(64, 2, 8, 256, 512)
+    ws = moe.workspace_size(p)
+    assert L.moe_forward_mx_packed(ctypes.byref(p), 5, A16, A4, A4, A16, A16, A16, A16, None, A4,
+                                   A16, A16, ws, None) == 1
+    assert L.moe_gate_up_mx_packed(ctypes.byref(p), 16, A16, A4, A16, A16, A16, None) == 1

@@ -119,3 +119,48 @@ def test_forward_packed_ep_decode_full_size(name):
     pgu, pd = ops.skinny_pack(wgu, True), ops.skinny_pack(wd, False)
     got, _ = ops.forward_packed(p, x, ids, w, pgu, pd)
     assert torch.equal(got.view(torch.int16), ref.view(torch.int16))
+
+
+# ---------------------------------------------------------------------------
+# MX codes in the pack layout: bit-identical to the row-major MX path (which
+# test_gpu_mx checks against the oracle)
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("fmt", ["mxfp8", "mxfp4"])
+@pytest.mark.parametrize("name", ["tiny_down", "fused_skinny_down", "multi_launch"])
+def test_forward_mx_packed_bit_identical(fmt, name):
+    T, K, E, H, I, lo, hi = SHAPES[name]
+    x, ids, w, wgu, wd = case(T, K, E, H, I, 23, lo, hi)
+    p = moe.problem(T, K, E, H, I)
+    qgu, sgu = ops.mx_quantize(wgu, fmt)
+    qd, sd = ops.mx_quantize(wd, fmt)
+    ref, ref_off = ops.forward_mx(p, x, ids, w, qgu, sgu, qd, sd, fmt)
+    pgu, pd = ops.mx_pack(qgu, True, fmt), ops.mx_pack(qd, False, fmt)
+    # the MX pack is the bf16 pack of the code bytes viewed as 16-bit values
+    assert np.array_equal(bits(pgu.view(torch.bfloat16)),
+                          expected_pack(bits(qgu.view(torch.bfloat16)), True))
+    got, off = ops.forward_mx(p, x, ids, w, pgu, sgu, pd, sd, fmt, packed=True)
+    assert torch.equal(off, ref_off)
+    assert torch.equal(got.view(torch.int16), ref.view(torch.int16))
+    x_disp, o2, _, _ = ops.dispatch(p, x, ids)
+    h_ref = ops.gate_up_mx(p, x_disp, o2, qgu, sgu, fmt)
+    h = ops.gate_up_mx(p, x_disp, o2, pgu, sgu, fmt, packed=True)
+    R = int(o2[-1])
+    assert torch.equal(h[:R].view(torch.int16), h_ref[:R].view(torch.int16))
+
+
+@pytest.mark.parametrize("fmt", ["mxfp8", "mxfp4"])
+@pytest.mark.parametrize("name", ["ep_decode_T1", "ep_decode_T32"])
+def test_forward_mx_packed_ep_decode_full_size(fmt, name):
+    cfg = W.CONFIGS[name]
+    T, K, E, H, I = cfg.num_tokens, cfg.top_k, cfg.num_experts, cfg.hidden, cfg.intermediate
+    x = W.make_x(cfg, 1).to(DEV)
+    ids, w = (t.to(DEV) for t in W.make_routing(cfg, 1))
+    wgu, wd = W.make_weights(cfg, 1, DEV)
+    qgu, sgu = ops.mx_quantize(wgu, fmt)
+    qd, sd = ops.mx_quantize(wd, fmt)
+    del wgu, wd
+    p = moe.problem(T, K, E, H, I)
+    ref, _ = ops.forward_mx(p, x, ids, w, qgu, sgu, qd, sd, fmt)
+    pgu, pd = ops.mx_pack(qgu, True, fmt), ops.mx_pack(qd, False, fmt)
+    got, _ = ops.forward_mx(p, x, ids, w, pgu, sgu, pd, sd, fmt, packed=True)
+    assert torch.equal(got.view(torch.int16), ref.view(torch.int16))
