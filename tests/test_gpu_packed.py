@@ -164,3 +164,54 @@ def test_forward_mx_packed_ep_decode_full_size(fmt, name):
     pgu, pd = ops.mx_pack(qgu, True, fmt), ops.mx_pack(qd, False, fmt)
     got, _ = ops.forward_mx(p, x, ids, w, pgu, sgu, pd, sd, fmt, packed=True)
     assert torch.equal(got.view(torch.int16), ref.view(torch.int16))
+
+
+# ---------------------------------------------------------------------------
+# static capacity + graph replay on the packed and MX entry points: every one
+# of them only enqueues kernels (no allocation, memset or host read), so a
+# caller can record it into a HIP graph and replay it with a new device token
+# count; each replay must equal the eager call with that count, bit for bit
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("kind", ["packed", "mxfp8", "mxfp4", "mxfp8_packed"])
+def test_graph_replays_with_device_token_count(kind):
+    cfg = W.CONFIGS["static_capacity"]
+    T, K, E, H, I = cfg.num_tokens, cfg.top_k, cfg.num_experts, cfg.hidden, cfg.intermediate
+    x = W.make_x(cfg, 4).to(DEV)
+    ids, w = (t.to(DEV) for t in W.make_routing(cfg, 4))
+    wgu, wd = W.make_weights(cfg, 4, DEV)
+    p = moe.problem(T, K, E, H, I, cfg.capacity)
+    if kind == "packed":
+        a, b = ops.skinny_pack(wgu, True), ops.skinny_pack(wd, False)
+        run = lambda nt, out, off, ws: ops.forward_packed(p, x, ids, w, a, b, nt, off, out, ws)
+    else:
+        fmt = kind.split("_")[0]
+        qgu, sgu = ops.mx_quantize(wgu, fmt)
+        qd, sd = ops.mx_quantize(wd, fmt)
+        packed = kind.endswith("packed")
+        if packed:
+            qgu, qd = ops.mx_pack(qgu, True, fmt), ops.mx_pack(qd, False, fmt)
+        run = lambda nt, out, off, ws: ops.forward_mx(p, x, ids, w, qgu, sgu, qd, sd, fmt, nt, off,
+                                                      out, ws, packed=packed)
+    nt = torch.tensor([T], dtype=torch.int32, device=DEV)
+    out = torch.empty((T, H), dtype=torch.bfloat16, device=DEV)
+    off = torch.empty((E + 1,), dtype=torch.int32, device=DEV)
+    ws = ops.make_workspace(p, DEV)
+    run(nt, out, off, ws)                                  # warm-up outside the capture
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        run(nt, out, off, ws)
+    ref_out = torch.empty_like(out)
+    ref_off = torch.empty_like(off)
+    ref_ws = ops.make_workspace(p, DEV)
+    for tv in (2048, 1, 700, 0, 1999, 64):
+        nt.fill_(tv)
+        out.view(torch.int16).fill_(0x7FC1)                # a NaN pattern no kernel writes
+        g.replay()
+        torch.cuda.synchronize()
+        nt_e = torch.tensor([tv], dtype=torch.int32, device=DEV)
+        run(nt_e, ref_out, ref_off, ref_ws)                # eager work between the replays
+        torch.cuda.synchronize()
+        assert torch.equal(off, ref_off), tv
+        assert torch.equal(out[:tv].view(torch.int16), ref_out[:tv].view(torch.int16)), tv
+        assert bool((out[tv:].view(torch.int16) == 0x7FC1).all()), tv   # rows >= T_v untouched
