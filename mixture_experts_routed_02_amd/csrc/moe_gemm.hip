@@ -1115,7 +1115,7 @@ __device__ __forceinline__ int wave_tile_lookup(const int32_t* offsets, int E, i
     return __builtin_amdgcn_readfirstlane(carry);
 }
 
-template <int BM, int BN, int WGM, int WGN, bool GATED>
+template <int BM, int BN, int WGM, int WGN, bool GATED, bool SUBSKIP = false>
 __global__ __launch_bounds__(64 * WGM * WGN) void gemm_tiled_kernel(
     const uint16_t* __restrict__ A, const int32_t* __restrict__ row_src, int topk,
     const int32_t* __restrict__ offsets, const uint16_t* __restrict__ W,
@@ -1200,6 +1200,12 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_tiled_kernel(
         const int mrows = (me - m_tile * BM) < BM ? (me - m_tile * BM) : BM;
         // a wave whose token rows all lie past the valid rows skips its MFMAs
         const bool active = wm * WM < mrows;
+        // SUBSKIP: the 32-row sub-tiles of this wave that hold valid rows
+        // (wave-uniform); the others skip their MFMAs too.  A branch per MFMA:
+        // it pays where most tiles are partial (EP prefill T = 8192, ~128 rows
+        // per expert: 6% faster) and costs 4% where they are full (Mixtral), so
+        // the host picks the instance (GemmPlan::subskip).
+        const int jlive = __builtin_amdgcn_readfirstlane((mrows - wm * WM + 31) / 32);
 
         // global source of each group this wave fills (stage 0): token groups
         // gather rows through row_src (rows past the valid ones repeat the
@@ -1266,7 +1272,8 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_tiled_kernel(
                     for (int i = 0; i < NS; ++i) {
 #pragma unroll
                         for (int j = 0; j < MS; ++j) {
-                            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fw[sk][i], fa[sk][j], acc[i][j], 0, 0, 0);
+                            if (!SUBSKIP || j == 0 || jlive > j)
+                                acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fw[sk][i], fa[sk][j], acc[i][j], 0, 0, 0);
                             if (i == NS - 1) read_a(h + 1, sk, j);
                         }
                         read_w(h + 1, sk, i);
@@ -1394,11 +1401,11 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_tiled_kernel(
     }
 }
 
-template <int BM, int BN, int WGM, int WGN, bool GATED>
+template <int BM, int BN, int WGM, int WGN, bool GATED, bool SUBSKIP = false>
 hipError_t launch_tiled(int grid, const uint16_t* A, const int32_t* row_src, int topk,
                         const int32_t* offsets, const uint16_t* W, uint16_t* C, int E, int Kd,
                         int N, hipStream_t st) {
-    hipLaunchKernelGGL((gemm_tiled_kernel<BM, BN, WGM, WGN, GATED>), dim3(grid),
+    hipLaunchKernelGGL((gemm_tiled_kernel<BM, BN, WGM, WGN, GATED, SUBSKIP>), dim3(grid),
                        dim3(64 * WGM * WGN), 0, st, A, row_src, topk, offsets, W, C, E, Kd, N);
     return hipGetLastError();
 }
@@ -1583,6 +1590,12 @@ GemmPlan choose_plan(const Shape& s, int hint) {
             if (fill(256) >= 0.9 * fill(128)) p.bn_down = 256;
         }
         p.grid_gateup = p.grid_down = kNumCUs;
+        // fewer than four 192-row tiles per expert even if every assignment
+        // were local (T*K/E counts the ids other ranks own too: the 96-of-384
+        // share at T = 8192 gives 512 for ~128 local rows): partial tiles hold
+        // much of the MFMA work, so skip it per 32-row sub-tile.  Mixtral's
+        // 1024 rows per expert stay on the branch-free instance.
+        p.subskip = (double)s.T * s.K / s.E < 768.0;
     } else {
         p.bn_gateup = 128;                          // 64 gate + 64 up rows
         p.bn_down = (s.H % 128 == 0) ? 128 : 64;
@@ -1599,6 +1612,8 @@ hipError_t launch_grouped_gemm(const Shape& s, const GemmPlan& plan, bool gated,
     const int bn = gated ? plan.bn_gateup : plan.bn_down;
 #define MOE_TILED(BM, BN, WGM, WGN, G) \
     launch_tiled<BM, BN, WGM, WGN, G>(grid, A, row_src, topk, offsets, W, C, s.E, Kd, N, st)
+#define MOE_TILED_S(BM, BN, WGM, WGN, G) \
+    launch_tiled<BM, BN, WGM, WGN, G, true>(grid, A, row_src, topk, offsets, W, C, s.E, Kd, N, st)
     switch (plan.kind) {
         case kSkinny:
             if (gated)
@@ -1619,11 +1634,17 @@ hipError_t launch_grouped_gemm(const Shape& s, const GemmPlan& plan, bool gated,
             return bn == 128 ? MOE_TILED(128, 128, 2, 2, false) : MOE_TILED(128, 64, 2, 2, false);
         default:
             // 192 = 2 x 96 token rows: a wave holds 3 x 2 sub-tiles of 32 x 32
+            if (plan.subskip) {
+                if (gated) return bn == 256 ? MOE_TILED_S(192, 256, 2, 4, true) : MOE_TILED_S(256, 128, 4, 2, true);
+                return bn == 256 ? MOE_TILED_S(192, 256, 2, 4, false)
+                     : bn == 128 ? MOE_TILED_S(192, 128, 2, 4, false) : MOE_TILED(128, 64, 2, 2, false);
+            }
             if (gated) return bn == 256 ? MOE_TILED(192, 256, 2, 4, true) : MOE_TILED(256, 128, 4, 2, true);
             return bn == 256 ? MOE_TILED(192, 256, 2, 4, false)
                  : bn == 128 ? MOE_TILED(192, 128, 2, 4, false) : MOE_TILED(128, 64, 2, 2, false);
     }
 #undef MOE_TILED
+#undef MOE_TILED_S
 }
 
 }  // namespace moe

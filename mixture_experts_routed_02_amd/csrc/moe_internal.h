@@ -25,6 +25,7 @@ struct GemmPlan {
     int kind;
     int grid_gateup, grid_down;
     int bn_gateup, bn_down;  // weight rows per tile (tiled kinds)
+    bool subskip;            // tiled large: skip MFMAs per 32-row sub-tile of partial tiles
 };
 
 GemmPlan choose_plan(const Shape& s, int hint);
