@@ -26,6 +26,7 @@ struct GemmPlan {
     int grid_gateup, grid_down;
     int bn_gateup, bn_down;  // weight rows per tile (tiled kinds)
     bool subskip;            // tiled large: skip MFMAs per 32-row sub-tile of partial tiles
+    bool split;              // tiled: XCDs 0-3 and 4-7 walk the two halves of the tile list
 };
 
 GemmPlan choose_plan(const Shape& s, int hint);

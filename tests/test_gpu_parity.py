@@ -49,6 +49,8 @@ SMALL = {
     "one_expert": (200, 1, 4, 256, 128, 2, 3),
     "sparse_many_experts": (40, 2, 128, 256, 256, 0, 128),
     "single_token": (1, 2, 3, 128, 64, 0, 3),
+    # >= 32 experts and >= 2 grids of tiles: the tiled plans split the tile list in two
+    "many_experts_split": (2048, 2, 64, 256, 1024, 0, 64),
 }
 
 
