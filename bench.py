@@ -76,10 +76,15 @@ def pmc_traffic(kernel_key: str, src_hash: str, units: int):
     return ent.get("bytes_per_launch")
 
 
+# The sources the grouped-GEMM kernels are compiled from: a change to any of
+# them voids the committed counter figures (host-side API code does not).
+GEMM_SOURCES = ("moe_gemm.hip", "moe_internal.h")
+
+
 def kernel_src_hash() -> str:
     h = hashlib.sha256()
     csrc = os.path.join(REPO, "mixture_experts_routed_02_amd", "csrc")
-    for name in sorted(os.listdir(csrc)):
+    for name in GEMM_SOURCES:
         with open(os.path.join(csrc, name), "rb") as fh:
             h.update(name.encode() + b"\0" + fh.read())
     return h.hexdigest()

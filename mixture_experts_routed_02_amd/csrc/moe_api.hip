@@ -431,7 +431,9 @@ moe_status_t moe_skinny_pack(const uint16_t* w, int32_t experts, int32_t rows, i
         return MOE_ERROR_INVALID_VALUE;
     if ((long long)experts * rows > (1ll << 40) / k) return MOE_ERROR_NOT_SUPPORTED;
     if (experts == 0) return MOE_SUCCESS;
-    if (bad_bf16(w) || bad_bf16(packed) || w == packed) return MOE_ERROR_INVALID_VALUE;
+    if (bad_bf16(w) || bad_bf16(packed)) return MOE_ERROR_INVALID_VALUE;
+    const uintptr_t n = (uintptr_t)experts * rows * k * 2, a = (uintptr_t)w, b = (uintptr_t)packed;
+    if (a < b + n && b < a + n) return MOE_ERROR_INVALID_VALUE;   // overlapping buffers
     return launched(moe::launch_skinny_pack(w, experts, rows, k, gated != 0, packed,
                                             static_cast<hipStream_t>(stream)));
 }

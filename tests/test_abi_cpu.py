@@ -190,3 +190,11 @@ def test_mx_pack_entry_points_fail_closed():
     assert L.moe_forward_mx_packed(ctypes.byref(p), 5, A16, A4, A4, A16, A16, A16, A16, None, A4,
                                    A16, A16, ws, None) == 1
     assert L.moe_gate_up_mx_packed(ctypes.byref(p), 16, A16, A4, A16, A16, A16, None) == 1
+
+
+def test_skinny_pack_rejects_overlap():
+    L = moe.lib()
+    n = 2 * 32 * 64 * 2                                                   # bytes of w
+    assert L.moe_skinny_pack(A16, 2, 32, 64, 0, A16 + n - 16, None) == 1  # tail overlaps
+    assert L.moe_skinny_pack(A16 + 64, 2, 32, 64, 0, A16, None) == 1      # head overlaps
+    assert L.moe_mx_pack(A16, 2, 32, 128, 8, 0, A16 + 64, None) == 1
