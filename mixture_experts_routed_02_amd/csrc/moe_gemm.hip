@@ -23,6 +23,14 @@
 //
 // gated: W = [E, 2N, Kd] (rows [0,N) gate, [N,2N) up), C = bf16(silu(g)*u) [cap, N]
 // plain: W = [E, N, Kd],                                 C = bf16(acc)      [cap, N]
+//
+// Contents: the skinny kernels (weight-streaming regime, 16-row tiles with
+// split-K over the waves; the variants with the dispatch or the combine
+// inside), the skinny pack layout and its kernel, the MX skinny kernels
+// (MXFP8 / MXFP4 weights dequantized in registers) with the MX quantizer and
+// dequantizer, and the tiled kernel (LDS-staged 192x256 / 128 / 64-row tiles
+// for the MFMA-bound and prefill regimes), then the host launchers and the
+// plan choice.
 #include "moe_internal.h"
 
 #include <cmath>
