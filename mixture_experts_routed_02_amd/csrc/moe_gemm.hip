@@ -592,18 +592,22 @@ struct MxFmt<4> {
 
 // Block size (segments) and grid of the MX skinny kernels.  MXFP8: blocks of 4
 // segments (4 KB of codes per wave and buffer, 8 KB in flight, as the bf16
-// kernel keeps) need ~148 VGPRs, so 3 workgroups fit per CU and the grid is
-// 3 x CUs.  Measured against 2-segment blocks at 4 x CUs: 12-14% faster on the
-// 96-expert decode shapes (T = 8 .. 128), 7% at T = 1; 6-segment blocks at 2 x
-// CUs and 32-weight-row gated tiles (half the token-row loads per weight byte)
-// were no faster.  MXFP4: a segment carries twice the token values, so 2
-// segments keep the token registers, and the VGPR count, of MXFP8's 4 (4
-// segments at 2 x CUs: within 2%).  Loading the token operand only in the
-// lanes that hold valid rows (exec-masked) was 0-2% slower on all three
-// formats.
+// kernel keeps) fit 3 workgroups per CU, so the grid is 3 x CUs.  Measured
+// against 2-segment blocks at 4 x CUs: 12-14% faster on the 96-expert decode
+// shapes (T = 8 .. 128), 7% at T = 1; 6-segment blocks at 2 x CUs and
+// 32-weight-row gated tiles (half the token-row loads per weight byte) were no
+// faster.  MXFP4: a segment carries twice the token values, so 2 segments
+// keep the token registers of MXFP8's 4; the kernels fit 4 workgroups per CU
+// and run on 4 x CUs (1-1.5% faster than 3 x CUs at T >= 8; 4 segments at
+// 2 x CUs: within 2%).  The grid factor is also the kernels' waves-per-SIMD
+// bound (__launch_bounds__), so the compiler keeps them within 168 (MXFP8) or
+// 128 (MXFP4) registers and the whole grid is resident.  Loading the token
+// operand only in the lanes that hold valid rows (exec-masked) was 0-2% slower
+// on all three formats.
 template <int FMT>
 constexpr int mx_segs() { return FMT == 8 ? 4 : 2; }
-constexpr int kMxGrid = 3;
+template <int FMT>
+constexpr int mx_grid() { return FMT == 8 ? 3 : 4; }
 
 // Skinny tiles on MX weights: codes Wq [E, rows, Kd * FMT / 8 bytes], scales
 // Ws [E, rows, Kd / 32].  Same tiles, tile order, k split over the waves (in
@@ -624,7 +628,8 @@ __device__ __forceinline__ void skinny_tiles_mx(const uint16_t* __restrict__ A, 
     constexpr int XS = F::G / 8;                   // 16-byte token pieces per lane and segment
     constexpr int COLS = GATED ? 8 * RB : 16 * RB;
 
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform: scalar loop bounds
     const int li = lane & 15, lg = lane >> 4;
     const int n_tiles = N / COLS;
     const int w_rows = GATED ? 2 * N : N;
@@ -703,18 +708,31 @@ __device__ __forceinline__ void skinny_tiles_mx(const uint16_t* __restrict__ A, 
                 for (int rb = 0; rb < RB; ++rb) seg_mma(q[rb][u], sc[rb][u], xv[u], acc[rb]);
         };
         if (nblk > 0) load_x(xa, 0);
+        // Refills inside the loop are unconditional and the last one or two
+        // blocks are peeled: a refill under a branch leaves the compiler's
+        // wait counts at the join as if it had not been issued, so the next
+        // block's multiply would wait for every load in flight (vmcnt(0)).
+        // Measured 4-7% faster on the MXFP4 decode shapes, 1-3% on MXFP8,
+        // bit-identical; the same change in the bf16 kernels was neutral on
+        // packed weights and 3-8% slower on row-major ones, so they keep the
+        // conditional refill.
         int b = 0;
-        for (; b + 2 <= nblk; b += 2) {
+        for (; b + 2 < nblk; b += 2) {
             load_w(qb, sb, b + 1);
             load_x(xb, b + 1);
             mma(qa, sa, xa);
-            if (b + 2 < nblk) {
-                load_w(qa, sa, b + 2);
-                load_x(xa, b + 2);
-            }
+            load_w(qa, sa, b + 2);
+            load_x(xa, b + 2);
             mma(qb, sb, xb);
         }
-        if (b < nblk) mma(qa, sa, xa);
+        if (b + 1 < nblk) {
+            load_w(qb, sb, b + 1);
+            load_x(xb, b + 1);
+            mma(qa, sa, xa);
+            mma(qb, sb, xb);
+        } else if (b < nblk) {
+            mma(qa, sa, xa);
+        }
         for (int sg = sg0 + nblk * US; sg < sg1; ++sg) {   // tail segments
             const int o = sg - sg0;
             moe_bf16x8 xv[XS];
@@ -728,7 +746,7 @@ __device__ __forceinline__ void skinny_tiles_mx(const uint16_t* __restrict__ A, 
 }
 
 template <int FMT, bool GATED, int RB, bool PACKED = false>
-__global__ __launch_bounds__(256) void gemm_skinny_mx_kernel(
+__global__ __launch_bounds__(256, mx_grid<FMT>()) void gemm_skinny_mx_kernel(
     const uint16_t* __restrict__ A, const int32_t* __restrict__ row_src, int topk,
     const int32_t* __restrict__ offsets, const uint8_t* __restrict__ Wq,
     const uint8_t* __restrict__ Ws, uint16_t* __restrict__ C, int E, int Kd, int N) {
@@ -741,7 +759,7 @@ __global__ __launch_bounds__(256) void gemm_skinny_mx_kernel(
 
 // Gate-up on MX weights with the dispatch inside (T*K <= kFusedDispatchMax).
 template <int FMT, bool PACKED = false>
-__global__ __launch_bounds__(256) void gemm_skinny_gateup_dispatch_mx_kernel(
+__global__ __launch_bounds__(256, mx_grid<FMT>()) void gemm_skinny_gateup_dispatch_mx_kernel(
     const uint16_t* __restrict__ x, const int32_t* __restrict__ ids,
     const int32_t* __restrict__ ntok, int T, int topk, int E, int32_t* __restrict__ offsets,
     int32_t* __restrict__ row_src, int32_t* __restrict__ token_row,
@@ -776,7 +794,8 @@ __global__ __launch_bounds__(256) void down_combine_tiny_mx_kernel(
     __shared__ float s_part[kTinyRows][4][16][17];
     __shared__ uint16_t s_y[kTinyRows][16][16];
 
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform: scalar loop bounds
     const int li = lane & 15, lg = lane >> 4;
     const int n0 = blockIdx.x * 16;
     tiny_expert_slots(offsets, E, s_e, s_r0, s_m, &s_ne);
@@ -831,13 +850,19 @@ __global__ __launch_bounds__(256) void down_combine_tiny_mx_kernel(
     };
     if (total > 0) load(qa, sa, xa, 0);
     int b = 0;
-    for (; b + 2 <= total; b += 2) {
+    for (; b + 2 < total; b += 2) {   // refills unconditional, tail peeled (see skinny_tiles_mx)
         load(qb, sb, xb, b + 1);
         step(qa, sa, xa, b);
-        if (b + 2 < total) load(qa, sa, xa, b + 2);
+        load(qa, sa, xa, b + 2);
         step(qb, sb, xb, b + 1);
     }
-    if (b < total) step(qa, sa, xa, b);
+    if (b + 1 < total) {
+        load(qb, sb, xb, b + 1);
+        step(qa, sa, xa, b);
+        step(qb, sb, xb, b + 1);
+    } else if (b < total) {
+        step(qa, sa, xa, b);
+    }
     __syncthreads();
     tiny_combine(ne, s_r0, &s_part[0][0][0][0], &s_y[0][0][0], token_row, wts, ntok, T, topk, N, n0, out);
 }
@@ -1469,7 +1494,7 @@ static void launch_fused_mx(const Shape& s, const uint16_t* x, const int32_t* id
                             const int32_t* ntok, int32_t* offsets, int32_t* row_src,
                             int32_t* token_row, const uint8_t* Wq, const uint8_t* Ws, uint16_t* h,
                             hipStream_t st) {
-    hipLaunchKernelGGL((gemm_skinny_gateup_dispatch_mx_kernel<FMT, P>), dim3(kMxGrid * kNumCUs),
+    hipLaunchKernelGGL((gemm_skinny_gateup_dispatch_mx_kernel<FMT, P>), dim3(mx_grid<FMT>() * kNumCUs),
                        dim3(256), 0, st, x, ids, ntok, s.T, s.K, s.E, offsets, row_src, token_row,
                        Wq, Ws, h, s.H, s.I);
 }
@@ -1526,7 +1551,7 @@ hipError_t launch_grouped_gemm_mx(const Shape& s, int fmt, bool gated, const uin
                                   const int32_t* row_src, int topk, const int32_t* offsets,
                                   const uint8_t* Wq, const uint8_t* Ws, uint16_t* C, int Kd, int N,
                                   hipStream_t st, bool packed) {
-    const int g = kMxGrid * kNumCUs;
+    const int g = (fmt == 8 ? mx_grid<8>() : mx_grid<4>()) * kNumCUs;
     if (fmt == 8 && packed)
         launch_skinny_mx<8, true>(gated, g, A, row_src, topk, offsets, Wq, Ws, C, s.E, Kd, N, st);
     else if (fmt == 8)
