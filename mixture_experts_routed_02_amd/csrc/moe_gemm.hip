@@ -93,7 +93,7 @@ __device__ __forceinline__ moe_bf16x8 stream_load(const moe_bf16x8* p) { return 
 // added in wave order through LDS; gated tiles write bf16(silu(g) * u) for
 // their 8 columns, plain tiles bf16(y) for their 16*RB columns.  Ends with a
 // barrier, so s_red is free again.
-template <bool GATED, int RB>
+template <bool GATED, int RB, bool PACKED_GROUPS = false>
 __device__ __forceinline__ void skinny_epilogue(const moe_f32x4 (&acc)[RB], float* s_red,
                                                 uint16_t* __restrict__ C, int N, int r0,
                                                 int mrows, int n_tile) {
@@ -107,13 +107,17 @@ __device__ __forceinline__ void skinny_epilogue(const moe_f32x4 (&acc)[RB], floa
 #pragma unroll
         for (int i = 0; i < 4; ++i) red(wave, rb * 16 + 4 * lg + i, li) = acc[rb][i];
     __syncthreads();
-    if (GATED) {   // tile rows [0, COLS) gate, [COLS, 2 COLS) the matching up rows
+    if (GATED) {
         if (tid < 16 * COLS) {
             const int m = tid / COLS, c = tid % COLS;
             if (m < mrows) {
                 float g = 0.f, u = 0.f;
+                // 32-row gated tiles of packed weights hold two 16-row groups
+                // (8 gate + 8 up rows each); otherwise gate rows come first
+                const int rg = (RB == 2 && PACKED_GROUPS) ? ((c & 8) << 1) | (c & 7) : c;
+                const int ru = (RB == 2 && PACKED_GROUPS) ? rg + 8 : COLS + c;
 #pragma unroll
-                for (int w = 0; w < 4; ++w) { g += red(w, c, m); u += red(w, COLS + c, m); }
+                for (int w = 0; w < 4; ++w) { g += red(w, rg, m); u += red(w, ru, m); }
                 C[(size_t)(r0 + m) * N + n_tile * COLS + c] = moe_f32_to_bf16(silu_f32(g) * u);
             }
         }
@@ -590,24 +594,28 @@ struct MxFmt<4> {
     }
 };
 
-// Block size (segments) and grid of the MX skinny kernels.  MXFP8: blocks of 4
-// segments (4 KB of codes per wave and buffer, 8 KB in flight, as the bf16
-// kernel keeps) fit 3 workgroups per CU, so the grid is 3 x CUs.  Measured
-// against 2-segment blocks at 4 x CUs: 12-14% faster on the 96-expert decode
-// shapes (T = 8 .. 128), 7% at T = 1; 6-segment blocks at 2 x CUs and
-// 32-weight-row gated tiles (half the token-row loads per weight byte) were no
-// faster.  MXFP4: a segment carries twice the token values, so 2 segments
-// keep the token registers of MXFP8's 4; the kernels fit 4 workgroups per CU
-// and run on 4 x CUs (1-1.5% faster than 3 x CUs at T >= 8; 4 segments at
-// 2 x CUs: within 2%).  The grid factor is also the kernels' waves-per-SIMD
-// bound (__launch_bounds__), so the compiler keeps them within 168 (MXFP8) or
-// 128 (MXFP4) registers and the whole grid is resident.  Loading the token
-// operand only in the lanes that hold valid rows (exec-masked) was 0-2% slower
-// on all three formats.
+// Tile, block size (segments) and grid of the MX skinny kernels.  Gated
+// (gate-up) tiles are 32 weight rows (RB = 2: 16 gate + 16 up rows, or two
+// packed 16-row groups), so one set of token registers feeds twice the code
+// bytes; plain tiles are 32 rows too when N allows.  A block is 4 segments
+// (MXFP8: 8 KB of codes per wave and buffer, 2 workgroups per CU) or 2
+// (MXFP4: a segment carries twice the token values; 4 KB of codes per wave
+// and buffer, 3 workgroups per CU).  Measured, interleaved and bit-identical,
+// on the 96-expert decode shapes at T = 8 .. 128: 32-row gated tiles took
+// MXFP4 15-20% and MXFP8 6-12% below 16-row gated tiles (MXFP4 2-segment
+// blocks at 4 x CUs, MXFP8 4-segment blocks at 3 x CUs); 3-segment blocks
+// (both formats) and 4-segment MXFP4 blocks at 2 x CUs were slower, and
+// MXFP8 at 3 x CUs (spilling) no faster.  T = 1 moves by -4% (MXFP4) and
+// +-2% (MXFP8).  Earlier: 6-segment MXFP8 blocks at 2 x CUs no faster than
+// 4; loading the token operand only in the lanes that hold valid rows
+// (exec-masked) 0-2% slower on all three formats.  The grid factor is also
+// the kernels' waves-per-SIMD bound (__launch_bounds__), so the compiler
+// keeps the whole persistent grid resident.
 template <int FMT>
 constexpr int mx_segs() { return FMT == 8 ? 4 : 2; }
 template <int FMT>
-constexpr int mx_grid() { return FMT == 8 ? 3 : 4; }
+constexpr int mx_grid() { return FMT == 8 ? 2 : 3; }
+constexpr int kMxGatedRB = 2;
 
 // Skinny tiles on MX weights: codes Wq [E, rows, Kd * FMT / 8 bytes], scales
 // Ws [E, rows, Kd / 32].  Same tiles, tile order, k split over the waves (in
@@ -624,7 +632,7 @@ __device__ __forceinline__ void skinny_tiles_mx(const uint16_t* __restrict__ A, 
     typedef MxFmt<FMT> F;
     typedef typename F::scale_t scale_t;
     constexpr int BM = 16;
-    constexpr int US = mx_segs<FMT>() / RB;        // segments per block
+    constexpr int US = mx_segs<FMT>();              // segments per block
     constexpr int XS = F::G / 8;                   // 16-byte token pieces per lane and segment
     constexpr int COLS = GATED ? 8 * RB : 16 * RB;
 
@@ -656,12 +664,16 @@ __device__ __forceinline__ void skinny_tiles_mx(const uint16_t* __restrict__ A, 
         const scale_t* wsc[RB];
 #pragma unroll
         for (int rb = 0; rb < RB; ++rb) {
-            const int tr = rb * 16 + li;   // gated: rows [0, COLS) gate, then the matching up rows
+            // packed: block rb is 16-row group n_tile * RB + rb (gated: 8 gate
+            // rows, then the matching 8 up rows); row-major gated: rows
+            // [0, COLS) of the tile are gate rows, then the matching up rows
+            const int tr = rb * 16 + li, grp16 = n_tile * RB + rb;
             const int wrow = !GATED ? n_tile * COLS + tr
+                           : PACKED ? (li < 8 ? 8 * grp16 + li : N + 8 * grp16 + (li - 8))
                            : tr < COLS ? n_tile * COLS + tr : N + n_tile * COLS + (tr - COLS);
             const size_t grow = (size_t)e * w_rows + wrow;
             if (PACKED) {
-                const size_t grp = (size_t)e * (w_rows / 16) + (GATED ? n_tile : n_tile * RB + rb);
+                const size_t grp = (size_t)e * (w_rows / 16) + grp16;
                 wq[rb] = reinterpret_cast<const moe_u32x4*>(Wq) + (grp * nseg + sg0) * 64 + lane;
             } else {
                 wq[rb] = reinterpret_cast<const moe_u32x4*>(Wq + grow * row_bytes + (size_t)sg0 * 64 + lg * 16);
@@ -741,7 +753,7 @@ __device__ __forceinline__ void skinny_tiles_mx(const uint16_t* __restrict__ A, 
 #pragma unroll
             for (int rb = 0; rb < RB; ++rb) seg_mma(wq[rb][o * QS], wsc[rb][o], xv, acc[rb]);
         }
-        skinny_epilogue<GATED, RB>(acc, s_red, C, N, r0, mrows, n_tile);
+        skinny_epilogue<GATED, RB, PACKED>(acc, s_red, C, N, r0, mrows, n_tile);
     }
 }
 
@@ -770,10 +782,11 @@ __global__ __launch_bounds__(256, mx_grid<FMT>()) void gemm_skinny_gateup_dispat
     __shared__ int s_rows[kFusedDispatchMax];
     __shared__ int s_start[kMaxExperts + 1];
     __shared__ int s_wave[4];
-    __shared__ float s_red[4 * 16 * 17];
+    constexpr int RB = kMxGatedRB;
+    __shared__ float s_red[4 * 16 * RB * 17];
     fused_dispatch(ids, ntok, T, topk, E, offsets, row_src, token_row, s_off, s_wc, s_rows, s_wave);
-    skinny_tiles_mx<FMT, true, 1, PACKED>(x, s_rows, topk, s_off, Wq, Ws, C, E, Kd, N, s_start,
-                                          s_wave, s_red);
+    skinny_tiles_mx<FMT, true, RB, PACKED>(x, s_rows, topk, s_off, Wq, Ws, C, E, Kd, N, s_start,
+                                           s_wave, s_red);
 }
 
 // Down GEMM + combine for tiny batches on MX weights: down_combine_tiny_kernel
@@ -1537,7 +1550,7 @@ static void launch_skinny_mx(bool gated, int grid, const uint16_t* A, const int3
                              const uint8_t* Ws, uint16_t* C, int E, int Kd, int N,
                              hipStream_t st) {
     if (gated)
-        hipLaunchKernelGGL((gemm_skinny_mx_kernel<FMT, true, 1, P>), dim3(grid), dim3(256), 0, st,
+        hipLaunchKernelGGL((gemm_skinny_mx_kernel<FMT, true, kMxGatedRB, P>), dim3(grid), dim3(256), 0, st,
                            A, row_src, topk, offsets, Wq, Ws, C, E, Kd, N);
     else if (N % 32 == 0)
         hipLaunchKernelGGL((gemm_skinny_mx_kernel<FMT, false, 2, P>), dim3(grid), dim3(256), 0, st,
