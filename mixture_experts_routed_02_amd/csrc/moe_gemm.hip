@@ -108,14 +108,15 @@ __device__ __forceinline__ void skinny_epilogue(const moe_f32x4 (&acc)[RB], floa
         for (int i = 0; i < 4; ++i) red(wave, rb * 16 + 4 * lg + i, li) = acc[rb][i];
     __syncthreads();
     if (GATED) {
-        if (tid < 16 * COLS) {
-            const int m = tid / COLS, c = tid % COLS;
+        for (int o = tid; o < 16 * COLS; o += 256) {
+            const int m = o / COLS, c = o % COLS;
             if (m < mrows) {
                 float g = 0.f, u = 0.f;
-                // 32-row gated tiles of packed weights hold two 16-row groups
-                // (8 gate + 8 up rows each); otherwise gate rows come first
-                const int rg = (RB == 2 && PACKED_GROUPS) ? ((c & 8) << 1) | (c & 7) : c;
-                const int ru = (RB == 2 && PACKED_GROUPS) ? rg + 8 : COLS + c;
+                // packed weights: the tile's 16-row groups each hold 8 gate
+                // rows and the matching 8 up rows; row-major: the tile's gate
+                // rows come first, then the matching up rows
+                const int rg = PACKED_GROUPS ? (c >> 3) * 16 + (c & 7) : c;
+                const int ru = PACKED_GROUPS ? rg + 8 : COLS + c;
 #pragma unroll
                 for (int w = 0; w < 4; ++w) { g += red(w, rg, m); u += red(w, ru, m); }
                 C[(size_t)(r0 + m) * N + n_tile * COLS + c] = moe_f32_to_bf16(silu_f32(g) * u);
@@ -597,25 +598,32 @@ struct MxFmt<4> {
 // Tile, block size (segments) and grid of the MX skinny kernels.  Gated
 // (gate-up) tiles are 32 weight rows (RB = 2: 16 gate + 16 up rows, or two
 // packed 16-row groups), so one set of token registers feeds twice the code
-// bytes; plain tiles are 32 rows too when N allows.  A block is 4 segments
-// (MXFP8: 8 KB of codes per wave and buffer, 2 workgroups per CU) or 2
-// (MXFP4: a segment carries twice the token values; 4 KB of codes per wave
-// and buffer, 3 workgroups per CU).  Measured, interleaved and bit-identical,
-// on the 96-expert decode shapes at T = 8 .. 128: 32-row gated tiles took
-// MXFP4 15-20% and MXFP8 6-12% below 16-row gated tiles (MXFP4 2-segment
-// blocks at 4 x CUs, MXFP8 4-segment blocks at 3 x CUs); 3-segment blocks
-// (both formats) and 4-segment MXFP4 blocks at 2 x CUs were slower, and
-// MXFP8 at 3 x CUs (spilling) no faster.  T = 1 moves by -4% (MXFP4) and
-// +-2% (MXFP8).  Earlier: 6-segment MXFP8 blocks at 2 x CUs no faster than
-// 4; loading the token operand only in the lanes that hold valid rows
+// bytes; plain tiles are 32 rows too when N allows.  From T*K = 128 on,
+// MXFP4 gated tiles are 64 rows (RB = 4, 2 workgroups per CU): a segment
+// of MXFP4 codes needs twice the token bytes of MXFP8, and 64 rows halve
+// them per code byte; below that count 64-row tiles leave CUs idle.  A block
+// is 4 segments (MXFP8: 8 KB of codes per wave and buffer at RB = 2, 2
+// workgroups per CU) or 2 (MXFP4; 3 workgroups per CU at RB = 2).
+// Measured, interleaved and bit-identical, on the 96-expert decode shapes at
+// T = 8 .. 128: 32-row gated tiles took MXFP4 15-20% and MXFP8 6-12% below
+// 16-row gated tiles (MXFP4 2-segment blocks at 4 x CUs, MXFP8 4-segment
+// blocks at 3 x CUs); MXFP4 64-row tiles another 4-6% at T = 32 and 128
+// (0% at T = 8, 3-5% slower at T = 1, hence the threshold).  Slower or no
+// faster: 3-segment blocks (both formats), 4-segment MXFP4 blocks at 2 x
+// CUs, MXFP8 at 3 x CUs (spills), 64-row MXFP8 tiles with 2-segment blocks
+// (1-17% slower).  Earlier: 6-segment MXFP8 blocks at 2 x CUs no faster
+// than 4; loading the token operand only in the lanes that hold valid rows
 // (exec-masked) 0-2% slower on all three formats.  The grid factor is also
 // the kernels' waves-per-SIMD bound (__launch_bounds__), so the compiler
 // keeps the whole persistent grid resident.
 template <int FMT>
 constexpr int mx_segs() { return FMT == 8 ? 4 : 2; }
-template <int FMT>
-constexpr int mx_grid() { return FMT == 8 ? 2 : 3; }
-constexpr int kMxGatedRB = 2;
+template <int FMT, int RB>
+constexpr int mx_grid() { return RB == 4 || FMT == 8 ? 2 : 3; }
+// MXFP4 gate-up tiles are 64 weight rows (RB = 4) from this many assignments
+// (T*K) on, 32 rows below it, where 64-row tiles would leave CUs idle
+constexpr int kMxWideMinAssign = 128;
+inline bool mx_wide(int fmt, const Shape& s) { return fmt == 4 && s.T * s.K >= kMxWideMinAssign; }
 
 // Skinny tiles on MX weights: codes Wq [E, rows, Kd * FMT / 8 bytes], scales
 // Ws [E, rows, Kd / 32].  Same tiles, tile order, k split over the waves (in
@@ -628,7 +636,7 @@ __device__ __forceinline__ void skinny_tiles_mx(const uint16_t* __restrict__ A, 
                                                 const uint8_t* __restrict__ Ws,
                                                 uint16_t* __restrict__ C, int E, int Kd, int N,
                                                 int* s_start, int* s_wave, float* s_red) {
-    static_assert(RB == 1 || RB == 2, "tile rows");
+    static_assert(RB == 1 || RB == 2 || (GATED && RB == 4), "tile rows");
     typedef MxFmt<FMT> F;
     typedef typename F::scale_t scale_t;
     constexpr int BM = 16;
@@ -758,7 +766,7 @@ __device__ __forceinline__ void skinny_tiles_mx(const uint16_t* __restrict__ A, 
 }
 
 template <int FMT, bool GATED, int RB, bool PACKED = false>
-__global__ __launch_bounds__(256, mx_grid<FMT>()) void gemm_skinny_mx_kernel(
+__global__ __launch_bounds__(256, (mx_grid<FMT, RB>())) void gemm_skinny_mx_kernel(
     const uint16_t* __restrict__ A, const int32_t* __restrict__ row_src, int topk,
     const int32_t* __restrict__ offsets, const uint8_t* __restrict__ Wq,
     const uint8_t* __restrict__ Ws, uint16_t* __restrict__ C, int E, int Kd, int N) {
@@ -770,8 +778,8 @@ __global__ __launch_bounds__(256, mx_grid<FMT>()) void gemm_skinny_mx_kernel(
 }
 
 // Gate-up on MX weights with the dispatch inside (T*K <= kFusedDispatchMax).
-template <int FMT, bool PACKED = false>
-__global__ __launch_bounds__(256, mx_grid<FMT>()) void gemm_skinny_gateup_dispatch_mx_kernel(
+template <int FMT, bool PACKED, int RB>
+__global__ __launch_bounds__(256, (mx_grid<FMT, RB>())) void gemm_skinny_gateup_dispatch_mx_kernel(
     const uint16_t* __restrict__ x, const int32_t* __restrict__ ids,
     const int32_t* __restrict__ ntok, int T, int topk, int E, int32_t* __restrict__ offsets,
     int32_t* __restrict__ row_src, int32_t* __restrict__ token_row,
@@ -782,7 +790,6 @@ __global__ __launch_bounds__(256, mx_grid<FMT>()) void gemm_skinny_gateup_dispat
     __shared__ int s_rows[kFusedDispatchMax];
     __shared__ int s_start[kMaxExperts + 1];
     __shared__ int s_wave[4];
-    constexpr int RB = kMxGatedRB;
     __shared__ float s_red[4 * 16 * RB * 17];
     fused_dispatch(ids, ntok, T, topk, E, offsets, row_src, token_row, s_off, s_wc, s_rows, s_wave);
     skinny_tiles_mx<FMT, true, RB, PACKED>(x, s_rows, topk, s_off, Wq, Ws, C, E, Kd, N, s_start,
@@ -1507,9 +1514,17 @@ static void launch_fused_mx(const Shape& s, const uint16_t* x, const int32_t* id
                             const int32_t* ntok, int32_t* offsets, int32_t* row_src,
                             int32_t* token_row, const uint8_t* Wq, const uint8_t* Ws, uint16_t* h,
                             hipStream_t st) {
-    hipLaunchKernelGGL((gemm_skinny_gateup_dispatch_mx_kernel<FMT, P>), dim3(mx_grid<FMT>() * kNumCUs),
-                       dim3(256), 0, st, x, ids, ntok, s.T, s.K, s.E, offsets, row_src, token_row,
-                       Wq, Ws, h, s.H, s.I);
+    if constexpr (FMT == 4) {
+        if (mx_wide(FMT, s)) {
+            hipLaunchKernelGGL((gemm_skinny_gateup_dispatch_mx_kernel<FMT, P, 4>),
+                               dim3(mx_grid<FMT, 4>() * kNumCUs), dim3(256), 0, st, x, ids, ntok,
+                               s.T, s.K, s.E, offsets, row_src, token_row, Wq, Ws, h, s.H, s.I);
+            return;
+        }
+    }
+    hipLaunchKernelGGL((gemm_skinny_gateup_dispatch_mx_kernel<FMT, P, 2>),
+                       dim3(mx_grid<FMT, 2>() * kNumCUs), dim3(256), 0, st, x, ids, ntok, s.T,
+                       s.K, s.E, offsets, row_src, token_row, Wq, Ws, h, s.H, s.I);
 }
 
 hipError_t launch_gateup_fused_dispatch_mx(const Shape& s, int fmt, const uint16_t* x,
@@ -1545,34 +1560,44 @@ hipError_t launch_down_combine_tiny_mx(const Shape& s, int fmt, const uint16_t* 
 }
 
 template <int FMT, bool P>
-static void launch_skinny_mx(bool gated, int grid, const uint16_t* A, const int32_t* row_src,
+static void launch_skinny_mx(bool gated, bool wide, const uint16_t* A, const int32_t* row_src,
                              int topk, const int32_t* offsets, const uint8_t* Wq,
                              const uint8_t* Ws, uint16_t* C, int E, int Kd, int N,
                              hipStream_t st) {
-    if (gated)
-        hipLaunchKernelGGL((gemm_skinny_mx_kernel<FMT, true, kMxGatedRB, P>), dim3(grid), dim3(256), 0, st,
-                           A, row_src, topk, offsets, Wq, Ws, C, E, Kd, N);
-    else if (N % 32 == 0)
-        hipLaunchKernelGGL((gemm_skinny_mx_kernel<FMT, false, 2, P>), dim3(grid), dim3(256), 0, st,
-                           A, row_src, topk, offsets, Wq, Ws, C, E, Kd, N);
-    else
-        hipLaunchKernelGGL((gemm_skinny_mx_kernel<FMT, false, 1, P>), dim3(grid), dim3(256), 0, st,
-                           A, row_src, topk, offsets, Wq, Ws, C, E, Kd, N);
+    const dim3 block(256), grid2(mx_grid<FMT, 2>() * kNumCUs), grid1(mx_grid<FMT, 1>() * kNumCUs);
+    if (gated) {
+        if constexpr (FMT == 4) {
+            if (wide) {
+                hipLaunchKernelGGL((gemm_skinny_mx_kernel<FMT, true, 4, P>),
+                                   dim3(mx_grid<FMT, 4>() * kNumCUs), block, 0, st, A, row_src,
+                                   topk, offsets, Wq, Ws, C, E, Kd, N);
+                return;
+            }
+        }
+        hipLaunchKernelGGL((gemm_skinny_mx_kernel<FMT, true, 2, P>), grid2, block, 0, st, A,
+                           row_src, topk, offsets, Wq, Ws, C, E, Kd, N);
+    } else if (N % 32 == 0) {
+        hipLaunchKernelGGL((gemm_skinny_mx_kernel<FMT, false, 2, P>), grid2, block, 0, st, A,
+                           row_src, topk, offsets, Wq, Ws, C, E, Kd, N);
+    } else {
+        hipLaunchKernelGGL((gemm_skinny_mx_kernel<FMT, false, 1, P>), grid1, block, 0, st, A,
+                           row_src, topk, offsets, Wq, Ws, C, E, Kd, N);
+    }
 }
 
 hipError_t launch_grouped_gemm_mx(const Shape& s, int fmt, bool gated, const uint16_t* A,
                                   const int32_t* row_src, int topk, const int32_t* offsets,
                                   const uint8_t* Wq, const uint8_t* Ws, uint16_t* C, int Kd, int N,
                                   hipStream_t st, bool packed) {
-    const int g = (fmt == 8 ? mx_grid<8>() : mx_grid<4>()) * kNumCUs;
+    const bool wide = mx_wide(fmt, s);
     if (fmt == 8 && packed)
-        launch_skinny_mx<8, true>(gated, g, A, row_src, topk, offsets, Wq, Ws, C, s.E, Kd, N, st);
+        launch_skinny_mx<8, true>(gated, wide, A, row_src, topk, offsets, Wq, Ws, C, s.E, Kd, N, st);
     else if (fmt == 8)
-        launch_skinny_mx<8, false>(gated, g, A, row_src, topk, offsets, Wq, Ws, C, s.E, Kd, N, st);
+        launch_skinny_mx<8, false>(gated, wide, A, row_src, topk, offsets, Wq, Ws, C, s.E, Kd, N, st);
     else if (packed)
-        launch_skinny_mx<4, true>(gated, g, A, row_src, topk, offsets, Wq, Ws, C, s.E, Kd, N, st);
+        launch_skinny_mx<4, true>(gated, wide, A, row_src, topk, offsets, Wq, Ws, C, s.E, Kd, N, st);
     else
-        launch_skinny_mx<4, false>(gated, g, A, row_src, topk, offsets, Wq, Ws, C, s.E, Kd, N, st);
+        launch_skinny_mx<4, false>(gated, wide, A, row_src, topk, offsets, Wq, Ws, C, s.E, Kd, N, st);
     return hipGetLastError();
 }
 
