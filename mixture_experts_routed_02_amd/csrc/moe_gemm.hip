@@ -89,10 +89,13 @@ __device__ __forceinline__ int find_expert(const int* s_start, int E, int tile) 
 __device__ __forceinline__ moe_bf16x8 stream_load(const moe_bf16x8* p) { return *p; }
 
 // Tile epilogue of the skinny kernels: the four waves' partial sums of the
-// tile (accumulator i of lane l = weight row 4*(l/16)+i, token row l%16) are
-// added in wave order through LDS; gated tiles write bf16(silu(g) * u) for
-// their 8 columns, plain tiles bf16(y) for their 16*RB columns.  Ends with a
-// barrier, so s_red is free again.
+// tile (accumulator i of lane l in block rb = tile row 16*rb + 4*(l/16) + i,
+// token row l%16) are added in wave order through LDS; gated tiles write
+// bf16(silu(g) * u) for their 8*RB columns, plain tiles bf16(y) for their
+// 16*RB columns.  PACKED_GROUPS: the tile's 16-row blocks are packed groups
+// of 8 gate rows and the matching 8 up rows (else a gated tile holds its
+// gate rows first, then the matching up rows).  Ends with a barrier, so
+// s_red is free again.
 template <bool GATED, int RB, bool PACKED_GROUPS = false>
 __device__ __forceinline__ void skinny_epilogue(const moe_f32x4 (&acc)[RB], float* s_red,
                                                 uint16_t* __restrict__ C, int N, int r0,
@@ -626,9 +629,12 @@ constexpr int kMxWideMinAssign = 128;
 inline bool mx_wide(int fmt, const Shape& s) { return fmt == 4 && s.T * s.K >= kMxWideMinAssign; }
 
 // Skinny tiles on MX weights: codes Wq [E, rows, Kd * FMT / 8 bytes], scales
-// Ws [E, rows, Kd / 32].  Same tiles, tile order, k split over the waves (in
-// segments), double-buffered blocks and epilogue as skinny_tiles; a block is
-// US segments.
+// Ws [E, rows, Kd / 32].  Same tile order, k split over the waves (in
+// segments), double-buffered blocks and epilogue as skinny_tiles, with RB
+// 16-row weight blocks per tile (gated: 2 or 4, plain: 1 or 2); a block is
+// US segments.  PACKED: block rb of a tile is 16-row pack group
+// n_tile * RB + rb, whose scales are read from the row-major scale rows of
+// the same weight rows.
 template <int FMT, bool GATED, int RB, bool PACKED = false>
 __device__ __forceinline__ void skinny_tiles_mx(const uint16_t* __restrict__ A, const int32_t* rows,
                                                 int topk, const int32_t* offsets,
