@@ -20,6 +20,16 @@ touch fewer experts (or none) count their time.  static_capacity adds
 T_i ~ U{1..T}, with median/p10/p90 µs and the per-replay fraction of the
 binding roof.
 
+With the default workload the same line also carries `per_config`: every
+other full-size workload measured in the same run, each with µs/layer, its
+binding-roof fraction (and MFMA / HBM fractions beside it) and the gate-up
+kernel's own roofline: the 96-of-384 decode shares T = 1, 8, 32, 128 (cold:
+L2/MALL evicted before each step, 32 routing draws cycled), the prefill
+shares T = 2048, 8192 with uniform routing (seeds 0-2) and Zipf s = 1.2
+routing (seeds 0-4, reported per seed), and the static-capacity layer (50
+HIP-graph replays with a device token count T_i ~ U{1..2048}, and the full
+buffer called eagerly).  --no-per-config leaves it out.
+
 Algorithmic work (what the method must do, not what an implementation moves):
   F = 6*H*I*R flop, R = valid dispatched rows (2*H*2I gate-up + 2*I*H down per row)
   B = 6*H*I*n_touched + 2*H*T (x) + 2*H*T (out) + 8*T*K (ids, weights) bytes
@@ -147,6 +157,202 @@ def cpu_baseline(inp_host, wgu, wd, cfg, budget_tokens: int, mx=None, fmt="bf16"
             "host": {"nproc": os.cpu_count(), "cpu_model": model}}
 
 
+# ---------------------------------------------------------------------------
+# per_config: the other full-size workloads, measured in the same run
+# ---------------------------------------------------------------------------
+PER_CONFIG = (
+    ("ep_decode_T1", "decode"), ("ep_decode_T8", "decode"), ("ep_decode_T32", "decode"),
+    ("ep_decode_T128", "decode"),
+    ("ep_prefill_T2048", "prefill"), ("ep_prefill_T8192", "prefill"),
+    ("ep_prefill_T2048_zipf", "prefill"), ("ep_prefill_T8192_zipf", "prefill"),
+    ("static_capacity", "static"),
+)
+DECODE_DRAWS = 32          # routing draws (seeds 1000..1031), one per step
+PREFILL_SEEDS = {"ep_uniform": (0, 1, 2), "ep_zipf": (0, 1, 2, 3, 4)}
+PREFILL_STEPS = 10         # timed calls per seed
+
+
+def _layer_work(ids_h, E, H, I, K, t_valid):
+    """(F, B, R, n_touched): algorithmic flop and bytes of one layer call."""
+    import torch
+    v = ids_h[:t_valid]
+    v = v[(v >= 0) & (v < E)]
+    r = int(v.numel())
+    n_t = int(torch.unique(v).numel()) if r else 0
+    return 6.0 * H * I * r, 6.0 * H * I * n_t + 4.0 * H * t_valid + 8.0 * t_valid * K, r, n_t
+
+
+def _roof(F, B, sec):
+    mf = F / sec / 1e12 / PEAK_BF16_TFLOPS
+    hf = B / sec / 1e9 / PEAK_HBM_GBPS
+    binding = "mfma" if F / max(B, 1.0) >= RIDGE else "hbm"
+    return {"binding": binding, "binding_frac": mf if binding == "mfma" else hf,
+            "mfma_frac": mf, "hbm_frac": hf}
+
+
+def per_config_sweep(dev, kernel_reps: int):
+    """Measure every workload of PER_CONFIG (see the module docstring)."""
+    import torch
+
+    import mixture_experts_routed_02_amd as moe
+    from mixture_experts_routed_02_amd import ops
+    import workloads as W
+
+    stream = torch.cuda.current_stream(dev)
+    scratch = torch.ones((1 << 29,), dtype=torch.float16, device=dev)   # 1 GiB
+
+    def evict():
+        scratch.max()
+
+    def ev():
+        return torch.cuda.Event(enable_timing=True)
+
+    def timed_us(call, reps, cold):
+        """Event-timed µs per call (mean); short calls wait behind a spin so
+        that the events see the GPU's time, not the host's."""
+        call()
+        torch.cuda.synchronize()
+        evs = [(ev(), ev()) for _ in range(reps)]
+        torch.cuda._sleep(5_000_000)
+        for a, b in evs:
+            if cold:
+                evict()
+            a.record(stream)
+            call()
+            b.record(stream)
+        torch.cuda.synchronize()
+        return statistics.fmean(a.elapsed_time(b) for a, b in evs) * 1e3
+
+    out_all = {}
+    weights = {}
+    for name, kind in PER_CONFIG:
+        cfg = W.CONFIGS[name]
+        T, K, E, H, I = cfg.num_tokens, cfg.top_k, cfg.num_experts, cfg.hidden, cfg.intermediate
+        key = (E, H, I)
+        if key not in weights:
+            weights.clear()
+            torch.cuda.empty_cache()
+            weights[key] = W.make_weights(cfg, 0, dev)
+        wgu, wd = weights[key]
+        p = moe.problem(T, K, E, H, I, cfg.capacity)
+        ws = ops.make_workspace(p, dev)
+        out = torch.empty((T, H), dtype=torch.bfloat16, device=dev)
+        off = torch.empty((E + 1,), dtype=torch.int32, device=dev)
+        if kind == "decode":
+            seeds = [1000 + d for d in range(DECODE_DRAWS)]
+        elif kind == "prefill":
+            seeds = list(PREFILL_SEEDS[cfg.routing])
+        else:
+            seeds = [0]
+        routes = []
+        for sd in seeds:
+            ids_h, w_h = W.make_routing(cfg, sd)
+            x_d = W.make_x(cfg, sd if kind == "prefill" else 0).to(dev)
+            routes.append((sd, ids_h, x_d, ids_h.to(dev), w_h.to(dev)))
+        cold = kind == "decode"
+
+        def call(i, nt=None):
+            _, _, x_d, ids_d, w_d = routes[i % len(routes)]
+            ops.forward(p, x_d, ids_d, w_d, wgu, wd, num_tokens_dev=nt, expert_offsets=off,
+                        out=out, workspace=ws)
+
+        steps = len(routes) * (1 if kind == "decode" else PREFILL_STEPS)
+        for i in range(max(len(routes), 5)):
+            call(i)
+        torch.cuda.synchronize()
+        evs = [(ev(), ev()) for _ in range(steps)]
+        for i, (a, b) in enumerate(evs):
+            if cold:
+                evict()
+            a.record(stream)
+            call(i)
+            b.record(stream)
+        torch.cuda.synchronize()
+        us = [a.elapsed_time(b) * 1e3 for a, b in evs]
+        work = [_layer_work(r[1], E, H, I, K, T) for r in routes]
+        F = sum(work[i % len(routes)][0] for i in range(steps))
+        B = sum(work[i % len(routes)][1] for i in range(steps))
+        sec = sum(us) * 1e-6
+        ent = {"us_per_layer": statistics.fmean(us), "us_median": statistics.median(us),
+               "tflops": F / sec / 1e12, "hbm_gbps": B / sec / 1e9, **_roof(F, B, sec),
+               "steps": steps, "timing": ("cold: L2/MALL evicted before each step; "
+                                          f"{len(routes)} routing draws cycled" if cold else
+                                          f"back-to-back, {PREFILL_STEPS} calls per seed, "
+                                          f"seeds {seeds}"),
+               "valid_rows_mean": statistics.fmean(w_[2] for w_ in work),
+               "experts_touched_mean": statistics.fmean(w_[3] for w_ in work)}
+        if kind == "prefill":
+            per_seed = []
+            for j, (sd, ids_h, _, _, _) in enumerate(routes):
+                us_j = [us[i] for i in range(steps) if i % len(routes) == j]
+                F_j, B_j, R_j, n_j = work[j]
+                v = ids_h[(ids_h >= 0)]
+                cnt = torch.bincount(v.reshape(-1).long(), minlength=cfg.pool)
+                ent_j = {"seed": sd, "us_per_layer": statistics.fmean(us_j),
+                         **_roof(F_j, B_j, statistics.fmean(us_j) * 1e-6),
+                         "valid_rows": R_j, "experts_touched": n_j,
+                         "max_rows_per_local_expert": int(cnt[:E].max())}
+                if cfg.routing == "ep_zipf":
+                    ent_j["most_popular_expert_is_local"] = bool(int(cnt.argmax()) < E)
+                per_seed.append(ent_j)
+            ent["per_seed"] = per_seed
+        # the dominant kernel alone: gate-up grouped GEMM + SiLU epilogue (first route)
+        _, ids_h0, x0, ids0, _ = routes[0]
+        x_disp, off2, _, _ = ops.dispatch(p, x0, ids0)
+        hbuf = torch.empty((p.capacity or T * K, I), dtype=torch.bfloat16, device=dev)
+        gu_us = timed_us(lambda: ops.gate_up(p, x_disp, off2, wgu, h=hbuf), kernel_reps, cold)
+        _, _, R0, n0 = work[0]
+        F_gu = 4.0 * H * I * R0
+        B_gu = 4.0 * H * I * n0 + 2.0 * H * R0 + 2.0 * I * R0
+        if F_gu / max(B_gu, 1.0) >= RIDGE:
+            gu = {"bound": "mfma", "achieved": F_gu / (gu_us * 1e-6) / 1e12, "unit": "TFLOP/s",
+                  "peak": PEAK_BF16_TFLOPS}
+        else:
+            gu = {"bound": "hbm", "achieved": B_gu / (gu_us * 1e-6) / 1e9, "unit": "GB/s",
+                  "peak": PEAK_HBM_GBPS}
+        gu.update({"frac": gu["achieved"] / gu["peak"], "avg_launch_us": gu_us,
+                   "algorithmic_flop": F_gu, "algorithmic_bytes": B_gu,
+                   "route": f"seed {routes[0][0]}", "cold": cold})
+        ent["gate_up"] = gu
+        del x_disp, hbuf
+        if kind == "static":
+            # HIP-graph replays with a device token count T_i ~ U{1..T}
+            _, ids_h, x_d, ids_d, w_d = routes[0]
+            ntok = torch.full((1,), T, dtype=torch.int32, device=dev)
+            g = ops.MoEGraph(p, x_d, ids_d, w_d, wgu, wd, num_tokens_dev=ntok, expert_offsets=off,
+                             out=out, workspace=ws)
+            t_i = W.make_static_token_counts(0, W.STATIC_REPLAYS, T)
+            for _ in range(3):
+                g.launch()
+            torch.cuda.synchronize()
+            rev = [(ev(), ev()) for _ in t_i]
+            for (a, b), tv in zip(rev, t_i):
+                ntok.fill_(tv)
+                a.record(stream)
+                g.launch()
+                b.record(stream)
+            torch.cuda.synchronize()
+            rus = [a.elapsed_time(b) * 1e3 for a, b in rev]
+            fr = []
+            for tv, u in zip(t_i, rus):
+                f_i, b_i, _, _ = _layer_work(ids_h, E, H, I, K, tv)
+                fr.append(max(f_i / (PEAK_BF16_TFLOPS * 1e12), b_i / (PEAK_HBM_GBPS * 1e9))
+                          / (u * 1e-6))
+            q = statistics.quantiles(rus, n=10, method="inclusive")
+            ent["replays"] = {"n": len(t_i), "tokens_min": min(t_i), "tokens_max": max(t_i),
+                              "us_median": statistics.median(rus), "us_p10": q[0],
+                              "us_p90": q[8], "binding_frac_median": statistics.median(fr),
+                              "binding_frac_min": min(fr), "binding_frac_max": max(fr)}
+            g.close()
+        ent["workload"] = describe(cfg)
+        out_all[name] = ent
+        del routes, ws, out, off
+        torch.cuda.synchronize()
+    del weights, scratch
+    torch.cuda.empty_cache()
+    return out_all
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawTextHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -177,6 +383,8 @@ def main():
                     help="expert weights (bf16) or codes (MX) in the skinny pack layout, packed "
                          "on the device before timing; the skinny plan serves every batch size")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-per-config", action="store_true",
+                    help="leave out the per_config sweep over the other workloads")
     args = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -464,6 +672,13 @@ def main():
         result["cpu_baseline"] = cpu_baseline({"x": x_h, "topk_ids": ids_h, "topk_weights": w_h},
                                               wgu, wd, cfg, budget,
                                               (qgu, sgu, qd, sd) if mx else None, args.weights)
+    sweep = (cfg.name == "mixtral" and not args.no_per_config and not mx and not packed
+             and not args.graph and args.hint == 0)
+    if sweep:
+        del x_disp, hbuf, x_disp_s, y_s, out_s, wgu, wd, ws, out, scratch
+        torch.cuda.synchronize()
+        torch.cuda.empty_cache()
+        result["per_config"] = per_config_sweep(dev, args.kernel_reps)
     print(json.dumps(result), flush=True)
 
 

@@ -49,7 +49,7 @@ import numpy as np
 __all__ = [
     "bf16_to_f64", "f64_to_bf16_bits", "router_topk", "dispatch", "silu", "expert_mlp",
     "expert_mlp_f64",
-    "expert_compute", "combine", "forward", "forward_tokens",
+    "expert_compute", "combine", "forward", "forward_tokens", "forward_tokens_widened",
     "e4m3_to_f64", "e8m0_to_f64", "mxfp8_quantize", "mxfp8_to_f64",
     "forward_tokens_mxfp8", "forward_mxfp8", "e2m1_to_f64", "mxfp4_quantize", "mxfp4_to_f64",
     "forward_tokens_mxfp4", "forward_mxfp4",
@@ -237,21 +237,31 @@ def combine(y_rows, token_row, topk_weights, num_valid_tokens: int | None = None
 # Whole layer
 # ---------------------------------------------------------------------------
 def forward_tokens(x, topk_ids, topk_weights, w_gateup, w_down, tokens,
-                   num_valid_tokens: int | None = None):
+                   num_valid_tokens: int | None = None, workers: int = 1):
     """out[t,:] for the listed tokens only (float64 [len(tokens), H]), straight
     from the definition: sum over the token's valid assignments of
     w[t,j] * y(ids[t,j], x[t]).  x: bf16 bits [T, H]; w_gateup: bf16 bits
     [E, 2I, H]; w_down: bf16 bits [E, H, I] (any object indexable by expert
-    that yields such arrays)."""
-    return _forward_tokens_widened(
+    that yields such arrays).  workers > 1 evaluates the experts' MLPs on that
+    many threads; the result is the same to the bit (see
+    forward_tokens_widened)."""
+    return forward_tokens_widened(
         x, topk_ids, topk_weights, len(w_gateup),
         lambda e: (bf16_to_f64(np.asarray(w_gateup[e])), bf16_to_f64(np.asarray(w_down[e]))),
-        tokens, num_valid_tokens)
+        tokens, num_valid_tokens, workers)
 
 
-def _forward_tokens_widened(x, topk_ids, topk_weights, E, widen, tokens, num_valid_tokens):
+def forward_tokens_widened(x, topk_ids, topk_weights, E, widen, tokens,
+                           num_valid_tokens: int | None = None, workers: int = 1):
     """forward_tokens with the expert weights supplied as float64 by
-    widen(e) -> (W_gateup[e] [2I, H], W_down[e] [H, I])."""
+    widen(e) -> (W_gateup[e] [2I, H], W_down[e] [H, I]) (for instance the
+    exact widening bf16_to_f64 of the bf16 weights, computed once and reused
+    across calls).
+
+    workers only changes where the per-expert products run: each expert's
+    y rows are the same library calls on the same operands either way, and
+    they are added into out in the same (increasing expert) order, so the
+    result does not depend on it."""
     ids = np.asarray(topk_ids, dtype=np.int64)
     wts = np.asarray(topk_weights, dtype=np.float32).astype(np.float64)
     T, K = ids.shape
@@ -269,19 +279,39 @@ def _forward_tokens_widened(x, topk_ids, topk_weights, E, widen, tokens, num_val
             e = ids[t, j]
             if 0 <= e < E:
                 pairs.setdefault(int(e), []).append((i, int(t), j))
-    for e, lst in sorted(pairs.items()):
+    items = sorted(pairs.items())
+
+    def expert_rows(item):
+        e, lst = item
         xr = bf16_to_f64(np.asarray(x)[[t for _, t, _ in lst]])
-        y = expert_mlp_f64(xr, *widen(e))
+        return expert_mlp_f64(xr, *widen(e))
+
+    if workers > 1 and len(items) > 1:
+        import contextlib
+        from concurrent.futures import ThreadPoolExecutor
+        try:
+            from threadpoolctl import threadpool_limits
+            one_blas_thread = threadpool_limits(1)
+        except ImportError:  # pragma: no cover
+            one_blas_thread = contextlib.nullcontext()
+        # one BLAS thread per worker: the per-expert products are small, and a
+        # BLAS thread pool per worker oversubscribes the cores many times over
+        with one_blas_thread, ThreadPoolExecutor(max_workers=workers) as pool:
+            ys = list(pool.map(expert_rows, items))
+    else:
+        ys = [expert_rows(it) for it in items]
+    for (e, lst), y in zip(items, ys):
         for (i, t, j), yrow in zip(lst, y):
             out[i] += wts[t, j] * yrow
     return out
 
 
-def forward(x, topk_ids, topk_weights, w_gateup, w_down, num_valid_tokens: int | None = None):
+def forward(x, topk_ids, topk_weights, w_gateup, w_down, num_valid_tokens: int | None = None,
+            workers: int = 1):
     """The whole layer for every token: float64 [T, H]; rows t >= T_v are 0."""
     T = np.asarray(topk_ids).shape[0]
     return forward_tokens(x, topk_ids, topk_weights, w_gateup, w_down, np.arange(T),
-                          num_valid_tokens)
+                          num_valid_tokens, workers)
 
 
 # ---------------------------------------------------------------------------
@@ -392,23 +422,23 @@ def mxfp8_to_f64(codes, scales) -> np.ndarray:
 
 
 def forward_tokens_mxfp8(x, topk_ids, topk_weights, wgu_codes, wgu_scales, wd_codes, wd_scales,
-                         tokens, num_valid_tokens: int | None = None):
+                         tokens, num_valid_tokens: int | None = None, workers: int = 1):
     """forward_tokens with MXFP8 expert weights: codes [E, 2I, H] / scales
     [E, 2I, H/32] for W_gateup, codes [E, H, I] / scales [E, H, I/32] for
     W_down (any objects indexable by expert), dequantized exactly to float64
     and then the same layer definition."""
-    return _forward_tokens_widened(
+    return forward_tokens_widened(
         x, topk_ids, topk_weights, len(wgu_codes),
         lambda e: (mxfp8_to_f64(wgu_codes[e], wgu_scales[e]), mxfp8_to_f64(wd_codes[e], wd_scales[e])),
-        tokens, num_valid_tokens)
+        tokens, num_valid_tokens, workers)
 
 
 def forward_mxfp8(x, topk_ids, topk_weights, wgu_codes, wgu_scales, wd_codes, wd_scales,
-                  num_valid_tokens: int | None = None):
+                  num_valid_tokens: int | None = None, workers: int = 1):
     """The whole MXFP8-weight layer for every token: float64 [T, H]."""
     T = np.asarray(topk_ids).shape[0]
     return forward_tokens_mxfp8(x, topk_ids, topk_weights, wgu_codes, wgu_scales, wd_codes,
-                                wd_scales, np.arange(T), num_valid_tokens)
+                                wd_scales, np.arange(T), num_valid_tokens, workers)
 
 
 # ---------------------------------------------------------------------------
@@ -501,19 +531,19 @@ def mxfp4_to_f64(packed, scales) -> np.ndarray:
 
 
 def forward_tokens_mxfp4(x, topk_ids, topk_weights, wgu_packed, wgu_scales, wd_packed, wd_scales,
-                         tokens, num_valid_tokens: int | None = None):
+                         tokens, num_valid_tokens: int | None = None, workers: int = 1):
     """forward_tokens with MXFP4 expert weights (packed codes [E, 2I, H/2] /
     scales [E, 2I, H/32], packed codes [E, H, I/2] / scales [E, H, I/32]),
     dequantized exactly to float64, then the same layer definition."""
-    return _forward_tokens_widened(
+    return forward_tokens_widened(
         x, topk_ids, topk_weights, len(wgu_packed),
         lambda e: (mxfp4_to_f64(wgu_packed[e], wgu_scales[e]), mxfp4_to_f64(wd_packed[e], wd_scales[e])),
-        tokens, num_valid_tokens)
+        tokens, num_valid_tokens, workers)
 
 
 def forward_mxfp4(x, topk_ids, topk_weights, wgu_packed, wgu_scales, wd_packed, wd_scales,
-                  num_valid_tokens: int | None = None):
+                  num_valid_tokens: int | None = None, workers: int = 1):
     """The whole MXFP4-weight layer for every token: float64 [T, H]."""
     T = np.asarray(topk_ids).shape[0]
     return forward_tokens_mxfp4(x, topk_ids, topk_weights, wgu_packed, wgu_scales, wd_packed,
-                                wd_scales, np.arange(T), num_valid_tokens)
+                                wd_scales, np.arange(T), num_valid_tokens, workers)

@@ -70,3 +70,58 @@ def sample_tokens(T: int, n: int, seed: int = 0) -> np.ndarray:
     rng = np.random.default_rng(seed)
     mid = rng.choice(np.arange(1, T - 1), size=n - 2, replace=False)
     return np.sort(np.concatenate([[0, T - 1], mid]))
+
+
+def covering_tokens(topk_ids, num_experts: int, n: int, seed: int = 0,
+                    tile_rows=(64, 128, 192, 256)) -> np.ndarray:
+    """At least n distinct tokens (all of them if T <= n) that include, for
+    every expert holding rows: the token of its first and of its last
+    dispatched row, and the token of the first row of its last m-tile for
+    each tile height in tile_rows (the rows where a ragged last tile starts).
+    The rest are drawn uniformly; the first and last token are always in."""
+    ids = np.asarray(topk_ids)
+    T, K = ids.shape
+    if T <= n:
+        return np.arange(T)
+    _, off, rs, _ = oracle.dispatch(ids, num_experts, T)
+    want = {0, T - 1}
+    for e in range(num_experts):
+        m = int(off[e + 1] - off[e])
+        if m == 0:
+            continue
+        rows = {int(off[e]), int(off[e + 1]) - 1}
+        rows.update(int(off[e]) + ((m - 1) // bm) * bm for bm in tile_rows)
+        want.update(int(rs[r]) // K for r in rows)
+    rng = np.random.default_rng(seed)
+    rest = np.setdiff1d(np.arange(T), np.fromiter(want, dtype=np.int64))
+    extra = max(0, n - len(want))
+    if extra:
+        want.update(int(t) for t in rng.choice(rest, size=min(extra, rest.size), replace=False))
+    return np.array(sorted(want), dtype=np.int64)
+
+
+def oracle_workers() -> int:
+    """Threads for the oracle's per-expert products (the host's cores, at most 16)."""
+    import os
+    return max(1, min(16, os.cpu_count() or 1))
+
+
+class WidenedExperts:
+    """widen(e) for oracle.forward_tokens_widened: expert e's weights of the
+    device tensors w_gateup [E, 2I, H] and w_down [E, H, I], copied to the host
+    and widened with oracle.bf16_to_f64 once, then kept for later calls."""
+
+    def __init__(self, w_gateup: torch.Tensor, w_down: torch.Tensor):
+        self.wgu, self.wd = w_gateup, w_down
+        self.cache = {}
+
+    def __len__(self):
+        return self.wgu.shape[0]
+
+    def __call__(self, e):
+        e = int(e)
+        hit = self.cache.get(e)
+        if hit is None:
+            hit = (oracle.bf16_to_f64(bits(self.wgu[e])), oracle.bf16_to_f64(bits(self.wd[e])))
+            self.cache[e] = hit
+        return hit

@@ -52,15 +52,33 @@ CASES = {
     # the 192-row tiles of the large plan: one short, exact, one past, two
     # tiles (+1), and the 96-row half a wave pair covers (+1)
     "tile_edges_192": (1, 1, 9, 256, 256, 0, None),
+    # T*K/E >= 768: the large plan without per-sub-tile skipping (the
+    # Mixtral-style instances), on uneven expert sizes with ragged last tiles.
+    # gate-up 192 x 256 (gated), down 192 x 128
+    "large_branch_free": (1, 1, 4, 256, 256, 0, None),
+    # I % 128 != 0: gate-up on 256 x 128 tiles (4 x 2 waves)
+    "large_branch_free_i320": (1, 1, 4, 256, 320, 0, None),
+    # H % 256 != 0: down on 192 x 128 tiles
+    "large_branch_free_h384": (1, 1, 4, 384, 256, 0, None),
+    # top-2 over 4 experts, H = 512, I = 1024
+    "large_branch_free_k2": (1, 2, 4, 512, 1024, 0, None),
+    # eight experts near 1024 rows (the Mixtral routing's spread), H = 1024:
+    # down on 192 x 256 tiles
+    "large_branch_free_down256": (1, 2, 8, 1024, 512, 0, None),
 }
 TILE_EDGE_COUNTS = {"tile_edges": [256, 257, 128, 129, 64, 1, 0],
-                    "tile_edges_192": [191, 192, 193, 384, 385, 96, 97, 1, 0]}
+                    "tile_edges_192": [191, 192, 193, 384, 385, 96, 97, 1, 0],
+                    "large_branch_free": [1000, 1100, 1153, 0],
+                    "large_branch_free_i320": [1000, 1100, 1153, 0],
+                    "large_branch_free_h384": [1000, 1100, 1153, 0],
+                    "large_branch_free_k2": [769, 960, 1023, 1280],
+                    "large_branch_free_down256": [1023, 1024, 1025, 974, 1083, 1100, 960, 1003]}
 
 
 def build(name):
     T, K, E, H, I, cap, mk = CASES[name]
     if name in TILE_EDGE_COUNTS:
-        ids = exact_rows_ids(TILE_EDGE_COUNTS[name], 1)
+        ids = exact_rows_ids(TILE_EDGE_COUNTS[name], K)
         T = ids.shape[0]
     else:
         ids = mk()

@@ -7,15 +7,17 @@
   moe_forward / moe_gate_up with the skinny plan on the row-major weights,
   bit for bit, on every launch path (fused dispatch + tiny down/combine,
   fused dispatch + skinny down, multi-launch dispatch), with a device token
-  count, and on the full-size expert-parallel decode share.  The row-major
-  path is the one checked against the oracle in test_gpu_parity.
+  count, and on the full-size expert-parallel decode share;
+* the packed layers directly against the oracle: bf16 packed weights, and MX
+  codes quantized on the host by the oracle, then packed on the device.
 """
 import numpy as np
 import pytest
 import torch
 
+import oracle
 import workloads as W
-from helpers import bits
+from helpers import DeviceExperts, bits, check_close, f64, oracle_workers
 
 pytestmark = pytest.mark.gpu
 
@@ -215,3 +217,59 @@ def test_graph_replays_with_device_token_count(kind):
         assert torch.equal(off, ref_off), tv
         assert torch.equal(out[:tv].view(torch.int16), ref_out[:tv].view(torch.int16)), tv
         assert bool((out[tv:].view(torch.int16) == 0x7FC1).all()), tv   # rows >= T_v untouched
+
+
+# ---------------------------------------------------------------------------
+# the packed layers against the oracle directly
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("name", list(SHAPES))
+def test_forward_packed_vs_oracle(name):
+    T, K, E, H, I, lo, hi = SHAPES[name]
+    x, ids, w, wgu, wd = case(T, K, E, H, I, 24, lo, hi)
+    p = moe.problem(T, K, E, H, I)
+    pgu, pd = ops.skinny_pack(wgu, True), ops.skinny_pack(wd, False)
+    got, off = ops.forward_packed(p, x, ids, w, pgu, pd)
+    ids_h = ids.cpu().numpy()
+    _, o_off, _, _ = oracle.dispatch(ids_h, E, T)
+    assert np.array_equal(off.cpu().numpy(), o_off)
+    ref = oracle.forward(bits(x), ids_h, w.cpu().numpy(), bits(wgu), bits(wd))
+    check_close(f64(got), ref, f"packed {name}")
+
+
+@pytest.mark.parametrize("fmt", ["mxfp8", "mxfp4"])
+@pytest.mark.parametrize("name", list(SHAPES))
+def test_forward_mx_packed_vs_oracle(fmt, name):
+    """MX codes and scales from the oracle's quantizer (host), packed on the
+    device, through moe_forward_mx_packed, against the oracle's MX layer."""
+    T, K, E, H, I, lo, hi = SHAPES[name]
+    if fmt == "mxfp4" and (H % 128 or I % 128):
+        pytest.skip("MXFP4 needs H and I multiples of 128")
+    x, ids, w, wgu, wd = case(T, K, E, H, I, 25, lo, hi)
+    quant = oracle.mxfp8_quantize if fmt == "mxfp8" else oracle.mxfp4_quantize
+    cg, sg = quant(bits(wgu))
+    cd, sd = quant(bits(wd))
+    d = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(DEV)
+    qgu, sgu, qd, sdd = d(cg), d(sg), d(cd), d(sd)
+    p = moe.problem(T, K, E, H, I)
+    pgu, pd = ops.mx_pack(qgu, True, fmt), ops.mx_pack(qd, False, fmt)
+    got, _ = ops.forward_mx(p, x, ids, w, pgu, sgu, pd, sdd, fmt, packed=True)
+    fwd = oracle.forward_mxfp8 if fmt == "mxfp8" else oracle.forward_mxfp4
+    ref = fwd(bits(x), ids.cpu().numpy(), w.cpu().numpy(), cg, sg, cd, sd)
+    check_close(f64(got), ref, f"{fmt} packed {name}")
+
+
+@pytest.mark.parametrize("name", ["ep_decode_T8", "ep_decode_T32"])
+def test_forward_packed_ep_decode_vs_oracle(name):
+    cfg = W.CONFIGS[name]
+    T, K, E, H, I = cfg.num_tokens, cfg.top_k, cfg.num_experts, cfg.hidden, cfg.intermediate
+    x_h = W.make_x(cfg, 2)
+    ids_h, w_h = W.make_routing(cfg, 2)
+    wgu, wd = W.make_weights(cfg, 2, DEV)
+    pgu, pd = ops.skinny_pack(wgu, True), ops.skinny_pack(wd, False)
+    p = moe.problem(T, K, E, H, I)
+    got, _ = ops.forward_packed(p, x_h.to(DEV), ids_h.to(DEV), w_h.to(DEV), pgu, pd)
+    torch.cuda.synchronize()
+    del pgu, pd
+    ref = oracle.forward(bits(x_h), ids_h.numpy(), w_h.numpy(), DeviceExperts(wgu),
+                         DeviceExperts(wd), workers=oracle_workers())
+    check_close(f64(got), ref, f"packed {name}")

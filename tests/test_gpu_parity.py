@@ -2,10 +2,13 @@
 
 Dispatch results are compared bit for bit; floating-point results to the
 bar in helpers.check_close.  Small and ragged shapes run the oracle on every
-token; the full-size workloads run it on sampled tokens (the oracle evaluates
-each sampled token straight from its definition) and check the dispatch on
-every assignment.  Every kernel plan (skinny split-K, tiled 64, tiled 128) is
-exercised on the small shapes (skinny, tiled 64/128/256).
+token, and so do the Mixtral-style layer (seeds 0-2) and the 96-expert decode
+shares (T = 1 .. 128, seeds 0-2).  The 96-expert prefill shares (uniform
+seeds 0-2, Zipf seeds 0-4) run it on at least 256 tokens chosen to include
+every touched expert's first and last dispatched row and the first row of
+its last m-tile; the dispatch is checked on every assignment.  Every kernel
+plan (skinny split-K, tiled 64, tiled 128, tiled large) is exercised on the
+small shapes.
 """
 import numpy as np
 import pytest
@@ -13,7 +16,7 @@ import torch
 
 import oracle
 import workloads as W
-from helpers import DeviceExperts, bits, check_close, f64, sample_tokens
+from helpers import WidenedExperts, bits, check_close, covering_tokens, f64, oracle_workers
 
 pytestmark = pytest.mark.gpu
 
@@ -238,9 +241,6 @@ def test_forward_tiny_seeds(seed):
 # ---------------------------------------------------------------------------
 # full-size workloads, sampled tokens
 # ---------------------------------------------------------------------------
-FULL = ["ep_decode_T1", "ep_decode_T8", "ep_decode_T32", "ep_decode_T128", "ep_prefill_T2048",
-        "ep_prefill_T8192", "ep_prefill_T2048_zipf", "ep_prefill_T8192_zipf", "mixtral"]
-
 _weights_cache = {}
 
 
@@ -253,26 +253,84 @@ def device_weights(cfg, seed):
     return _weights_cache[key]
 
 
-@pytest.mark.parametrize("name", FULL)
-def test_forward_full_sampled(name):
+def run_full_size(name, seed, weights=None):
+    """One moe_forward of a full-size workload: x and routing of `seed`, the
+    given device weights (else those of `seed`).  Returns (cfg, host x, ids,
+    w, out)."""
     cfg = W.CONFIGS[name]
-    seed = 0
-    wgu, wd = device_weights(cfg, seed)
+    wgu, wd = weights if weights is not None else device_weights(cfg, seed)
     x = W.make_x(cfg, seed)
     ids, w = W.make_routing(cfg, seed)
     p = moe.problem(cfg.num_tokens, cfg.top_k, cfg.num_experts, cfg.hidden, cfg.intermediate)
+    print(f"[full] {name} seed {seed}", flush=True)
     out, off = ops.forward(p, x.to(DEV), ids.to(DEV), w.to(DEV), wgu, wd)
     torch.cuda.synchronize()
     _, o_off, _, _ = oracle.dispatch(ids.numpy(), cfg.num_experts, cfg.num_tokens)
     assert np.array_equal(off.cpu().numpy(), o_off)
-    toks = sample_tokens(cfg.num_tokens, 12, seed=1)
-    ref = oracle.forward_tokens(bits(x), ids.numpy(), w.numpy(), DeviceExperts(wgu),
-                                DeviceExperts(wd), toks)
+    return cfg, x, ids, w, out
+
+
+def check_tokens(name, seed, cfg, x, ids, w, widen, out, toks, workers):
+    ref = oracle.forward_tokens_widened(bits(x), ids.numpy(), w.numpy(), cfg.num_experts, widen,
+                                        toks, workers=workers)
     got = f64(out)[toks]
-    check_close(got, ref, name)
+    fro, mx = check_close(got, ref, f"{name} seed {seed}")
+    print(f"[full] {name} seed {seed}: {len(toks)} tokens, rel_fro={fro:.2e} max_rel={mx:.2e}",
+          flush=True)
     # tokens with no local expert produce exact zeros
     local = ((ids >= 0) & (ids < cfg.num_experts)).any(dim=1).numpy()
     assert np.all(f64(out)[~local] == 0)
+
+
+@pytest.mark.parametrize("seed", [0, 1, 2])
+def test_forward_mixtral_every_token(seed):
+    """The Mixtral-style layer (~1024 ragged rows per expert: the branch-free
+    192 x 256 tiled instances) against the oracle on all 4096 tokens."""
+    cfg = W.CONFIGS["mixtral"]
+    wgu, wd = device_weights(cfg, seed)
+    cfg, x, ids, w, out = run_full_size("mixtral", seed, (wgu, wd))
+    check_tokens("mixtral", seed, cfg, x, ids, w, WidenedExperts(wgu, wd), out,
+                 np.arange(cfg.num_tokens), 1)
+
+
+@pytest.fixture(scope="module")
+def ep_share():
+    """The 96-expert, 7168 x 3072 expert-parallel share's weights (seed 0,
+    drawn on the device) and a cache of their widened host copies, shared by
+    every decode and prefill case below (x and routing vary by seed)."""
+    _weights_cache.clear()
+    torch.cuda.empty_cache()
+    wgu, wd = W.make_weights(W.CONFIGS["ep_prefill_T8192"], 0, DEV)
+    yield wgu, wd, WidenedExperts(wgu, wd)
+    del wgu, wd
+    torch.cuda.empty_cache()
+
+
+DECODE = ["ep_decode_T1", "ep_decode_T8", "ep_decode_T32", "ep_decode_T128"]
+
+
+@pytest.mark.parametrize("name", DECODE)
+@pytest.mark.parametrize("seed", [0, 1, 2])
+def test_forward_ep_decode_every_token(name, seed, ep_share):
+    wgu, wd, widen = ep_share
+    cfg, x, ids, w, out = run_full_size(name, seed, (wgu, wd))
+    check_tokens(name, seed, cfg, x, ids, w, widen, out, np.arange(cfg.num_tokens),
+                 oracle_workers())
+
+
+PREFILL = [(n, s) for n in ("ep_prefill_T2048", "ep_prefill_T8192") for s in (0, 1, 2)] + \
+          [(n, s) for n in ("ep_prefill_T2048_zipf", "ep_prefill_T8192_zipf") for s in range(5)]
+
+
+@pytest.mark.parametrize("name,seed", PREFILL)
+def test_forward_ep_prefill_sampled(name, seed, ep_share):
+    """96-of-384 prefill (uniform seeds 0-2, Zipf s = 1.2 seeds 0-4) on at
+    least 256 tokens that include every touched expert's first and last
+    dispatched row and the first row of its last m-tile at each tile height."""
+    wgu, wd, widen = ep_share
+    cfg, x, ids, w, out = run_full_size(name, seed, (wgu, wd))
+    toks = covering_tokens(ids.numpy(), cfg.num_experts, 256, seed=seed + 1)
+    check_tokens(name, seed, cfg, x, ids, w, widen, out, toks, oracle_workers())
 
 
 # ---------------------------------------------------------------------------
@@ -292,6 +350,7 @@ def test_static_capacity_graph_replays():
     ex_off = torch.empty((E + 1,), dtype=torch.int32, device=DEV)
     ex_out = torch.empty((T, H), dtype=torch.bfloat16, device=DEV)
     ws = ops.make_workspace(p, DEV)
+    widen = WidenedExperts(wgu, wd)
     for i, tv in enumerate(tvs):
         x = W.make_x(cfg, 100 + i)
         ids, w = W.make_routing(cfg, 100 + i)
@@ -307,9 +366,9 @@ def test_static_capacity_graph_replays():
         got = graph.out.clone()
         # rows past T_v are untouched
         assert bool((got[tv:].view(torch.int16) == 0x7FC1).all()), f"replay {i}"
-        toks = sample_tokens(tv, 6, seed=i)
-        ref = oracle.forward_tokens(bits(x), ids.numpy(), w.numpy(), DeviceExperts(wgu),
-                                    DeviceExperts(wd), toks, num_valid_tokens=tv)
+        toks = covering_tokens(ids.numpy()[:tv], E, 16, seed=i)
+        ref = oracle.forward_tokens_widened(bits(x), ids.numpy(), w.numpy(), E, widen, toks,
+                                            num_valid_tokens=tv, workers=oracle_workers())
         check_close(f64(got)[toks], ref, f"replay {i} T_v={tv}")
         # the graph replays exactly what an eager call computes
         ops.forward(p, x_buf, ids_buf, w_buf, wgu, wd, num_tokens_dev=nt, expert_offsets=ex_off,

@@ -350,3 +350,24 @@ def test_router_matches_generator():
         ids, w = oracle.router_topk(lg.numpy(), cfg.top_k)
         assert np.array_equal(ids, ids_g.numpy())
         assert np.abs(w - w_g.numpy().astype(np.float64)).max() < 1e-6
+
+
+@pytest.mark.parametrize("fmt", ["bf16", "mxfp8", "mxfp4"])
+def test_thread_pool_changes_nothing(fmt):
+    """forward with its per-expert products on a thread pool equals the serial
+    evaluation bit for bit (same operands, same accumulation order)."""
+    T, K, E, H, I = 40, 3, 6, 64, 64
+    xt, idt, wt, wgut, wdt = rand_problem(T, K, E, H, I, 77, -1, E + 1)
+    x, ids, w, wgu, wd = bits(xt), idt.numpy(), wt.numpy(), bits(wgut), bits(wdt)
+    if fmt == "bf16":
+        a = oracle.forward(x, ids, w, wgu, wd, num_valid_tokens=33)
+        b = oracle.forward(x, ids, w, wgu, wd, num_valid_tokens=33, workers=4)
+    else:
+        q = oracle.mxfp8_quantize if fmt == "mxfp8" else oracle.mxfp4_quantize
+        f = oracle.forward_mxfp8 if fmt == "mxfp8" else oracle.forward_mxfp4
+        cg, sg = q(wgu)
+        cd, sd = q(wd)
+        a = f(x, ids, w, cg, sg, cd, sd, num_valid_tokens=33)
+        b = f(x, ids, w, cg, sg, cd, sd, num_valid_tokens=33, workers=4)
+    assert np.array_equal(a.view(np.uint64), b.view(np.uint64))
+    assert np.abs(a[:33]).max() > 0 and not a[33:].any()
