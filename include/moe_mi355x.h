@@ -186,6 +186,33 @@ MOE_API moe_status_t moe_graph_create(const moe_problem_t* p, const uint16_t* x,
 MOE_API moe_status_t moe_graph_launch(void* graph, void* stream);
 MOE_API moe_status_t moe_graph_destroy(void* graph);
 
+/* moe_forward for callers that cannot allocate device memory: code under HIP
+ * graph capture, tight serving loops, harnesses that forbid allocation.  The
+ * same layer, kernels, plan, checks and results (bit for bit) as moe_forward,
+ * with the workspace taken from a library-owned file-scope device array of
+ * 128 MiB instead of a caller buffer; each GPU holds its own copy of that
+ * array from the library's first call there until the process ends.
+ *  - Problems whose moe_forward workspace (moe_workspace_size) exceeds 128 MiB
+ *    return MOE_ERROR_NOT_SUPPORTED, checked on the host before anything
+ *    else happens (for example the 96-expert decode shares up to T = 128 and
+ *    the static-capacity layer of 16384 rows fit; a 4096-token Mixtral-style
+ *    layer does not).
+ *  - It calls no hipMalloc / hipFree and no allocating routine.  The first call
+ *    on a device looks up the array's address there (hipGetSymbolAddress, with
+ *    the calling thread's current device, which must be the device of
+ *    `stream`); make that first call outside a graph capture.
+ *  - Every call on one GPU shares that GPU's array, whose contents are left
+ *    from the last call (nothing in it needs clearing: each region is written
+ *    before it is read).  Calls that may overlap on one GPU (concurrent
+ *    streams, or a replayed graph holding this call racing an eager one) race
+ *    on it and must be serialised by the caller.
+ * Arguments as for moe_forward without workspace / ws_bytes. */
+MOE_API moe_status_t moe_forward_noalloc(const moe_problem_t* p, const uint16_t* x,
+                                         const int32_t* topk_ids, const float* topk_weights,
+                                         const uint16_t* w_gateup, const uint16_t* w_down,
+                                         const int32_t* num_tokens_dev, int32_t* expert_offsets,
+                                         uint16_t* out, void* stream);
+
 /* ---------------------------------------------------------------------------
  * Pre-packed bf16 expert weights for the weight-streaming (skinny) kernels
  * (DeepGEMM PR #394, Summary and Motivation: expert weights laid out once, at

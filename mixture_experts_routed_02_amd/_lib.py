@@ -26,7 +26,12 @@ EXPORTS = (
     "moe_gate_up_mxfp8", "moe_forward_mxfp8", "moe_mxfp4_quantize", "moe_mxfp4_dequantize",
     "moe_gate_up_mxfp4", "moe_forward_mxfp4", "moe_skinny_pack", "moe_gate_up_packed",
     "moe_forward_packed", "moe_mx_pack", "moe_gate_up_mx_packed", "moe_forward_mx_packed",
+    "moe_forward_noalloc",
 )
+
+# Largest moe_forward workspace that moe_forward_noalloc serves from its
+# library-owned array (bytes).
+NOALLOC_MAX_WORKSPACE = 128 << 20
 
 
 class MoeProblem(ctypes.Structure):
@@ -82,6 +87,7 @@ _SIGS = {
     "moe_gate_up_mxfp4": (ctypes.c_int, [_PP, _P, _P, _P, _P, _P, _P]),
     "moe_forward_mxfp4": (ctypes.c_int, [_PP, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _SZ, _P]),
     "moe_graph_destroy": (ctypes.c_int, [_P]),
+    "moe_forward_noalloc": (ctypes.c_int, [_PP, _P, _P, _P, _P, _P, _P, _P, _P, _P]),
 }
 
 _lib = None

@@ -4,7 +4,16 @@
 #include "../../include/moe_mi355x.h"
 #include "moe_internal.h"
 
+#include <mutex>
 #include <new>
+
+// Workspace of moe_forward_noalloc: a file-scope device array, one copy per
+// GPU the library runs on, held until the process ends.  Host code never uses
+// this name as an address (on the host it is only a stand-in for the symbol):
+// each device's address comes from hipGetSymbolAddress, taken once per device
+// with that device current (scratch_on_current_device below).
+constexpr size_t kScratchBytes = size_t(128) << 20;
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
 
 using moe::GemmPlan;
 using moe::Shape;
@@ -95,10 +104,11 @@ moe_status_t expert_compute_impl(const Shape& s, const GemmPlan& plan, const uin
     return launched(e);
 }
 
-moe_status_t check_forward_args(const moe_problem_t* p, Shape* s, const uint16_t* x,
+// Everything moe_forward checks except the workspace.
+moe_status_t check_forward_ptrs(const moe_problem_t* p, Shape* s, const uint16_t* x,
                                 const int32_t* ids, const float* w, const uint16_t* wgu,
                                 const uint16_t* wd, const int32_t* ntok, const int32_t* offsets,
-                                const uint16_t* out, const void* ws, size_t ws_bytes) {
+                                const uint16_t* out) {
     moe_status_t st = check_problem(p, s);
     if (st != MOE_SUCCESS) return st;
     const long long tk = (long long)s->T * s->K;
@@ -106,7 +116,36 @@ moe_status_t check_forward_args(const moe_problem_t* p, Shape* s, const uint16_t
         bad_bf16(wd) || bad_i32(offsets) || bad_bf16(out, s->T))
         return MOE_ERROR_INVALID_VALUE;
     if (ntok && !aligned(ntok, 4)) return MOE_ERROR_INVALID_VALUE;
+    return MOE_SUCCESS;
+}
+
+moe_status_t check_forward_args(const moe_problem_t* p, Shape* s, const uint16_t* x,
+                                const int32_t* ids, const float* w, const uint16_t* wgu,
+                                const uint16_t* wd, const int32_t* ntok, const int32_t* offsets,
+                                const uint16_t* out, const void* ws, size_t ws_bytes) {
+    moe_status_t st = check_forward_ptrs(p, s, x, ids, w, wgu, wd, ntok, offsets, out);
+    if (st != MOE_SUCCESS) return st;
     return check_ws(*s, ws, ws_bytes);
+}
+
+// Device address of `scratch` on the calling thread's current device, looked
+// up once per device (the first call there) and kept.
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+moe_status_t scratch_on_current_device(void** ptr) {
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return MOE_ERROR_LAUNCH;
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        void* p = nullptr;
+        if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p)
+            return MOE_ERROR_LAUNCH;
+        g_scratch_ptr[dev] = p;
+    }
+    *ptr = g_scratch_ptr[dev];
+    return MOE_SUCCESS;
 }
 
 moe_status_t forward_impl(const Shape& s, int hint, const uint16_t* x, const int32_t* ids,
@@ -296,7 +335,7 @@ const char* moe_status_string(moe_status_t status) {
     switch (status) {
         case MOE_SUCCESS: return "MOE_SUCCESS";
         case MOE_ERROR_INVALID_VALUE: return "MOE_ERROR_INVALID_VALUE: bad argument (null/misaligned pointer, size out of range, capacity < T*K, workspace too small)";
-        case MOE_ERROR_NOT_SUPPORTED: return "MOE_ERROR_NOT_SUPPORTED: shape outside the supported range (H, I multiples of 64; K <= 64; E <= 512; T*K <= 2^28)";
+        case MOE_ERROR_NOT_SUPPORTED: return "MOE_ERROR_NOT_SUPPORTED: shape outside the supported range (H, I multiples of 64; K <= 64; E <= 512; T*K <= 2^28; moe_forward_noalloc: workspace <= 128 MiB)";
         case MOE_ERROR_LAUNCH: return "MOE_ERROR_LAUNCH: a kernel launch failed";
     }
     return "unknown moe_status_t";
@@ -422,6 +461,24 @@ moe_status_t moe_forward(const moe_problem_t* p, const uint16_t* x, const int32_
     return forward_impl(s, p->kernel_hint, x, topk_ids, topk_weights, w_gateup, w_down,
                         num_tokens_dev, expert_offsets, out, workspace,
                         static_cast<hipStream_t>(stream));
+}
+
+moe_status_t moe_forward_noalloc(const moe_problem_t* p, const uint16_t* x,
+                                 const int32_t* topk_ids, const float* topk_weights,
+                                 const uint16_t* w_gateup, const uint16_t* w_down,
+                                 const int32_t* num_tokens_dev, int32_t* expert_offsets,
+                                 uint16_t* out, void* stream) {
+    Shape s;
+    moe_status_t st = check_forward_ptrs(p, &s, x, topk_ids, topk_weights, w_gateup, w_down,
+                                         num_tokens_dev, expert_offsets, out);
+    if (st != MOE_SUCCESS) return st;
+    if (layout(s).total > kScratchBytes) return MOE_ERROR_NOT_SUPPORTED;
+    void* ws = nullptr;
+    if ((st = scratch_on_current_device(&ws)) != MOE_SUCCESS) return st;
+    // the workspace regions are written before they are read on every call,
+    // so nothing in the shared array needs clearing
+    return forward_impl(s, p->kernel_hint, x, topk_ids, topk_weights, w_gateup, w_down,
+                        num_tokens_dev, expert_offsets, out, ws, static_cast<hipStream_t>(stream));
 }
 
 moe_status_t moe_skinny_pack(const uint16_t* w, int32_t experts, int32_t rows, int32_t k,

@@ -20,7 +20,7 @@ __all__ = [
     "down", "combine",
     "forward", "MoEGraph", "MoeProblem", "mx_quantize", "mx_dequantize", "gate_up_mx", "forward_mx",
     "mxfp8_quantize", "mxfp8_dequantize", "gate_up_mxfp8", "forward_mxfp8", "skinny_pack",
-    "gate_up_packed", "forward_packed", "mx_pack",
+    "gate_up_packed", "forward_packed", "mx_pack", "forward_noalloc",
 ]
 
 
@@ -194,6 +194,8 @@ def _forward_args(p, x, topk_ids, topk_weights, w_gateup, w_down, num_tokens_dev
     if out is None:
         out = torch.empty((T, H), dtype=torch.bfloat16, device=dev)
     _need(out, "out", torch.bfloat16, (T, H), dev)
+    if workspace is False:      # the caller passes no workspace
+        return nt, offsets, out, None
     ws = make_workspace(p, dev) if workspace is None else workspace
     return nt, offsets, out, ws
 
@@ -207,6 +209,19 @@ def forward(p: MoeProblem, x, topk_ids, topk_weights, w_gateup, w_down, num_toke
         ctypes.byref(p), _ptr(x), _ptr(topk_ids), _ptr(topk_weights), _ptr(w_gateup),
         _ptr(w_down), _ptr(nt), _ptr(offsets), _ptr(out), _ptr(ws), ws.numel(),
         _stream_ptr(x.device)))
+    return out, offsets
+
+
+def forward_noalloc(p: MoeProblem, x, topk_ids, topk_weights, w_gateup, w_down,
+                    num_tokens_dev=None, expert_offsets=None, out=None):
+    """moe_forward with the library's own device array as workspace (no
+    allocation by the library; at most NOALLOC_MAX_WORKSPACE bytes of
+    workspace).  Returns (out [T,H], expert_offsets [E+1])."""
+    nt, offsets, out, _ = _forward_args(p, x, topk_ids, topk_weights, w_gateup, w_down,
+                                        num_tokens_dev, expert_offsets, out, workspace=False)
+    check("moe_forward_noalloc", lib().moe_forward_noalloc(
+        ctypes.byref(p), _ptr(x), _ptr(topk_ids), _ptr(topk_weights), _ptr(w_gateup),
+        _ptr(w_down), _ptr(nt), _ptr(offsets), _ptr(out), _stream_ptr(x.device)))
     return out, offsets
 
 

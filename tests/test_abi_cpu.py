@@ -25,7 +25,7 @@ def declared_functions():
 
 def test_exports_every_declared_symbol():
     names = declared_functions()
-    assert len(names) == 26, names
+    assert len(names) == 27, names
     L = moe.lib()
     for n in names:
         assert hasattr(L, n), n
@@ -198,3 +198,27 @@ def test_skinny_pack_rejects_overlap():
     assert L.moe_skinny_pack(A16, 2, 32, 64, 0, A16 + n - 16, None) == 1  # tail overlaps
     assert L.moe_skinny_pack(A16 + 64, 2, 32, 64, 0, A16, None) == 1      # head overlaps
     assert L.moe_mx_pack(A16, 2, 32, 128, 8, 0, A16 + 64, None) == 1
+
+
+def test_noalloc_refuses_large_workspace_before_touching_the_gpu():
+    """moe_forward_noalloc checks the workspace bound on the host first: a
+    problem whose moe_forward workspace exceeds the library's array is
+    refused with MOE_ERROR_NOT_SUPPORTED (no HIP call is made), and bad
+    arguments fail closed as in moe_forward."""
+    L = moe.lib()
+    big = moe.problem(4096, 2, 8, 4096, 14336)
+    assert moe.workspace_size(big) > _lib.NOALLOC_MAX_WORKSPACE
+    r = L.moe_forward_noalloc(ctypes.byref(big), A16, A4, A4, A16, A16, None, A4, A16, None)
+    assert r == _lib.MOE_ERROR_NOT_SUPPORTED
+    fits = moe.problem(2048, 8, 128, 2048, 768, capacity=16384)
+    assert moe.workspace_size(fits) <= _lib.NOALLOC_MAX_WORKSPACE
+    good = [A16, A4, A4, A16, A16, None, A4, A16, None]
+    for i in (0, 1, 2, 3, 4, 6, 7):      # each required pointer nulled
+        args = list(good)
+        args[i] = None
+        assert L.moe_forward_noalloc(ctypes.byref(fits), *args) == _lib.MOE_ERROR_INVALID_VALUE, i
+    args = list(good)
+    args[0] = A16 + 2                      # misaligned bf16 pointer
+    assert L.moe_forward_noalloc(ctypes.byref(fits), *args) == _lib.MOE_ERROR_INVALID_VALUE
+    bad = moe.problem(64, 0, 8, 256, 512)
+    assert L.moe_forward_noalloc(ctypes.byref(bad), *good) == _lib.MOE_ERROR_INVALID_VALUE
