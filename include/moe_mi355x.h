@@ -78,12 +78,21 @@ typedef enum moe_status {
     MOE_ERROR_LAUNCH = 3
 } moe_status_t;
 
-/* Human-readable text of a status (static storage). */
+/* Human-readable text of a status (static storage).  The statuses are those
+ * of the host-side validation that rejects unsupported shapes before any work
+ * is enqueued (DeepGEMM PR #394, Scope and fallback: unsupported shapes fail
+ * closed during host validation). */
 MOE_API const char* moe_status_string(moe_status_t status);
 
 /* Bytes of device workspace every entry point below needs for `p` (the
  * largest of them, moe_forward).  Host-only.  Returns MOE_ERROR_* for an
- * invalid problem and leaves *bytes untouched. */
+ * invalid problem and leaves *bytes untouched.  The workspace is a
+ * caller-owned buffer passed into each call (TileOps PR #1738, Scope: buffers
+ * injected by the caller; FlashInfer PR #3980, commit notes on the workspace
+ * contract: a workspace is set up once and every launch leaves it ready for
+ * the next).  Unlike the counters of that contract, nothing in this
+ * workspace needs initialising or cleaning: each call writes every region it
+ * reads before reading it. */
 MOE_API moe_status_t moe_workspace_size(const moe_problem_t* p, size_t* bytes);
 
 /* Local dispatch (TileOps PR #1738, Summary: local dispatch into a tight

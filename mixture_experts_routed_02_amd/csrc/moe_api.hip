@@ -48,7 +48,8 @@ moe_status_t check_problem(const moe_problem_t* p, Shape* s) {
 }
 
 // Workspace layout (every region 256-byte aligned):
-//   blk_counts int32 [nblk * E]   (multi-block dispatch only)
+//   blk_counts int32 [(nblk + 1) * E]   (multi-block dispatch only: per-block
+//                                        histograms, scanned in place, + totals)
 //   row_src    int32 [cap]        (moe_forward)
 //   token_row  int32 [T*K]        (moe_forward)
 //   h          bf16  [cap, I]     (expert compute)
@@ -62,7 +63,7 @@ Layout layout(const Shape& s) {
     const int nblk = moe::dispatch_blocks(s);
     size_t off = 0;
     L.counts = off;
-    off += align_up(nblk > 1 ? (size_t)nblk * s.E * 4 : 0);
+    off += align_up(nblk > 1 ? (size_t)(nblk + 1) * s.E * 4 : 0);
     L.row_src = off;
     off += align_up((size_t)s.cap * 4);
     L.token_row = off;

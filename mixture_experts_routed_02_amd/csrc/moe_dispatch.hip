@@ -6,9 +6,12 @@
 // order a = t*K + j.
 //
 // Small problems (T*K <= kDispatchSingleMax) run as one 1024-thread block.
-// Larger ones run two fixed grids: a per-block histogram into the workspace,
-// then a scatter pass in which every block rebuilds its own prefix from those
-// histograms (no atomics across blocks, nothing to reset between calls).
+// Larger ones run three fixed grids: a per-block histogram into the
+// workspace, an exclusive scan of each expert's column of those histograms
+// over the blocks (one block per expert; the column total goes to an extra
+// row), then the scatter, in which every block reads its own start inside
+// each expert and the totals (no atomics across blocks, nothing to reset
+// between calls; the work grows linearly with the number of blocks).
 // Within a block, ranks among equal experts come from wave64 ballots: one
 // ballot per bit of the expert id gives each lane the mask of lanes holding
 // its expert, and the lane's rank is the popcount of that mask below it plus
@@ -45,9 +48,44 @@ __global__ __launch_bounds__(kDispatchThreads) void dispatch_count_kernel(
         blk_counts[(long long)blockIdx.x * E + e] = s_hist[e];
 }
 
+// Column e of the per-block histograms blk_counts [nblk + 1][E] becomes, in
+// place, the exclusive prefix over the blocks (row b = the rows of expert e
+// that blocks 0..b-1 hold), and row nblk receives the column total.  One
+// workgroup per expert, 256 blocks per pass with a carry.
+__global__ __launch_bounds__(256) void dispatch_block_scan_kernel(int32_t* __restrict__ blk_counts,
+                                                                  int nblk, int E) {
+    __shared__ int s_wave[4];
+    const int e = blockIdx.x;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    int carry = 0;
+    for (int b0 = 0; b0 < nblk; b0 += 256) {
+        const int b = b0 + tid;
+        const int v = b < nblk ? blk_counts[(long long)b * E + e] : 0;
+        int incl = v;
+#pragma unroll
+        for (int d = 1; d < 64; d <<= 1) {
+            const int t = __shfl_up(incl, d, 64);
+            if (lane >= d) incl += t;
+        }
+        if (lane == 63) s_wave[wave] = incl;
+        __syncthreads();
+        int before = 0, tot = 0;
+#pragma unroll
+        for (int w = 0; w < 4; ++w) {
+            before += w < wave ? s_wave[w] : 0;
+            tot += s_wave[w];
+        }
+        if (b < nblk) blk_counts[(long long)b * E + e] = carry + before + incl - v;
+        carry += tot;
+        __syncthreads();
+    }
+    if (tid == 0) blk_counts[(long long)nblk * E + e] = carry;
+}
+
 // SINGLE: one block handles all T*K assignments and builds its own histogram.
-// Otherwise block b handles assignments [b*chunk, (b+1)*chunk) and reads every
-// block's histogram from blk_counts.
+// Otherwise block b handles assignments [b*chunk, (b+1)*chunk) and reads its
+// start inside each expert (row b of the scanned histograms) and the totals
+// (row nblk).
 //
 // Wave w of the block owns the contiguous slice of kPer*64 assignments that
 // starts at a0 + w*kPer*64 and walks it 64 at a time in increasing order, so
@@ -118,14 +156,8 @@ __global__ __launch_bounds__(kDispatchThreads) void dispatch_scatter_kernel(
             s_base[e] = 0;
             s_scan[e] = tot;
         } else {
-            int pre = 0, tot = 0;
-            for (int b = 0; b < nblk; ++b) {
-                const int c = blk_counts[(long long)b * E + e];
-                tot += c;
-                pre += (b < (int)blockIdx.x) ? c : 0;
-            }
-            s_base[e] = pre;
-            s_scan[e] = tot;
+            s_base[e] = blk_counts[(long long)blockIdx.x * E + e];
+            s_scan[e] = blk_counts[(long long)nblk * E + e];
         }
     }
     __syncthreads();
@@ -191,6 +223,8 @@ hipError_t launch_dispatch(const Shape& s, const int32_t* ids, const int32_t* nt
     } else {
         hipLaunchKernelGGL(dispatch_count_kernel, dim3(nblk), dim3(kDispatchThreads), 0, st, ids,
                            ntok, s.T, s.K, s.E, blk_counts);
+        hipLaunchKernelGGL(dispatch_block_scan_kernel, dim3(s.E), dim3(256), 0, st, blk_counts,
+                           nblk, s.E);
         hipLaunchKernelGGL(dispatch_scatter_kernel<false>, dim3(nblk), dim3(kDispatchThreads), 0,
                            st, ids, ntok, s.T, s.K, s.E, blk_counts, nblk, offsets, row_src,
                            token_row);

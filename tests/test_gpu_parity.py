@@ -152,6 +152,29 @@ def test_dispatch_edges(case):
                            x.view(torch.int16)[torch.from_numpy(o_rs // K).long()])
 
 
+@pytest.mark.parametrize("T,K,E,skew,tv", [
+    (1 << 19, 8, 128, False, None),          # T*K = 2^22: 1024 dispatch blocks
+    (1 << 19, 8, 128, False, 300001),        # device token count mid-block
+    (1 << 20, 4, 512, True, None),           # 2^22 over 512 experts, three hold half of them
+])
+def test_dispatch_many_blocks(T, K, E, skew, tv):
+    """The multi-block dispatch far past the five workloads' sizes: 1024
+    blocks, whose per-block histograms are scanned over the blocks by a
+    separate kernel, bit-exact against the oracle."""
+    g = torch.Generator().manual_seed(T + E)
+    ids = torch.randint(-1, E + 2, (T, K), generator=g, dtype=torch.int32)
+    if skew:
+        hot = torch.randint(0, 3, (T, K), generator=g, dtype=torch.int32) + 200
+        ids = torch.where(torch.rand((T, K), generator=g) < 0.5, hot, ids)
+    p = moe.problem(T, K, E, 64, 64)
+    x = torch.zeros((T, 64), dtype=torch.bfloat16, device=DEV)
+    nt = None if tv is None else torch.tensor([tv], dtype=torch.int32, device=DEV)
+    _, off, rs, tr = ops.dispatch(p, x, ids.to(DEV), num_tokens_dev=nt)
+    tvv = T if tv is None else tv
+    check_dispatch(off, rs, tr, ids, E, tvv)
+    assert bool((tr[tvv * K:] == -1).all())
+
+
 # ---------------------------------------------------------------------------
 # combine
 # ---------------------------------------------------------------------------
