@@ -1269,15 +1269,25 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_tiled_kernel(
         const int mt = (me + BM - 1) / BM;
         const int local = tile - first;
         const int m_tile = local % mt, n_tile = local / mt;
-        const int r0 = row0 + m_tile * BM;
-        const int mrows = (me - m_tile * BM) < BM ? (me - m_tile * BM) : BM;
+        // The expert's rows, in 32-row units, are split over its mt m-tiles as
+        // evenly as whole units allow (heights differ by at most 32 rows and
+        // never exceed BM), rather than mt - 1 full tiles and a ragged last
+        // one: the m-tiles that share a weight tile and a token block then take
+        // about the same time and stay in step, so the blocks they share are
+        // fetched once.  Each output row's arithmetic does not depend on its
+        // tile, so the result is the same bit for bit.
+        const int units = (me + 31) / 32;
+        const int ub = units / mt, ux = units % mt;
+        const int u0 = m_tile * ub + (m_tile < ux ? m_tile : ux);
+        const int r0 = row0 + 32 * u0;
+        const int mrows = (me - 32 * u0) < 32 * (ub + (m_tile < ux)) ? (me - 32 * u0)
+                                                                       : 32 * (ub + (m_tile < ux));
         // a wave whose token rows all lie past the valid rows skips its MFMAs
         const bool active = wm * WM < mrows;
         // SUBSKIP: the 32-row sub-tiles of this wave that hold valid rows
-        // (wave-uniform); the others skip their MFMAs too.  A branch per MFMA:
-        // it pays where most tiles are partial (EP prefill T = 8192, ~128 rows
-        // per expert: 6% faster) and costs 4% where they are full (Mixtral), so
-        // the host picks the instance (GemmPlan::subskip).
+        // (wave-uniform); the others skip their MFMAs too.  The k loop exists
+        // twice: without any test for waves whose sub-tiles all hold rows, and
+        // with a test per MFMA for the others, so full tiles pay nothing for it.
         const int jlive = __builtin_amdgcn_readfirstlane((mrows - wm * WM + 31) / 32);
 
         // global source of each group this wave fills (stage 0): token groups
@@ -1331,8 +1341,9 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_tiled_kernel(
         // same registers (each fragment right after its last MFMA of half h),
         // and, if rf, spread the loads of one refill between the MFMA groups:
         // tokens of stage `stage` (KIND 1) or weights of stage `stage` (KIND 2)
-        auto half = [&](int h, auto KIND, bool rf, int stage) {
+        auto half = [&](int h, auto KIND, bool rf, int stage, auto FULL) {
             constexpr int kKind = decltype(KIND)::value;
+            constexpr bool kFull = decltype(FULL)::value;
             constexpr int GP = kKind == 1 ? GA : (kKind == 2 ? GW : 0);
             auto issue = [&](int q) {
                 if (kKind == 1) issue_one(stage, 0, q);
@@ -1345,7 +1356,7 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_tiled_kernel(
                     for (int i = 0; i < NS; ++i) {
 #pragma unroll
                         for (int j = 0; j < MS; ++j) {
-                            if (!SUBSKIP || j == 0 || jlive > j)
+                            if (kFull || j == 0 || jlive > j)
                                 acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fw[sk][i], fa[sk][j], acc[i][j], 0, 0, 0);
                             if (i == NS - 1) read_a(h + 1, sk, j);
                         }
@@ -1397,25 +1408,29 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_tiled_kernel(
         // Stage d: half 2d refills weights of stage d+SW-1 (slot of stage d-1,
         // whose reads were done at the barrier of half 2d-1); half 2d+1 waits
         // for stage d+1, then refills tokens of stage d+SA.
-        int d = 0;
-        for (; d + SW < nk; ++d) {
-            half(2 * d, weights, true, d + SW - 1);
-            // stage d+1 landed everywhere and stage d's slots are free (see
-            // above; the wave's own reads of them have returned before the
-            // barrier)
-            asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-            wait_vmcnt_barrier<N_STEADY>();
-            half(2 * d + 1, tokens, true, d + SA);
-        }
-        // last SW stages: refills only while below nk, full waits.  On the
-        // last stage the read-ahead takes stale but valid LDS data that is
-        // never used.
-        for (; d < nk; ++d) {
-            half(2 * d, weights, d + SW - 1 < nk, d + SW - 1);
-            asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-            wait_vmcnt_barrier<0>();
-            half(2 * d + 1, tokens, d + SA < nk, d + SA);
-        }
+        auto k_loop = [&](auto FULL) {
+            int d = 0;
+            for (; d + SW < nk; ++d) {
+                half(2 * d, weights, true, d + SW - 1, FULL);
+                // stage d+1 landed everywhere and stage d's slots are free (see
+                // above; the wave's own reads of them have returned before the
+                // barrier)
+                asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+                wait_vmcnt_barrier<N_STEADY>();
+                half(2 * d + 1, tokens, true, d + SA, FULL);
+            }
+            // last SW stages: refills only while below nk, full waits.  On the
+            // last stage the read-ahead takes stale but valid LDS data that is
+            // never used.
+            for (; d < nk; ++d) {
+                half(2 * d, weights, d + SW - 1 < nk, d + SW - 1, FULL);
+                asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+                wait_vmcnt_barrier<0>();
+                half(2 * d + 1, tokens, d + SA < nk, d + SA, FULL);
+            }
+        };
+        if (!SUBSKIP || jlive >= MS) k_loop(std::true_type{});
+        else k_loop(std::false_type{});
         // drain the rings before the epilogue reuses them
         wait_vmcnt_barrier<0>();
 
@@ -1683,12 +1698,6 @@ GemmPlan choose_plan(const Shape& s, int hint) {
             if (fill(256) >= 0.9 * fill(128)) p.bn_down = 256;
         }
         p.grid_gateup = p.grid_down = kNumCUs;
-        // fewer than four 192-row tiles per expert even if every assignment
-        // were local (T*K/E counts the ids other ranks own too: the 96-of-384
-        // share at T = 8192 gives 512 for ~128 local rows): partial tiles hold
-        // much of the MFMA work, so skip it per 32-row sub-tile.  Mixtral's
-        // 1024 rows per expert stay on the branch-free instance.
-        p.subskip = (double)s.T * s.K / s.E < 768.0;
     } else {
         p.bn_gateup = 128;                          // 64 gate + 64 up rows
         p.bn_down = (s.H % 128 == 0) ? 128 : 64;
@@ -1727,15 +1736,12 @@ hipError_t launch_grouped_gemm(const Shape& s, const GemmPlan& plan, bool gated,
             if (gated) return MOE_TILED(128, 128, 2, 2, true);
             return bn == 128 ? MOE_TILED(128, 128, 2, 2, false) : MOE_TILED(128, 64, 2, 2, false);
         default:
-            // 192 = 2 x 96 token rows: a wave holds 3 x 2 sub-tiles of 32 x 32
-            if (plan.subskip) {
-                if (gated) return bn == 256 ? MOE_TILED_S(192, 256, 2, 4, true) : MOE_TILED_S(256, 128, 4, 2, true);
-                return bn == 256 ? MOE_TILED_S(192, 256, 2, 4, false)
-                     : bn == 128 ? MOE_TILED_S(192, 128, 2, 4, false) : MOE_TILED(128, 64, 2, 2, false);
-            }
-            if (gated) return bn == 256 ? MOE_TILED(192, 256, 2, 4, true) : MOE_TILED(256, 128, 4, 2, true);
-            return bn == 256 ? MOE_TILED(192, 256, 2, 4, false)
-                 : bn == 128 ? MOE_TILED(192, 128, 2, 4, false) : MOE_TILED(128, 64, 2, 2, false);
+            // 192 = 2 x 96 token rows: a wave holds 3 x 2 sub-tiles of 32 x 32.
+            // Sub-tiles past the valid rows skip their MFMAs (SUBSKIP); waves
+            // whose sub-tiles all hold rows run a k loop without that test.
+            if (gated) return bn == 256 ? MOE_TILED_S(192, 256, 2, 4, true) : MOE_TILED_S(256, 128, 4, 2, true);
+            return bn == 256 ? MOE_TILED_S(192, 256, 2, 4, false)
+                 : bn == 128 ? MOE_TILED_S(192, 128, 2, 4, false) : MOE_TILED(128, 64, 2, 2, false);
     }
 #undef MOE_TILED
 #undef MOE_TILED_S

@@ -25,7 +25,6 @@ struct GemmPlan {
     int kind;
     int grid_gateup, grid_down;
     int bn_gateup, bn_down;  // weight rows per tile (tiled kinds)
-    bool subskip;            // tiled large: skip MFMAs per 32-row sub-tile of partial tiles
     bool split;              // tiled: XCDs 0-3 and 4-7 walk the two halves of the tile list
 };
 
