@@ -9,8 +9,9 @@ selects another workload of the same family (see workloads.CONFIGS).
 
 Printed (one JSON line): expert-compute TFLOP/s of the layer (value), µs per
 layer (mean, median, p10, p90), HBM GB/s, the stages timed alone
-(stages_us: dispatch, expert compute, combine, and the router top-k ahead of
-dispatch for the softmax-routed workloads), the roofline of the dominant
+(stages_us: dispatch, expert compute, combine, and for the softmax-routed
+workloads the router top-k ahead of dispatch, alone and fused into the
+dispatch kernels), the roofline of the dominant
 kernel (the gate-up grouped GEMM, timed alone with HIP events on the stream it
 is launched on), and the CPU oracle timed on a bounded sample of the same
 workload.  The decode workloads cycle 32 routing draws (seeds 1000..1031) one
@@ -558,9 +559,13 @@ def main():
         w_r = torch.empty_like(w)
         stage_calls = {"router": lambda: ops.router_topk(p, logits, topk_ids=ids_r, topk_weights=w_r),
                        **stage_calls}
+        # the router fused into the dispatch kernels (one launch fewer)
+        stage_calls["router_dispatch"] = lambda: ops.router_dispatch(
+            p, logits, x, topk_ids=ids_r, topk_weights=w_r, workspace=ws,
+            out=(x_disp_s, off_s, row_src_s, token_row_s))
     # long calls first: the spin that short calls sit behind lowers the clock
     # for a while after it
-    order = ["expert_compute", "gate_up", "combine", "dispatch", "router"]
+    order = ["expert_compute", "gate_up", "combine", "dispatch", "router_dispatch", "router"]
     stages_us = {name: timed(stage_calls[name]) * 1e3 for name in order if name in stage_calls}
 
     F_gu = 4.0 * H * I * R

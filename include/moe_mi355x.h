@@ -168,6 +168,43 @@ MOE_API moe_status_t moe_router_topk(const moe_problem_t* p, const float* logits
                                      const int32_t* num_tokens_dev, int32_t* topk_ids,
                                      float* topk_weights, void* stream);
 
+/* The router step fused ahead of dispatch: the dispatch kernels take each
+ * token's top-K of its router logits themselves, with no launch of their own
+ * (TileOps PR #1738, Summary: the routing weights are produced outside expert
+ * compute and carried beside the ids).  For t < T_v and the G = router_experts
+ * logits of token t (fp32 [T, G], finite; -0 equal to +0):
+ *   topk_ids[t, 0..K-1]   out: indices of the K largest logits, decreasing,
+ *                         equal values in increasing index (global ids: only
+ *                         those below num_experts are local, the rest are
+ *                         dropped by the dispatch like any non-local id)
+ *   topk_weights[t, j]    out: exp(l_j - l_0) / sum_{i<K} exp(l_i - l_0) over
+ *                         the selected logits, fp32, summed in increasing j
+ * (the ids and weights moe_router_topk gives with num_experts = G, bit for
+ * bit), then moe_dispatch on those ids: x_disp, expert_offsets, row_src,
+ * token_row as there.  Rows t >= T_v of topk_ids / topk_weights are not
+ * written.  Requires 1 <= K <= G <= 65536 (MOE_ERROR_INVALID_VALUE /
+ * MOE_ERROR_NOT_SUPPORTED otherwise).  topk_ids int32 [T, K], topk_weights
+ * fp32 [T, K], logits 4-byte aligned. */
+MOE_API moe_status_t moe_router_dispatch(const moe_problem_t* p, int32_t router_experts,
+                                         const float* logits, const int32_t* num_tokens_dev,
+                                         int32_t* topk_ids, float* topk_weights,
+                                         const uint16_t* x, uint16_t* x_disp,
+                                         int32_t* expert_offsets, int32_t* row_src,
+                                         int32_t* token_row, void* workspace, size_t ws_bytes,
+                                         void* stream);
+
+/* The whole layer from router logits: the router step fused into the dispatch
+ * (as in moe_router_dispatch; topk_ids / topk_weights are written), then
+ * expert compute and combine.  Equal bit for bit to moe_router_topk (with
+ * num_experts = router_experts) followed by moe_forward on its outputs. */
+MOE_API moe_status_t moe_forward_logits(const moe_problem_t* p, int32_t router_experts,
+                                        const float* logits, const uint16_t* x,
+                                        const uint16_t* w_gateup, const uint16_t* w_down,
+                                        const int32_t* num_tokens_dev, int32_t* topk_ids,
+                                        float* topk_weights, int32_t* expert_offsets,
+                                        uint16_t* out, void* workspace, size_t ws_bytes,
+                                        void* stream);
+
 /* The whole layer: dispatch, expert compute (the row gather fused into the
  * gate-up GEMM's operand loads) and combine, enqueued back to back.
  *   expert_offsets  out int32 [E+1] (the GPU-resident valid-row view)

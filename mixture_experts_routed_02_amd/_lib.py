@@ -26,7 +26,7 @@ EXPORTS = (
     "moe_gate_up_mxfp8", "moe_forward_mxfp8", "moe_mxfp4_quantize", "moe_mxfp4_dequantize",
     "moe_gate_up_mxfp4", "moe_forward_mxfp4", "moe_skinny_pack", "moe_gate_up_packed",
     "moe_forward_packed", "moe_mx_pack", "moe_gate_up_mx_packed", "moe_forward_mx_packed",
-    "moe_forward_noalloc",
+    "moe_forward_noalloc", "moe_router_dispatch", "moe_forward_logits",
 )
 
 # Largest moe_forward workspace that moe_forward_noalloc serves from its
@@ -88,6 +88,10 @@ _SIGS = {
     "moe_forward_mxfp4": (ctypes.c_int, [_PP, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _SZ, _P]),
     "moe_graph_destroy": (ctypes.c_int, [_P]),
     "moe_forward_noalloc": (ctypes.c_int, [_PP, _P, _P, _P, _P, _P, _P, _P, _P, _P]),
+    "moe_router_dispatch": (ctypes.c_int, [_PP, ctypes.c_int32, _P, _P, _P, _P, _P, _P, _P, _P,
+                                           _P, _P, _SZ, _P]),
+    "moe_forward_logits": (ctypes.c_int, [_PP, ctypes.c_int32, _P, _P, _P, _P, _P, _P, _P, _P,
+                                          _P, _P, _SZ, _P]),
 }
 
 _lib = None

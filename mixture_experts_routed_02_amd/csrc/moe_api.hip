@@ -48,8 +48,9 @@ moe_status_t check_problem(const moe_problem_t* p, Shape* s) {
 }
 
 // Workspace layout (every region 256-byte aligned):
-//   blk_counts int32 [(nblk + 1) * E]   (multi-block dispatch only: per-block
-//                                        histograms, scanned in place, + totals)
+//   blk_counts int32 [(rows + 1) * E]   (multi-block dispatch or routed counting
+//                                        only: per-block histograms, scanned in
+//                                        place, + totals)
 //   row_src    int32 [cap]        (moe_forward)
 //   token_row  int32 [T*K]        (moe_forward)
 //   h          bf16  [cap, I]     (expert compute)
@@ -60,10 +61,14 @@ struct Layout {
 
 Layout layout(const Shape& s) {
     Layout L{};
+    // histogram rows: the multi-block dispatch's, or the routed counting's
     const int nblk = moe::dispatch_blocks(s);
+    const int rows = nblk > 1 ? nblk : 0;
+    const int rrows = moe::route_count_rows(s);
+    const int nrows = rows > rrows ? rows : rrows;
     size_t off = 0;
     L.counts = off;
-    off += align_up(nblk > 1 ? (size_t)(nblk + 1) * s.E * 4 : 0);
+    off += align_up(nrows > 0 ? (size_t)(nrows + 1) * s.E * 4 : 0);
     L.row_src = off;
     off += align_up((size_t)s.cap * 4);
     L.token_row = off;
@@ -180,6 +185,47 @@ moe_status_t forward_impl(const Shape& s, int hint, const uint16_t* x, const int
     }
     if (s.T == 0) return MOE_SUCCESS;
     return launched(moe::launch_combine(s, y, token_row, w, ntok, out, st));
+}
+
+// The layer from router logits: the router step fused into the dispatch
+// kernels, then expert compute and combine as in forward_impl.
+moe_status_t forward_logits_impl(const Shape& s, int hint, int G, const float* logits,
+                                 const uint16_t* x, const uint16_t* wgu, const uint16_t* wd,
+                                 const int32_t* ntok, int32_t* ids, float* w, int32_t* offsets,
+                                 uint16_t* out, void* ws, hipStream_t st) {
+    const Layout L = layout(s);
+    int32_t* counts = at<int32_t>(ws, L.counts);
+    int32_t* row_src = at<int32_t>(ws, L.row_src);
+    int32_t* token_row = at<int32_t>(ws, L.token_row);
+    uint16_t* h = at<uint16_t>(ws, L.h);
+    uint16_t* y = at<uint16_t>(ws, L.y);
+    const GemmPlan plan = moe::choose_plan(s, hint);
+    if (moe::launch_router_dispatch(s, logits, G, ntok, ids, w, offsets, row_src, token_row,
+                                    counts, st) != hipSuccess)
+        return MOE_ERROR_LAUNCH;
+    if (plan.kind == moe::kSkinny && moe::tiny_down_ok(s)) {
+        // tiny batch: gate-up, then the down GEMM with the combine inside
+        if (moe::launch_grouped_gemm(s, plan, true, x, row_src, s.K, offsets, wgu, h, s.H, s.I,
+                                     st) != hipSuccess)
+            return MOE_ERROR_LAUNCH;
+        return launched(moe::launch_down_combine_tiny(s, h, offsets, wd, token_row, w, ntok, out,
+                                                      st));
+    }
+    moe_status_t r = expert_compute_impl(s, plan, x, row_src, offsets, wgu, wd, h, y, st);
+    if (r != MOE_SUCCESS) return r;
+    if (s.T == 0) return MOE_SUCCESS;
+    return launched(moe::launch_combine(s, y, token_row, w, ntok, out, st));
+}
+
+// Router arguments: G router experts (logits [T, G]), K <= G.
+moe_status_t check_router(const Shape& s, int32_t G, const float* logits, const int32_t* ids,
+                          const float* w) {
+    if (G < 1 || G > (1 << 16)) return MOE_ERROR_NOT_SUPPORTED;
+    if (s.K > G) return MOE_ERROR_INVALID_VALUE;
+    const long long tk = (long long)s.T * s.K;
+    if (bad_i32(logits, (long long)s.T * G) || bad_i32(ids, tk) || bad_i32(w, tk))
+        return MOE_ERROR_INVALID_VALUE;
+    return MOE_SUCCESS;
 }
 
 // bf16 weights in the skinny pack layout: the skinny plan for every batch size.
@@ -462,6 +508,50 @@ moe_status_t moe_forward(const moe_problem_t* p, const uint16_t* x, const int32_
     return forward_impl(s, p->kernel_hint, x, topk_ids, topk_weights, w_gateup, w_down,
                         num_tokens_dev, expert_offsets, out, workspace,
                         static_cast<hipStream_t>(stream));
+}
+
+moe_status_t moe_router_dispatch(const moe_problem_t* p, int32_t router_experts,
+                                 const float* logits, const int32_t* num_tokens_dev,
+                                 int32_t* topk_ids, float* topk_weights, const uint16_t* x,
+                                 uint16_t* x_disp, int32_t* expert_offsets, int32_t* row_src,
+                                 int32_t* token_row, void* workspace, size_t ws_bytes,
+                                 void* stream) {
+    Shape s;
+    moe_status_t st = check_problem(p, &s);
+    if (st != MOE_SUCCESS) return st;
+    if ((st = check_router(s, router_experts, logits, topk_ids, topk_weights)) != MOE_SUCCESS)
+        return st;
+    const long long tk = (long long)s.T * s.K;
+    if (bad_bf16(x, s.T) || bad_bf16(x_disp, s.cap) || bad_i32(expert_offsets) ||
+        bad_i32(row_src, s.cap) || bad_i32(token_row, tk))
+        return MOE_ERROR_INVALID_VALUE;
+    if (num_tokens_dev && !aligned(num_tokens_dev, 4)) return MOE_ERROR_INVALID_VALUE;
+    if ((st = check_ws(s, workspace, ws_bytes)) != MOE_SUCCESS) return st;
+    hipStream_t hs = static_cast<hipStream_t>(stream);
+    int32_t* counts = at<int32_t>(workspace, layout(s).counts);
+    if (moe::launch_router_dispatch(s, logits, router_experts, num_tokens_dev, topk_ids,
+                                    topk_weights, expert_offsets, row_src, token_row, counts,
+                                    hs) != hipSuccess)
+        return MOE_ERROR_LAUNCH;
+    return launched(moe::launch_gather(s, x, expert_offsets, row_src, x_disp, hs));
+}
+
+moe_status_t moe_forward_logits(const moe_problem_t* p, int32_t router_experts,
+                                const float* logits, const uint16_t* x, const uint16_t* w_gateup,
+                                const uint16_t* w_down, const int32_t* num_tokens_dev,
+                                int32_t* topk_ids, float* topk_weights, int32_t* expert_offsets,
+                                uint16_t* out, void* workspace, size_t ws_bytes, void* stream) {
+    Shape s;
+    // topk_ids / topk_weights are outputs here; the shared checks see them as
+    // the routing arguments
+    moe_status_t st = check_forward_args(p, &s, x, topk_ids, topk_weights, w_gateup, w_down,
+                                         num_tokens_dev, expert_offsets, out, workspace, ws_bytes);
+    if (st != MOE_SUCCESS) return st;
+    if ((st = check_router(s, router_experts, logits, topk_ids, topk_weights)) != MOE_SUCCESS)
+        return st;
+    return forward_logits_impl(s, p->kernel_hint, router_experts, logits, x, w_gateup, w_down,
+                               num_tokens_dev, topk_ids, topk_weights, expert_offsets, out,
+                               workspace, static_cast<hipStream_t>(stream));
 }
 
 moe_status_t moe_forward_noalloc(const moe_problem_t* p, const uint16_t* x,

@@ -36,10 +36,30 @@ inline int dispatch_blocks(const Shape& s) {
     return (int)((n + kDispatchChunk - 1) / kDispatchChunk);
 }
 
+// The router fused into dispatch: up to kRouteSingleMax assignments one
+// block routes and dispatches; above it the routing is done by a counting
+// grid over chunks of kDispatchChunk / ratio assignments (ratio 4 when K <= 4,
+// so that no thread routes more than one token), with route_count_rows(s)
+// histogram rows, then scanned and scattered as in the multi-block dispatch.
+constexpr int kRouteSingleMax = 1024;
+inline int route_count_ratio(int K) { return K <= 4 ? 4 : 1; }
+inline int route_count_rows(const Shape& s) {
+    const long long n = (long long)s.T * s.K;
+    if (n <= kRouteSingleMax) return 0;
+    const long long chunk = kDispatchChunk / route_count_ratio(s.K);
+    return (int)((n + chunk - 1) / chunk);
+}
+
 // ---- launches (each returns hipGetLastError() of its launches) ----------
 hipError_t launch_dispatch(const Shape& s, const int32_t* ids, const int32_t* ntok,
                            int32_t* offsets, int32_t* row_src, int32_t* token_row,
                            int32_t* blk_counts, hipStream_t st);
+// The router step fused ahead of dispatch: ids [T,K] and weights [T,K] (rows
+// t < T_v) from fp32 logits [T,G] (G >= 1 router experts; ids >= E are
+// dropped by the dispatch like any non-local id), then the dispatch on them.
+hipError_t launch_router_dispatch(const Shape& s, const float* logits, int G, const int32_t* ntok,
+                                  int32_t* ids, float* wts, int32_t* offsets, int32_t* row_src,
+                                  int32_t* token_row, int32_t* blk_counts, hipStream_t st);
 hipError_t launch_gather(const Shape& s, const uint16_t* x, const int32_t* offsets,
                          const int32_t* row_src, uint16_t* x_disp, hipStream_t st);
 // C[r, :] for the dispatched rows r < R:

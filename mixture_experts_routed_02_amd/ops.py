@@ -20,7 +20,8 @@ __all__ = [
     "down", "combine",
     "forward", "MoEGraph", "MoeProblem", "mx_quantize", "mx_dequantize", "gate_up_mx", "forward_mx",
     "mxfp8_quantize", "mxfp8_dequantize", "gate_up_mxfp8", "forward_mxfp8", "skinny_pack",
-    "gate_up_packed", "forward_packed", "mx_pack", "forward_noalloc",
+    "gate_up_packed", "forward_packed", "mx_pack", "forward_noalloc", "router_dispatch",
+    "forward_logits",
 ]
 
 
@@ -176,6 +177,61 @@ def router_topk(p: MoeProblem, logits, num_tokens_dev=None, topk_ids=None, topk_
         ctypes.byref(p), _ptr(logits), _ptr(nt), _ptr(topk_ids), _ptr(topk_weights),
         _stream_ptr(dev)))
     return topk_ids, topk_weights
+
+
+def _routing_outs(p, logits, topk_ids, topk_weights):
+    T, K = p.num_tokens, p.top_k
+    dev = logits.device
+    _need(logits, "logits", torch.float32)
+    if logits.dim() != 2 or logits.shape[0] != T:
+        raise ValueError(f"logits must be [{T}, router_experts], got {tuple(logits.shape)}")
+    if topk_ids is None:
+        topk_ids = torch.empty((T, K), dtype=torch.int32, device=dev)
+    if topk_weights is None:
+        topk_weights = torch.empty((T, K), dtype=torch.float32, device=dev)
+    _need(topk_ids, "topk_ids", torch.int32, (T, K), dev)
+    _need(topk_weights, "topk_weights", torch.float32, (T, K), dev)
+    return topk_ids, topk_weights
+
+
+def router_dispatch(p: MoeProblem, logits, x, num_tokens_dev=None, topk_ids=None,
+                    topk_weights=None, workspace=None, out=None):
+    """The router step fused ahead of dispatch, from fp32 logits [T, G] (G router
+    experts; ids >= num_experts are dropped as non-local).  Returns (topk_ids,
+    topk_weights, x_disp, expert_offsets, row_src, token_row)."""
+    T, K, E, H = p.num_tokens, p.top_k, p.num_experts, p.hidden
+    dev = x.device
+    _need(x, "x", torch.bfloat16, (T, H), dev)
+    topk_ids, topk_weights = _routing_outs(p, logits, topk_ids, topk_weights)
+    nt = _ntok(num_tokens_dev, dev)
+    cap = _cap(p)
+    if out is None:
+        out = (torch.empty((cap, H), dtype=torch.bfloat16, device=dev),
+               torch.empty((E + 1,), dtype=torch.int32, device=dev),
+               torch.empty((max(cap, 1),), dtype=torch.int32, device=dev),
+               torch.empty((max(T * K, 1),), dtype=torch.int32, device=dev))
+    x_disp, offsets, row_src, token_row = out
+    ws = make_workspace(p, dev) if workspace is None else workspace
+    check("moe_router_dispatch", lib().moe_router_dispatch(
+        ctypes.byref(p), int(logits.shape[1]), _ptr(logits), _ptr(nt), _ptr(topk_ids),
+        _ptr(topk_weights), _ptr(x), _ptr(x_disp), _ptr(offsets), _ptr(row_src), _ptr(token_row),
+        _ptr(ws), ws.numel(), _stream_ptr(dev)))
+    return topk_ids, topk_weights, x_disp, offsets, row_src, token_row
+
+
+def forward_logits(p: MoeProblem, logits, x, w_gateup, w_down, num_tokens_dev=None,
+                   topk_ids=None, topk_weights=None, expert_offsets=None, out=None,
+                   workspace=None):
+    """The whole layer from router logits [T, G] (router fused into dispatch).
+    Returns (out [T,H], expert_offsets [E+1], topk_ids, topk_weights)."""
+    topk_ids, topk_weights = _routing_outs(p, logits, topk_ids, topk_weights)
+    nt, offsets, out, ws = _forward_args(p, x, topk_ids, topk_weights, w_gateup, w_down,
+                                         num_tokens_dev, expert_offsets, out, workspace)
+    check("moe_forward_logits", lib().moe_forward_logits(
+        ctypes.byref(p), int(logits.shape[1]), _ptr(logits), _ptr(x), _ptr(w_gateup),
+        _ptr(w_down), _ptr(nt), _ptr(topk_ids), _ptr(topk_weights), _ptr(offsets), _ptr(out),
+        _ptr(ws), ws.numel(), _stream_ptr(x.device)))
+    return out, offsets, topk_ids, topk_weights
 
 
 def _forward_args(p, x, topk_ids, topk_weights, w_gateup, w_down, num_tokens_dev, offsets, out,
