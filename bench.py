@@ -383,6 +383,9 @@ def main():
     ap.add_argument("--packed", action="store_true",
                     help="expert weights (bf16) or codes (MX) in the skinny pack layout, packed "
                          "on the device before timing; the skinny plan serves every batch size")
+    ap.add_argument("--tiled-packed", action="store_true",
+                    help="bf16 expert weights in the tiled pack layout (packed on the device "
+                         "before timing); the tiled plans serve every batch size")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-per-config", action="store_true",
                     help="leave out the per_config sweep over the other workloads")
@@ -414,6 +417,12 @@ def main():
     x, ids, w = x_h.to(dev), ids_h.to(dev), w_h.to(dev)
     mx = args.weights in ("mxfp8", "mxfp4")
     packed = args.packed
+    tpacked = args.tiled_packed
+    if tpacked and (mx or packed or args.graph or args.replays):
+        raise SystemExit("--tiled-packed takes bf16 row-major weights and eager launches")
+    if tpacked:
+        tgu, td = ops.tiled_pack(wgu), ops.tiled_pack(wd)
+        torch.cuda.synchronize()
     if packed and not mx:
         if args.graph or args.replays:
             raise SystemExit("--graph / --replays record the row-major layer; use --weights bf16")
@@ -464,6 +473,9 @@ def main():
             elif packed:
                 ops.forward_packed(p, x, ri, rw, pgu, pd, expert_offsets=off, out=out,
                                    workspace=ws)
+            elif tpacked:
+                ops.forward_tiled_packed(p, x, ri, rw, tgu, td, expert_offsets=off, out=out,
+                                         workspace=ws)
             else:
                 ops.forward(p, x, ri, rw, wgu, wd, expert_offsets=off, out=out, workspace=ws)
 
@@ -534,6 +546,8 @@ def main():
                                          packed=packed)
     elif packed:
         gu_call = lambda: ops.gate_up_packed(p, x_disp, off2, pgu, h=hbuf)
+    elif tpacked:
+        gu_call = lambda: ops.gate_up_tiled_packed(p, x_disp, off2, tgu, h=hbuf)
     else:
         gu_call = lambda: ops.gate_up(p, x_disp, off2, wgu, h=hbuf)
     gu_call()
@@ -550,7 +564,7 @@ def main():
                                                      y_disp=y_s),
         "combine": lambda: ops.combine(p, y_s, token_row_s, w, out=out_s),
     }
-    if mx or packed:   # the staged MX / packed calls: the gate-up grouped GEMM alone
+    if mx or packed or tpacked:   # the staged MX / packed calls: the gate-up grouped GEMM alone
         del stage_calls["expert_compute"]
         stage_calls["gate_up"] = gu_call
     if cfg.routing == "softmax_topk":   # the router step ahead of dispatch, on the same seed's logits
@@ -576,11 +590,15 @@ def main():
     kind = args.hint if args.hint in (1, 2, 3, 4) else (1 if rpe <= 24 else 2 if rpe <= 96 else 4)
     if packed:
         kind = 1
+    if tpacked and kind == 1:
+        kind = 2
     kernel_name = "gemm_skinny_kernel" if kind == 1 else "gemm_tiled_kernel"
     if mx:
         kernel_name = f"gemm_skinny_mx_kernel<{8 if args.weights == 'mxfp8' else 4}>"
     if packed:
         kernel_name += " (packed weights)"
+    if tpacked:
+        kernel_name += " (tiled pack layout)"
     traffic = pmc_traffic(f"{kernel_name}<gated>@{cfg.name}", kernel_src_hash(), 1)
     if mfma_bound:
         ach = F_gu / (k_ms / 1e3) / 1e12
@@ -661,7 +679,7 @@ def main():
                                                  else "back-to-back")
                    + (", HIP graph replay" if args.graph else ", eager launches"),
                    "kernel_hint": args.hint,
-                   "packed": packed,
+                   "packed": packed, "tiled_packed": tpacked,
                    "weights": {"bf16": "bf16",
                                "mxfp8": "mxfp8: e4m3 codes + one e8m0 scale per 32 values along K",
                                "mxfp4": "mxfp4: e2m1 codes (two per byte) + one e8m0 scale per "
@@ -678,7 +696,7 @@ def main():
                                               wgu, wd, cfg, budget,
                                               (qgu, sgu, qd, sd) if mx else None, args.weights)
     sweep = (cfg.name == "mixtral" and not args.no_per_config and not mx and not packed
-             and not args.graph and args.hint == 0)
+             and not tpacked and not args.graph and args.hint == 0)
     if sweep:
         del x_disp, hbuf, x_disp_s, y_s, out_s, wgu, wd, ws, out, scratch
         torch.cuda.synchronize()

@@ -293,6 +293,40 @@ MOE_API moe_status_t moe_forward_packed(const moe_problem_t* p, const uint16_t* 
                                         void* stream);
 
 /* ---------------------------------------------------------------------------
+ * Pre-packed bf16 expert weights for the tiled (prefill) kernels (DeepGEMM PR
+ * #394, Summary and Motivation: weights laid out once in the kernel's access
+ * order; Correctness: checked bit for bit against the row-major path).
+ *
+ * moe_tiled_pack rewrites w [experts, rows, k] (bf16; rows % 32 == 0, k % 64
+ * == 0) into packed of the same size: for expert e, 8-row group g and stage s
+ * (k-values 64s .. 64s+63) one contiguous 1 KiB block of 64 pieces of 8
+ * values, piece L = row 8g + L/8, k-values 64s + 8c .. +7 with
+ * c = (L % 8) ^ swz((8g + L/8) % 32), swz(r) = ((r >> 1) & 3) | ((r >> 2) & 4):
+ * exactly the 1 KiB one DMA instruction of the tiled kernels stages, in LDS
+ * slot order.  Both W_gateup [E, 2I, H] and W_down [E, H, I] are packed the
+ * same way.  w and packed must not overlap; both 16-byte aligned.
+ * ------------------------------------------------------------------------- */
+MOE_API moe_status_t moe_tiled_pack(const uint16_t* w, int32_t experts, int32_t rows, int32_t k,
+                                    uint16_t* packed, void* stream);
+
+/* moe_gate_up / moe_forward on weights packed by moe_tiled_pack.  They run a
+ * tiled plan (kernel_hint 2, 3, 4, or 0: the automatic choice, with the
+ * 64-row tiled plan where it would pick the skinny one; kernel_hint 1 returns
+ * MOE_ERROR_NOT_SUPPORTED) and are bit-identical to moe_gate_up / moe_forward
+ * with that plan on the row-major weights. */
+MOE_API moe_status_t moe_gate_up_tiled_packed(const moe_problem_t* p, const uint16_t* x_disp,
+                                              const int32_t* expert_offsets,
+                                              const uint16_t* w_gateup_packed, uint16_t* h,
+                                              void* stream);
+MOE_API moe_status_t moe_forward_tiled_packed(const moe_problem_t* p, const uint16_t* x,
+                                              const int32_t* topk_ids, const float* topk_weights,
+                                              const uint16_t* w_gateup_packed,
+                                              const uint16_t* w_down_packed,
+                                              const int32_t* num_tokens_dev,
+                                              int32_t* expert_offsets, uint16_t* out,
+                                              void* workspace, size_t ws_bytes, void* stream);
+
+/* ---------------------------------------------------------------------------
  * MXFP8 expert weights (FlashInfer PR #3980: the MXFP8 MegaMoE backend; its
  * combine-wire notes name the format, 32 e4m3 values sharing one e8m0 scale).
  * TileOps PR #1738, Scope, leaves FP8 outside its BF16 path; this is the

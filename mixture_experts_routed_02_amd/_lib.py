@@ -26,7 +26,8 @@ EXPORTS = (
     "moe_gate_up_mxfp8", "moe_forward_mxfp8", "moe_mxfp4_quantize", "moe_mxfp4_dequantize",
     "moe_gate_up_mxfp4", "moe_forward_mxfp4", "moe_skinny_pack", "moe_gate_up_packed",
     "moe_forward_packed", "moe_mx_pack", "moe_gate_up_mx_packed", "moe_forward_mx_packed",
-    "moe_forward_noalloc", "moe_router_dispatch", "moe_forward_logits",
+    "moe_forward_noalloc", "moe_router_dispatch", "moe_forward_logits", "moe_tiled_pack",
+    "moe_gate_up_tiled_packed", "moe_forward_tiled_packed",
 )
 
 # Largest moe_forward workspace that moe_forward_noalloc serves from its
@@ -92,6 +93,9 @@ _SIGS = {
                                            _P, _P, _SZ, _P]),
     "moe_forward_logits": (ctypes.c_int, [_PP, ctypes.c_int32, _P, _P, _P, _P, _P, _P, _P, _P,
                                           _P, _P, _SZ, _P]),
+    "moe_tiled_pack": (ctypes.c_int, [_P, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, _P, _P]),
+    "moe_gate_up_tiled_packed": (ctypes.c_int, [_PP, _P, _P, _P, _P, _P]),
+    "moe_forward_tiled_packed": (ctypes.c_int, [_PP, _P, _P, _P, _P, _P, _P, _P, _P, _P, _SZ, _P]),
 }
 
 _lib = None

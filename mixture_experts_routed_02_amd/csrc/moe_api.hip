@@ -102,12 +102,22 @@ moe_status_t check_ws(const Shape& s, const void* ws, size_t ws_bytes) {
 moe_status_t expert_compute_impl(const Shape& s, const GemmPlan& plan, const uint16_t* a,
                                  const int32_t* row_src, const int32_t* offsets,
                                  const uint16_t* wgu, const uint16_t* wd, uint16_t* h,
-                                 uint16_t* y, hipStream_t st) {
+                                 uint16_t* y, hipStream_t st, bool tiled_packed = false) {
     hipError_t e = moe::launch_grouped_gemm(s, plan, true, a, row_src, s.K, offsets, wgu, h, s.H,
-                                            s.I, st);
+                                            s.I, st, tiled_packed);
     if (e != hipSuccess) return MOE_ERROR_LAUNCH;
-    e = moe::launch_grouped_gemm(s, plan, false, h, nullptr, 1, offsets, wd, y, s.I, s.H, st);
+    e = moe::launch_grouped_gemm(s, plan, false, h, nullptr, 1, offsets, wd, y, s.I, s.H, st,
+                                 tiled_packed);
     return launched(e);
+}
+
+// Plan for weights in the tiled pack layout: a tiled plan (hint 2..4, or the
+// automatic choice with the skinny plan replaced by the 64-row tiled one).
+bool tiled_plan(const moe_problem_t* p, const Shape& s, GemmPlan* plan) {
+    if (p->kernel_hint == moe::kSkinny) return false;
+    *plan = moe::choose_plan(s, p->kernel_hint);
+    if (plan->kind == moe::kSkinny) *plan = moe::choose_plan(s, moe::kTiled64);
+    return true;
 }
 
 // Everything moe_forward checks except the workspace.
@@ -552,6 +562,65 @@ moe_status_t moe_forward_logits(const moe_problem_t* p, int32_t router_experts,
     return forward_logits_impl(s, p->kernel_hint, router_experts, logits, x, w_gateup, w_down,
                                num_tokens_dev, topk_ids, topk_weights, expert_offsets, out,
                                workspace, static_cast<hipStream_t>(stream));
+}
+
+moe_status_t moe_tiled_pack(const uint16_t* w, int32_t experts, int32_t rows, int32_t k,
+                            uint16_t* packed, void* stream) {
+    if (experts < 0 || rows <= 0 || k <= 0 || rows % 32 != 0 || k % 64 != 0)
+        return MOE_ERROR_INVALID_VALUE;
+    if ((long long)experts * rows > (1ll << 40) / k) return MOE_ERROR_NOT_SUPPORTED;
+    if (experts == 0) return MOE_SUCCESS;
+    if (bad_bf16(w) || bad_bf16(packed)) return MOE_ERROR_INVALID_VALUE;
+    const uintptr_t n = (uintptr_t)experts * rows * k * 2, a = (uintptr_t)w, b = (uintptr_t)packed;
+    if (a < b + n && b < a + n) return MOE_ERROR_INVALID_VALUE;   // overlapping buffers
+    return launched(moe::launch_tiled_pack(w, experts, rows, k, packed,
+                                           static_cast<hipStream_t>(stream)));
+}
+
+moe_status_t moe_gate_up_tiled_packed(const moe_problem_t* p, const uint16_t* x_disp,
+                                      const int32_t* expert_offsets,
+                                      const uint16_t* w_gateup_packed, uint16_t* h,
+                                      void* stream) {
+    Shape s;
+    moe_status_t st = check_problem(p, &s);
+    if (st != MOE_SUCCESS) return st;
+    GemmPlan plan;
+    if (!tiled_plan(p, s, &plan)) return MOE_ERROR_NOT_SUPPORTED;
+    if (bad_bf16(x_disp, s.cap) || bad_i32(expert_offsets) || bad_bf16(w_gateup_packed) ||
+        bad_bf16(h, s.cap))
+        return MOE_ERROR_INVALID_VALUE;
+    return launched(moe::launch_grouped_gemm(s, plan, true, x_disp, nullptr, s.K, expert_offsets,
+                                             w_gateup_packed, h, s.H, s.I,
+                                             static_cast<hipStream_t>(stream), true));
+}
+
+moe_status_t moe_forward_tiled_packed(const moe_problem_t* p, const uint16_t* x,
+                                      const int32_t* topk_ids, const float* topk_weights,
+                                      const uint16_t* w_gateup_packed,
+                                      const uint16_t* w_down_packed,
+                                      const int32_t* num_tokens_dev, int32_t* expert_offsets,
+                                      uint16_t* out, void* workspace, size_t ws_bytes,
+                                      void* stream) {
+    Shape s;
+    moe_status_t st = check_forward_args(p, &s, x, topk_ids, topk_weights, w_gateup_packed,
+                                         w_down_packed, num_tokens_dev, expert_offsets, out,
+                                         workspace, ws_bytes);
+    if (st != MOE_SUCCESS) return st;
+    GemmPlan plan;
+    if (!tiled_plan(p, s, &plan)) return MOE_ERROR_NOT_SUPPORTED;
+    hipStream_t hs = static_cast<hipStream_t>(stream);
+    const Layout L = layout(s);
+    int32_t* row_src = at<int32_t>(workspace, L.row_src);
+    int32_t* token_row = at<int32_t>(workspace, L.token_row);
+    if (moe::launch_dispatch(s, topk_ids, num_tokens_dev, expert_offsets, row_src, token_row,
+                             at<int32_t>(workspace, L.counts), hs) != hipSuccess)
+        return MOE_ERROR_LAUNCH;
+    st = expert_compute_impl(s, plan, x, row_src, expert_offsets, w_gateup_packed, w_down_packed,
+                             at<uint16_t>(workspace, L.h), at<uint16_t>(workspace, L.y), hs, true);
+    if (st != MOE_SUCCESS) return st;
+    if (s.T == 0) return MOE_SUCCESS;
+    return launched(moe::launch_combine(s, at<uint16_t>(workspace, L.y), token_row, topk_weights,
+                                        num_tokens_dev, out, hs));
 }
 
 moe_status_t moe_forward_noalloc(const moe_problem_t* p, const uint16_t* x,

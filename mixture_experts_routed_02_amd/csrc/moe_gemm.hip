@@ -1174,7 +1174,7 @@ __device__ __forceinline__ int wave_tile_lookup(const int32_t* offsets, int E, i
     return __builtin_amdgcn_readfirstlane(carry);
 }
 
-template <int BM, int BN, int WGM, int WGN, bool GATED, bool SUBSKIP = false>
+template <int BM, int BN, int WGM, int WGN, bool GATED, bool SUBSKIP = false, bool PACKED = false>
 __global__ __launch_bounds__(64 * WGM * WGN) void gemm_tiled_kernel(
     const uint16_t* __restrict__ A, const int32_t* __restrict__ row_src, int topk,
     const int32_t* __restrict__ offsets, const uint16_t* __restrict__ W,
@@ -1301,7 +1301,11 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_tiled_kernel(
             const long long arow = row_src ? (long long)(row_src[rr] / topk) : (long long)rr;
             asrc[q] = A + (size_t)arow * Kd + dma_chunk * 8;
         }
-        const uint16_t* wbase = W + (size_t)e * w_rows * Kd + (size_t)dma_row * Kd + dma_chunk * 8;
+        // row-major: lane (dma_row, slot) reads chunk dma_chunk of its row;
+        // PACKED (tiled pack layout): the 1 KiB of a group and stage is
+        // contiguous and already in slot order, so lane L reads piece L
+        const uint16_t* wbase = PACKED ? W + (size_t)e * w_rows * Kd + lane * 8
+                                       : W + (size_t)e * w_rows * Kd + (size_t)dma_row * Kd + dma_chunk * 8;
         auto wrow0 = [&](int q) {   // first weight row of this wave's weight group q
             const int tr = (wave + NW * q) * 8;
             if (GATED) return (tr < BN / 2) ? (n_tile * (BN / 2) + tr) : (N + n_tile * (BN / 2) + tr - BN / 2);
@@ -1314,7 +1318,9 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_tiled_kernel(
                           ringA0 + (sa % SA) * A_STAGE + (wave + NW * q) * 1024);
             } else {
                 const int qw = q - GA;
-                lds_dma16(wbase + (size_t)wrow0(qw) * Kd + (size_t)sw * kBK,
+                // packed: group wrow0/8 holds Kd/64 stages of 512 values each
+                lds_dma16(PACKED ? wbase + (size_t)wrow0(qw) * Kd + (size_t)sw * 512
+                                 : wbase + (size_t)wrow0(qw) * Kd + (size_t)sw * kBK,
                           ringW0 + (sw % SW) * W_STAGE + (wave + NW * qw) * 1024);
             }
         };
@@ -1492,11 +1498,46 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_tiled_kernel(
 template <int BM, int BN, int WGM, int WGN, bool GATED, bool SUBSKIP = false>
 hipError_t launch_tiled(int grid, const uint16_t* A, const int32_t* row_src, int topk,
                         const int32_t* offsets, const uint16_t* W, uint16_t* C, int E, int Kd,
-                        int N, int split, hipStream_t st) {
-    hipLaunchKernelGGL((gemm_tiled_kernel<BM, BN, WGM, WGN, GATED, SUBSKIP>), dim3(grid),
-                       dim3(64 * WGM * WGN), 0, st, A, row_src, topk, offsets, W, C, E, Kd, N,
-                       split);
+                        int N, int split, hipStream_t st, bool packed) {
+    if (packed)
+        hipLaunchKernelGGL((gemm_tiled_kernel<BM, BN, WGM, WGN, GATED, SUBSKIP, true>), dim3(grid),
+                           dim3(64 * WGM * WGN), 0, st, A, row_src, topk, offsets, W, C, E, Kd, N,
+                           split);
+    else
+        hipLaunchKernelGGL((gemm_tiled_kernel<BM, BN, WGM, WGN, GATED, SUBSKIP, false>), dim3(grid),
+                           dim3(64 * WGM * WGN), 0, st, A, row_src, topk, offsets, W, C, E, Kd, N,
+                           split);
     return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// Tiled pack layout (DeepGEMM PR #394, Summary and Motivation: weights laid
+// out once in the order the kernel reads them).  The tiled kernel stages a
+// weight tile as 1 KiB DMA pieces of 8 rows x 64 k-values, row r's 16-byte
+// chunk c in LDS slot c ^ ring_swz(r % 32).  The pack stores, for expert e,
+// 8-row group g and stage s (k-values 64s .. 64s+63), those 1 KiB
+// contiguously and in slot order: piece L (0..63) = row 8g + L/8, k-values
+// 64s + 8c .. +7 with c = (L % 8) ^ ring_swz((8g + L/8) % 32).  Weight tiles
+// start at rows that are multiples of 32, so the swizzle a row gets in LDS is
+// the one applied here.  Same size as the row-major weights.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void tiled_pack_kernel(const uint16_t* __restrict__ w,
+                                                         long long pieces, int rows, int Kd,
+                                                         uint16_t* __restrict__ out) {
+    const long long i = (long long)blockIdx.x * blockDim.x + threadIdx.x;   // output piece
+    if (i >= pieces) return;
+    const int nk = Kd / kBK;
+    const int L = (int)(i & 63);
+    const long long t = i >> 6;
+    const int st = (int)(t % nk);
+    const long long eg = t / nk;                       // e * (rows / 8) + g
+    const int groups = rows / 8;
+    const long long e = eg / groups;
+    const int r = (int)(eg % groups) * 8 + (L >> 3);
+    const int c = (L & 7) ^ ring_swz(r & 31);
+    const moe_bf16x8* src = reinterpret_cast<const moe_bf16x8*>(
+        w + ((size_t)e * rows + r) * (size_t)Kd + (size_t)st * kBK + c * 8);
+    reinterpret_cast<moe_bf16x8*>(out)[i] = *src;
 }
 
 }  // namespace
@@ -1661,6 +1702,15 @@ hipError_t launch_grouped_gemm_packed(const Shape& s, bool gated, const uint16_t
     return hipGetLastError();
 }
 
+hipError_t launch_tiled_pack(const uint16_t* w, int experts, int rows, int Kd, uint16_t* out,
+                             hipStream_t st) {
+    const long long pieces = (long long)experts * rows * (Kd / 8);
+    if (pieces == 0) return hipSuccess;
+    hipLaunchKernelGGL(tiled_pack_kernel, dim3((unsigned)((pieces + 255) / 256)), dim3(256), 0, st,
+                       w, pieces, rows, Kd, out);
+    return hipGetLastError();
+}
+
 hipError_t launch_skinny_pack(const uint16_t* w, int experts, int rows, int Kd, bool gated,
                               uint16_t* out, hipStream_t st) {
     const long long pieces = (long long)experts * rows * (Kd / 8);
@@ -1709,14 +1759,15 @@ GemmPlan choose_plan(const Shape& s, int hint) {
 hipError_t launch_grouped_gemm(const Shape& s, const GemmPlan& plan, bool gated,
                                const uint16_t* A, const int32_t* row_src, int topk,
                                const int32_t* offsets, const uint16_t* W, uint16_t* C, int Kd,
-                               int N, hipStream_t st) {
+                               int N, hipStream_t st, bool tiled_packed) {
     const int grid = gated ? plan.grid_gateup : plan.grid_down;
     const int bn = gated ? plan.bn_gateup : plan.bn_down;
     const int split = plan.split ? 1 : 0;
 #define MOE_TILED(BM, BN, WGM, WGN, G) \
-    launch_tiled<BM, BN, WGM, WGN, G>(grid, A, row_src, topk, offsets, W, C, s.E, Kd, N, split, st)
+    launch_tiled<BM, BN, WGM, WGN, G>(grid, A, row_src, topk, offsets, W, C, s.E, Kd, N, split, st, tiled_packed)
 #define MOE_TILED_S(BM, BN, WGM, WGN, G) \
-    launch_tiled<BM, BN, WGM, WGN, G, true>(grid, A, row_src, topk, offsets, W, C, s.E, Kd, N, split, st)
+    launch_tiled<BM, BN, WGM, WGN, G, true>(grid, A, row_src, topk, offsets, W, C, s.E, Kd, N, split, st, tiled_packed)
+    if (tiled_packed && plan.kind == kSkinny) return hipErrorInvalidValue;   // checked on the host
     switch (plan.kind) {
         case kSkinny:
             if (gated)

@@ -66,10 +66,17 @@ hipError_t launch_gather(const Shape& s, const uint16_t* x, const int32_t* offse
 //   gated: C = bf16(silu(A W_gate^T) * (A W_up^T)), W = [E, 2N, Kd], C: [cap, N]
 //   plain: C = bf16(A W^T),                            W = [E, N, Kd],  C: [cap, N]
 // A row of dispatched row r is A[row_src ? row_src[r] / topk : r].
+// tiled_packed: W is in the tiled pack layout (launch_tiled_pack); the plan
+// must be a tiled one.
 hipError_t launch_grouped_gemm(const Shape& s, const GemmPlan& plan, bool gated,
                                const uint16_t* A, const int32_t* row_src, int topk,
                                const int32_t* offsets, const uint16_t* W, uint16_t* C,
-                               int Kd, int N, hipStream_t st);
+                               int Kd, int N, hipStream_t st, bool tiled_packed = false);
+// bf16 weights [experts, rows, Kd] (rows % 32 == 0, Kd % 64 == 0) -> tiled pack
+// layout: per expert, 8-row group and 64-value stage, the 1 KiB the tiled
+// kernel's DMA instruction stages, contiguous and in LDS slot order.
+hipError_t launch_tiled_pack(const uint16_t* w, int experts, int rows, int Kd, uint16_t* out,
+                             hipStream_t st);
 // Gate-up GEMM of the skinny plan with the local dispatch done inside: every
 // workgroup builds the dispatch of the T*K (<= kFusedDispatchMax) assignments
 // in LDS; workgroup 0 also writes expert_offsets, row_src and token_row.

@@ -21,7 +21,7 @@ __all__ = [
     "forward", "MoEGraph", "MoeProblem", "mx_quantize", "mx_dequantize", "gate_up_mx", "forward_mx",
     "mxfp8_quantize", "mxfp8_dequantize", "gate_up_mxfp8", "forward_mxfp8", "skinny_pack",
     "gate_up_packed", "forward_packed", "mx_pack", "forward_noalloc", "router_dispatch",
-    "forward_logits",
+    "forward_logits", "tiled_pack", "gate_up_tiled_packed", "forward_tiled_packed",
 ]
 
 
@@ -296,6 +296,52 @@ def skinny_pack(w, gated: bool, out=None):
     check("moe_skinny_pack", lib().moe_skinny_pack(_ptr(w), E, rows, K, int(bool(gated)), _ptr(out),
                                                    _stream_ptr(w.device)))
     return out
+
+
+def tiled_pack(w, out=None):
+    """Pack bf16 weights [E, rows, K] for the tiled kernels (W_gateup or W_down)."""
+    _need(w, "w", torch.bfloat16)
+    if w.dim() != 3:
+        raise ValueError("w must be [experts, rows, k]")
+    E, rows, K = w.shape
+    if out is None:
+        out = torch.empty_like(w)
+    _need(out, "out", torch.bfloat16, tuple(w.shape), w.device)
+    check("moe_tiled_pack", lib().moe_tiled_pack(_ptr(w), E, rows, K, _ptr(out),
+                                                 _stream_ptr(w.device)))
+    return out
+
+
+def gate_up_tiled_packed(p: MoeProblem, x_disp, expert_offsets, w_gateup_packed, h=None):
+    """Gate-up grouped GEMM on weights in the tiled pack layout.  Returns h [cap, I]."""
+    E, H, I = p.num_experts, p.hidden, p.intermediate
+    dev = x_disp.device
+    cap = _cap(p)
+    _need(x_disp, "x_disp", torch.bfloat16, (cap, H))
+    _need(expert_offsets, "expert_offsets", torch.int32, (E + 1,), dev)
+    _need(w_gateup_packed, "w_gateup_packed", torch.bfloat16, (E, 2 * I, H), dev)
+    if h is None:
+        h = torch.empty((cap, I), dtype=torch.bfloat16, device=dev)
+    _need(h, "h", torch.bfloat16, (cap, I), dev)
+    check("moe_gate_up_tiled_packed", lib().moe_gate_up_tiled_packed(
+        ctypes.byref(p), _ptr(x_disp), _ptr(expert_offsets), _ptr(w_gateup_packed), _ptr(h),
+        _stream_ptr(dev)))
+    return h
+
+
+def forward_tiled_packed(p: MoeProblem, x, topk_ids, topk_weights, w_gateup_packed,
+                         w_down_packed, num_tokens_dev=None, expert_offsets=None, out=None,
+                         workspace=None):
+    """The routed-expert layer on weights in the tiled pack layout (tiled plans).
+    Returns (out, expert_offsets)."""
+    nt, offsets, out, ws = _forward_args(p, x, topk_ids, topk_weights, w_gateup_packed,
+                                         w_down_packed, num_tokens_dev, expert_offsets, out,
+                                         workspace)
+    check("moe_forward_tiled_packed", lib().moe_forward_tiled_packed(
+        ctypes.byref(p), _ptr(x), _ptr(topk_ids), _ptr(topk_weights), _ptr(w_gateup_packed),
+        _ptr(w_down_packed), _ptr(nt), _ptr(offsets), _ptr(out), _ptr(ws), ws.numel(),
+        _stream_ptr(x.device)))
+    return out, offsets
 
 
 def gate_up_packed(p: MoeProblem, x_disp, expert_offsets, w_gateup_packed, h=None):

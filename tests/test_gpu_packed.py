@@ -273,3 +273,98 @@ def test_forward_packed_ep_decode_vs_oracle(name):
     ref = oracle.forward(bits(x_h), ids_h.numpy(), w_h.numpy(), DeviceExperts(wgu),
                          DeviceExperts(wd), workers=oracle_workers())
     check_close(f64(got), ref, f"packed {name}")
+
+
+# ---------------------------------------------------------------------------
+# the tiled pack layout (moe_tiled_pack) and the tiled plans on it
+# ---------------------------------------------------------------------------
+def expected_tiled_pack(w_bits):
+    """Written from the layout's definition: per expert, 8-row group g and
+    64-value stage s, piece L = row 8g + L/8, k-values 64s + 8c .. +7 with
+    c = (L % 8) ^ swz((8g + L/8) % 32)."""
+    E, rows, K = w_bits.shape
+    G, S = rows // 8, K // 64
+    L = np.arange(64)
+    r = 8 * np.arange(G)[:, None] + (L // 8)[None, :]                   # [G, 64]
+    rm = r % 32
+    c = (L % 8)[None, :] ^ (((rm >> 1) & 3) | ((rm >> 2) & 4))          # [G, 64]
+    k = 64 * np.arange(S)[None, :, None, None] + 8 * c[:, None, :, None] + np.arange(8)
+    out = w_bits[:, r[:, None, :, None], k]                              # [E, G, S, 64, 8]
+    return out.reshape(E, rows, K)
+
+
+@pytest.mark.parametrize("E,rows,K", [(3, 64, 256), (2, 96, 192), (1, 2048, 64), (5, 32, 512)])
+def test_tiled_pack_layout(E, rows, K):
+    g = torch.Generator().manual_seed(E * rows + K + 1)
+    w = torch.randn((E, rows, K), generator=g).to(torch.bfloat16)
+    got = ops.tiled_pack(w.to(DEV))
+    assert np.array_equal(bits(got), expected_tiled_pack(bits(w)))
+
+
+TILED_SHAPES = {
+    "ragged": (300, 4, 16, 512, 384, -1, 18),
+    "i_320": (97, 3, 5, 192, 320, 0, 5),            # gate-up on 128-row weight tiles
+    "many_experts_split": (2048, 2, 64, 256, 1024, 0, 64),
+    "large_plan": (2016, 2, 4, 512, 1024, 0, 4),    # ~1008 rows per expert: 192 x 256 tiles
+}
+
+
+@pytest.mark.parametrize("name", list(TILED_SHAPES))
+@pytest.mark.parametrize("hint", [0, 2, 3, 4])
+def test_forward_tiled_packed(name, hint):
+    """Bit-identical to moe_forward with the same tiled plan on row-major
+    weights, and within the oracle's bar."""
+    T, K, E, H, I, lo, hi = TILED_SHAPES[name]
+    x, ids, w, wgu, wd = case(T, K, E, H, I, 26, lo, hi)
+    p = moe.problem(T, K, E, H, I, 0, hint)
+    pgu, pd = ops.tiled_pack(wgu), ops.tiled_pack(wd)
+    got, off = ops.forward_tiled_packed(p, x, ids, w, pgu, pd)
+    ref_hint = hint if hint else (2 if T * K / E <= 24 else 0)
+    ref, ref_off = ops.forward(p if ref_hint == hint else moe.problem(T, K, E, H, I, 0, ref_hint),
+                               x, ids, w, wgu, wd)
+    assert torch.equal(off, ref_off)
+    assert torch.equal(got.view(torch.int16), ref.view(torch.int16))
+    x_disp, o2, _, _ = ops.dispatch(p, x, ids)
+    pr = moe.problem(T, K, E, H, I, 0, ref_hint)
+    h_ref = ops.gate_up(pr, x_disp, o2, wgu)
+    h = ops.gate_up_tiled_packed(p, x_disp, o2, pgu)
+    R = int(o2[-1])
+    assert torch.equal(h[:R].view(torch.int16), h_ref[:R].view(torch.int16))
+    ids_h = ids.cpu().numpy()
+    ref_o = oracle.forward(bits(x), ids_h, w.cpu().numpy(), bits(wgu), bits(wd))
+    check_close(f64(got), ref_o, f"tiled packed {name}/hint{hint}")
+
+
+def test_tiled_packed_refuses_the_skinny_plan():
+    T, K, E, H, I, lo, hi = TILED_SHAPES["ragged"]
+    x, ids, w, wgu, wd = case(T, K, E, H, I, 27, lo, hi)
+    p = moe.problem(T, K, E, H, I, 0, moe.HINT_SKINNY)
+    with pytest.raises(moe.MoeError):
+        ops.forward_tiled_packed(p, x, ids, w, ops.tiled_pack(wgu), ops.tiled_pack(wd))
+
+
+@pytest.mark.parametrize("name,seed", [("ep_prefill_T8192", 0), ("ep_prefill_T2048_zipf", 1),
+                                       ("mixtral", 0)])
+def test_forward_tiled_packed_full_size(name, seed):
+    """Full-size prefill and Mixtral-style layers: bit-identical to the
+    row-major tiled path (which test_gpu_parity checks against the oracle),
+    and 64 covering tokens against the oracle directly."""
+    cfg = W.CONFIGS[name]
+    T, K, E, H, I = cfg.num_tokens, cfg.top_k, cfg.num_experts, cfg.hidden, cfg.intermediate
+    x_h = W.make_x(cfg, seed)
+    ids_h, w_h = W.make_routing(cfg, seed)
+    wgu, wd = W.make_weights(cfg, seed, DEV)
+    p = moe.problem(T, K, E, H, I)
+    x, ids, w = x_h.to(DEV), ids_h.to(DEV), w_h.to(DEV)
+    ref, _ = ops.forward(p, x, ids, w, wgu, wd)
+    pgu = ops.tiled_pack(wgu)
+    pd = ops.tiled_pack(wd)
+    got, _ = ops.forward_tiled_packed(p, x, ids, w, pgu, pd)
+    torch.cuda.synchronize()
+    del pgu, pd
+    assert torch.equal(got.view(torch.int16), ref.view(torch.int16))
+    from helpers import covering_tokens
+    toks = covering_tokens(ids_h.numpy(), E, 64, seed=seed)
+    r = oracle.forward_tokens(bits(x_h), ids_h.numpy(), w_h.numpy(), DeviceExperts(wgu),
+                              DeviceExperts(wd), toks, workers=oracle_workers())
+    check_close(f64(got)[toks], r, f"tiled packed {name}")
