@@ -277,10 +277,11 @@ moe_status_t forward_packed_impl(const Shape& s, const uint16_t* x, const int32_
 bool bad_codes(const void* p) { return !p || !aligned(p, 16); }
 bool bad_scales(const void* p, int fmt) { return !p || !aligned(p, fmt == 8 ? 2 : 4); }
 
-moe_status_t check_mx_problem(const moe_problem_t* p, int fmt, Shape* s) {
+moe_status_t check_mx_problem(const moe_problem_t* p, int fmt, Shape* s, bool packed = false) {
     moe_status_t st = check_problem(p, s);
     if (st != MOE_SUCCESS) return st;
-    if (p->kernel_hint != 0 && p->kernel_hint != moe::kSkinny) return MOE_ERROR_NOT_SUPPORTED;
+    // packed codes: the skinny kernels only
+    if (packed && p->kernel_hint != 0 && p->kernel_hint != moe::kSkinny) return MOE_ERROR_NOT_SUPPORTED;
     if (fmt == 4 && (s->H % 128 != 0 || s->I % 128 != 0)) return MOE_ERROR_NOT_SUPPORTED;
     return MOE_SUCCESS;
 }
@@ -289,14 +290,15 @@ moe_status_t forward_mx_impl(const Shape& s, int fmt, const uint16_t* x, const i
                              const float* w, const uint8_t* qgu, const uint8_t* sgu,
                              const uint8_t* qd, const uint8_t* sd, const int32_t* ntok,
                              int32_t* offsets, uint16_t* out, void* ws, hipStream_t st,
-                             bool packed) {
+                             bool packed, int hint) {
     const Layout L = layout(s);
     int32_t* counts = at<int32_t>(ws, L.counts);
     int32_t* row_src = at<int32_t>(ws, L.row_src);
     int32_t* token_row = at<int32_t>(ws, L.token_row);
     uint16_t* h = at<uint16_t>(ws, L.h);
     uint16_t* y = at<uint16_t>(ws, L.y);
-    if ((long long)s.T * s.K <= moe::kFusedDispatchMax) {
+    const bool skinny = packed || moe::choose_plan(s, hint).kind == moe::kSkinny;
+    if (skinny && (long long)s.T * s.K <= moe::kFusedDispatchMax) {
         if (moe::launch_gateup_fused_dispatch_mx(s, fmt, x, ids, ntok, offsets, row_src, token_row,
                                                  qgu, sgu, h, st, packed) != hipSuccess)
             return MOE_ERROR_LAUNCH;
@@ -308,11 +310,11 @@ moe_status_t forward_mx_impl(const Shape& s, int fmt, const uint16_t* x, const i
             hipSuccess)
             return MOE_ERROR_LAUNCH;
         if (moe::launch_grouped_gemm_mx(s, fmt, true, x, row_src, s.K, offsets, qgu, sgu, h, s.H,
-                                        s.I, st, packed) != hipSuccess)
+                                        s.I, st, packed, hint) != hipSuccess)
             return MOE_ERROR_LAUNCH;
     }
     if (moe::launch_grouped_gemm_mx(s, fmt, false, h, nullptr, 1, offsets, qd, sd, y, s.I, s.H,
-                                    st, packed) != hipSuccess)
+                                    st, packed, hint) != hipSuccess)
         return MOE_ERROR_LAUNCH;
     if (s.T == 0) return MOE_SUCCESS;
     return launched(moe::launch_combine(s, y, token_row, w, ntok, out, st));
@@ -350,14 +352,15 @@ moe_status_t gate_up_mx(int fmt, const moe_problem_t* p, const uint16_t* x_disp,
                         const int32_t* expert_offsets, const uint8_t* codes, const uint8_t* scales,
                         uint16_t* h, void* stream, bool packed = false) {
     Shape s;
-    moe_status_t st = check_mx_problem(p, fmt, &s);
+    moe_status_t st = check_mx_problem(p, fmt, &s, packed);
     if (st != MOE_SUCCESS) return st;
     if (bad_bf16(x_disp, s.cap) || bad_i32(expert_offsets) || bad_codes(codes) ||
         bad_scales(scales, fmt) || bad_bf16(h, s.cap))
         return MOE_ERROR_INVALID_VALUE;
     return launched(moe::launch_grouped_gemm_mx(s, fmt, true, x_disp, nullptr, s.K,
                                                 expert_offsets, codes, scales, h, s.H, s.I,
-                                                static_cast<hipStream_t>(stream), packed));
+                                                static_cast<hipStream_t>(stream), packed,
+                                                p->kernel_hint));
 }
 
 moe_status_t forward_mx(int fmt, const moe_problem_t* p, const uint16_t* x,
@@ -366,7 +369,7 @@ moe_status_t forward_mx(int fmt, const moe_problem_t* p, const uint16_t* x,
                         const int32_t* num_tokens_dev, int32_t* expert_offsets, uint16_t* out,
                         void* workspace, size_t ws_bytes, void* stream, bool packed = false) {
     Shape s;
-    moe_status_t st = check_mx_problem(p, fmt, &s);
+    moe_status_t st = check_mx_problem(p, fmt, &s, packed);
     if (st != MOE_SUCCESS) return st;
     const long long tk = (long long)s.T * s.K;
     if (bad_bf16(x, s.T) || bad_i32(topk_ids, tk) || bad_i32(topk_weights, tk) ||
@@ -377,7 +380,7 @@ moe_status_t forward_mx(int fmt, const moe_problem_t* p, const uint16_t* x,
     if ((st = check_ws(s, workspace, ws_bytes)) != MOE_SUCCESS) return st;
     return forward_mx_impl(s, fmt, x, topk_ids, topk_weights, qgu, sgu, qd, sd, num_tokens_dev,
                            expert_offsets, out, workspace, static_cast<hipStream_t>(stream),
-                           packed);
+                           packed, p->kernel_hint);
 }
 
 struct GraphHandle {

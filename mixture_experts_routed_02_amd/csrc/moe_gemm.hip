@@ -1107,7 +1107,7 @@ typedef __attribute__((address_space(3))) unsigned char lds_u8;
 // the whole ring with vmcnt(0) before each read); the ring's own explicit
 // vmcnt waits and barriers order these writes against the reads.  m0 is
 // written here only; the kernels below use it for nothing else.
-__device__ __forceinline__ void lds_dma16(const uint16_t* g, uint32_t lds_base) {
+__device__ __forceinline__ void lds_dma16(const void* g, uint32_t lds_base) {
     asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off"
                  :: "v"(g), "s"(__builtin_amdgcn_readfirstlane(lds_base)) : "memory", "m0");
 }
@@ -1138,6 +1138,18 @@ __device__ __forceinline__ void lds_barrier() {
 
 // chunk swizzle of row r (see above)
 __device__ __forceinline__ int ring_swz(int r) { return ((r >> 1) & 3) | ((r >> 2) & 4); }
+
+// MX weight stages (see gemm_tiled_kernel, WF != 16): a 64-value stage of a
+// weight row is 64 bytes of e4m3 codes (four 16-byte chunks) or 32 bytes of
+// e2m1 codes (two), chunk c of row r stored in slot c ^ swz(r % 32).  The 16
+// lanes of a ds_read_b128 pass read one chunk of rows {r..r+7, r+16..r+23},
+// which these swizzles put on 16 distinct 16-byte bank groups.
+__device__ __forceinline__ int mx8_swz(int r) { return ((r >> 2) & 1) | ((r >> 3) & 2); }
+__device__ __forceinline__ int mx4_swz(int r) { return (r >> 4) & 1; }
+
+// Scale bytes of one weight row kept in LDS by the MX tiled kernels: up to
+// this many 32-value blocks (K <= 7168).
+constexpr int kMxMaxKBlocks = 224;
 
 // Tile table of the tiled kernel, recomputed by each wave from expert_offsets
 // when it needs it (no LDS): expert e owns ceil(M_e / BM) * n_tiles logical
@@ -1174,24 +1186,33 @@ __device__ __forceinline__ int wave_tile_lookup(const int32_t* offsets, int E, i
     return __builtin_amdgcn_readfirstlane(carry);
 }
 
-template <int BM, int BN, int WGM, int WGN, bool GATED, bool SUBSKIP = false, bool PACKED = false>
+template <int BM, int BN, int WGM, int WGN, bool GATED, bool SUBSKIP = false, bool PACKED = false,
+          int WF = 16>
 __global__ __launch_bounds__(64 * WGM * WGN) void gemm_tiled_kernel(
     const uint16_t* __restrict__ A, const int32_t* __restrict__ row_src, int topk,
     const int32_t* __restrict__ offsets, const uint16_t* __restrict__ W,
-    uint16_t* __restrict__ C, int E, int Kd, int N, int split) {
+    uint16_t* __restrict__ C, int E, int Kd, int N, int split,
+    const uint8_t* __restrict__ Ws = nullptr) {
+    // WF: weight format, 16 = bf16, 8 = MXFP8 (e4m3 codes), 4 = MXFP4 (e2m1
+    // codes, two per byte); the MX formats take e8m0 scales Ws [E, rows, Kd/32]
+    constexpr bool MX = WF != 16;
     constexpr int NT = 64 * WGM * WGN, NW = NT / 64;  // threads, waves
     constexpr int WM = BM / WGM, WN = BN / WGN;       // per-wave extent
     constexpr int MS = WM / 32, NS = WN / 32;         // 32x32 sub-tiles per wave
     constexpr int COLS = GATED ? BN / 2 : BN;         // output columns per tile
-    constexpr int AG = BM / 8, WG = BN / 8;           // 1 KiB groups per stage
+    constexpr int RBW = WF == 16 ? 128 : (WF == 8 ? 64 : 32);   // weight-row bytes per stage
+    constexpr int WROWS = 1024 / RBW;                 // weight rows per 1 KiB DMA group
+    constexpr int AG = BM / 8, WG = BN / WROWS;       // 1 KiB groups per stage
     constexpr int GA = AG / NW, GW = WG / NW;         // DMA instructions per wave per stage
     constexpr int A_STAGE = AG * 1024, W_STAGE = WG * 1024;
-    constexpr int BUDGET = ring_budget(NW);
+    constexpr int SCL = MX ? BN * kMxMaxKBlocks : 0;  // the tile's scales (MX), bytes
+    constexpr int BUDGET = ring_budget(NW) - SCL;
     constexpr int SA = ring_sa(A_STAGE, W_STAGE, BUDGET);
     constexpr int SW = ring_sw(A_STAGE, W_STAGE, BUDGET);
     constexpr int OP = 2 * COLS + 8;                  // epilogue staging pitch, bytes
     constexpr int RINGS = SA * A_STAGE + SW * W_STAGE;
-    constexpr int LDS = RINGS > BM * OP ? RINGS : BM * OP;
+    constexpr int SCL_OFF = RINGS > BM * OP ? RINGS : BM * OP;
+    constexpr int LDS = SCL_OFF + SCL;
     // loads issued after the ones a wait needs: at an odd half (stage d+1),
     // and in the prologue (stage 0)
     constexpr int N_STEADY = SW > SA ? (SA - 1) * GW + (SA - 2) * GA : (SA - 2) * (GA + GW);
@@ -1199,7 +1220,8 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_tiled_kernel(
     static_assert(WM % 32 == 0 && WN % 32 == 0 && AG % NW == 0 && WG % NW == 0, "tile shape");
     static_assert(NW % 4 == 0, "a wave's DMA groups share one row-swizzle phase");
     static_assert(!GATED || NS % 2 == 0, "gated tiles pair gate and up sub-tiles");
-    static_assert(SA >= 2 && SW >= SA && LDS <= BUDGET, "ring sizes");
+    static_assert(SA >= 2 && SW >= SA && LDS <= ring_budget(NW), "ring sizes");
+    static_assert(!MX || (!PACKED && (WF == 8 || WF == 4)), "MX: row-major codes");
     static_assert(N_FIRST < 64 && N_STEADY < 64, "vmcnt range");
 
     __shared__ __attribute__((aligned(1024))) unsigned char s_lds[LDS];
@@ -1229,13 +1251,36 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_tiled_kernel(
     // wave % 4 for every group this wave fills (g = wave + NW*q).
     const int dma_row = lane >> 3;
     const int dma_chunk = (lane & 7) ^ ring_swz((wave & 3) * 8 + dma_row);
-    // fragment-read offsets of this lane inside a 32-row block for the four
-    // 16-wide k steps of a stage: row l%32, chunk 2*s + l/32
+    // MX weight groups: 16 rows x 64 bytes (lane: row lane/4, slot lane%4) or
+    // 32 rows x 32 bytes (row lane/2, slot lane%2); a 16-row group's rows are
+    // rows 16*(g%2).. of its 32-row block, and g % 2 = wave % 2 for every
+    // group this wave fills
+    const int wdma_row = WF == 16 ? dma_row : (WF == 8 ? lane >> 2 : lane >> 1);
+    const int wdma_chunk = WF == 16 ? dma_chunk
+                         : WF == 8 ? (lane & 3) ^ mx8_swz((wave & 1) * 16 + wdma_row)
+                                   : (lane & 1) ^ mx4_swz(wdma_row);
+    // fragment-read offsets of this lane inside a 32-row token block for the
+    // four 16-wide k steps m of a stage: row l%32 and the k-chunk (8 values)
+    // that lane group l/32 supplies to MFMA m.  bf16 weights: chunk 2m + l/32
+    // on both operands.  MX weights set the k order: a lane group reads 16
+    // consecutive codes of its row per half-stage (e4m3: k = 32q + 16g + 0..15
+    // for MFMAs 2q, 2q+1) or 32 per stage (e2m1: k = 32g + 0..31 for MFMAs
+    // 0..3), so the token chunk of MFMA m is 4(m/2) + 2g + m%2, or 4g + m.
     const int fr = lane & 31, fh = lane >> 5;
     int rd_off[4];
 #pragma unroll
-    for (int s = 0; s < 4; ++s) rd_off[s] = fr * 128 + (((2 * s + fh) ^ ring_swz(fr)) << 4);
-    int ga[MS], gw[NS];   // byte offsets of this wave's 32-row blocks in a stage
+    for (int s = 0; s < 4; ++s) {
+        const int ch = WF == 16 ? 2 * s + fh : WF == 8 ? 4 * (s >> 1) + 2 * fh + (s & 1) : 4 * fh + s;
+        rd_off[s] = fr * 128 + ((ch ^ ring_swz(fr)) << 4);
+    }
+    // MX weight fragments: byte offset of this lane's 16 code bytes in its
+    // 32-row block for half-stage q (e4m3) / the stage (e2m1)
+    int wro[2];
+#pragma unroll
+    for (int q = 0; q < 2; ++q)
+        wro[q] = WF == 8 ? fr * 64 + (((2 * q + fh) ^ mx8_swz(fr)) << 4)
+                         : fr * 32 + ((fh ^ mx4_swz(fr)) << 4);
+    int ga[MS], gw[NS], wtr[NS];   // byte offsets of this wave's 32-row blocks in a stage
 #pragma unroll
     for (int j = 0; j < MS; ++j) ga[j] = (wm * WM + j * 32) * 128;
 #pragma unroll
@@ -1244,8 +1289,11 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_tiled_kernel(
         if (GATED) trow = (i < NS / 2) ? (wn * (WN / 2) + i * 32)
                                        : (BN / 2 + wn * (WN / 2) + (i - NS / 2) * 32);
         else trow = wn * WN + i * 32;
-        gw[i] = trow * 128;
+        gw[i] = trow * RBW;
+        wtr[i] = trow;
     }
+    const int sp = Kd / 32;                           // scale bytes per weight row (MX)
+    const size_t wrow_bytes = (size_t)Kd * WF / 8;    // bytes of one weight row
 
     // split (many experts): XCDs 0-3 walk the first half of the tile list and
     // XCDs 4-7 the second, each XCD still over contiguous runs, so that the
@@ -1306,8 +1354,12 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_tiled_kernel(
         // contiguous and already in slot order, so lane L reads piece L
         const uint16_t* wbase = PACKED ? W + (size_t)e * w_rows * Kd + lane * 8
                                        : W + (size_t)e * w_rows * Kd + (size_t)dma_row * Kd + dma_chunk * 8;
+        // MX: byte address of this lane's 16 code bytes (row wdma_row of a group,
+        // chunk wdma_chunk), stage 0
+        const unsigned char* wbase_mx = reinterpret_cast<const unsigned char*>(W) +
+                                        ((size_t)e * w_rows + wdma_row) * wrow_bytes + wdma_chunk * 16;
         auto wrow0 = [&](int q) {   // first weight row of this wave's weight group q
-            const int tr = (wave + NW * q) * 8;
+            const int tr = (wave + NW * q) * WROWS;
             if (GATED) return (tr < BN / 2) ? (n_tile * (BN / 2) + tr) : (N + n_tile * (BN / 2) + tr - BN / 2);
             return n_tile * BN + tr;
         };
@@ -1318,10 +1370,12 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_tiled_kernel(
                           ringA0 + (sa % SA) * A_STAGE + (wave + NW * q) * 1024);
             } else {
                 const int qw = q - GA;
-                // packed: group wrow0/8 holds Kd/64 stages of 512 values each
-                lds_dma16(PACKED ? wbase + (size_t)wrow0(qw) * Kd + (size_t)sw * 512
-                                 : wbase + (size_t)wrow0(qw) * Kd + (size_t)sw * kBK,
-                          ringW0 + (sw % SW) * W_STAGE + (wave + NW * qw) * 1024);
+                const uint32_t dst = ringW0 + (sw % SW) * W_STAGE + (wave + NW * qw) * 1024;
+                if constexpr (MX)
+                    lds_dma16(wbase_mx + (size_t)wrow0(qw) * wrow_bytes + (size_t)sw * RBW, dst);
+                else    // packed: group wrow0/8 holds Kd/64 stages of 512 values each
+                    lds_dma16(PACKED ? wbase + (size_t)wrow0(qw) * Kd + (size_t)sw * 512
+                                     : wbase + (size_t)wrow0(qw) * Kd + (size_t)sw * kBK, dst);
             }
         };
 
@@ -1343,6 +1397,35 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_tiled_kernel(
             const unsigned char* st = s_ringW + ((h >> 1) % SW) * W_STAGE;
             fw[sk][i] = *reinterpret_cast<const moe_bf16x8*>(st + gw[i] + rd_off[2 * (h & 1) + sk]);
         };
+        // MX weights: the lane's 16 code bytes for half h (e4m3) or for stage
+        // h/2 (e2m1), and the two scale bytes of its row for stage d (blocks
+        // 2d, 2d+1), read a half ahead; dequant_w turns them into the half's
+        // two bf16 fragments at its start
+        moe_u32x4 wraw[MX ? NS : 1];
+        uint32_t wsc[MX ? NS : 1];
+        auto read_w_raw = [&](int h, int i) {
+            const unsigned char* st = s_ringW + ((h >> 1) % SW) * W_STAGE;
+            wraw[i] = *reinterpret_cast<const moe_u32x4*>(st + gw[i] + wro[WF == 8 ? (h & 1) : 0]);
+        };
+        auto read_w_scale = [&](int d, int i) {
+            const int dd = d < nk ? d : nk - 1;   // past the last stage: any valid byte
+            wsc[i] = *reinterpret_cast<const uint16_t*>(s_lds + SCL_OFF + (wtr[i] + fr) * sp + 2 * dd);
+        };
+        auto dequant_w = [&](auto PAR) {
+            constexpr int P = decltype(PAR)::value;   // half parity
+#pragma unroll
+            for (int i = 0; i < NS; ++i) {
+                if constexpr (WF == 8) {   // block 2d + P for both fragments
+                    const float sc = mx_scale_operand((wsc[i] >> (8 * P)) & 0xffu);
+                    fw[0][i] = mx_dequant8(wraw[i][0], wraw[i][1], sc);
+                    fw[1][i] = mx_dequant8(wraw[i][2], wraw[i][3], sc);
+                } else if constexpr (WF == 4) {   // block 2d + lane group
+                    const float sc = mx_scale_operand((wsc[i] >> (8 * fh)) & 0xffu);
+                    fw[0][i] = mx_dequant8_fp4(wraw[i][2 * P], sc);
+                    fw[1][i] = mx_dequant8_fp4(wraw[i][2 * P + 1], sc);
+                }
+            }
+        };
         // half h: multiply it from registers while reading half h+1 into the
         // same registers (each fragment right after its last MFMA of half h),
         // and, if rf, spread the loads of one refill between the MFMA groups:
@@ -1355,7 +1438,10 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_tiled_kernel(
                 if (kKind == 1) issue_one(stage, 0, q);
                 else issue_one(0, stage, GA + q);
             };
+            // weight refills happen in even halves, token refills in odd ones
+            constexpr int kPar = kKind == 1 ? 1 : 0;
             if (active) {
+                if constexpr (MX) dequant_w(std::integral_constant<int, kPar>{});
 #pragma unroll
                 for (int sk = 0; sk < 2; ++sk)
 #pragma unroll
@@ -1366,7 +1452,12 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_tiled_kernel(
                                 acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fw[sk][i], fa[sk][j], acc[i][j], 0, 0, 0);
                             if (i == NS - 1) read_a(h + 1, sk, j);
                         }
-                        read_w(h + 1, sk, i);
+                        if constexpr (!MX) {
+                            read_w(h + 1, sk, i);
+                        } else if (sk == 1) {   // codes (and at a new stage, scales) of half h+1
+                            if (WF == 8 || kPar == 1) read_w_raw(h + 1, i);
+                            if (kPar == 1) read_w_scale((h + 1) >> 1, i);
+                        }
                         constexpr int SLOTS = 2 * NS;
                         const int slot = sk * NS + i;
                         if (GP > 0 && (GP >= SLOTS || (slot * GP) / SLOTS != ((slot + 1) * GP) / SLOTS)) {
@@ -1383,6 +1474,22 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_tiled_kernel(
         const std::integral_constant<int, 1> tokens{};
         const std::integral_constant<int, 2> weights{};
 
+        // MX: the tile's scale rows into LDS first (the wait for stage 0 below
+        // covers them): tile-row order, i.e. gated the BN/2 gate rows, then the
+        // BN/2 up rows, each part a contiguous run of Ws copied in 1 KiB pieces
+        if constexpr (MX) {
+            const int part_bytes = (GATED ? BN / 2 : BN) * sp;   // a multiple of 1024
+            const int pieces = (GATED ? 2 : 1) * (part_bytes >> 10);
+            const unsigned char* s0 =
+                Ws + ((size_t)e * w_rows + (GATED ? n_tile * (BN / 2) : n_tile * BN)) * sp;
+            const unsigned char* s1 = Ws + ((size_t)e * w_rows + N + n_tile * (BN / 2)) * sp;
+            const uint32_t ringS0 = lds_addr(s_lds + SCL_OFF);
+            for (int pc = wave; pc < pieces; pc += NW) {
+                const int part = (pc << 10) >= part_bytes ? 1 : 0;
+                lds_dma16((part ? s1 : s0) + ((pc << 10) - part * part_bytes) + lane * 16,
+                          ringS0 + (pc << 10));
+            }
+        }
         // prologue: the loads the k loop would have issued in earlier halves,
         // in that order (weights s in half 2(s-SW+1), tokens s in half
         // 2(s-SA)+1); then wait for stage 0
@@ -1407,8 +1514,17 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_tiled_kernel(
             for (int sk = 0; sk < 2; ++sk) {
 #pragma unroll
                 for (int j = 0; j < MS; ++j) read_a(0, sk, j);
+                if constexpr (!MX) {
 #pragma unroll
-                for (int i = 0; i < NS; ++i) read_w(0, sk, i);
+                    for (int i = 0; i < NS; ++i) read_w(0, sk, i);
+                }
+            }
+            if constexpr (MX) {
+#pragma unroll
+                for (int i = 0; i < NS; ++i) {
+                    read_w_raw(0, i);
+                    read_w_scale(0, i);
+                }
             }
         }
         // Stage d: half 2d refills weights of stage d+SW-1 (slot of stage d-1,
@@ -1508,6 +1624,50 @@ hipError_t launch_tiled(int grid, const uint16_t* A, const int32_t* row_src, int
                            dim3(64 * WGM * WGN), 0, st, A, row_src, topk, offsets, W, C, E, Kd, N,
                            split);
     return hipGetLastError();
+}
+
+template <int WF, int BM, int BN, int WGM, int WGN, bool GATED>
+hipError_t launch_tiled_mx(int grid, const uint16_t* A, const int32_t* row_src, int topk,
+                           const int32_t* offsets, const uint8_t* Wq, const uint8_t* Ws,
+                           uint16_t* C, int E, int Kd, int N, int split, hipStream_t st) {
+    // every wave fills whole weight groups (16 rows for e4m3, 32 for e2m1):
+    // the plan below never asks for the shapes that cannot
+    if constexpr ((BN / (WF == 8 ? 16 : 32)) % (WGM * WGN) != 0) {
+        return hipErrorInvalidValue;
+    } else {
+        hipLaunchKernelGGL((gemm_tiled_kernel<BM, BN, WGM, WGN, GATED, true, false, WF>), dim3(grid),
+                           dim3(64 * WGM * WGN), 0, st, A, row_src, topk, offsets,
+                           reinterpret_cast<const uint16_t*>(Wq), C, E, Kd, N, split, Ws);
+        return hipGetLastError();
+    }
+}
+
+template <int WF>
+hipError_t launch_grouped_gemm_mx_tiled(const GemmPlan& plan, bool gated, const uint16_t* A,
+                                        const int32_t* row_src, int topk, const int32_t* offsets,
+                                        const uint8_t* Wq, const uint8_t* Ws, uint16_t* C, int E,
+                                        int Kd, int N, hipStream_t st) {
+    const int grid = gated ? plan.grid_gateup : plan.grid_down;
+    const int bn = gated ? plan.bn_gateup : plan.bn_down;
+    const int split = plan.split ? 1 : 0;
+#define MOE_TILED_MX(BM, BN, WGM, WGN, G) \
+    launch_tiled_mx<WF, BM, BN, WGM, WGN, G>(grid, A, row_src, topk, offsets, Wq, Ws, C, E, Kd, N, split, st)
+    switch (plan.kind) {
+        case kTiled64:
+            if (gated) return MOE_TILED_MX(64, 128, 2, 2, true);
+            return bn == 128 ? MOE_TILED_MX(64, 128, 2, 2, false) : MOE_TILED_MX(64, 64, 2, 2, false);
+        case kTiled128:
+            if (gated) return MOE_TILED_MX(128, 128, 2, 2, true);
+            return bn == 128 ? MOE_TILED_MX(128, 128, 2, 2, false) : MOE_TILED_MX(128, 64, 2, 2, false);
+        default:
+            if (gated) return bn == 256 ? MOE_TILED_MX(192, 256, 2, 4, true) : MOE_TILED_MX(256, 128, 4, 2, true);
+            if (bn == 256) return MOE_TILED_MX(192, 256, 2, 4, false);
+            // 128 weight rows hold four 32-row e2m1 groups: too few for 8 waves
+            if (bn == 128) return WF == 4 ? MOE_TILED_MX(128, 128, 2, 2, false)
+                                          : MOE_TILED_MX(192, 128, 2, 4, false);
+            return MOE_TILED_MX(128, 64, 2, 2, false);
+    }
+#undef MOE_TILED_MX
 }
 
 // ---------------------------------------------------------------------------
@@ -1647,10 +1807,22 @@ static void launch_skinny_mx(bool gated, bool wide, const uint16_t* A, const int
     }
 }
 
+bool mx_tiled_ok(int Kd) { return Kd % 512 == 0 && Kd / 32 <= kMxMaxKBlocks; }
+
 hipError_t launch_grouped_gemm_mx(const Shape& s, int fmt, bool gated, const uint16_t* A,
                                   const int32_t* row_src, int topk, const int32_t* offsets,
                                   const uint8_t* Wq, const uint8_t* Ws, uint16_t* C, int Kd, int N,
-                                  hipStream_t st, bool packed) {
+                                  hipStream_t st, bool packed, int hint) {
+    // the tiled plan where the bf16 layer would take one and the tile's scales
+    // fit in LDS (row-major codes only); else the skinny kernels
+    const GemmPlan plan = choose_plan(s, hint);
+    if (!packed && plan.kind != kSkinny && mx_tiled_ok(Kd)) {
+        if (fmt == 8)
+            return launch_grouped_gemm_mx_tiled<8>(plan, gated, A, row_src, topk, offsets, Wq, Ws,
+                                                   C, s.E, Kd, N, st);
+        return launch_grouped_gemm_mx_tiled<4>(plan, gated, A, row_src, topk, offsets, Wq, Ws, C,
+                                               s.E, Kd, N, st);
+    }
     const bool wide = mx_wide(fmt, s);
     if (fmt == 8 && packed)
         launch_skinny_mx<8, true>(gated, wide, A, row_src, topk, offsets, Wq, Ws, C, s.E, Kd, N, st);

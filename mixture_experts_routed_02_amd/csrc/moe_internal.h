@@ -122,10 +122,15 @@ hipError_t launch_down_combine_tiny_mx(const Shape& s, int fmt, const uint16_t* 
                                        const uint8_t* Ws, const int32_t* token_row, const float* w,
                                        const int32_t* ntok, uint16_t* out, hipStream_t st,
                                        bool packed = false);
+// The grouped GEMM on MX weights: the tiled plan (MFMA tiles of the bf16
+// plan, codes staged through LDS and dequantized on the fragment reads, the
+// tile's scales in LDS) when choose_plan(s, hint) is a tiled one, the codes
+// are row-major and mx_tiled_ok(Kd); else the skinny MX kernels.
+bool mx_tiled_ok(int Kd);
 hipError_t launch_grouped_gemm_mx(const Shape& s, int fmt, bool gated, const uint16_t* A,
                                   const int32_t* row_src, int topk, const int32_t* offsets,
                                   const uint8_t* Wq, const uint8_t* Ws, uint16_t* C, int Kd, int N,
-                                  hipStream_t st, bool packed = false);
+                                  hipStream_t st, bool packed = false, int hint = 0);
 // nblocks blocks of 32 consecutive bf16 values <-> 32 codes + 1 scale each
 hipError_t launch_mx_quantize(int fmt, const uint16_t* w, long long nblocks, uint8_t* codes,
                               uint8_t* scales, hipStream_t st);

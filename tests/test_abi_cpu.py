@@ -128,10 +128,10 @@ def test_mxfp8_entry_points_fail_closed():
     args = list(good)
     args[11] = ws - 1
     assert fwd(p, *args) == _lib.MOE_ERROR_INVALID_VALUE
-    for hint in (2, 3, 4):                      # only the skinny plan serves MXFP8 weights
+    for hint in (2, 3, 4):                      # codes in the skinny pack layout: skinny plan only
         q = moe.problem(64, 2, 8, 256, 512, kernel_hint=hint)
-        assert fwd(q, *good) == _lib.MOE_ERROR_NOT_SUPPORTED
-        assert L.moe_gate_up_mxfp8(ctypes.byref(q), A16, A4, A16, A16, A16, None) == 2
+        assert L.moe_forward_mx_packed(ctypes.byref(q), 8, *good) == _lib.MOE_ERROR_NOT_SUPPORTED
+        assert L.moe_gate_up_mx_packed(ctypes.byref(q), 8, A16, A4, A16, A16, A16, None) == 2
     assert L.moe_gate_up_mxfp8(ctypes.byref(p), A16, A4, A16, A16 + 1, A16, None) == 1
     # quantize / dequantize: k a positive multiple of 32, aligned buffers
     assert L.moe_mxfp8_quantize(A16, 4, 48, A16, A16, None) == 1
@@ -158,8 +158,8 @@ def test_mxfp4_entry_points_fail_closed():
         args = list(good)
         args[i] = bad
         assert L.moe_forward_mxfp4(ctypes.byref(p), *args) == _lib.MOE_ERROR_INVALID_VALUE, i
-    assert L.moe_gate_up_mxfp4(ctypes.byref(moe.problem(64, 2, 8, 256, 512, kernel_hint=4)),
-                               A16, A4, A16, A16, A16, None) == 2
+    assert L.moe_gate_up_mx_packed(ctypes.byref(moe.problem(64, 2, 8, 256, 512, kernel_hint=4)),
+                                   4, A16, A4, A16, A16, A16, None) == 2
     assert L.moe_mxfp4_quantize(A16, 4, 48, A16, A16, None) == 1
     assert L.moe_mxfp4_dequantize(A16, A16, 4, 32, A16 + 2, None) == 1
 

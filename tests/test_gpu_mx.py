@@ -222,3 +222,110 @@ def test_forward_mx_ep_decode_full_size(fmt, name, seed):
         del wgu_e, wd_e
     ref = ORACLE[fmt][3](bits(x), ids.numpy(), w.numpy(), *Q, toks)
     check_close(f64(out)[toks], ref, name)
+
+
+# ---------------------------------------------------------------------------
+# the tiled (prefill) plans on MX weights: codes staged through LDS and
+# dequantized on the fragment reads, the tile's scales in LDS; chosen where
+# the bf16 layer takes a tiled plan and K is a multiple of 512 (<= 7168)
+# ---------------------------------------------------------------------------
+TILED = {
+    # name: (T, K, E, H, I, id_lo, id_hi)
+    "ragged_64": (300, 4, 16, 512, 512, -1, 18),        # ~75 rows per expert: 64-row tiles
+    "gate_only_tiled": (97, 3, 5, 1024, 1536, 0, 5),    # down K = 1536: 512-multiple too
+    "large_ragged": (2016, 2, 4, 512, 1024, 0, 4),      # ~1008 rows per expert: 192 x 256
+    "many_experts_split": (2048, 2, 64, 512, 512, 0, 64),
+}
+
+
+@pytest.mark.parametrize("fmt", FMTS)
+@pytest.mark.parametrize("name", list(TILED))
+@pytest.mark.parametrize("hint", [0, 2, 3, 4])
+def test_forward_mx_tiled(fmt, name, hint):
+    T, K, E, H, I, lo, hi = TILED[name]
+    x, ids, w, qgu, sgu, qd, sd = quantized_case(fmt, T, K, E, H, I, 15, lo, hi)
+    p = moe.problem(T, K, E, H, I, 0, hint)
+    out, off = run_forward(fmt, p, x, ids, w, qgu, sgu, qd, sd)
+    _, ref_off, _, _ = oracle.dispatch(ids.numpy(), E)
+    assert np.array_equal(off.cpu().numpy(), ref_off)
+    ref = ORACLE[fmt][2](bits(x), ids.numpy(), w.numpy(), qgu, sgu, qd, sd)
+    check_close(f64(out), ref, f"{name}/hint{hint}")
+    out2, _ = run_forward(fmt, p, x, ids, w, qgu, sgu, qd, sd)
+    assert torch.equal(out.view(torch.int16), out2.view(torch.int16))
+
+
+def test_forward_mxfp8_tiled_gate_up_128_rows():
+    """I % 128 != 0: the large plan's gate-up on 256 x 128 tiles (4 x 2 waves)
+    with MXFP8 codes; the down GEMM (K = I = 320) stays on the skinny
+    kernels."""
+    T, K, E, H, I = 2016, 2, 4, 512, 320
+    x, ids, w, qgu, sgu, qd, sd = quantized_case("mxfp8", T, K, E, H, I, 16, 0, 4)
+    p = moe.problem(T, K, E, H, I, 0, 4)
+    out, _ = run_forward("mxfp8", p, x, ids, w, qgu, sgu, qd, sd)
+    ref = ORACLE["mxfp8"][2](bits(x), ids.numpy(), w.numpy(), qgu, sgu, qd, sd)
+    check_close(f64(out), ref, "gate-up 256 x 128")
+
+
+@pytest.mark.parametrize("fmt", FMTS)
+def test_forward_mx_tiled_device_token_count_and_dropped(fmt):
+    T, K, E, H, I = 700, 4, 16, 512, 512
+    x, ids, w, qgu, sgu, qd, sd = quantized_case(fmt, T, K, E, H, I, 17, -2, 20)
+    p = moe.problem(T, K, E, H, I, 0, 4)
+    for tv in (0, 1, 333, 700):
+        nt = torch.tensor([tv], dtype=torch.int32, device=DEV)
+        out, off = run_forward(fmt, p, x, ids, w, qgu, sgu, qd, sd, nt)
+        _, ref_off, _, _ = oracle.dispatch(ids.numpy(), E, tv)
+        assert np.array_equal(off.cpu().numpy(), ref_off)
+        ref = ORACLE[fmt][2](bits(x), ids.numpy(), w.numpy(), qgu, sgu, qd, sd, tv)
+        check_close(f64(out[:tv]), ref[:tv], f"tv={tv}")
+
+
+@pytest.mark.parametrize("fmt", FMTS)
+@pytest.mark.parametrize("hint", [2, 4])
+def test_gate_up_mx_tiled_staged(fmt, hint):
+    T, K, E, H, I = 600, 2, 6, 1024, 512
+    x, ids, w, qgu, sgu, qd, sd = quantized_case(fmt, T, K, E, H, I, 18)
+    p = moe.problem(T, K, E, H, I, 0, hint)
+    x_disp, off, rs, _ = ops.dispatch(p, x.to(DEV), ids.to(DEV))
+    h = ops.gate_up_mx(p, x_disp, off, torch.from_numpy(qgu).to(DEV), torch.from_numpy(sgu).to(DEV),
+                       fmt)
+    o = off.cpu().numpy()
+    R = int(o[-1])
+    xr = oracle.bf16_to_f64(bits(x_disp)[:R])
+    ref = np.zeros((R, I))
+    for e in range(E):
+        a, b = int(o[e]), int(o[e + 1])
+        if a == b:
+            continue
+        wgu = ORACLE[fmt][1](qgu[e], sgu[e])
+        ref[a:b] = oracle.silu(xr[a:b] @ wgu[:I].T) * (xr[a:b] @ wgu[I:].T)
+    check_close(f64(h)[:R], ref, f"h hint {hint}")
+
+
+@pytest.mark.parametrize("fmt", FMTS)
+@pytest.mark.parametrize("name,seed", [("ep_prefill_T8192", 0), ("ep_prefill_T2048_zipf", 1)])
+def test_forward_mx_ep_prefill_full_size(fmt, name, seed):
+    """The 96-expert prefill share at full size on device-quantized weights
+    (the quantizer is checked bit for bit above): at least 128 covering
+    tokens against the oracle's MX layer."""
+    from helpers import covering_tokens, oracle_workers
+    cfg = W.CONFIGS[name]
+    T, K, E, H, I = cfg.num_tokens, cfg.top_k, cfg.num_experts, cfg.hidden, cfg.intermediate
+    x = W.make_x(cfg, seed)
+    ids, w = W.make_routing(cfg, seed)
+    wgu, wd = W.make_weights(cfg, seed, DEV)
+    qgu, sgu = ops.mx_quantize(wgu, fmt)
+    qd, sd = ops.mx_quantize(wd, fmt)
+    del wgu, wd
+    torch.cuda.empty_cache()
+    p = moe.problem(T, K, E, H, I)
+    out, off = ops.forward_mx(p, x.to(DEV), ids.to(DEV), w.to(DEV), qgu, sgu, qd, sd, fmt)
+    torch.cuda.synchronize()
+    _, ref_off, _, _ = oracle.dispatch(ids.numpy(), E)
+    assert np.array_equal(off.cpu().numpy(), ref_off)
+    toks = covering_tokens(ids.numpy(), E, 128, seed=seed)
+    deq = ORACLE[fmt][1]
+    widen = lambda e: (deq(u8(qgu[e]), u8(sgu[e])), deq(u8(qd[e]), u8(sd[e])))
+    ref = oracle.forward_tokens_widened(bits(x), ids.numpy(), w.numpy(), E, widen, toks,
+                                        workers=oracle_workers())
+    check_close(f64(out)[toks], ref, f"{fmt} {name}")
