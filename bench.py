@@ -25,7 +25,9 @@ With the default workload the same line also carries `per_config`: every
 other full-size workload measured in the same run, each with µs/layer, its
 binding-roof fraction (and MFMA / HBM fractions beside it) and the gate-up
 kernel's own roofline: the 96-of-384 decode shares T = 1, 8, 32, 128 (cold:
-L2/MALL evicted before each step, 32 routing draws cycled), the prefill
+L2/MALL evicted before each step, 32 routing draws cycled; each also timed
+as replays of the layer recorded as a HIP graph, `graph_replay`, and at T = 1
+through the single-launch forward, `single_launch`), the prefill
 shares T = 2048, 8192 with uniform routing (seeds 0-2) and Zipf s = 1.2
 routing (seeds 0-4, reported per seed), and the static-capacity layer (50
 HIP-graph replays with a device token count T_i ~ U{1..2048}, and the full
@@ -282,6 +284,46 @@ def per_config_sweep(dev, kernel_reps: int):
                                           f"seeds {seeds}"),
                "valid_rows_mean": statistics.fmean(w_[2] for w_ in work),
                "experts_touched_mean": statistics.fmean(w_[3] for w_ in work)}
+        if kind == "decode":
+            # the same draws, cold, through (a) replays of the layer recorded as
+            # a HIP graph (no host launch gaps) and (b) the single-launch
+            # forward where it applies (T*K <= 8, I % 1024 == 0)
+            ids_c, w_c = routes[0][3].clone(), routes[0][4].clone()
+            g = ops.MoEGraph(p, routes[0][2], ids_c, w_c, wgu, wd, expert_offsets=off, out=out,
+                             workspace=ws)
+
+            def replay(i):
+                ids_c.copy_(routes[i % len(routes)][3])
+                w_c.copy_(routes[i % len(routes)][4])
+                return g.launch
+
+            def single(i):
+                _, _, x_d, ids_d, w_d = routes[i % len(routes)]
+                return lambda: ops.forward_single(p, x_d, ids_d, w_d, wgu, wd, expert_offsets=off,
+                                                  out=out, workspace=ws)
+
+            variants = [("graph_replay", replay)]
+            if T * K <= 8 and I % 1024 == 0:
+                variants.append(("single_launch", single))
+            for vname, prep in variants:
+                for i in range(len(routes)):
+                    prep(i)()
+                torch.cuda.synchronize()
+                vev = [(ev(), ev()) for _ in range(steps)]
+                for i, (a, b) in enumerate(vev):
+                    fn = prep(i)
+                    evict()
+                    a.record(stream)
+                    fn()
+                    b.record(stream)
+                torch.cuda.synchronize()
+                vus = [a.elapsed_time(b) * 1e3 for a, b in vev]
+                ent[vname] = {"us_per_layer": statistics.fmean(vus),
+                              "us_median": statistics.median(vus),
+                              **_roof(F, B, sum(vus) * 1e-6)}
+            g.close()
+            if len(variants) > 1:
+                ent["single_launch"]["barrier_timeouts"] = ops.single_launch_status()
         if kind == "prefill":
             per_seed = []
             for j, (sd, ids_h, _, _, _) in enumerate(routes):

@@ -217,6 +217,34 @@ MOE_API moe_status_t moe_forward(const moe_problem_t* p, const uint16_t* x, cons
                          int32_t* expert_offsets, uint16_t* out,
                          void* workspace, size_t ws_bytes, void* stream);
 
+/* The whole layer in ONE launch, for tiny batches (TileOps PR #1738, review
+ * comments: one megakernel for dispatch, expert compute and combine;
+ * FlashInfer PR #3980, kernel API migration notes: the top-k combine reduced
+ * inside the kernel).  Same arguments, checks and result as moe_forward, bit
+ * for bit.  Serves T*K <= 8 with I % 1024 == 0 and kernel_hint 0 or 1 (the
+ * latency-bound decode regime, where a launch is a large part of the layer);
+ * other problems return MOE_ERROR_NOT_SUPPORTED, as does a device that cannot
+ * hold the launch's grid at once.  The launch is cooperative: a persistent
+ * grid runs the dispatch and the gate-up tiles, waits at a grid-wide barrier,
+ * then runs the down GEMM and the combine.  The barrier lives in one
+ * library-owned device variable per GPU; its wait is bounded: past about 0.3 s
+ * it records a timeout (read with moe_single_launch_status) and the launch
+ * finishes with undefined output rather than hanging.  Launches of it on one
+ * GPU must not overlap (they cannot share the device anyway: each takes all of
+ * it).  Not for graph capture (a cooperative launch). */
+MOE_API moe_status_t moe_forward_single(const moe_problem_t* p, const uint16_t* x,
+                                        const int32_t* topk_ids, const float* topk_weights,
+                                        const uint16_t* w_gateup, const uint16_t* w_down,
+                                        const int32_t* num_tokens_dev, int32_t* expert_offsets,
+                                        uint16_t* out, void* workspace, size_t ws_bytes,
+                                        void* stream);
+
+/* Barrier timeouts recorded by moe_forward_single on the current device since
+ * the last call (0 when every launch completed normally), then resets the
+ * barrier state.  Host-synchronous: call it with no moe_forward_single in
+ * flight on the device. */
+MOE_API moe_status_t moe_single_launch_status(uint32_t* barrier_timeouts);
+
 /* Static-capacity graph replay (TileOps PR #1738, Summary: GPU-resident row
  * counts, static capacity and graph replay).  Records one moe_forward with
  * these fixed pointers into an instantiated HIP graph; every launch in it has

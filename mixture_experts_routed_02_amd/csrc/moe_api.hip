@@ -567,6 +567,34 @@ moe_status_t moe_forward_logits(const moe_problem_t* p, int32_t router_experts,
                                workspace, static_cast<hipStream_t>(stream));
 }
 
+moe_status_t moe_forward_single(const moe_problem_t* p, const uint16_t* x, const int32_t* topk_ids,
+                                const float* topk_weights, const uint16_t* w_gateup,
+                                const uint16_t* w_down, const int32_t* num_tokens_dev,
+                                int32_t* expert_offsets, uint16_t* out, void* workspace,
+                                size_t ws_bytes, void* stream) {
+    Shape s;
+    moe_status_t st = check_forward_args(p, &s, x, topk_ids, topk_weights, w_gateup, w_down,
+                                         num_tokens_dev, expert_offsets, out, workspace, ws_bytes);
+    if (st != MOE_SUCCESS) return st;
+    if (p->kernel_hint > moe::kSkinny || !moe::tiny_down_ok(s) || s.T == 0)
+        return MOE_ERROR_NOT_SUPPORTED;
+    const Layout L = layout(s);
+    const hipError_t e = moe::launch_forward_tiny_single(
+        s, x, topk_ids, num_tokens_dev, expert_offsets, at<int32_t>(workspace, L.row_src),
+        at<int32_t>(workspace, L.token_row), w_gateup, at<uint16_t>(workspace, L.h), w_down,
+        topk_weights, out, static_cast<hipStream_t>(stream));
+    if (e == hipErrorCooperativeLaunchTooLarge) return MOE_ERROR_NOT_SUPPORTED;
+    return launched(e);
+}
+
+moe_status_t moe_single_launch_status(uint32_t* barrier_timeouts) {
+    if (!barrier_timeouts) return MOE_ERROR_INVALID_VALUE;
+    unsigned int t = 0;
+    if (moe::single_launch_status(&t) != hipSuccess) return MOE_ERROR_LAUNCH;
+    *barrier_timeouts = t;
+    return MOE_SUCCESS;
+}
+
 moe_status_t moe_tiled_pack(const uint16_t* w, int32_t experts, int32_t rows, int32_t k,
                             uint16_t* packed, void* stream) {
     if (experts < 0 || rows <= 0 || k <= 0 || rows % 32 != 0 || k % 64 != 0)

@@ -34,6 +34,7 @@
 #include "moe_internal.h"
 
 #include <cmath>
+#include <mutex>
 
 namespace moe {
 namespace {
@@ -94,9 +95,11 @@ __device__ __forceinline__ moe_bf16x8 stream_load(const moe_bf16x8* p) { return 
 // bf16(silu(g) * u) for their 8*RB columns, plain tiles bf16(y) for their
 // 16*RB columns.  PACKED_GROUPS: the tile's 16-row blocks are packed groups
 // of 8 gate rows and the matching 8 up rows (else a gated tile holds its
-// gate rows first, then the matching up rows).  Ends with a barrier, so
+// gate rows first, then the matching up rows).  Gated tiles store column
+// pairs as 32-bit words; COHERENT makes those device-scope atomic stores
+// (visible to every XCD without an L2 writeback).  Ends with a barrier, so
 // s_red is free again.
-template <bool GATED, int RB, bool PACKED_GROUPS = false>
+template <bool GATED, int RB, bool PACKED_GROUPS = false, bool COHERENT = false>
 __device__ __forceinline__ void skinny_epilogue(const moe_f32x4 (&acc)[RB], float* s_red,
                                                 uint16_t* __restrict__ C, int N, int r0,
                                                 int mrows, int n_tile) {
@@ -111,18 +114,29 @@ __device__ __forceinline__ void skinny_epilogue(const moe_f32x4 (&acc)[RB], floa
         for (int i = 0; i < 4; ++i) red(wave, rb * 16 + 4 * lg + i, li) = acc[rb][i];
     __syncthreads();
     if (GATED) {
-        for (int o = tid; o < 16 * COLS; o += 256) {
-            const int m = o / COLS, c = o % COLS;
+        constexpr int PAIRS = COLS / 2;
+        for (int o = tid; o < 16 * PAIRS; o += 256) {
+            const int m = o / PAIRS, c0 = 2 * (o % PAIRS);
             if (m < mrows) {
-                float g = 0.f, u = 0.f;
-                // packed weights: the tile's 16-row groups each hold 8 gate
-                // rows and the matching 8 up rows; row-major: the tile's gate
-                // rows come first, then the matching up rows
-                const int rg = PACKED_GROUPS ? (c >> 3) * 16 + (c & 7) : c;
-                const int ru = PACKED_GROUPS ? rg + 8 : COLS + c;
+                uint32_t v = 0;
 #pragma unroll
-                for (int w = 0; w < 4; ++w) { g += red(w, rg, m); u += red(w, ru, m); }
-                C[(size_t)(r0 + m) * N + n_tile * COLS + c] = moe_f32_to_bf16(silu_f32(g) * u);
+                for (int j = 0; j < 2; ++j) {
+                    const int c = c0 + j;
+                    float g = 0.f, u = 0.f;
+                    // packed weights: the tile's 16-row groups each hold 8
+                    // gate rows and the matching 8 up rows; row-major: the
+                    // tile's gate rows come first, then the matching up rows
+                    const int rg = PACKED_GROUPS ? (c >> 3) * 16 + (c & 7) : c;
+                    const int ru = PACKED_GROUPS ? rg + 8 : COLS + c;
+#pragma unroll
+                    for (int w = 0; w < 4; ++w) { g += red(w, rg, m); u += red(w, ru, m); }
+                    v |= (uint32_t)moe_f32_to_bf16(silu_f32(g) * u) << (16 * j);
+                }
+                uint32_t* dst = reinterpret_cast<uint32_t*>(C + (size_t)(r0 + m) * N + n_tile * COLS + c0);
+                if (COHERENT)
+                    __hip_atomic_store(dst, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                else
+                    *dst = v;
             }
         }
     } else {
@@ -145,7 +159,8 @@ __device__ __forceinline__ void skinny_epilogue(const moe_f32x4 (&acc)[RB], floa
 // offsets and rows may point to global memory or LDS; s_red is
 // [4 waves][16*RB rows][17].  PACKED: W is in the skinny pack layout (see
 // skinny_pack_kernel), so a wave's load of one k-step is 1 KB contiguous.
-template <bool GATED, int RB, bool PACKED = false>
+// COHERENT: the epilogue's stores of C are device-scope atomic stores.
+template <bool GATED, int RB, bool PACKED = false, bool COHERENT = false>
 __device__ __forceinline__ void skinny_tiles(const uint16_t* __restrict__ A, const int32_t* rows,
                                              int topk, const int32_t* offsets,
                                              const uint16_t* __restrict__ W,
@@ -242,7 +257,7 @@ __device__ __forceinline__ void skinny_tiles(const uint16_t* __restrict__ A, con
                                                                   acc[rb], 0, 0, 0);
         }
 
-        skinny_epilogue<GATED, RB>(acc, s_red, C, N, r0, mrows, n_tile);
+        skinny_epilogue<GATED, RB, false, COHERENT>(acc, s_red, C, N, r0, mrows, n_tile);
     }
 }
 
@@ -331,24 +346,27 @@ __device__ __forceinline__ void tiny_combine(int ne, const int* s_r0, const floa
 // one launch fewer and no y rows through memory.  Needs the per-wave k range
 // to be whole blocks of 8 k-steps (I % 1024 == 0).
 // ---------------------------------------------------------------------------
-template <bool PACKED>
-__global__ __launch_bounds__(256) void down_combine_tiny_kernel(
-    const uint16_t* __restrict__ A, const int32_t* __restrict__ offsets,
-    const uint16_t* __restrict__ W, int E, int Kd, int N,
-    const int32_t* __restrict__ token_row, const float* __restrict__ wts,
-    const int32_t* __restrict__ ntok, int T, int topk, uint16_t* __restrict__ out) {
+// The body, for output columns [16*cb, 16*cb+16).  mid() runs after the
+// first block of weights is requested and before the first token rows are
+// (the single-launch forward puts its grid barrier there, so the first
+// weights are already in flight when the rows of h become readable).
+// COHERENT: the rows of A are read with device-scope atomic loads (64-bit),
+// which see stores made by other XCDs without an L2 invalidate.  LDS:
+// s_e, s_r0, s_m [kTinyRows], s_ne, s_part [kTinyRows][4][16][17] floats,
+// s_y [kTinyRows][16][16].
+template <bool PACKED, bool COHERENT, typename MID>
+__device__ __forceinline__ void tiny_down_combine(
+    const uint16_t* __restrict__ A, const int32_t* offsets, const uint16_t* __restrict__ W, int E,
+    int Kd, int N, const int32_t* __restrict__ token_row, const float* __restrict__ wts,
+    const int32_t* __restrict__ ntok, int T, int topk, uint16_t* __restrict__ out, int cb,
+    int* s_e, int* s_r0, int* s_m, int* s_ne, float* s_part, uint16_t* s_y, MID mid) {
     constexpr int U = 8;   // 16 KB of weights in flight per wave
-    __shared__ int s_e[kTinyRows], s_r0[kTinyRows], s_m[kTinyRows];
-    __shared__ int s_ne;
-    __shared__ float s_part[kTinyRows][4][16][17];   // [expert slot][wave][weight row][token row]
-    __shared__ uint16_t s_y[kTinyRows][16][16];      // [expert slot][token row][column]
-
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int li = lane & 15, lg = lane >> 4;
-    const int n0 = blockIdx.x * 16;
+    const int n0 = cb * 16;
 
-    tiny_expert_slots(offsets, E, s_e, s_r0, s_m, &s_ne);
-    const int ne = s_ne;
+    tiny_expert_slots(offsets, E, s_e, s_r0, s_m, s_ne);
+    const int ne = *s_ne;
 
     const int ksteps = Kd / 32;
     const int ks0 = (wave * ksteps) / 4;
@@ -360,7 +378,7 @@ __global__ __launch_bounds__(256) void down_combine_tiny_kernel(
     auto wptr = [&](int i) {
         if (PACKED)
             return reinterpret_cast<const moe_bf16x8*>(W) +
-                   (((size_t)s_e[i] * (N / 16) + blockIdx.x) * ksteps + ks0) * 64 + lane;
+                   (((size_t)s_e[i] * (N / 16) + cb) * ksteps + ks0) * 64 + lane;
         return reinterpret_cast<const moe_bf16x8*>(
             W + ((size_t)s_e[i] * N + n0 + li) * (size_t)Kd + (size_t)ks0 * 32 + lg * 8);
     };
@@ -369,17 +387,31 @@ __global__ __launch_bounds__(256) void down_combine_tiny_kernel(
         return reinterpret_cast<const moe_bf16x8*>(A + (size_t)rr * Kd + (size_t)ks0 * 32 + lg * 8);
     };
     moe_bf16x8 wa[U], wb[U], xa[U], xb[U];
-    auto load = [&](moe_bf16x8* wv, moe_bf16x8* xv, int b) {
+    auto load_w = [&](moe_bf16x8* wv, int b) {
         const int i = b / nblk, kb = b - i * nblk;
         const moe_bf16x8* wp = wptr(i);
-        const moe_bf16x8* ap = xptr(i);
 #pragma unroll
         for (int u = 0; u < U; ++u) wv[u] = stream_load(wp + (kb * U + u) * WS);
+    };
+    auto load_x = [&](moe_bf16x8* xv, int b) {
+        const int i = b / nblk, kb = b - i * nblk;
+        const moe_bf16x8* ap = xptr(i);
 #pragma unroll
         for (int u = 0; u < U; ++u) {
-            const moe_bf16x8 v = ap[(kb * U + u) * 4];
-            xv[u] = v;
+            if (COHERENT) {
+                const uint64_t* q = reinterpret_cast<const uint64_t*>(ap + (kb * U + u) * 4);
+                const uint64_t lo = __hip_atomic_load(q, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                const uint64_t hi = __hip_atomic_load(q + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                const uint64_t both[2] = {lo, hi};
+                __builtin_memcpy(&xv[u], both, sizeof(both));
+            } else {
+                xv[u] = ap[(kb * U + u) * 4];
+            }
         }
+    };
+    auto load = [&](moe_bf16x8* wv, moe_bf16x8* xv, int b) {
+        load_w(wv, b);
+        load_x(xv, b);
     };
     moe_f32x4 acc = {0.f, 0.f, 0.f, 0.f};
     auto step = [&](const moe_bf16x8* wv, const moe_bf16x8* xv, int b) {
@@ -388,11 +420,13 @@ __global__ __launch_bounds__(256) void down_combine_tiny_kernel(
         if ((b + 1) % nblk == 0) {   // last block of expert slot b / nblk
             const int i = b / nblk;
 #pragma unroll
-            for (int q = 0; q < 4; ++q) s_part[i][wave][4 * lg + q][li] = acc[q];
+            for (int q = 0; q < 4; ++q) s_part[((i * 4 + wave) * 16 + 4 * lg + q) * 17 + li] = acc[q];
             acc = (moe_f32x4){0.f, 0.f, 0.f, 0.f};
         }
     };
-    if (total > 0) load(wa, xa, 0);
+    if (total > 0) load_w(wa, 0);
+    mid();
+    if (total > 0) load_x(xa, 0);
     int b = 0;
     for (; b + 2 <= total; b += 2) {
         load(wb, xb, b + 1);
@@ -402,13 +436,29 @@ __global__ __launch_bounds__(256) void down_combine_tiny_kernel(
     }
     if (b < total) step(wa, xa, b);
     __syncthreads();
-    tiny_combine(ne, s_r0, &s_part[0][0][0][0], &s_y[0][0][0], token_row, wts, ntok, T, topk, N, n0, out);
+    tiny_combine(ne, s_r0, s_part, s_y, token_row, wts, ntok, T, topk, N, n0, out);
+}
+
+template <bool PACKED>
+__global__ __launch_bounds__(256) void down_combine_tiny_kernel(
+    const uint16_t* __restrict__ A, const int32_t* __restrict__ offsets,
+    const uint16_t* __restrict__ W, int E, int Kd, int N,
+    const int32_t* __restrict__ token_row, const float* __restrict__ wts,
+    const int32_t* __restrict__ ntok, int T, int topk, uint16_t* __restrict__ out) {
+    __shared__ int s_e[kTinyRows], s_r0[kTinyRows], s_m[kTinyRows];
+    __shared__ int s_ne;
+    __shared__ float s_part[kTinyRows][4][16][17];   // [expert slot][wave][weight row][token row]
+    __shared__ uint16_t s_y[kTinyRows][16][16];      // [expert slot][token row][column]
+    tiny_down_combine<PACKED, false>(A, offsets, W, E, Kd, N, token_row, wts, ntok, T, topk, out,
+                              (int)blockIdx.x, s_e, s_r0, s_m, &s_ne, &s_part[0][0][0][0],
+                              &s_y[0][0][0], [] {});
 }
 
 // The dispatch of the fused kernels: counts, scans and ranks the T*K (<=
 // kFusedDispatchMax) assignments in LDS (s_off: exclusive expert offsets,
 // s_off[E] = valid rows; s_rows: row -> assignment); workgroup 0 also
-// publishes expert_offsets, row_src and token_row.  The ids are read once,
+// publishes expert_offsets, row_src and token_row (and, if s_trow is given,
+// every workgroup keeps its own LDS copy of token_row).  The ids are read once,
 // into registers, together with the valid-token count; wave w ranks the
 // contiguous slice of 256 assignments starting at 256*w with per-bit ballot
 // masks and a wave-local running count per expert, and the per-wave counts
@@ -418,7 +468,8 @@ __device__ __forceinline__ void fused_dispatch(const int32_t* __restrict__ ids,
                                                int E, int32_t* __restrict__ offsets,
                                                int32_t* __restrict__ row_src,
                                                int32_t* __restrict__ token_row, int* s_off,
-                                               int* s_wc, int* s_rows, int* s_wave) {
+                                               int* s_wc, int* s_rows, int* s_wave,
+                                               int* s_trow = nullptr) {
     constexpr int kWaves = 4;
     constexpr int kPer = kFusedDispatchMax / (64 * kWaves);   // assignments per lane
     static_assert(kPer * 64 * kWaves == kFusedDispatchMax, "whole slices");
@@ -484,6 +535,7 @@ __device__ __forceinline__ void fused_dispatch(const int32_t* __restrict__ ids,
             const int e = my_e[k];
             const int r = e >= 0 ? wc[e] + my_rank[k] : -1;
             if (r >= 0) s_rows[r] = a;
+            if (s_trow) s_trow[a] = r;
             if (publish) {
                 token_row[a] = r;
                 if (r >= 0) row_src[r] = a;
@@ -511,6 +563,156 @@ __global__ __launch_bounds__(256) void gemm_skinny_gateup_dispatch_kernel(
     __shared__ float s_red[4 * 16 * 17];
     fused_dispatch(ids, ntok, T, topk, E, offsets, row_src, token_row, s_off, s_wc, s_rows, s_wave);
     skinny_tiles<true, 1, PACKED>(x, s_rows, topk, s_off, W, C, E, Kd, N, s_start, s_wave, s_red);
+}
+
+// ---------------------------------------------------------------------------
+// Single-launch forward for tiny batches (TileOps PR #1738, review comments:
+// the question of one megakernel for the whole layer; FlashInfer PR #3980,
+// kernel API migration notes: the top-k combine reduced inside the kernel).
+// One cooperative, persistent launch does what the small-batch path does in
+// two: every workgroup runs the dispatch in LDS and its gate-up tiles; a
+// grid-wide barrier makes h visible everywhere; then workgroup b does the
+// down GEMM and the combine for output columns [16b, 16b+16) (the tiny
+// path's arithmetic, so the result is bit-identical to it, with the token ->
+// row map taken from the workgroup's own dispatch in LDS, so h is the only
+// data that crosses workgroups).  Before waiting
+// at the barrier a workgroup requests its first block of down weights, which
+// do not depend on h, so that stream overlaps the end of the gate-up phase.
+//
+// The barrier: h is the only data that crosses workgroups, and it is
+// written with device-scope atomic stores and read with device-scope atomic
+// loads, which are coherent across the XCDs' L2 caches by themselves.  So
+// the barrier needs no L2 writeback or invalidate (a per-workgroup one
+// serializes in each XCD's L2 and costs several microseconds at this grid);
+// it only has to order completed stores before later loads.  Arrive: every
+// thread waits for its own memory operations to complete, then thread 0
+// raises the workgroup's flag to the next generation.  Wait: workgroup 0
+// polls every flag, then publishes the generation; the others poll the
+// generation.  Flags and generation live in a file-scope device variable
+// (zero when the code object loads); the generation only grows, so no reset
+// is needed between launches.  Every poll is bounded: past the bound a
+// workgroup records a timeout and goes on (the launch then computes garbage,
+// and moe_single_launch_status reports it and clears the state) instead of
+// hanging.  The host launches the kernel cooperatively, with a grid it has
+// checked fits on the device at once.
+// ---------------------------------------------------------------------------
+constexpr int kMaxSingleGrid = 2048;
+struct __attribute__((aligned(256))) BarrierLine {
+    unsigned int v;
+    unsigned int pad[63];
+};
+struct GridSync {
+    BarrierLine gen, timeouts;
+    unsigned int flag[kMaxSingleGrid];
+};
+__device__ GridSync g_grid_sync;
+constexpr unsigned int kBarrierSpins = 1u << 22;   // ~0.3 s of polling
+
+__device__ __forceinline__ unsigned int sync_load(const unsigned int* p) {
+    return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Polls *p until it differs from (NE) or equals (!NE) v, within the bound.
+template <bool NE>
+__device__ __forceinline__ void sync_poll(const unsigned int* p, unsigned int v) {
+    unsigned int spins = 0;
+    while ((sync_load(p) == v) == NE) {
+        __builtin_amdgcn_s_sleep(1);
+        if (++spins == kBarrierSpins) {
+            __hip_atomic_fetch_add(&g_grid_sync.timeouts.v, 1u, __ATOMIC_RELAXED,
+                                   __HIP_MEMORY_SCOPE_AGENT);
+            break;
+        }
+    }
+}
+
+// Arrive: returns (in *s_gen, LDS) the generation this barrier ends.
+__device__ __forceinline__ void grid_arrive(unsigned int* s_gen) {
+    __builtin_amdgcn_s_waitcnt(0);   // this thread's stores have completed
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        const unsigned int g = sync_load(&g_grid_sync.gen.v);
+        *s_gen = g;
+        __hip_atomic_store(&g_grid_sync.flag[blockIdx.x], g + 1, __ATOMIC_RELAXED,
+                           __HIP_MEMORY_SCOPE_AGENT);
+    }
+    __syncthreads();
+}
+
+__device__ __forceinline__ void grid_wait(const unsigned int* s_gen, unsigned int nblocks) {
+    const unsigned int g = *s_gen;
+    if (blockIdx.x == 0) {
+        for (unsigned int b = threadIdx.x; b < nblocks; b += blockDim.x)
+            sync_poll<false>(&g_grid_sync.flag[b], g + 1);
+        __builtin_amdgcn_s_waitcnt(0);
+        __syncthreads();
+        if (threadIdx.x == 0)
+            __hip_atomic_store(&g_grid_sync.gen.v, g + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    } else if (threadIdx.x == 0) {
+        sync_poll<true>(&g_grid_sync.gen.v, g);
+    }
+    __syncthreads();
+}
+
+// LDS of the single-launch kernel: the dispatch offsets stay for both phases;
+// the rest is the gate-up phase's arrays, then reused by the down phase.
+constexpr int kSingleP1Bytes = (4 * kMaxExperts + kFusedDispatchMax + kMaxExperts + 1) * 4 + 4 * 16 * 17 * 4;
+constexpr int kSingleP2Bytes = (3 * kTinyRows + 1) * 4 + kTinyRows * 4 * 16 * 17 * 4 + kTinyRows * 16 * 16 * 2;
+constexpr int kSingleLds = kSingleP1Bytes > kSingleP2Bytes ? kSingleP1Bytes : kSingleP2Bytes;
+
+template <bool PACKED>
+__global__ __launch_bounds__(256, 3) void forward_tiny_single_kernel(
+    const uint16_t* __restrict__ x, const int32_t* __restrict__ ids,
+    const int32_t* __restrict__ ntok, int T, int topk, int E, int32_t* __restrict__ offsets,
+    int32_t* __restrict__ row_src, int32_t* __restrict__ token_row,
+    const uint16_t* __restrict__ Wgu, uint16_t* __restrict__ h, const uint16_t* __restrict__ Wd,
+    const float* __restrict__ wts, uint16_t* __restrict__ out, int H, int I) {
+    __shared__ int s_off[kMaxExperts + 1];
+    __shared__ int s_wave[4];
+    __shared__ int s_trow[kTinyRows];
+    __shared__ unsigned int s_gen;
+    __shared__ __attribute__((aligned(16))) unsigned char s_mem[kSingleLds];
+    // gate-up phase
+    int* s_wc = reinterpret_cast<int*>(s_mem);
+    int* s_rows = s_wc + 4 * kMaxExperts;
+    int* s_start = s_rows + kFusedDispatchMax;
+    float* s_red = reinterpret_cast<float*>(s_start + kMaxExperts + 1);
+    fused_dispatch(ids, ntok, T, topk, E, offsets, row_src, token_row, s_off, s_wc, s_rows, s_wave,
+                   s_trow);
+    skinny_tiles<true, 1, PACKED, true>(x, s_rows, topk, s_off, Wgu, h, E, H, I, s_start, s_wave,
+                                        s_red);
+    grid_arrive(&s_gen);
+    // down phase (every LDS read of the gate-up phase is behind its last barrier)
+    int* s_e = reinterpret_cast<int*>(s_mem);
+    int* s_r0 = s_e + kTinyRows;
+    int* s_m = s_r0 + kTinyRows;
+    int* s_ne = s_m + kTinyRows;
+    float* s_part = reinterpret_cast<float*>(s_ne + 1);
+    uint16_t* s_y = reinterpret_cast<uint16_t*>(s_part + kTinyRows * 4 * 16 * 17);
+    const int ncb = H / 16;
+    if ((int)blockIdx.x < ncb) {
+        for (int cb = blockIdx.x; cb < ncb; cb += gridDim.x)
+            tiny_down_combine<PACKED, true>(h, s_off, Wd, E, I, H, s_trow, wts, ntok, T, topk, out,
+                                            cb, s_e, s_r0, s_m, s_ne, s_part, s_y, [&] {
+                                                if (cb == (int)blockIdx.x) grid_wait(&s_gen, gridDim.x);
+                                            });
+    } else {
+        grid_wait(&s_gen, gridDim.x);
+    }
+}
+
+template <bool PACKED>
+static hipError_t launch_tiny_single(const Shape& s, const uint16_t* x, const int32_t* ids,
+                                     const int32_t* ntok, int32_t* offsets, int32_t* row_src,
+                                     int32_t* token_row, const uint16_t* Wgu, uint16_t* h,
+                                     const uint16_t* Wd, const float* w, uint16_t* out,
+                                     int grid, hipStream_t st) {
+    int T = s.T, K = s.K, E = s.E, H = s.H, I = s.I;
+    void* args[] = {(void*)&x, (void*)&ids, (void*)&ntok, (void*)&T, (void*)&K, (void*)&E,
+                    (void*)&offsets, (void*)&row_src, (void*)&token_row, (void*)&Wgu, (void*)&h,
+                    (void*)&Wd, (void*)&w, (void*)&out, (void*)&H, (void*)&I};
+    return hipLaunchCooperativeKernel(reinterpret_cast<const void*>(&forward_tiny_single_kernel<PACKED>),
+                                      dim3(grid), dim3(256), args, 0, st);
 }
 
 // ---------------------------------------------------------------------------
@@ -1716,6 +1918,55 @@ hipError_t launch_gateup_fused_dispatch(const Shape& s, const GemmPlan& plan, co
                            dim3(256), 0, st, x, ids, ntok, s.T, s.K, s.E, offsets, row_src,
                            token_row, W, h, s.H, s.I);
     return hipGetLastError();
+}
+
+// Workgroups of the single-launch kernel that fit on the current device at
+// once (looked up once per device): 0 if the cooperative launch cannot be
+// made there.
+int single_launch_grid(bool packed) {
+    static std::mutex mu;
+    static int cache[2][64];
+    static bool have[2][64];
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
+    std::lock_guard<std::mutex> lock(mu);
+    if (!have[packed][dev]) {
+        int cus = 0, coop = 0, per_cu = 0;
+        (void)hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+        (void)hipDeviceGetAttribute(&coop, hipDeviceAttributeCooperativeLaunch, dev);
+        const hipError_t e = packed
+            ? hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, forward_tiny_single_kernel<true>, 256, 0)
+            : hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, forward_tiny_single_kernel<false>, 256, 0);
+        if (e != hipSuccess || coop == 0 || per_cu < 1 || cus < 1) per_cu = 0;
+        const int grid = (per_cu > 3 ? 3 : per_cu) * cus;
+        cache[packed][dev] = grid > kMaxSingleGrid ? kMaxSingleGrid : grid;
+        have[packed][dev] = true;
+    }
+    return cache[packed][dev];
+}
+
+hipError_t launch_forward_tiny_single(const Shape& s, const uint16_t* x, const int32_t* ids,
+                                      const int32_t* ntok, int32_t* offsets, int32_t* row_src,
+                                      int32_t* token_row, const uint16_t* Wgu, uint16_t* h,
+                                      const uint16_t* Wd, const float* w, uint16_t* out,
+                                      hipStream_t st, bool packed) {
+    const int grid = single_launch_grid(packed);
+    if (grid <= 0) return hipErrorCooperativeLaunchTooLarge;
+    if (packed)
+        return launch_tiny_single<true>(s, x, ids, ntok, offsets, row_src, token_row, Wgu, h, Wd,
+                                        w, out, grid, st);
+    return launch_tiny_single<false>(s, x, ids, ntok, offsets, row_src, token_row, Wgu, h, Wd, w,
+                                     out, grid, st);
+}
+
+hipError_t single_launch_status(unsigned int* timeouts) {
+    GridSync g{};
+    hipError_t e = hipMemcpyFromSymbol(&g, HIP_SYMBOL(g_grid_sync), sizeof(g), 0,
+                                       hipMemcpyDeviceToHost);
+    if (e != hipSuccess) return e;
+    *timeouts = g.timeouts.v;
+    const GridSync zero{};
+    return hipMemcpyToSymbol(HIP_SYMBOL(g_grid_sync), &zero, sizeof(zero), 0, hipMemcpyHostToDevice);
 }
 
 hipError_t launch_down_combine_tiny(const Shape& s, const uint16_t* h, const int32_t* offsets,

@@ -92,6 +92,17 @@ constexpr int kTinyRows = 8;
 inline bool tiny_down_ok(const Shape& s) {
     return (long long)s.T * s.K <= kTinyRows && s.I % 1024 == 0 && s.H % 16 == 0;
 }
+// The tiny-batch layer (tiny_down_ok, T*K <= kTinyRows) in one cooperative
+// launch: dispatch + gate-up, a grid barrier, down + combine.  Returns
+// hipErrorCooperativeLaunchTooLarge when the device cannot hold the grid.
+hipError_t launch_forward_tiny_single(const Shape& s, const uint16_t* x, const int32_t* ids,
+                                      const int32_t* ntok, int32_t* offsets, int32_t* row_src,
+                                      int32_t* token_row, const uint16_t* Wgu, uint16_t* h,
+                                      const uint16_t* Wd, const float* w, uint16_t* out,
+                                      hipStream_t st, bool packed = false);
+// Barrier timeouts recorded by single launches on the current device since
+// the last call (host synchronous; resets the barrier state).
+hipError_t single_launch_status(unsigned int* timeouts);
 hipError_t launch_down_combine_tiny(const Shape& s, const uint16_t* h, const int32_t* offsets,
                                     const uint16_t* W, const int32_t* token_row, const float* w,
                                     const int32_t* ntok, uint16_t* out, hipStream_t st,

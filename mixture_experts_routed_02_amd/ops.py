@@ -22,6 +22,7 @@ __all__ = [
     "mxfp8_quantize", "mxfp8_dequantize", "gate_up_mxfp8", "forward_mxfp8", "skinny_pack",
     "gate_up_packed", "forward_packed", "mx_pack", "forward_noalloc", "router_dispatch",
     "forward_logits", "tiled_pack", "gate_up_tiled_packed", "forward_tiled_packed",
+    "forward_single", "single_launch_status",
 ]
 
 
@@ -266,6 +267,27 @@ def forward(p: MoeProblem, x, topk_ids, topk_weights, w_gateup, w_down, num_toke
         _ptr(w_down), _ptr(nt), _ptr(offsets), _ptr(out), _ptr(ws), ws.numel(),
         _stream_ptr(x.device)))
     return out, offsets
+
+
+def forward_single(p: MoeProblem, x, topk_ids, topk_weights, w_gateup, w_down,
+                   num_tokens_dev=None, expert_offsets=None, out=None, workspace=None):
+    """The whole layer in one cooperative launch (tiny batches: T*K <= 8,
+    I % 1024 == 0).  Returns (out [T,H], expert_offsets [E+1])."""
+    nt, offsets, out, ws = _forward_args(p, x, topk_ids, topk_weights, w_gateup, w_down,
+                                         num_tokens_dev, expert_offsets, out, workspace)
+    check("moe_forward_single", lib().moe_forward_single(
+        ctypes.byref(p), _ptr(x), _ptr(topk_ids), _ptr(topk_weights), _ptr(w_gateup),
+        _ptr(w_down), _ptr(nt), _ptr(offsets), _ptr(out), _ptr(ws), ws.numel(),
+        _stream_ptr(x.device)))
+    return out, offsets
+
+
+def single_launch_status() -> int:
+    """Barrier timeouts of forward_single launches on the current device since
+    the last call (host-synchronous; resets the barrier state)."""
+    n = ctypes.c_uint32(0)
+    check("moe_single_launch_status", lib().moe_single_launch_status(ctypes.byref(n)))
+    return int(n.value)
 
 
 def forward_noalloc(p: MoeProblem, x, topk_ids, topk_weights, w_gateup, w_down,

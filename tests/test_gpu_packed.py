@@ -130,9 +130,12 @@ def test_forward_packed_ep_decode_full_size(name):
 @pytest.mark.parametrize("fmt", ["mxfp8", "mxfp4"])
 @pytest.mark.parametrize("name", ["tiny_down", "fused_skinny_down", "multi_launch"])
 def test_forward_mx_packed_bit_identical(fmt, name):
+    """Packed MX weights run the skinny kernels only, so the row-major
+    reference is pinned to the skinny plan too (left to itself it takes the
+    tiled MX kernels where those apply, whose accumulation order differs)."""
     T, K, E, H, I, lo, hi = SHAPES[name]
     x, ids, w, wgu, wd = case(T, K, E, H, I, 23, lo, hi)
-    p = moe.problem(T, K, E, H, I)
+    p = moe.problem(T, K, E, H, I, 0, moe.HINT_SKINNY)
     qgu, sgu = ops.mx_quantize(wgu, fmt)
     qd, sd = ops.mx_quantize(wd, fmt)
     ref, ref_off = ops.forward_mx(p, x, ids, w, qgu, sgu, qd, sd, fmt)
