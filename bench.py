@@ -74,10 +74,13 @@ def describe(cfg):
             f"{routing} routing")
 
 
-def pmc_traffic(kernel_key: str, src_hash: str, units: int):
+def pmc_traffic(kernel_key: str, src_hash: str, units: int, seed: int = 0, hint: int = 0):
     """HBM bytes per launch from a committed rocprofv3 counter summary, or None
-    when there is none for this kernel/workload or the kernel sources changed
-    since the counters were taken."""
+    when there is none for this kernel/workload, the kernel sources changed
+    since the counters were taken, the plan was forced (the counters are of the
+    automatic plan) or the entry is of another routing seed."""
+    if hint != 0:
+        return None
     path = os.path.join(REPO, "profiles", "pmc_traffic.json")
     if not os.path.exists(path):
         return None
@@ -85,6 +88,8 @@ def pmc_traffic(kernel_key: str, src_hash: str, units: int):
         data = json.load(fh)
     ent = data.get(kernel_key)
     if not ent or ent.get("src_sha256") != src_hash:
+        return None
+    if ent.get("seed") is not None and ent["seed"] != seed:
         return None
     return ent.get("bytes_per_launch")
 
@@ -641,7 +646,8 @@ def main():
         kernel_name += " (packed weights)"
     if tpacked:
         kernel_name += " (tiled pack layout)"
-    traffic = pmc_traffic(f"{kernel_name}<gated>@{cfg.name}", kernel_src_hash(), 1)
+    traffic = pmc_traffic(f"{kernel_name}<gated>@{cfg.name}", kernel_src_hash(), 1, args.seed,
+                          args.hint)
     if mfma_bound:
         ach = F_gu / (k_ms / 1e3) / 1e12
         roof = {"bound": "mfma", "achieved": ach, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
