@@ -29,7 +29,8 @@ L2/MALL evicted before each step, 32 routing draws cycled; each also timed
 as replays of the layer recorded as a HIP graph, `graph_replay`, and at T = 1
 through the single-launch forward, `single_launch`), the prefill
 shares T = 2048, 8192 with uniform routing (seeds 0-2) and Zipf s = 1.2
-routing (seeds 0-4, reported per seed), and the static-capacity layer (50
+routing (seeds 0-4, reported per seed), a supplementary T = 16384 point of
+the same shape (seed 0, labelled `supplementary`), and the static-capacity layer (50
 HIP-graph replays with a device token count T_i ~ U{1..2048}, and the full
 buffer called eagerly).  --no-per-config leaves it out.
 
@@ -174,7 +175,12 @@ PER_CONFIG = (
     ("ep_prefill_T2048", "prefill"), ("ep_prefill_T8192", "prefill"),
     ("ep_prefill_T2048_zipf", "prefill"), ("ep_prefill_T8192_zipf", "prefill"),
     ("static_capacity", "static"),
+    ("ep_prefill_T16384", "prefill"),   # supplementary: ~256 rows per expert
 )
+SUPPLEMENTARY = {"ep_prefill_T16384": "supplementary point of the EP prefill shape at 16384 tokens "
+                                      "(about 256 rows per local expert): one weight pass allows "
+                                      "up to 78.5% of the MFMA peak here"}
+PREFILL_SEED_OVERRIDE = {"ep_prefill_T16384": (0,)}
 DECODE_DRAWS = 32          # routing draws (seeds 1000..1031), one per step
 PREFILL_SEEDS = {"ep_uniform": (0, 1, 2), "ep_zipf": (0, 1, 2, 3, 4)}
 PREFILL_STEPS = 10         # timed calls per seed
@@ -249,7 +255,7 @@ def per_config_sweep(dev, kernel_reps: int):
         if kind == "decode":
             seeds = [1000 + d for d in range(DECODE_DRAWS)]
         elif kind == "prefill":
-            seeds = list(PREFILL_SEEDS[cfg.routing])
+            seeds = list(PREFILL_SEED_OVERRIDE.get(name, PREFILL_SEEDS[cfg.routing]))
         else:
             seeds = [0]
         routes = []
@@ -393,6 +399,8 @@ def per_config_sweep(dev, kernel_reps: int):
                               "binding_frac_min": min(fr), "binding_frac_max": max(fr)}
             g.close()
         ent["workload"] = describe(cfg)
+        if name in SUPPLEMENTARY:
+            ent["supplementary"] = SUPPLEMENTARY[name]
         out_all[name] = ent
         del routes, ws, out, off
         torch.cuda.synchronize()

@@ -342,7 +342,8 @@ def test_forward_ep_decode_every_token(name, seed, ep_share):
 
 
 PREFILL = [(n, s) for n in ("ep_prefill_T2048", "ep_prefill_T8192") for s in (0, 1, 2)] + \
-          [(n, s) for n in ("ep_prefill_T2048_zipf", "ep_prefill_T8192_zipf") for s in range(5)]
+          [(n, s) for n in ("ep_prefill_T2048_zipf", "ep_prefill_T8192_zipf") for s in range(5)] + \
+          [("ep_prefill_T16384", 0)]
 
 
 @pytest.mark.parametrize("name,seed", PREFILL)

@@ -80,6 +80,9 @@ def _cfg_table():
     for t in (2048, 8192):
         c[f"ep_prefill_T{t}"] = MoEConfig(f"ep_prefill_T{t}", t, 6, 96, 7168, 3072, "ep_uniform", 384)
         c[f"ep_prefill_T{t}_zipf"] = MoEConfig(f"ep_prefill_T{t}_zipf", t, 6, 96, 7168, 3072, "ep_zipf", 384)
+    # supplementary point of the same shape with about 256 rows per local
+    # expert, where one weight pass allows up to 78.5% of the MFMA peak
+    c["ep_prefill_T16384"] = MoEConfig("ep_prefill_T16384", 16384, 6, 96, 7168, 3072, "ep_uniform", 384)
     c["static_capacity"] = MoEConfig("static_capacity", 2048, 8, 128, 2048, 768, "ep_uniform", 128,
                                      capacity=16384)
     return c
