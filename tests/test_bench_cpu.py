@@ -1,0 +1,55 @@
+"""Host-side logic of bench.py: the committed counter figures it reports as
+`roofline.traffic`, and the contract of its command line (no GPU needed)."""
+import json
+import os
+import subprocess
+import sys
+
+import pytest
+
+REPO = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+sys.path.insert(0, REPO)
+import bench  # noqa: E402
+
+
+def _entries():
+    with open(os.path.join(REPO, "profiles", "pmc_traffic.json")) as fh:
+        return json.load(fh)
+
+
+def test_traffic_entries_carry_the_current_kernel_hash():
+    """Every committed counter figure was taken on the kernel sources in the
+    tree (otherwise the bench must report null, and the entry is stale)."""
+    h = bench.kernel_src_hash()
+    data = _entries()
+    assert data, "no counter figures committed"
+    for key, ent in data.items():
+        assert ent["src_sha256"] == h, key
+        assert ent["bytes_per_launch"] == pytest.approx(ent["fetch_bytes"] + ent["write_bytes"])
+        assert ent["fetch_factor"] > 0 and ent["write_factor"] > 0
+
+
+def test_traffic_lookup_rules():
+    h = bench.kernel_src_hash()
+    data = _entries()
+    key = "gemm_tiled_kernel<gated>@mixtral"
+    assert bench.pmc_traffic(key, h, 1) == data[key]["bytes_per_launch"]
+    # a forced plan runs other kernels than the counters saw
+    assert bench.pmc_traffic(key, h, 1, 0, 4) is None
+    # changed sources void the figure
+    assert bench.pmc_traffic(key, "0" * 64, 1) is None
+    # unknown workload
+    assert bench.pmc_traffic("gemm_tiled_kernel<gated>@tiny", h, 1) is None
+    # figures of one routing seed answer for that seed only
+    seeded = [k for k, e in data.items() if e.get("seed") is not None]
+    for k in seeded:
+        s = data[k]["seed"]
+        assert bench.pmc_traffic(k, h, 1, s) == data[k]["bytes_per_launch"]
+        assert bench.pmc_traffic(k, h, 1, s + 1) is None
+
+
+def test_several_gpus_is_refused():
+    r = subprocess.run([sys.executable, os.path.join(REPO, "bench.py"), "--gpus", "2"],
+                       capture_output=True, text=True, cwd=REPO, timeout=120)
+    assert r.returncode != 0
+    assert "one GPU" in (r.stdout + r.stderr) or "1 GPU" in (r.stdout + r.stderr)
