@@ -649,7 +649,8 @@ def main():
         kind = 2
     kernel_name = "gemm_skinny_kernel" if kind == 1 else "gemm_tiled_kernel"
     if mx:
-        kernel_name = f"gemm_skinny_mx_kernel<{8 if args.weights == 'mxfp8' else 4}>"
+        wf = 8 if args.weights == "mxfp8" else 4
+        kernel_name = f"gemm_skinny_mx_kernel<{wf}>" if kind == 1 else f"gemm_tiled_kernel<MXFP{wf}>"
     if packed:
         kernel_name += " (packed weights)"
     if tpacked:
