@@ -1287,6 +1287,7 @@ __global__ __launch_bounds__(256) void skinny_pack_kernel(const uint16_t* __rest
 // the loads that are meant to stay in flight.
 // ---------------------------------------------------------------------------
 constexpr int kBK = 64;   // k-values per stage
+constexpr int kMGroup = 8;   // m-tiles per group in the tile walk of a large expert
 
 // LDS per workgroup: all of it when one 8-wave workgroup fills a CU, half
 // when two 4-wave ones share it
@@ -1518,7 +1519,27 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_tiled_kernel(
         const int me = offsets[e + 1] - row0;
         const int mt = (me + BM - 1) / BM;
         const int local = tile - first;
-        const int m_tile = local % mt, n_tile = local / mt;
+        // An expert's tiles run m-tile fastest, so the 32 consecutive tiles an
+        // XCD holds share weight tiles and token blocks.  An expert with more
+        // than kMGroup m-tiles (a hot expert under skewed routing) is walked
+        // in groups of kMGroup m-tiles, each group over all weight columns
+        // before the next, so a window spans about 8 m-tiles x 4 columns
+        // instead of one column of all its m-tiles, and its token blocks are
+        // not fetched again for every column.  A permutation of the tiles:
+        // the output is the same bit for bit.  Measured: Zipf-routed prefill
+        // at 8192 tokens 1.6-2.4% faster on the seeds with a hot local expert,
+        // the other workloads unchanged.
+        int m_tile, n_tile;
+        if (mt <= kMGroup) {
+            m_tile = local % mt;
+            n_tile = local / mt;
+        } else {
+            const int grp = local / (kMGroup * n_tiles);
+            const int gm = mt - grp * kMGroup < kMGroup ? mt - grp * kMGroup : kMGroup;
+            const int idx = local - grp * kMGroup * n_tiles;
+            n_tile = idx / gm;
+            m_tile = grp * kMGroup + idx % gm;
+        }
         // The expert's rows, in 32-row units, are split over its mt m-tiles as
         // evenly as whole units allow (heights differ by at most 32 rows and
         // never exceed BM), rather than mt - 1 full tiles and a ragged last

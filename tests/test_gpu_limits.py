@@ -65,6 +65,9 @@ CASES = {
     # eight experts near 1024 rows (the Mixtral routing's spread), H = 1024:
     # down on 192 x 256 tiles
     "large_branch_free_down256": (1, 2, 8, 1024, 512, 0, None),
+    # experts with more m-tiles than one group of the tiled walk (8): 2600 rows
+    # (14 m-tiles of 192: groups of 8 and 6) and 1600 rows (9: 8 and 1)
+    "hot_expert_groups": (1, 1, 3, 256, 256, 0, None),
 }
 TILE_EDGE_COUNTS = {"tile_edges": [256, 257, 128, 129, 64, 1, 0],
                     "tile_edges_192": [191, 192, 193, 384, 385, 96, 97, 1, 0],
@@ -72,7 +75,8 @@ TILE_EDGE_COUNTS = {"tile_edges": [256, 257, 128, 129, 64, 1, 0],
                     "large_branch_free_i320": [1000, 1100, 1153, 0],
                     "large_branch_free_h384": [1000, 1100, 1153, 0],
                     "large_branch_free_k2": [769, 960, 1023, 1280],
-                    "large_branch_free_down256": [1023, 1024, 1025, 974, 1083, 1100, 960, 1003]}
+                    "large_branch_free_down256": [1023, 1024, 1025, 974, 1083, 1100, 960, 1003],
+                    "hot_expert_groups": [2600, 150, 1600]}
 
 
 def build(name):
