@@ -177,7 +177,8 @@ def test_forward_mx_packed_ep_decode_full_size(fmt, name):
 # caller can record it into a HIP graph and replay it with a new device token
 # count; each replay must equal the eager call with that count, bit for bit
 # ---------------------------------------------------------------------------
-@pytest.mark.parametrize("kind", ["packed", "mxfp8", "mxfp4", "mxfp8_packed"])
+@pytest.mark.parametrize("kind", ["packed", "mxfp8", "mxfp4", "mxfp8_packed", "tiled_packed",
+                                  "logits"])
 def test_graph_replays_with_device_token_count(kind):
     cfg = W.CONFIGS["static_capacity"]
     T, K, E, H, I = cfg.num_tokens, cfg.top_k, cfg.num_experts, cfg.hidden, cfg.intermediate
@@ -188,6 +189,19 @@ def test_graph_replays_with_device_token_count(kind):
     if kind == "packed":
         a, b = ops.skinny_pack(wgu, True), ops.skinny_pack(wd, False)
         run = lambda nt, out, off, ws: ops.forward_packed(p, x, ids, w, a, b, nt, off, out, ws)
+    elif kind == "tiled_packed":
+        a, b = ops.tiled_pack(wgu), ops.tiled_pack(wd)
+        run = lambda nt, out, off, ws: ops.forward_tiled_packed(p, x, ids, w, a, b, nt, off, out,
+                                                                ws)
+    elif kind == "logits":   # the router fused ahead of the dispatch
+        lg = torch.randn((T, E), generator=torch.Generator().manual_seed(4)).to(DEV)
+        bufs = {}
+
+        def run(nt, out, off, ws):
+            ib, wb = bufs.setdefault(out.data_ptr(), (
+                torch.full((T, K), -1, dtype=torch.int32, device=DEV),
+                torch.zeros((T, K), dtype=torch.float32, device=DEV)))
+            ops.forward_logits(p, lg, x, wgu, wd, nt, ib, wb, off, out, ws)
     else:
         fmt = kind.split("_")[0]
         qgu, sgu = ops.mx_quantize(wgu, fmt)
