@@ -439,8 +439,8 @@ def main():
                     help="expert weights (bf16) or codes (MX) in the skinny pack layout, packed "
                          "on the device before timing; the skinny plan serves every batch size")
     ap.add_argument("--tiled-packed", action="store_true",
-                    help="bf16 expert weights in the tiled pack layout (packed on the device "
-                         "before timing); the tiled plans serve every batch size")
+                    help="expert weights (bf16) or MX codes in the tiled pack layout (packed on "
+                         "the device before timing); the tiled plans serve every batch size")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-per-config", action="store_true",
                     help="leave out the per_config sweep over the other workloads")
@@ -473,9 +473,9 @@ def main():
     mx = args.weights in ("mxfp8", "mxfp4")
     packed = args.packed
     tpacked = args.tiled_packed
-    if tpacked and (mx or packed or args.graph or args.replays):
-        raise SystemExit("--tiled-packed takes bf16 row-major weights and eager launches")
-    if tpacked:
+    if tpacked and (packed or args.graph or args.replays):
+        raise SystemExit("--tiled-packed is a layout of its own, for eager launches")
+    if tpacked and not mx:
         tgu, td = ops.tiled_pack(wgu), ops.tiled_pack(wd)
         torch.cuda.synchronize()
     if packed and not mx:
@@ -490,6 +490,8 @@ def main():
         qd, sd = ops.mx_quantize(wd, args.weights)
         if packed:
             qgu, qd = ops.mx_pack(qgu, True, args.weights), ops.mx_pack(qd, False, args.weights)
+        if tpacked:   # the tiled (prefill) pack layout of the codes
+            qgu, qd = ops.mx_tiled_pack(qgu, args.weights), ops.mx_tiled_pack(qd, args.weights)
         torch.cuda.synchronize()
     # HBM bytes per weight value: bf16, or a code (1 or 1/2 byte) plus 1/32 of a scale byte
     wbytes = {"bf16": 2.0, "mxfp8": 1.0 + 1.0 / 32.0, "mxfp4": 0.5 + 1.0 / 32.0}[args.weights]
@@ -524,7 +526,7 @@ def main():
             ri, rw = routes[i % draws]
             if mx:
                 ops.forward_mx(p, x, ri, rw, qgu, sgu, qd, sd, args.weights, expert_offsets=off,
-                               out=out, workspace=ws, packed=packed)
+                               out=out, workspace=ws, packed=packed, tiled_packed=tpacked)
             elif packed:
                 ops.forward_packed(p, x, ri, rw, pgu, pd, expert_offsets=off, out=out,
                                    workspace=ws)
@@ -598,7 +600,7 @@ def main():
     hbuf = torch.empty((p.capacity or T * K, I), dtype=torch.bfloat16, device=dev)
     if mx:
         gu_call = lambda: ops.gate_up_mx(p, x_disp, off2, qgu, sgu, args.weights, h=hbuf,
-                                         packed=packed)
+                                         packed=packed, tiled_packed=tpacked)
     elif packed:
         gu_call = lambda: ops.gate_up_packed(p, x_disp, off2, pgu, h=hbuf)
     elif tpacked:

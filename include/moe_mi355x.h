@@ -491,6 +491,54 @@ MOE_API moe_status_t moe_forward_mx_packed(const moe_problem_t* p, int32_t bits,
                                            uint16_t* out, void* workspace, size_t ws_bytes,
                                            void* stream);
 
+/* ---------------------------------------------------------------------------
+ * MX codes in the tiled pack layout, for the tiled (prefill) kernels on MX
+ * weights (DeepGEMM PR #394, Summary and Motivation: weights laid out once in
+ * the kernel's access order; FlashInfer PR #3980, Summary: the MXFP8
+ * backend).  The tiled MX kernels stage a weight tile's codes as 1 KiB DMA
+ * pieces of 16 rows x 64 bytes (e4m3: 64 values of a row per stage) or 32
+ * rows x 32 bytes (e2m1), row r's 16-byte chunk c in LDS slot c ^ swz(r % 32)
+ * with swz8(r) = ((r >> 2) & 1) | ((r >> 3) & 2) and swz4(r) = (r >> 4) & 1.
+ * Row-major, each piece gathers 16 or 32 partial cache lines; packed, it is
+ * one contiguous 1 KiB.
+ *
+ * moe_mx_tiled_pack rewrites codes [experts, rows, k * bits / 8 bytes] (bits =
+ * 8: MXFP8, 4: MXFP4; k values per row; rows % 32 == 0, k % 64 == 0) into
+ * packed of the same size: for expert e, group g of 1024 / (64 * bits / 8)
+ * rows and stage s (values 64s .. 64s+63), one 1 KiB block whose 16-byte
+ * piece L holds row g * G + L / C (G rows per group, C = 64 * bits / 128
+ * chunks per row and stage), chunk (L % C) ^ swz(row % 32) of that row's
+ * stage.  codes and packed must not overlap; both 16-byte aligned; the
+ * scales stay row-major.  Both W_gateup [E, 2I, .] and W_down [E, H, .]
+ * codes are packed the same way. */
+MOE_API moe_status_t moe_mx_tiled_pack(const uint8_t* codes, int32_t experts, int32_t rows,
+                                       int32_t k, int32_t bits, uint8_t* packed, void* stream);
+
+/* moe_gate_up_mxfp8 / _mxfp4 and moe_forward_mxfp8 / _mxfp4 (bits = 8 / 4) on
+ * codes packed by moe_mx_tiled_pack, with the same row-major scales.  They run
+ * a tiled plan (kernel_hint 2, 3, 4, or 0: the automatic choice, with the
+ * 64-row tiled plan where it would pick the skinny one; kernel_hint 1 returns
+ * MOE_ERROR_NOT_SUPPORTED), need hidden (and, for the forward, intermediate)
+ * a multiple of 512 and at most 7168 (the tile's scales fit in LDS), else
+ * MOE_ERROR_NOT_SUPPORTED, and are bit-identical to the row-major entry
+ * points with that plan. */
+MOE_API moe_status_t moe_gate_up_mx_tiled_packed(const moe_problem_t* p, int32_t bits,
+                                                 const uint16_t* x_disp,
+                                                 const int32_t* expert_offsets,
+                                                 const uint8_t* w_gateup_codes_tiled,
+                                                 const uint8_t* w_gateup_scales, uint16_t* h,
+                                                 void* stream);
+MOE_API moe_status_t moe_forward_mx_tiled_packed(const moe_problem_t* p, int32_t bits,
+                                                 const uint16_t* x, const int32_t* topk_ids,
+                                                 const float* topk_weights,
+                                                 const uint8_t* w_gateup_codes_tiled,
+                                                 const uint8_t* w_gateup_scales,
+                                                 const uint8_t* w_down_codes_tiled,
+                                                 const uint8_t* w_down_scales,
+                                                 const int32_t* num_tokens_dev,
+                                                 int32_t* expert_offsets, uint16_t* out,
+                                                 void* workspace, size_t ws_bytes, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -28,7 +28,8 @@ EXPORTS = (
     "moe_forward_packed", "moe_mx_pack", "moe_gate_up_mx_packed", "moe_forward_mx_packed",
     "moe_forward_noalloc", "moe_router_dispatch", "moe_forward_logits", "moe_tiled_pack",
     "moe_gate_up_tiled_packed", "moe_forward_tiled_packed", "moe_forward_single",
-    "moe_single_launch_status",
+    "moe_single_launch_status", "moe_mx_tiled_pack", "moe_gate_up_mx_tiled_packed",
+    "moe_forward_mx_tiled_packed",
 )
 
 # Largest moe_forward workspace that moe_forward_noalloc serves from its
@@ -99,6 +100,11 @@ _SIGS = {
     "moe_forward_tiled_packed": (ctypes.c_int, [_PP, _P, _P, _P, _P, _P, _P, _P, _P, _P, _SZ, _P]),
     "moe_forward_single": (ctypes.c_int, [_PP, _P, _P, _P, _P, _P, _P, _P, _P, _P, _SZ, _P]),
     "moe_single_launch_status": (ctypes.c_int, [ctypes.POINTER(ctypes.c_uint32)]),
+    "moe_mx_tiled_pack": (ctypes.c_int, [_P, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
+                                         ctypes.c_int32, _P, _P]),
+    "moe_gate_up_mx_tiled_packed": (ctypes.c_int, [_PP, ctypes.c_int32, _P, _P, _P, _P, _P, _P]),
+    "moe_forward_mx_tiled_packed": (ctypes.c_int, [_PP, ctypes.c_int32, _P, _P, _P, _P, _P, _P,
+                                                   _P, _P, _P, _P, _P, _SZ, _P]),
 }
 
 _lib = None

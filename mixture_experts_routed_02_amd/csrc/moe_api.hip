@@ -804,6 +804,95 @@ moe_status_t moe_forward_mx_packed(const moe_problem_t* p, int32_t bits, const u
                       workspace, ws_bytes, stream, true);
 }
 
+moe_status_t moe_mx_tiled_pack(const uint8_t* codes, int32_t experts, int32_t rows, int32_t k,
+                               int32_t bits, uint8_t* packed, void* stream) {
+    if (bits != 8 && bits != 4) return MOE_ERROR_INVALID_VALUE;
+    if (experts < 0 || rows <= 0 || k <= 0 || rows % 32 != 0 || k % 64 != 0)
+        return MOE_ERROR_INVALID_VALUE;
+    const long long row_bytes = (long long)k * bits / 8;
+    if ((long long)experts * rows > (1ll << 40) / row_bytes) return MOE_ERROR_NOT_SUPPORTED;
+    if (experts == 0) return MOE_SUCCESS;
+    if (bad_codes(codes) || bad_codes(packed)) return MOE_ERROR_INVALID_VALUE;
+    const uintptr_t n = (uintptr_t)experts * rows * row_bytes, a = (uintptr_t)codes,
+                    b = (uintptr_t)packed;
+    if (a < b + n && b < a + n) return MOE_ERROR_INVALID_VALUE;   // overlapping buffers
+    return launched(moe::launch_mx_tiled_pack(bits, codes, experts, rows, k, packed,
+                                              static_cast<hipStream_t>(stream)));
+}
+
+// The tiled plan for codes in the tiled pack layout: as tiled_plan, and both
+// GEMMs' K (hidden for gate-up, intermediate for down) within mx_tiled_ok.
+static bool mx_tiled_packed_plan(const moe_problem_t* p, const Shape& s, GemmPlan* plan,
+                                 bool gate_up_only) {
+    if (!tiled_plan(p, s, plan)) return false;
+    return moe::mx_tiled_ok(s.H) && (gate_up_only || moe::mx_tiled_ok(s.I));
+}
+
+moe_status_t moe_gate_up_mx_tiled_packed(const moe_problem_t* p, int32_t bits,
+                                         const uint16_t* x_disp, const int32_t* expert_offsets,
+                                         const uint8_t* w_gateup_codes_tiled,
+                                         const uint8_t* w_gateup_scales, uint16_t* h,
+                                         void* stream) {
+    if (bits != 8 && bits != 4) return MOE_ERROR_INVALID_VALUE;
+    Shape s;
+    moe_status_t st = check_mx_problem(p, bits, &s);
+    if (st != MOE_SUCCESS) return st;
+    GemmPlan plan;
+    if (!mx_tiled_packed_plan(p, s, &plan, true)) return MOE_ERROR_NOT_SUPPORTED;
+    if (bad_bf16(x_disp, s.cap) || bad_i32(expert_offsets) || bad_codes(w_gateup_codes_tiled) ||
+        bad_scales(w_gateup_scales, bits) || bad_bf16(h, s.cap))
+        return MOE_ERROR_INVALID_VALUE;
+    return launched(moe::launch_grouped_gemm_mx(s, bits, true, x_disp, nullptr, s.K,
+                                                expert_offsets, w_gateup_codes_tiled,
+                                                w_gateup_scales, h, s.H, s.I,
+                                                static_cast<hipStream_t>(stream), false,
+                                                plan.kind, true));
+}
+
+moe_status_t moe_forward_mx_tiled_packed(const moe_problem_t* p, int32_t bits, const uint16_t* x,
+                                         const int32_t* topk_ids, const float* topk_weights,
+                                         const uint8_t* w_gateup_codes_tiled,
+                                         const uint8_t* w_gateup_scales,
+                                         const uint8_t* w_down_codes_tiled,
+                                         const uint8_t* w_down_scales,
+                                         const int32_t* num_tokens_dev, int32_t* expert_offsets,
+                                         uint16_t* out, void* workspace, size_t ws_bytes,
+                                         void* stream) {
+    if (bits != 8 && bits != 4) return MOE_ERROR_INVALID_VALUE;
+    Shape s;
+    moe_status_t st = check_mx_problem(p, bits, &s);
+    if (st != MOE_SUCCESS) return st;
+    GemmPlan plan;
+    if (!mx_tiled_packed_plan(p, s, &plan, false)) return MOE_ERROR_NOT_SUPPORTED;
+    const long long tk = (long long)s.T * s.K;
+    if (bad_bf16(x, s.T) || bad_i32(topk_ids, tk) || bad_i32(topk_weights, tk) ||
+        bad_codes(w_gateup_codes_tiled) || bad_scales(w_gateup_scales, bits) ||
+        bad_codes(w_down_codes_tiled) || bad_scales(w_down_scales, bits) ||
+        bad_i32(expert_offsets) || bad_bf16(out, s.T))
+        return MOE_ERROR_INVALID_VALUE;
+    if (num_tokens_dev && !aligned(num_tokens_dev, 4)) return MOE_ERROR_INVALID_VALUE;
+    if ((st = check_ws(s, workspace, ws_bytes)) != MOE_SUCCESS) return st;
+    hipStream_t hs = static_cast<hipStream_t>(stream);
+    const Layout L = layout(s);
+    int32_t* row_src = at<int32_t>(workspace, L.row_src);
+    int32_t* token_row = at<int32_t>(workspace, L.token_row);
+    uint16_t* h = at<uint16_t>(workspace, L.h);
+    uint16_t* y = at<uint16_t>(workspace, L.y);
+    if (moe::launch_dispatch(s, topk_ids, num_tokens_dev, expert_offsets, row_src, token_row,
+                             at<int32_t>(workspace, L.counts), hs) != hipSuccess)
+        return MOE_ERROR_LAUNCH;
+    if (moe::launch_grouped_gemm_mx(s, bits, true, x, row_src, s.K, expert_offsets,
+                                    w_gateup_codes_tiled, w_gateup_scales, h, s.H, s.I, hs, false,
+                                    plan.kind, true) != hipSuccess)
+        return MOE_ERROR_LAUNCH;
+    if (moe::launch_grouped_gemm_mx(s, bits, false, h, nullptr, 1, expert_offsets,
+                                    w_down_codes_tiled, w_down_scales, y, s.I, s.H, hs, false,
+                                    plan.kind, true) != hipSuccess)
+        return MOE_ERROR_LAUNCH;
+    if (s.T == 0) return MOE_SUCCESS;
+    return launched(moe::launch_combine(s, y, token_row, topk_weights, num_tokens_dev, out, hs));
+}
+
 moe_status_t moe_graph_create(const moe_problem_t* p, const uint16_t* x, const int32_t* topk_ids,
                               const float* topk_weights, const uint16_t* w_gateup,
                               const uint16_t* w_down, const int32_t* num_tokens_dev,

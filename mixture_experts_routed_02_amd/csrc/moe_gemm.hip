@@ -1424,7 +1424,7 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_tiled_kernel(
     static_assert(NW % 4 == 0, "a wave's DMA groups share one row-swizzle phase");
     static_assert(!GATED || NS % 2 == 0, "gated tiles pair gate and up sub-tiles");
     static_assert(SA >= 2 && SW >= SA && LDS <= ring_budget(NW), "ring sizes");
-    static_assert(!MX || (!PACKED && (WF == 8 || WF == 4)), "MX: row-major codes");
+    static_assert(!MX || WF == 8 || WF == 4, "MX: e4m3 or e2m1 codes");
     static_assert(N_FIRST < 64 && N_STEADY < 64, "vmcnt range");
 
     __shared__ __attribute__((aligned(1024))) unsigned char s_lds[LDS];
@@ -1578,9 +1578,14 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_tiled_kernel(
         const uint16_t* wbase = PACKED ? W + (size_t)e * w_rows * Kd + lane * 8
                                        : W + (size_t)e * w_rows * Kd + (size_t)dma_row * Kd + dma_chunk * 8;
         // MX: byte address of this lane's 16 code bytes (row wdma_row of a group,
-        // chunk wdma_chunk), stage 0
-        const unsigned char* wbase_mx = reinterpret_cast<const unsigned char*>(W) +
-                                        ((size_t)e * w_rows + wdma_row) * wrow_bytes + wdma_chunk * 16;
+        // chunk wdma_chunk), stage 0; PACKED (tiled pack layout of the codes):
+        // the 1 KiB of a group and stage is contiguous and in slot order, so
+        // lane L reads piece L, and group g's stages start g * WROWS rows'
+        // worth of bytes into the expert's block, as row-major rows would
+        const unsigned char* wbase_mx =
+            PACKED ? reinterpret_cast<const unsigned char*>(W) + (size_t)e * w_rows * wrow_bytes + lane * 16
+                   : reinterpret_cast<const unsigned char*>(W) +
+                         ((size_t)e * w_rows + wdma_row) * wrow_bytes + wdma_chunk * 16;
         auto wrow0 = [&](int q) {   // first weight row of this wave's weight group q
             const int tr = (wave + NW * q) * WROWS;
             if (GATED) return (tr < BN / 2) ? (n_tile * (BN / 2) + tr) : (N + n_tile * (BN / 2) + tr - BN / 2);
@@ -1595,7 +1600,8 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_tiled_kernel(
                 const int qw = q - GA;
                 const uint32_t dst = ringW0 + (sw % SW) * W_STAGE + (wave + NW * qw) * 1024;
                 if constexpr (MX)
-                    lds_dma16(wbase_mx + (size_t)wrow0(qw) * wrow_bytes + (size_t)sw * RBW, dst);
+                    lds_dma16(wbase_mx + (size_t)wrow0(qw) * wrow_bytes + (size_t)sw * (PACKED ? 1024 : RBW),
+                              dst);
                 else    // packed: group wrow0/8 holds Kd/64 stages of 512 values each
                     lds_dma16(PACKED ? wbase + (size_t)wrow0(qw) * Kd + (size_t)sw * 512
                                      : wbase + (size_t)wrow0(qw) * Kd + (size_t)sw * kBK, dst);
@@ -1852,15 +1858,21 @@ hipError_t launch_tiled(int grid, const uint16_t* A, const int32_t* row_src, int
 template <int WF, int BM, int BN, int WGM, int WGN, bool GATED>
 hipError_t launch_tiled_mx(int grid, const uint16_t* A, const int32_t* row_src, int topk,
                            const int32_t* offsets, const uint8_t* Wq, const uint8_t* Ws,
-                           uint16_t* C, int E, int Kd, int N, int split, hipStream_t st) {
+                           uint16_t* C, int E, int Kd, int N, int split, hipStream_t st,
+                           bool packed) {
     // every wave fills whole weight groups (16 rows for e4m3, 32 for e2m1):
     // the plan below never asks for the shapes that cannot
     if constexpr ((BN / (WF == 8 ? 16 : 32)) % (WGM * WGN) != 0) {
         return hipErrorInvalidValue;
     } else {
-        hipLaunchKernelGGL((gemm_tiled_kernel<BM, BN, WGM, WGN, GATED, true, false, WF>), dim3(grid),
-                           dim3(64 * WGM * WGN), 0, st, A, row_src, topk, offsets,
-                           reinterpret_cast<const uint16_t*>(Wq), C, E, Kd, N, split, Ws);
+        if (packed)
+            hipLaunchKernelGGL((gemm_tiled_kernel<BM, BN, WGM, WGN, GATED, true, true, WF>), dim3(grid),
+                               dim3(64 * WGM * WGN), 0, st, A, row_src, topk, offsets,
+                               reinterpret_cast<const uint16_t*>(Wq), C, E, Kd, N, split, Ws);
+        else
+            hipLaunchKernelGGL((gemm_tiled_kernel<BM, BN, WGM, WGN, GATED, true, false, WF>), dim3(grid),
+                               dim3(64 * WGM * WGN), 0, st, A, row_src, topk, offsets,
+                               reinterpret_cast<const uint16_t*>(Wq), C, E, Kd, N, split, Ws);
         return hipGetLastError();
     }
 }
@@ -1869,12 +1881,12 @@ template <int WF>
 hipError_t launch_grouped_gemm_mx_tiled(const GemmPlan& plan, bool gated, const uint16_t* A,
                                         const int32_t* row_src, int topk, const int32_t* offsets,
                                         const uint8_t* Wq, const uint8_t* Ws, uint16_t* C, int E,
-                                        int Kd, int N, hipStream_t st) {
+                                        int Kd, int N, hipStream_t st, bool packed) {
     const int grid = gated ? plan.grid_gateup : plan.grid_down;
     const int bn = gated ? plan.bn_gateup : plan.bn_down;
     const int split = plan.split ? 1 : 0;
 #define MOE_TILED_MX(BM, BN, WGM, WGN, G) \
-    launch_tiled_mx<WF, BM, BN, WGM, WGN, G>(grid, A, row_src, topk, offsets, Wq, Ws, C, E, Kd, N, split, st)
+    launch_tiled_mx<WF, BM, BN, WGM, WGN, G>(grid, A, row_src, topk, offsets, Wq, Ws, C, E, Kd, N, split, st, packed)
     switch (plan.kind) {
         case kTiled64:
             if (gated) return MOE_TILED_MX(64, 128, 2, 2, true);
@@ -1902,25 +1914,39 @@ hipError_t launch_grouped_gemm_mx_tiled(const GemmPlan& plan, bool gated, const 
 // contiguously and in slot order: piece L (0..63) = row 8g + L/8, k-values
 // 64s + 8c .. +7 with c = (L % 8) ^ ring_swz((8g + L/8) % 32).  Weight tiles
 // start at rows that are multiples of 32, so the swizzle a row gets in LDS is
-// the one applied here.  Same size as the row-major weights.
+// the one applied here.  Same size as the row-major weights.  MX codes
+// (FlashInfer PR #3980, Summary: the MXFP8 backend) the same way with their
+// own pieces: a stage of a row is 64 bytes of e4m3 codes (16 rows per 1 KiB,
+// chunk c of row r in slot c ^ mx8_swz(r % 32)) or 32 bytes of e2m1 codes
+// (32 rows, slot c ^ mx4_swz(r % 32)); the scales stay row-major.
 // ---------------------------------------------------------------------------
-__global__ __launch_bounds__(256) void tiled_pack_kernel(const uint16_t* __restrict__ w,
-                                                         long long pieces, int rows, int Kd,
-                                                         uint16_t* __restrict__ out) {
+// WF: the weight format (16 bf16, 8 e4m3 codes, 4 e2m1 codes), which sets the
+// bytes of a row per stage (RBW = 128, 64, 32), the rows per 1 KiB piece
+// (1024 / RBW) and the chunk swizzle the tiled kernel's DMA applies (see
+// ring_swz, mx8_swz, mx4_swz); row_bytes = the bytes of one row.
+template <int WF>
+__global__ __launch_bounds__(256) void tiled_pack_kernel(const unsigned char* __restrict__ w,
+                                                         long long pieces, int rows,
+                                                         long long row_bytes,
+                                                         unsigned char* __restrict__ out) {
+    constexpr int RBW = WF == 16 ? 128 : (WF == 8 ? 64 : 32);
+    constexpr int CH = RBW / 16;                       // 16-byte chunks of a row per stage
+    constexpr int WROWS = 1024 / RBW;                  // rows per 1 KiB piece
     const long long i = (long long)blockIdx.x * blockDim.x + threadIdx.x;   // output piece
     if (i >= pieces) return;
-    const int nk = Kd / kBK;
+    const int nk = (int)(row_bytes / RBW);
     const int L = (int)(i & 63);
     const long long t = i >> 6;
     const int st = (int)(t % nk);
-    const long long eg = t / nk;                       // e * (rows / 8) + g
-    const int groups = rows / 8;
+    const long long eg = t / nk;                       // e * (rows / WROWS) + g
+    const int groups = rows / WROWS;
     const long long e = eg / groups;
-    const int r = (int)(eg % groups) * 8 + (L >> 3);
-    const int c = (L & 7) ^ ring_swz(r & 31);
-    const moe_bf16x8* src = reinterpret_cast<const moe_bf16x8*>(
-        w + ((size_t)e * rows + r) * (size_t)Kd + (size_t)st * kBK + c * 8);
-    reinterpret_cast<moe_bf16x8*>(out)[i] = *src;
+    const int r = (int)(eg % groups) * WROWS + L / CH;
+    const int slot = L % CH;
+    const int c = WF == 16 ? slot ^ ring_swz(r & 31) : WF == 8 ? slot ^ mx8_swz(r & 31)
+                                                               : slot ^ mx4_swz(r & 31);
+    const unsigned char* src = w + ((size_t)e * rows + r) * (size_t)row_bytes + (size_t)st * RBW + c * 16;
+    reinterpret_cast<moe_bf16x8*>(out)[i] = *reinterpret_cast<const moe_bf16x8*>(src);
 }
 
 }  // namespace
@@ -2084,16 +2110,26 @@ bool mx_tiled_ok(int Kd) { return Kd % 512 == 0 && Kd / 32 <= kMxMaxKBlocks; }
 hipError_t launch_grouped_gemm_mx(const Shape& s, int fmt, bool gated, const uint16_t* A,
                                   const int32_t* row_src, int topk, const int32_t* offsets,
                                   const uint8_t* Wq, const uint8_t* Ws, uint16_t* C, int Kd, int N,
-                                  hipStream_t st, bool packed, int hint) {
+                                  hipStream_t st, bool packed, int hint, bool tiled_packed) {
     // the tiled plan where the bf16 layer would take one and the tile's scales
-    // fit in LDS (row-major codes only); else the skinny kernels
+    // fit in LDS (row-major codes, or codes in the tiled pack layout, which
+    // take the tiled plan of tiled_packed_plan); else the skinny kernels
+    if (tiled_packed) {   // hint: a tiled plan's kind (checked on the host)
+        const GemmPlan plan = choose_plan(s, hint);
+        if (packed || plan.kind == kSkinny || !mx_tiled_ok(Kd)) return hipErrorInvalidValue;
+        if (fmt == 8)
+            return launch_grouped_gemm_mx_tiled<8>(plan, gated, A, row_src, topk, offsets, Wq, Ws,
+                                                   C, s.E, Kd, N, st, true);
+        return launch_grouped_gemm_mx_tiled<4>(plan, gated, A, row_src, topk, offsets, Wq, Ws, C,
+                                               s.E, Kd, N, st, true);
+    }
     const GemmPlan plan = choose_plan(s, hint);
     if (!packed && plan.kind != kSkinny && mx_tiled_ok(Kd)) {
         if (fmt == 8)
             return launch_grouped_gemm_mx_tiled<8>(plan, gated, A, row_src, topk, offsets, Wq, Ws,
-                                                   C, s.E, Kd, N, st);
+                                                   C, s.E, Kd, N, st, false);
         return launch_grouped_gemm_mx_tiled<4>(plan, gated, A, row_src, topk, offsets, Wq, Ws, C,
-                                               s.E, Kd, N, st);
+                                               s.E, Kd, N, st, false);
     }
     const bool wide = mx_wide(fmt, s);
     if (fmt == 8 && packed)
@@ -2150,8 +2186,24 @@ hipError_t launch_tiled_pack(const uint16_t* w, int experts, int rows, int Kd, u
                              hipStream_t st) {
     const long long pieces = (long long)experts * rows * (Kd / 8);
     if (pieces == 0) return hipSuccess;
-    hipLaunchKernelGGL(tiled_pack_kernel, dim3((unsigned)((pieces + 255) / 256)), dim3(256), 0, st,
-                       w, pieces, rows, Kd, out);
+    hipLaunchKernelGGL(tiled_pack_kernel<16>, dim3((unsigned)((pieces + 255) / 256)), dim3(256), 0,
+                       st, reinterpret_cast<const unsigned char*>(w), pieces, rows,
+                       (long long)Kd * 2, reinterpret_cast<unsigned char*>(out));
+    return hipGetLastError();
+}
+
+hipError_t launch_mx_tiled_pack(int fmt, const uint8_t* codes, int experts, int rows, int Kd,
+                                uint8_t* out, hipStream_t st) {
+    const long long row_bytes = (long long)Kd * fmt / 8;
+    const long long pieces = (long long)experts * rows * (row_bytes / 16);
+    if (pieces == 0) return hipSuccess;
+    const dim3 grid((unsigned)((pieces + 255) / 256)), block(256);
+    if (fmt == 8)
+        hipLaunchKernelGGL(tiled_pack_kernel<8>, grid, block, 0, st, codes, pieces, rows, row_bytes,
+                           out);
+    else
+        hipLaunchKernelGGL(tiled_pack_kernel<4>, grid, block, 0, st, codes, pieces, rows, row_bytes,
+                           out);
     return hipGetLastError();
 }
 

@@ -136,12 +136,21 @@ hipError_t launch_down_combine_tiny_mx(const Shape& s, int fmt, const uint16_t* 
 // The grouped GEMM on MX weights: the tiled plan (MFMA tiles of the bf16
 // plan, codes staged through LDS and dequantized on the fragment reads, the
 // tile's scales in LDS) when choose_plan(s, hint) is a tiled one, the codes
-// are row-major and mx_tiled_ok(Kd); else the skinny MX kernels.
+// are row-major and mx_tiled_ok(Kd); else the skinny MX kernels (packed:
+// codes in the skinny pack layout).  tiled_packed: codes in the tiled pack
+// layout (launch_mx_tiled_pack); hint must then name a tiled plan and
+// mx_tiled_ok(Kd) hold.
 bool mx_tiled_ok(int Kd);
 hipError_t launch_grouped_gemm_mx(const Shape& s, int fmt, bool gated, const uint16_t* A,
                                   const int32_t* row_src, int topk, const int32_t* offsets,
                                   const uint8_t* Wq, const uint8_t* Ws, uint16_t* C, int Kd, int N,
-                                  hipStream_t st, bool packed = false, int hint = 0);
+                                  hipStream_t st, bool packed = false, int hint = 0,
+                                  bool tiled_packed = false);
+// MX codes [experts, rows, Kd * fmt / 8 bytes] (rows % 32 == 0, Kd % 64 == 0)
+// -> the tiled pack layout of those codes (1 KiB DMA pieces of 16 rows x 64
+// bytes for e4m3, 32 rows x 32 bytes for e2m1, contiguous, in slot order).
+hipError_t launch_mx_tiled_pack(int fmt, const uint8_t* codes, int experts, int rows, int Kd,
+                                uint8_t* out, hipStream_t st);
 // nblocks blocks of 32 consecutive bf16 values <-> 32 codes + 1 scale each
 hipError_t launch_mx_quantize(int fmt, const uint16_t* w, long long nblocks, uint8_t* codes,
                               uint8_t* scales, hipStream_t st);

@@ -22,7 +22,7 @@ __all__ = [
     "mxfp8_quantize", "mxfp8_dequantize", "gate_up_mxfp8", "forward_mxfp8", "skinny_pack",
     "gate_up_packed", "forward_packed", "mx_pack", "forward_noalloc", "router_dispatch",
     "forward_logits", "tiled_pack", "gate_up_tiled_packed", "forward_tiled_packed",
-    "forward_single", "single_launch_status",
+    "forward_single", "single_launch_status", "mx_tiled_pack",
 ]
 
 
@@ -477,9 +477,26 @@ def mx_pack(codes, gated: bool, fmt="mxfp8", out=None):
     return out
 
 
+def mx_tiled_pack(codes, fmt="mxfp8", out=None):
+    """MX codes [E, rows, K*bits/8] -> the tiled pack layout (for the tiled,
+    prefill kernels; both W_gateup and W_down codes the same way)."""
+    bits_, _ = _mx(fmt)
+    _need(codes, "codes", torch.uint8)
+    if codes.dim() != 3:
+        raise ValueError("codes must be [experts, rows, bytes]")
+    E, rows, nb = codes.shape
+    if out is None:
+        out = torch.empty_like(codes)
+    _need(out, "out", torch.uint8, tuple(codes.shape), codes.device)
+    check("moe_mx_tiled_pack", lib().moe_mx_tiled_pack(_ptr(codes), E, rows, nb * 8 // bits_, bits_,
+                                                       _ptr(out), _stream_ptr(codes.device)))
+    return out
+
+
 def gate_up_mx(p: MoeProblem, x_disp, expert_offsets, w_gateup_codes, w_gateup_scales,
-               fmt="mxfp8", h=None, packed=False):
-    """Gate-up grouped GEMM on MX weights (packed: codes from mx_pack).  Returns h [cap, I]."""
+               fmt="mxfp8", h=None, packed=False, tiled_packed=False):
+    """Gate-up grouped GEMM on MX weights (packed: codes from mx_pack;
+    tiled_packed: codes from mx_tiled_pack).  Returns h [cap, I]."""
     bits_, name = _mx(fmt)
     E, H, I = p.num_experts, p.hidden, p.intermediate
     dev = x_disp.device
@@ -491,8 +508,11 @@ def gate_up_mx(p: MoeProblem, x_disp, expert_offsets, w_gateup_codes, w_gateup_s
     if h is None:
         h = torch.empty((cap, I), dtype=torch.bfloat16, device=dev)
     _need(h, "h", torch.bfloat16, (cap, I), dev)
-    if packed:
-        check("moe_gate_up_mx_packed", lib().moe_gate_up_mx_packed(
+    if packed and tiled_packed:
+        raise ValueError("packed and tiled_packed are two different layouts")
+    if packed or tiled_packed:
+        fn = "moe_gate_up_mx_packed" if packed else "moe_gate_up_mx_tiled_packed"
+        check(fn, getattr(lib(), fn)(
             ctypes.byref(p), bits_, _ptr(x_disp), _ptr(expert_offsets), _ptr(w_gateup_codes),
             _ptr(w_gateup_scales), _ptr(h), _stream_ptr(dev)))
         return h
@@ -509,9 +529,11 @@ def gate_up_mxfp8(p: MoeProblem, x_disp, expert_offsets, w_gateup_codes, w_gateu
 
 def forward_mx(p: MoeProblem, x, topk_ids, topk_weights, w_gateup_codes, w_gateup_scales,
                w_down_codes, w_down_scales, fmt="mxfp8", num_tokens_dev=None,
-               expert_offsets=None, out=None, workspace=None, packed=False):
-    """The routed-expert layer on MX expert weights (packed: codes from mx_pack).
-    Returns (out, expert_offsets)."""
+               expert_offsets=None, out=None, workspace=None, packed=False, tiled_packed=False):
+    """The routed-expert layer on MX expert weights (packed: codes from mx_pack;
+    tiled_packed: codes from mx_tiled_pack).  Returns (out, expert_offsets)."""
+    if packed and tiled_packed:
+        raise ValueError("packed and tiled_packed are two different layouts")
     bits_, name = _mx(fmt)
     T, K, E, H, I = p.num_tokens, p.top_k, p.num_experts, p.hidden, p.intermediate
     dev = x.device
@@ -535,6 +557,9 @@ def forward_mx(p: MoeProblem, x, topk_ids, topk_weights, w_gateup_codes, w_gateu
             _ptr(expert_offsets), _ptr(out), _ptr(ws), ws.numel(), _stream_ptr(dev))
     if packed:
         check("moe_forward_mx_packed", lib().moe_forward_mx_packed(ctypes.byref(p), bits_, *args))
+    elif tiled_packed:
+        check("moe_forward_mx_tiled_packed",
+              lib().moe_forward_mx_tiled_packed(ctypes.byref(p), bits_, *args))
     else:
         fn = f"moe_forward_{name}"
         check(fn, getattr(lib(), fn)(ctypes.byref(p), *args))

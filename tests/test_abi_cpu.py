@@ -25,7 +25,7 @@ def declared_functions():
 
 def test_exports_every_declared_symbol():
     names = declared_functions()
-    assert len(names) == 34, names
+    assert len(names) == 37, names
     L = moe.lib()
     for n in names:
         assert hasattr(L, n), n
@@ -190,6 +190,28 @@ def test_mx_pack_entry_points_fail_closed():
     assert L.moe_forward_mx_packed(ctypes.byref(p), 5, A16, A4, A4, A16, A16, A16, A16, None, A4,
                                    A16, A16, ws, None) == 1
     assert L.moe_gate_up_mx_packed(ctypes.byref(p), 16, A16, A4, A16, A16, A16, None) == 1
+
+
+def test_mx_tiled_pack_entry_points_fail_closed():
+    L = moe.lib()
+    assert L.moe_mx_tiled_pack(A16, 2, 32, 64, 6, A16 * 2, None) == 1        # bits 8 or 4
+    assert L.moe_mx_tiled_pack(A16, 2, 16, 64, 8, A16 * 2, None) == 1        # rows % 32
+    assert L.moe_mx_tiled_pack(A16, 2, 32, 96, 4, A16 * 2, None) == 1        # k % 64
+    assert L.moe_mx_tiled_pack(A16, 2, 32, 128, 8, A16 + 64, None) == 1      # overlap
+    assert L.moe_mx_tiled_pack(A16 + 8, 2, 32, 128, 8, A16 * 2, None) == 1   # misaligned
+    assert L.moe_mx_tiled_pack(None, 0, 32, 128, 4, None, None) == 0         # nothing to do
+    # a skinny plan is refused; K outside the tiled MX range (H % 512) too
+    p1 = moe.problem(64, 2, 8, 512, 512, kernel_hint=1)
+    ws = moe.workspace_size(p1)
+    args = (A16, A4, A4, A16, A16, A16, A16, None, A4, A16, A16, ws, None)
+    assert L.moe_forward_mx_tiled_packed(ctypes.byref(p1), 8, *args) == 2
+    p2 = moe.problem(64, 2, 8, 256, 512, kernel_hint=4)
+    assert L.moe_forward_mx_tiled_packed(ctypes.byref(p2), 8, *args) == 2
+    assert L.moe_gate_up_mx_tiled_packed(ctypes.byref(p2), 8, A16, A4, A16, A16, A16, None) == 2
+    p3 = moe.problem(64, 2, 8, 512, 512, kernel_hint=4)
+    assert L.moe_forward_mx_tiled_packed(ctypes.byref(p3), 5, *args) == 1      # bits
+    assert L.moe_gate_up_mx_tiled_packed(ctypes.byref(p3), 8, A16, A4, A16, A16 + 1, A16,
+                                         None) == 1                         # scales misaligned
 
 
 def test_skinny_pack_rejects_overlap():

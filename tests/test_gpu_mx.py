@@ -329,3 +329,84 @@ def test_forward_mx_ep_prefill_full_size(fmt, name, seed):
     ref = oracle.forward_tokens_widened(bits(x), ids.numpy(), w.numpy(), E, widen, toks,
                                         workers=oracle_workers())
     check_close(f64(out)[toks], ref, f"{fmt} {name}")
+
+
+# ---------------------------------------------------------------------------
+# MX codes in the tiled pack layout (moe_mx_tiled_pack): the layout against a
+# numpy re-layout written from its definition, and the tiled MX layers on
+# packed codes bit-identical to the row-major ones with the same plan (and
+# within the oracle's bar)
+# ---------------------------------------------------------------------------
+def expected_mx_tiled_pack(codes, fmt):
+    """Per expert, group g of G rows (16 for e4m3, 32 for e2m1) and stage s
+    (64 values: RBW = 64 or 32 bytes of a row), piece L = row G*g + L/C (C =
+    RBW / 16 chunks), bytes RBW*s + 16c .. +15 with c = (L % C) ^ swz(row % 32)."""
+    E, rows, nb = codes.shape
+    rbw = 64 if fmt == "mxfp8" else 32
+    ch, wrows = rbw // 16, 1024 // rbw
+    G, S = rows // wrows, nb // rbw
+    L = np.arange(64)
+    r = wrows * np.arange(G)[:, None] + (L // ch)[None, :]                 # [G, 64]
+    rm = r % 32
+    swz = (((rm >> 2) & 1) | ((rm >> 3) & 2)) if fmt == "mxfp8" else ((rm >> 4) & 1)
+    c = (L % ch)[None, :] ^ swz                                            # [G, 64]
+    byte = rbw * np.arange(S)[None, :, None, None] + 16 * c[:, None, :, None] + np.arange(16)
+    return codes[:, r[:, None, :, None], byte].reshape(E, rows, nb)        # [E, G, S, 64, 16]
+
+
+@pytest.mark.parametrize("fmt", FMTS)
+@pytest.mark.parametrize("E,rows,K", [(3, 64, 512), (2, 96, 1024), (1, 2048, 64), (4, 32, 7168)])
+def test_mx_tiled_pack_layout(fmt, E, rows, K):
+    g = torch.Generator().manual_seed(E * rows + K)
+    nb = K * (8 if fmt == "mxfp8" else 4) // 8
+    codes = torch.randint(0, 256, (E, rows, nb), generator=g, dtype=torch.uint8)
+    got = ops.mx_tiled_pack(codes.to(DEV), fmt)
+    assert np.array_equal(got.cpu().numpy(), expected_mx_tiled_pack(codes.numpy(), fmt))
+
+
+@pytest.mark.parametrize("fmt", FMTS)
+@pytest.mark.parametrize("name", list(TILED))
+@pytest.mark.parametrize("hint", [0, 2, 3, 4])
+def test_forward_mx_tiled_packed(fmt, name, hint):
+    T, K, E, H, I, lo, hi = TILED[name]
+    x, ids, w, qgu, sgu, qd, sd = quantized_case(fmt, T, K, E, H, I, 19, lo, hi)
+    t = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(DEV)
+    qgu_d, sgu_d, qd_d, sd_d = t(qgu), t(sgu), t(qd), t(sd)
+    pgu, pd = ops.mx_tiled_pack(qgu_d, fmt), ops.mx_tiled_pack(qd_d, fmt)
+    p = moe.problem(T, K, E, H, I, 0, hint)
+    xd, idd, wdv = x.to(DEV), ids.to(DEV), w.to(DEV)
+    got, off = ops.forward_mx(p, xd, idd, wdv, pgu, sgu_d, pd, sd_d, fmt, tiled_packed=True)
+    # the same tiled plan on row-major codes (the automatic choice, or the
+    # 64-row tiled plan where it would be the skinny one)
+    ref_hint = hint if hint else (2 if T * K / E <= 24 else 0)
+    pr = moe.problem(T, K, E, H, I, 0, ref_hint)
+    ref, ref_off = ops.forward_mx(pr, xd, idd, wdv, qgu_d, sgu_d, qd_d, sd_d, fmt)
+    assert torch.equal(off, ref_off)
+    assert torch.equal(got.view(torch.int16), ref.view(torch.int16))
+    x_disp, o2, _, _ = ops.dispatch(p, xd, idd)
+    h_ref = ops.gate_up_mx(pr, x_disp, o2, qgu_d, sgu_d, fmt)
+    h = ops.gate_up_mx(p, x_disp, o2, pgu, sgu_d, fmt, tiled_packed=True)
+    R = int(o2[-1])
+    assert torch.equal(h[:R].view(torch.int16), h_ref[:R].view(torch.int16))
+    ref_o = ORACLE[fmt][2](bits(x), ids.numpy(), w.numpy(), qgu, sgu, qd, sd)
+    check_close(f64(got), ref_o, f"{fmt} tiled packed {name}/hint{hint}")
+
+
+@pytest.mark.parametrize("fmt", FMTS)
+def test_forward_mx_tiled_packed_full_size(fmt):
+    """EP prefill at 8192 tokens: packed codes bit-identical to row-major."""
+    cfg = W.CONFIGS["ep_prefill_T8192"]
+    T, K, E, H, I = cfg.num_tokens, cfg.top_k, cfg.num_experts, cfg.hidden, cfg.intermediate
+    x = W.make_x(cfg, 2).to(DEV)
+    ids, w = (a.to(DEV) for a in W.make_routing(cfg, 2))
+    wgu, wd = W.make_weights(cfg, 2, DEV)
+    qgu, sgu = ops.mx_quantize(wgu, fmt)
+    qd, sd = ops.mx_quantize(wd, fmt)
+    del wgu, wd
+    torch.cuda.empty_cache()
+    p = moe.problem(T, K, E, H, I)
+    ref, _ = ops.forward_mx(p, x, ids, w, qgu, sgu, qd, sd, fmt)
+    pgu, pd = ops.mx_tiled_pack(qgu, fmt), ops.mx_tiled_pack(qd, fmt)
+    got, _ = ops.forward_mx(p, x, ids, w, pgu, sgu, pd, sd, fmt, tiled_packed=True)
+    torch.cuda.synchronize()
+    assert torch.equal(got.view(torch.int16), ref.view(torch.int16))
