@@ -44,6 +44,7 @@ from __future__ import annotations
 
 import argparse
 import hashlib
+import re
 import json
 import os
 import statistics
@@ -95,17 +96,26 @@ def pmc_traffic(kernel_key: str, src_hash: str, units: int, seed: int = 0, hint:
     return ent.get("bytes_per_launch")
 
 
-# The sources the grouped-GEMM kernels are compiled from: a change to any of
-# them voids the committed counter figures (host-side API code does not).
+# The sources the grouped-GEMM kernels are compiled from: a change to their
+# code (not to their comments) voids the committed counter figures; host-side
+# API code does not.
 GEMM_SOURCES = ("moe_gemm.hip", "moe_internal.h")
+
+
+def _code_only(text: str) -> str:
+    """The source with comments and layout removed: a comment edit leaves the
+    kernels, and so the counter figures, unchanged."""
+    text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+    text = re.sub(r"//[^\n]*", " ", text)
+    return " ".join(text.split())
 
 
 def kernel_src_hash() -> str:
     h = hashlib.sha256()
     csrc = os.path.join(REPO, "mixture_experts_routed_02_amd", "csrc")
     for name in GEMM_SOURCES:
-        with open(os.path.join(csrc, name), "rb") as fh:
-            h.update(name.encode() + b"\0" + fh.read())
+        with open(os.path.join(csrc, name), encoding="utf-8") as fh:
+            h.update(name.encode() + b"\0" + _code_only(fh.read()).encode())
     return h.hexdigest()
 
 

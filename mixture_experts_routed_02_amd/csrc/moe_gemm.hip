@@ -575,9 +575,9 @@ __global__ __launch_bounds__(256) void gemm_skinny_gateup_dispatch_kernel(
 // down GEMM and the combine for output columns [16b, 16b+16) (the tiny
 // path's arithmetic, so the result is bit-identical to it, with the token ->
 // row map taken from the workgroup's own dispatch in LDS, so h is the only
-// data that crosses workgroups).  Before waiting
-// at the barrier a workgroup requests its first block of down weights, which
-// do not depend on h, so that stream overlaps the end of the gate-up phase.
+// data that crosses workgroups).  Between arriving at the barrier and waiting
+// on it, a workgroup requests its first block of down weights, which do not
+// depend on h, so that stream overlaps the end of the gate-up phase.
 //
 // The barrier: h is the only data that crosses workgroups, and it is
 // written with device-scope atomic stores and read with device-scope atomic
