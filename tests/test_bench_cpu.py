@@ -52,3 +52,11 @@ def test_several_gpus_is_refused():
                        capture_output=True, text=True, cwd=REPO, timeout=120)
     assert r.returncode != 0
     assert "one GPU" in (r.stdout + r.stderr) or "1 GPU" in (r.stdout + r.stderr)
+
+
+def test_source_hash_ignores_comments_only():
+    a = "int f(int x) {\n  return x + 1;  // one more\n}\n/* block\n comment */\n"
+    b = "int f(int x) {\n    return x + 1;\n}\n"
+    c = "int f(int x) {\n  return x + 2;\n}\n"
+    assert bench._code_only(a) == bench._code_only(b)
+    assert bench._code_only(a) != bench._code_only(c)
