@@ -347,14 +347,14 @@ PREFILL = [(n, s) for n in ("ep_prefill_T2048", "ep_prefill_T8192") for s in (0,
 
 
 @pytest.mark.parametrize("name,seed", PREFILL)
-def test_forward_ep_prefill_sampled(name, seed, ep_share):
-    """96-of-384 prefill (uniform seeds 0-2, Zipf s = 1.2 seeds 0-4) on at
-    least 256 tokens that include every touched expert's first and last
-    dispatched row and the first row of its last m-tile at each tile height."""
+def test_forward_ep_prefill_every_token(name, seed, ep_share):
+    """96-of-384 prefill (uniform seeds 0-2, Zipf s = 1.2 seeds 0-4, 2048 and
+    8192 tokens, and the 16384-token point) on every token against the
+    oracle; the Zipf layers include local experts with up to 37 m-tiles."""
     wgu, wd, widen = ep_share
     cfg, x, ids, w, out = run_full_size(name, seed, (wgu, wd))
-    toks = covering_tokens(ids.numpy(), cfg.num_experts, 256, seed=seed + 1)
-    check_tokens(name, seed, cfg, x, ids, w, widen, out, toks, oracle_workers())
+    check_tokens(name, seed, cfg, x, ids, w, widen, out, np.arange(cfg.num_tokens),
+                 oracle_workers())
 
 
 # ---------------------------------------------------------------------------
