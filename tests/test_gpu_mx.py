@@ -306,9 +306,9 @@ def test_gate_up_mx_tiled_staged(fmt, hint):
 @pytest.mark.parametrize("name,seed", [("ep_prefill_T8192", 0), ("ep_prefill_T2048_zipf", 1)])
 def test_forward_mx_ep_prefill_full_size(fmt, name, seed):
     """The 96-expert prefill share at full size on device-quantized weights
-    (the quantizer is checked bit for bit above): at least 128 covering
-    tokens against the oracle's MX layer."""
-    from helpers import covering_tokens, oracle_workers
+    (the quantizer is checked bit for bit above): every token against the
+    oracle's MX layer."""
+    from helpers import oracle_workers
     cfg = W.CONFIGS[name]
     T, K, E, H, I = cfg.num_tokens, cfg.top_k, cfg.num_experts, cfg.hidden, cfg.intermediate
     x = W.make_x(cfg, seed)
@@ -323,7 +323,7 @@ def test_forward_mx_ep_prefill_full_size(fmt, name, seed):
     torch.cuda.synchronize()
     _, ref_off, _, _ = oracle.dispatch(ids.numpy(), E)
     assert np.array_equal(off.cpu().numpy(), ref_off)
-    toks = covering_tokens(ids.numpy(), E, 128, seed=seed)
+    toks = np.arange(T)                                     # every token
     deq = ORACLE[fmt][1]
     widen = lambda e: (deq(u8(qgu[e]), u8(sgu[e])), deq(u8(qd[e]), u8(sd[e])))
     ref = oracle.forward_tokens_widened(bits(x), ids.numpy(), w.numpy(), E, widen, toks,
