@@ -26,6 +26,7 @@ struct GemmPlan {
     int grid_gateup, grid_down;
     int bn_gateup, bn_down;  // weight rows per tile (tiled kinds)
     bool split;              // tiled: XCDs 0-3 and 4-7 walk the two halves of the tile list
+    bool prod;               // large tiles: waves 0-3 issue every DMA of the rings
 };
 
 GemmPlan choose_plan(const Shape& s, int hint);
