@@ -1276,7 +1276,11 @@ __global__ __launch_bounds__(256) void skinny_pack_kernel(const uint16_t* __rest
 // stage d+SW during half 2d+2, each refill spread between the MFMAs of its
 // half, so that the loads of the eight waves do not arrive at the address
 // unit in one burst.  Even halves wait for nothing.  The vmcnt of each wait
-// counts the loads this wave issued after the ones it needs.
+// counts the loads this wave issued after the ones it needs.  In the PROD
+// instances only waves 0-3 issue loads (twice as many each) and waves 4-7
+// only read fragments and multiply; a wave that issued nothing passes its
+// vmcnt waits at once, and the barrier still orders every read against the
+// next refill.
 //
 // WGM x WGN waves; each wave owns (BM/WGM) token rows x (BN/WGN) weight rows
 // of the tile as 32x32 MFMA sub-tiles (weights = MFMA rows, tokens = MFMA
