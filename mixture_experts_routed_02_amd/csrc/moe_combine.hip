@@ -64,7 +64,11 @@ __global__ __launch_bounds__(kCombineThreads) void combine_kernel(
             o.y = (uint32_t)moe_f32_to_bf16(acc[2]) | ((uint32_t)moe_f32_to_bf16(acc[3]) << 16);
             o.z = (uint32_t)moe_f32_to_bf16(acc[4]) | ((uint32_t)moe_f32_to_bf16(acc[5]) << 16);
             o.w = (uint32_t)moe_f32_to_bf16(acc[6]) | ((uint32_t)moe_f32_to_bf16(acc[7]) << 16);
-            out[(long long)t * vec + c] = o;
+            // non-temporal: the output is for the next kernel, and L2 is
+            // better left to the rows being gathered (measured 0.5-0.8%
+            // faster on the prefill layers, decode unchanged)
+            const moe_u32x4 ov = {o.x, o.y, o.z, o.w};
+            __builtin_nontemporal_store(ov, reinterpret_cast<moe_u32x4*>(out + (long long)t * vec + c));
         }
         __syncthreads();
     }

@@ -170,6 +170,7 @@ hipError_t launch_router(const Shape& s, const float* logits, const int32_t* nto
 // ---------------------------------------------------------------------------
 #if defined(__HIPCC__)
 typedef __bf16 moe_bf16x8 __attribute__((__vector_size__(8 * sizeof(__bf16))));
+typedef uint32_t moe_u32x4 __attribute__((ext_vector_type(4)));
 typedef float moe_f32x4 __attribute__((__vector_size__(4 * sizeof(float))));
 typedef float moe_f32x16 __attribute__((__vector_size__(16 * sizeof(float))));
 
