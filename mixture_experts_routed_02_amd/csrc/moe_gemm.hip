@@ -91,7 +91,8 @@ __device__ __forceinline__ int find_expert(const int* s_start, int E, int tile) 
 // partial sums in L2; measured (cold, 32 routing draws, bit-identical) 10%
 // faster at decode T = 8, 32 and 128, 5% at T = 1.  Row-major weights stay
 // plain: there one load covers 64 bytes of each of 16 rows, half a line, and
-// the hint made the same workloads 12-25% slower.
+// the hint made the same workloads 12-25% slower (15-28% with it only on the
+// load that completes each line).
 template <bool NT>
 __device__ __forceinline__ moe_bf16x8 stream_load(const moe_bf16x8* p) {
     if constexpr (NT) return __builtin_nontemporal_load(p);
