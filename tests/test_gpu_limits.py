@@ -68,6 +68,12 @@ CASES = {
     # experts with more m-tiles than one group of the tiled walk (8): 2600 rows
     # (14 m-tiles of 192: groups of 8 and 6) and 1600 rows (9: 8 and 1)
     "hot_expert_groups": (1, 1, 3, 256, 256, 0, None),
+    # 32 experts, fewer than 768 rows per expert on the host's estimate (the
+    # large plan's issuing-wave instances under hints 0 and 4), a gate-up of
+    # 64 m-tiles x 8 columns (enough tiles for the split walk): one hot
+    # expert of 27 m-tiles (the grouped walk) and two of 5 and 4 (plain weight
+    # DMAs) beside one-m-tile experts (non-temporal weight DMAs)
+    "hot_expert_split": (1, 1, 32, 256, 1024, 0, None),
 }
 TILE_EDGE_COUNTS = {"tile_edges": [256, 257, 128, 129, 64, 1, 0],
                     "tile_edges_192": [191, 192, 193, 384, 385, 96, 97, 1, 0],
@@ -76,7 +82,8 @@ TILE_EDGE_COUNTS = {"tile_edges": [256, 257, 128, 129, 64, 1, 0],
                     "large_branch_free_h384": [1000, 1100, 1153, 0],
                     "large_branch_free_k2": [769, 960, 1023, 1280],
                     "large_branch_free_down256": [1023, 1024, 1025, 974, 1083, 1100, 960, 1003],
-                    "hot_expert_groups": [2600, 150, 1600]}
+                    "hot_expert_groups": [2600, 150, 1600],
+                    "hot_expert_split": [5000, 800, 600] + [20] * 28 + [0]}
 
 
 def build(name):
