@@ -1611,6 +1611,12 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_tiled_kernel(
         // (wave-uniform); the others skip their MFMAs too.  The k loop exists
         // twice: without any test for waves whose sub-tiles all hold rows, and
         // with a test per MFMA for the others, so full tiles pay nothing for it.
+        // Instances without PROD (many rows per expert) have a third copy for
+        // waves whose last sub-tile alone is empty (an expert's m-tiles of
+        // 160 rows, the common height at about 1000 rows per expert), which
+        // skips that sub-tile's MFMAs and fragment reads with no test:
+        // Mixtral 0.4-0.5% faster on three seeds, bit-identical (the PROD
+        // instances have no registers left for a third copy).
         const int jlive = __builtin_amdgcn_readfirstlane((mrows - wm * WM + 31) / 32);
 
         // global source of each group this wave fills (stage 0): token groups
@@ -1730,7 +1736,10 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_tiled_kernel(
         // tokens of stage `stage` (KIND 1) or weights of stage `stage` (KIND 2)
         auto half = [&](int h, auto KIND, bool rf, int stage, auto FULL) {
             constexpr int kKind = decltype(KIND)::value;
-            constexpr bool kFull = decltype(FULL)::value;
+            // FULL: 1 every sub-tile live, 0 the per-MFMA test, 2 the last
+            // sub-tile of the wave empty (the others live)
+            constexpr int kMode = decltype(FULL)::value;
+            constexpr bool kFull = kMode == 1;
             constexpr int GP = kKind == 1 ? GA : (kKind == 2 ? GW : 0);
             auto issue = [&](int q) {
                 if (kKind == 1) issue_one(stage, 0, q);
@@ -1746,9 +1755,9 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_tiled_kernel(
                     for (int i = 0; i < NS; ++i) {
 #pragma unroll
                         for (int j = 0; j < MS; ++j) {
-                            if (kFull || j == 0 || jlive > j)
+                            if (kMode == 2 ? j < MS - 1 : (kFull || j == 0 || jlive > j))
                                 acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fw[sk][i], fa[sk][j], acc[i][j], 0, 0, 0);
-                            if (i == NS - 1) read_a(h + 1, sk, j);
+                            if (i == NS - 1 && (kMode != 2 || j < MS - 1)) read_a(h + 1, sk, j);
                         }
                         if constexpr (!MX) {
                             read_w(h + 1, sk, i);
@@ -1849,8 +1858,9 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_tiled_kernel(
                 half(2 * d + 1, tokens, d + SA < nk, d + SA, FULL);
             }
         };
-        if (!SUBSKIP || jlive >= MS) k_loop(std::true_type{});
-        else k_loop(std::false_type{});
+        if (!SUBSKIP || jlive >= MS) k_loop(std::integral_constant<int, 1>{});
+        else if (!PROD && MS > 1 && jlive == MS - 1) k_loop(std::integral_constant<int, 2>{});
+        else k_loop(std::integral_constant<int, 0>{});
         // drain the rings before the epilogue reuses them
         wait_vmcnt_barrier<0>();
 
